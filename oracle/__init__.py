@@ -1,0 +1,251 @@
+"""CPU oracle for exact minimax FP16 group-scale selection -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the GPU library
+(``post_weight_quantization_group_amd``) and neither imports the other.
+
+The brute force itself is plain C (``cq_oracle.c``, built with gcc); this
+module marshals numpy arrays into it and adds the two steps that are plain
+array reshuffles or means:
+
+* GPTQ-v1 packing (Qwen3.5-0.8B-Base-CliffQuant-W4A16-G128 model card,
+  "Quantization configuration": GPTQ v1, 4 bits, group 128, symmetric);
+* the module-macro worst-environment weighted-MSE proxy (same card,
+  "Held-out reconstruction proxy"; CliffQuant README, "Held-out
+  reconstruction proxy").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+GROUP = 128
+FIRST_BITS, LAST_BITS = 0x0001, 0x7BFF
+N_SCALES = LAST_BITS - FIRST_BITS + 1  # 31,743
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cq_oracle.c")
+_LIB = os.path.join(_HERE, "libcq_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain IEEE arithmetic: no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64, I32, U32 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+        lib.oracle_fp16_value.restype = ctypes.c_double
+        lib.oracle_fp16_value.argtypes = [U32]
+        lib.oracle_solve.restype = None
+        lib.oracle_solve.argtypes = [P, P, I64, I32, I64, P, P, P, P, P, P, P, P, I32]
+        lib.oracle_codes.restype = None
+        lib.oracle_codes.argtypes = [P, I64, U32, P]
+        lib.oracle_env_errors.restype = None
+        lib.oracle_env_errors.argtypes = [P, P, I64, I32, I64, P, P, I32]
+        lib.oracle_curve.restype = None
+        lib.oracle_curve.argtypes = [P, P, I32, P, P]
+        lib.oracle_fp16_round.restype = U32
+        lib.oracle_fp16_round.argtypes = [ctypes.c_float]
+        lib.oracle_absmax.restype = None
+        lib.oracle_absmax.argtypes = [P, I64, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _groups(w, d, d_period):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    if w.ndim != 2 or w.shape[1] != GROUP:
+        raise ValueError("w must be [n_groups, 128]")
+    if d.ndim != 3 or d.shape[2] != GROUP:
+        raise ValueError("d must be [n_d, E, 128]")
+    if d_period is None:
+        d_period = d.shape[0]
+    if not (1 <= d_period <= d.shape[0]):
+        raise ValueError("bad d_period")
+    E = d.shape[1]
+    if not (1 <= E <= 32):
+        raise ValueError("E must be in 1..32")
+    return w, d, int(d_period), E
+
+
+def fp16_value(bits: int) -> float:
+    """Exact value of a positive binary16 bit pattern."""
+    return _load().oracle_fp16_value(int(bits))
+
+
+def fp16_round(x: float) -> int:
+    """Binary16 bit pattern nearest to a non-negative float32 (ties to even; 0x7C00 = overflow)."""
+    return int(_load().oracle_fp16_round(float(np.float32(x))))
+
+
+def codes_at(w, bits: int) -> np.ndarray:
+    """q_i = clip(round-half-even(fl32(w_i / s)), -8, 7) for every weight, at one scale."""
+    w = np.ascontiguousarray(w, dtype=np.float32).ravel()
+    out = np.empty(w.size, dtype=np.int8)
+    _load().oracle_codes(_ptr(w), w.size, int(bits), _ptr(out))
+    return out
+
+
+class Solution:
+    """Brute-force result per group (see ``solve``)."""
+
+    def __init__(self, n):
+        self.mm_bits = np.zeros(n, np.uint16)
+        self.mm_F1 = np.zeros(n, np.float64)
+        self.mm_F2 = np.zeros(n, np.float64)
+        self.pl_bits = np.zeros(n, np.uint16)
+        self.pl_P1 = np.zeros(n, np.float64)
+        self.pl_P2 = np.zeros(n, np.float64)
+        self.codes = np.zeros((n, GROUP), np.int8)
+        self.ok = np.zeros(n, np.uint8)
+
+    @staticmethod
+    def _gap(f1, f2):
+        f1, f2 = np.asarray(f1, np.float64), np.asarray(f2, np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            g = (f2 - f1) / f1
+        return np.where(f1 == 0.0, np.where(f2 == 0.0, 0.0, np.inf), g)
+
+    @property
+    def mm_gap(self):
+        """(F2 - F1) / F1; 0 for an exact zero tie, +inf when only the winner is zero."""
+        return self._gap(self.mm_F1, self.mm_F2)
+
+    @property
+    def pl_gap(self):
+        return self._gap(self.pl_P1, self.pl_P2)
+
+
+def solve(w, d, d_period=None, n_threads: int = 0) -> Solution:
+    """Exhaustive minimax and pooled-WMSE scale selection over all 31,743 FP16 scales.
+
+    CliffQuant README, "What CliffQuant changes": the objective, the code rule,
+    the admissible set and the lower-bit-pattern tie rule; the pooled policy
+    averages the environments first (README opening question; proxy table).
+    """
+    w, d, d_period, E = _groups(w, d, d_period)
+    n = w.shape[0]
+    r = Solution(n)
+    _load().oracle_solve(_ptr(w), _ptr(d), d_period, E, n,
+                         _ptr(r.mm_bits), _ptr(r.mm_F1), _ptr(r.mm_F2),
+                         _ptr(r.pl_bits), _ptr(r.pl_P1), _ptr(r.pl_P2),
+                         _ptr(r.codes), _ptr(r.ok), int(n_threads))
+    return r
+
+
+def env_errors(w, d, bits, d_period=None, n_threads: int = 0) -> np.ndarray:
+    """[n_groups, E] per-environment weighted squared error at the given scales."""
+    w, d, d_period, E = _groups(w, d, d_period)
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if bits.shape != (w.shape[0],):
+        raise ValueError("one scale per group")
+    out = np.empty((w.shape[0], E), np.float64)
+    _load().oracle_env_errors(_ptr(w), _ptr(d), d_period, E, w.shape[0], _ptr(bits), _ptr(out),
+                              int(n_threads))
+    return out
+
+
+def objective(w, d, bits, d_period=None, n_threads: int = 0) -> np.ndarray:
+    """Worst-environment objective max_e F_e at the given scales."""
+    return env_errors(w, d, bits, d_period, n_threads).max(axis=1)
+
+
+def curve(w_group, d_group):
+    """(F[31743], P[31743]) over b = 1..0x7BFF for one group (w [128], d [E,128])."""
+    w = np.ascontiguousarray(w_group, dtype=np.float32).reshape(GROUP)
+    d = np.ascontiguousarray(d_group, dtype=np.float32)
+    E = d.shape[0]
+    F = np.empty(N_SCALES, np.float64)
+    P = np.empty(N_SCALES, np.float64)
+    _load().oracle_curve(_ptr(w), _ptr(d), E, _ptr(F), _ptr(P))
+    return F, P
+
+
+def absmax_bits(w) -> np.ndarray:
+    """AbsMax policy: fp16(fl32(max|w| / 7)), 0 -> 0x0001, overflow -> 0x7BFF."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    out = np.empty(w.shape[0], np.uint16)
+    _load().oracle_absmax(_ptr(w), w.shape[0], _ptr(out))
+    return out
+
+
+def codes_for(w, bits) -> np.ndarray:
+    """[n_groups, 128] codes of each group at its own scale."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    return np.stack([codes_at(w[g], int(bits[g])) for g in range(w.shape[0])]) if w.shape[0] else \
+        np.zeros((0, GROUP), np.int8)
+
+
+# ---------------------------------------------------------------- GPTQ-v1 packing
+def pack_gptq_v1(codes, grp_scale_bits, out: int, inp: int):
+    """GPTQ-v1 symmetric 4-bit packing of one matrix.
+
+    codes          -- [out, in] int8 in [-8, 7] (group g = row*(in/128) + in_chunk);
+    grp_scale_bits -- [out, in/128] binary16 bit patterns.
+    Returns (qweight [in/8, out] int32, scales [in/128, out] uint16): nibble j
+    (bits 4j..4j+3) of qweight[r, o] holds codes[o, 8r+j] + 8.
+    """
+    c = np.asarray(codes, dtype=np.int64).reshape(out, inp)
+    if inp % GROUP:
+        raise ValueError("in must be a multiple of 128")
+    u = (c + 8).reshape(out, inp // 8, 8)
+    word = np.zeros((out, inp // 8), dtype=np.uint64)
+    for j in range(8):
+        word |= (u[:, :, j].astype(np.uint64) << np.uint64(4 * j))
+    qweight = word.T.astype(np.uint32).view(np.int32)
+    scales = np.asarray(grp_scale_bits, dtype=np.uint16).reshape(out, inp // GROUP).T
+    return np.ascontiguousarray(qweight), np.ascontiguousarray(scales)
+
+
+def unpack_gptq_v1(qweight, scales):
+    """Inverse of ``pack_gptq_v1``: (codes [out, in] int8, grp_scale_bits [out, in/128])."""
+    q = np.asarray(qweight).view(np.uint32).astype(np.int64)
+    rows, out = q.shape
+    nib = np.stack([(q >> (4 * j)) & 0xF for j in range(8)], axis=1)  # [in/8, 8, out]
+    codes = (nib.reshape(rows * 8, out).T - 8).astype(np.int8)
+    return codes, np.ascontiguousarray(np.asarray(scales, np.uint16).T)
+
+
+# ---------------------------------------------------------------- proxy
+def proxy(w, d_eval, bits, module_of_group, n_modules: int, d_period=None, n_threads: int = 0):
+    """Module-macro worst-environment weighted MSE.
+
+    Per group p_g = max_e (1/128) sum_i d_eval[e][i] (w_i - s_g q_i)^2; then the
+    mean of p_g over each module's groups (in group order); then the mean over
+    modules (in module order).  Returns (per_group, module_mean, macro).
+    """
+    F = env_errors(w, d_eval, bits, d_period, n_threads)
+    per_group = (F / float(GROUP)).max(axis=1)
+    mod = np.asarray(module_of_group, dtype=np.int64)
+    module_mean = np.zeros(n_modules, np.float64)
+    for m in range(n_modules):
+        vals = per_group[mod == m]
+        acc = 0.0
+        for v in vals:
+            acc = acc + float(v)
+        module_mean[m] = acc / len(vals) if len(vals) else 0.0
+    acc = 0.0
+    for v in module_mean:
+        acc = acc + float(v)
+    return per_group, module_mean, acc / n_modules
