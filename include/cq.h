@@ -1,0 +1,169 @@
+/*
+ * cq.h -- C ABI of the MI355X (gfx950) library for exact minimax FP16
+ * group-scale selection in symmetric 4-bit, group-size-128 weight
+ * quantization, and GPTQ-v1 packing of the result.
+ *
+ * The operation (CliffQuant repository README, "What CliffQuant changes",
+ * displayed objective and the paragraph after it): for one group of 128
+ * weights w_i and E environment diagonals d_{e,i} >= 0, choose the positive
+ * finite IEEE binary16 scale s (bit patterns 0x0001..0x7BFF, 31,743 values)
+ * that minimises
+ *        F(s) = max_e sum_i d_{e,i} (w_i - s q_i(s))^2,
+ *        q_i(s) = clip(round-half-even(w_i / s), -8, 7)   (round, then clip),
+ * an exact objective tie going to the lower binary16 bit pattern.  The
+ * quotient w_i/s is taken as one correctly rounded binary32 division and the
+ * reported objective is summed in binary64, i = 0..127 in order, each
+ * operation rounded on its own.
+ *
+ * Conventions for every entry point:
+ *  - Array arguments are DEVICE pointers (HIP global memory on the current
+ *    device) owned by the caller; the library never frees or keeps them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on that stream and return after enqueueing; the
+ *    outputs are valid once the stream has reached that point.
+ *  - No entry point allocates device memory: scratch space comes from the
+ *    caller's `workspace` (device memory, 256-byte aligned, at least
+ *    cq_workspace_size(...) bytes, not shared between calls that may overlap).
+ *  - Pointers to float32 inputs (w, d) and to int8 codes must be 16-byte
+ *    aligned, other arrays naturally aligned (torch allocations are).
+ *  - Argument errors are reported before anything is enqueued; data errors
+ *    (non-finite weights or diagonals, negative diagonals) are reported per
+ *    group through CQ_FLAG_BAD_INPUT, never through the status.
+ *  - The library keeps no state between calls; distinct streams may be used
+ *    from distinct host threads at once.
+ *
+ * Layouts:
+ *   w      float32 [n_groups][128]   group g: 128 consecutive input channels
+ *                                    of one output row (row-major [out][in]
+ *                                    matrices give g = row*(in/128) + chunk).
+ *   d      float32 [n_d][E][128]     group g uses slice (g % d_period); a
+ *                                    matrix has d_period = in/128 (groups
+ *                                    inherit the diagonals of their input
+ *                                    channels), per-group diagonals have
+ *                                    d_period = n_groups.
+ *   scales uint16  [n_groups]        binary16 bit patterns (0x0001..0x7BFF).
+ *   codes  int8    [n_groups][128]   q_i in [-8, 7] at the chosen scale.
+ */
+#ifndef CQ_H
+#define CQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CQ_ABI_VERSION 1
+#define CQ_GROUP 128
+#define CQ_MAX_ENVS 32
+
+/* Status codes. */
+#define CQ_OK 0
+#define CQ_EINVAL (-1)       /* null required pointer, bad size or enum */
+#define CQ_EWORKSPACE (-2)   /* workspace missing, misaligned or too small */
+#define CQ_EHIP (-3)         /* a HIP launch failed (hipGetLastError) */
+#define CQ_EUNSUPPORTED (-4) /* valid arguments this entry point does not serve */
+
+/* Solvers (cq_quantize_groups `method`). */
+#define CQ_EXHAUSTIVE 0 /* evaluate every one of the 31,743 scales */
+#define CQ_CANDIDATE 1  /* code-transition / vertex / intersection candidates */
+
+/* Baseline policies (cq_baseline_scales `which`). */
+#define CQ_ABSMAX 0      /* s = fp16(fl32(max_i |w_i| / 7)); 0 -> 0x0001, overflow -> 0x7BFF */
+#define CQ_POOLED_WMSE 1 /* minimise P(s) = (1/E) sum_e F_e(s) over the same grid and tie rule */
+
+/* Per-group flag bits (cq_quantize_groups `flags`). */
+#define CQ_FLAG_BAD_INPUT 1u  /* non-finite w or d, or d < 0: scale 0, codes 0, objective NaN */
+#define CQ_FLAG_NEAR_TIE 2u   /* more than one scale survived the binary32 screen */
+#define CQ_FLAG_EXACT_TIE 4u  /* the winner's binary64 objective equals another scale's */
+#define CQ_FLAG_FALLBACK 8u   /* the candidate solver handed the group to the exhaustive one */
+#define CQ_FLAG_FP64_SWEEP 16u /* decided by a full binary64 sweep (screen inconclusive) */
+
+/* ABI version of the loaded library (CQ_ABI_VERSION). */
+int32_t cq_abi_version(void);
+
+/* Static description of a status code. */
+const char *cq_status_string(int32_t status);
+
+/* Bytes of workspace cq_quantize_groups needs for `method`, E and n_groups
+ * (also valid for cq_baseline_scales with CQ_POOLED_WMSE, method
+ * CQ_EXHAUSTIVE).  Returns 0 for invalid arguments. */
+size_t cq_workspace_size(int32_t method, int32_t E, int64_t n_groups);
+
+/*
+ * Minimax scale, codes and objective for n_groups groups.
+ *   method       CQ_EXHAUSTIVE or CQ_CANDIDATE; both return the same result.
+ *   scales       out, required.
+ *   codes        out, nullable.
+ *   objective    out, nullable: F(s) at the chosen scale, binary64.
+ *   flags        out, nullable: CQ_FLAG_* bits.
+ *   pooled_scales / pooled_objective
+ *                out, nullable, CQ_EXHAUSTIVE only (else CQ_EUNSUPPORTED):
+ *                the pooled-WMSE policy decided in the same sweep.
+ * E in 1..32, n_groups >= 0 (0 enqueues nothing), 1 <= d_period.
+ * The binary32 screen is followed by binary64 rescoring of every scale the
+ * screen's error bound cannot rule out, so the pick equals the binary64
+ * argmin over all scales with the lower-bit-pattern tie rule.
+ */
+int32_t cq_quantize_groups(const float *w, const float *d, int64_t d_period, int32_t E,
+                           int64_t n_groups, int32_t method,
+                           uint16_t *scales, int8_t *codes, double *objective, uint8_t *flags,
+                           uint16_t *pooled_scales, double *pooled_objective,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Baseline scale policies.
+ *   CQ_ABSMAX       d may be NULL when objective is NULL; no workspace needed.
+ *   CQ_POOLED_WMSE  exhaustive sweep of P(s); workspace as for
+ *                   cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups).
+ *   objective  nullable: for CQ_ABSMAX the worst-environment objective F at
+ *              the AbsMax scale; for CQ_POOLED_WMSE the pooled objective P.
+ */
+int32_t cq_baseline_scales(const float *w, const float *d, int64_t d_period, int32_t E,
+                           int64_t n_groups, int32_t which,
+                           uint16_t *scales, int8_t *codes, double *objective,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * GPTQ-v1 packing of one [out][in] matrix (Qwen3.5-0.8B-Base-CliffQuant-
+ * W4A16-G128 model card, "Quantization configuration": GPTQ v1, 4-bit,
+ * group size 128, symmetric).
+ *   codes       int8 [out][in], values in [-8, 7] (the cq_quantize_groups
+ *               codes of the matrix's groups, in group order).
+ *   grp_scales  uint16 [out][in/128] (the matrix's per-group scales).
+ *   qweight     out, int32 [in/8][out]: nibble j (bits 4j..4j+3) of
+ *               qweight[r][o] is codes[o][8r+j] + 8.
+ *   scales      out, uint16 [in/128][out]: scales[c][o] = grp_scales[o][c].
+ * out >= 0, in >= 0, in % 128 == 0.  Codes outside [-8, 7] are packed
+ * modulo 16 (the caller guarantees the range).
+ */
+int32_t cq_pack_gptq_v1(const int8_t *codes, const uint16_t *grp_scales, int64_t out, int64_t in,
+                        int32_t *qweight, uint16_t *scales, void *stream);
+
+/*
+ * Module-macro worst-environment weighted MSE (Qwen3.5-0.8B-Base-CliffQuant-
+ * W4A16-G128 model card, "Held-out reconstruction proxy"; CliffQuant README,
+ * "Held-out reconstruction proxy").
+ *   per group  p_g = max_e (1/128) sum_i d_eval_{e,i} (w_i - s_g q_i(s_g))^2
+ *   per module mean of p_g over groups [module_offsets[m], module_offsets[m+1])
+ *   macro      mean over the n_modules module means.
+ *   scales          device uint16 [n_groups] binary16 patterns (0x0001..0x7BFF).
+ *   module_offsets  device int64 [n_modules+1], non-decreasing, first 0, last
+ *                   n_groups; a module whose range is empty or out of bounds
+ *                   gets NaN.
+ *   module_mean     out, double [n_modules].   macro  out, double [1].
+ *   per_group       out, nullable, double [n_groups].
+ * workspace: cq_proxy_workspace_size(n_groups) bytes.
+ */
+size_t cq_proxy_workspace_size(int64_t n_groups);
+int32_t cq_proxy_worst_env_wmse(const float *w, const float *d_eval, int64_t d_period, int32_t E,
+                                int64_t n_groups, const uint16_t *scales,
+                                const int64_t *module_offsets, int32_t n_modules,
+                                double *module_mean, double *macro, double *per_group,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CQ_H */

@@ -1,0 +1,270 @@
+"""Exact minimax FP16 group scales for W4/G128 quantization on MI355X (gfx950).
+
+A thin ctypes binding over ``libcq.so`` (C ABI in ``include/cq.h``).  The
+functions named ``cq_*`` mirror the C entry points one to one and only
+marshal arguments: torch tensors already on the GPU are passed by pointer on
+the current stream, and a non-OK status raises ``CQError``.  The helpers
+without the prefix allocate outputs and a workspace with torch and call the
+``cq_*`` functions.  Every step of the computation runs in the HIP kernels;
+there is no CPU path, and importing this package on a machine without the
+built library raises.
+
+The method (CliffQuant repository README, "What CliffQuant changes"): per
+group of 128 weights, the positive finite binary16 scale minimising the worst
+environment's diagonal-weighted squared error, codes round-half-even then
+clipped to [-8, 7], exact ties to the lower bit pattern; the result is stored
+in the GPTQ-v1 layout (Qwen3.5-0.8B-Base-CliffQuant-W4A16-G128 model card,
+"Quantization configuration").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "CQError", "GROUP", "EXHAUSTIVE", "CANDIDATE", "ABSMAX", "POOLED_WMSE",
+    "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
+    "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
+    "cq_quantize_groups", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
+    "cq_proxy_worst_env_wmse", "quantize_groups", "baseline_scales", "pack_gptq_v1",
+    "proxy_worst_env_wmse", "solve_breakpoint_exact", "EXPORTED_SYMBOLS",
+]
+
+GROUP = 128
+EXHAUSTIVE, CANDIDATE = 0, 1
+ABSMAX, POOLED_WMSE = 0, 1
+FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 1, 2, 4, 8, 16
+_METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
+EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
+                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
+                    "cq_proxy_worst_env_wmse")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class CQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {cq_status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("CQ_LIBRARY", os.path.join(_HERE, "libcq.so"))
+
+
+def load():
+    """Load libcq.so (raises when it has not been built: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -m post_weight_quantization_group_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.cq_abi_version.restype = I32
+        lib.cq_abi_version.argtypes = []
+        lib.cq_status_string.restype = ctypes.c_char_p
+        lib.cq_status_string.argtypes = [I32]
+        lib.cq_workspace_size.restype = SZ
+        lib.cq_workspace_size.argtypes = [I32, I32, I64]
+        lib.cq_quantize_groups.restype = I32
+        lib.cq_quantize_groups.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, P, P, P, SZ, P]
+        lib.cq_baseline_scales.restype = I32
+        lib.cq_baseline_scales.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, SZ, P]
+        lib.cq_pack_gptq_v1.restype = I32
+        lib.cq_pack_gptq_v1.argtypes = [P, P, I64, I64, P, P, P]
+        lib.cq_proxy_workspace_size.restype = SZ
+        lib.cq_proxy_workspace_size.argtypes = [I64]
+        lib.cq_proxy_worst_env_wmse.restype = I32
+        lib.cq_proxy_worst_env_wmse.argtypes = [P, P, I64, I32, I64, P, P, I32, P, P, P, P, SZ, P]
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------- marshalling
+def _p(t):
+    """Device pointer of a CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("arrays passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("arrays passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CQError(status, where)
+
+
+# ---------------------------------------------------------------- C entry points
+def cq_abi_version() -> int:
+    return load().cq_abi_version()
+
+
+def cq_status_string(status: int) -> str:
+    return load().cq_status_string(status).decode()
+
+
+def cq_workspace_size(method: int, E: int, n_groups: int) -> int:
+    return load().cq_workspace_size(method, E, n_groups)
+
+
+def cq_proxy_workspace_size(n_groups: int) -> int:
+    return load().cq_proxy_workspace_size(n_groups)
+
+
+def cq_quantize_groups(w, d, d_period, E, n_groups, method, scales, codes=None, objective=None, flags=None,
+                       pooled_scales=None, pooled_objective=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_quantize_groups(_p(w), _p(d), d_period, E, n_groups, method, _p(scales), _p(codes),
+                                     _p(objective), _p(flags), _p(pooled_scales), _p(pooled_objective),
+                                     _p(workspace), ws_bytes, _stream(stream)), "cq_quantize_groups")
+
+
+def cq_baseline_scales(w, d, d_period, E, n_groups, which, scales, codes=None, objective=None, workspace=None,
+                       stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_baseline_scales(_p(w), _p(d), d_period, E, n_groups, which, _p(scales), _p(codes),
+                                     _p(objective), _p(workspace), ws_bytes, _stream(stream)),
+           "cq_baseline_scales")
+
+
+def cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream=None):
+    _check(load().cq_pack_gptq_v1(_p(codes), _p(grp_scales), out, inp, _p(qweight), _p(scales),
+                                  _stream(stream)), "cq_pack_gptq_v1")
+
+
+def cq_proxy_worst_env_wmse(w, d_eval, d_period, E, n_groups, scales, module_offsets, n_modules, module_mean,
+                            macro, per_group=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_proxy_worst_env_wmse(_p(w), _p(d_eval), d_period, E, n_groups, _p(scales),
+                                          _p(module_offsets), n_modules, _p(module_mean), _p(macro),
+                                          _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
+           "cq_proxy_worst_env_wmse")
+
+
+# ---------------------------------------------------------------- helpers
+def _workspace(nbytes: int, device):
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _shape_check(w, d):
+    if w.dim() != 2 or w.shape[1] != GROUP or w.dtype != torch.float32:
+        raise ValueError("w must be float32 [n_groups, 128]")
+    if d.dim() != 3 or d.shape[2] != GROUP or d.dtype != torch.float32:
+        raise ValueError("d must be float32 [n_d, E, 128]")
+
+
+def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled=False, workspace=None,
+                    stream=None):
+    """Minimax scales (and codes, objective, flags; optionally the pooled policy) for every group.
+
+    Returns a dict of device tensors: scales (uint16 bit patterns held in int16
+    storage -> use ``.view(torch.uint16)`` or ``& 0xFFFF``), codes, objective,
+    flags and, with ``pooled=True``, pooled_scales and pooled_objective.
+    """
+    _shape_check(w, d)
+    n, E = w.shape[0], d.shape[1]
+    d_period = d.shape[0] if d_period is None else int(d_period)
+    m = _METHODS[method] if isinstance(method, str) else int(method)
+    dev = w.device
+    out = {
+        "scales": torch.empty(n, dtype=torch.int16, device=dev),
+        "codes": torch.empty((n, GROUP), dtype=torch.int8, device=dev) if codes else None,
+        "objective": torch.empty(n, dtype=torch.float64, device=dev),
+        "flags": torch.empty(n, dtype=torch.uint8, device=dev),
+    }
+    if pooled:
+        out["pooled_scales"] = torch.empty(n, dtype=torch.int16, device=dev)
+        out["pooled_objective"] = torch.empty(n, dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = _workspace(cq_workspace_size(m, E, n), dev)
+    cq_quantize_groups(w, d, d_period, E, n, m, out["scales"], out["codes"], out["objective"], out["flags"],
+                       out.get("pooled_scales"), out.get("pooled_objective"), workspace, stream)
+    return out
+
+
+def baseline_scales(w, d, d_period=None, which="absmax", codes=True, objective=True, workspace=None,
+                    stream=None):
+    """AbsMax or pooled-WMSE scales: dict with scales, codes, objective."""
+    _shape_check(w, d)
+    n, E = w.shape[0], d.shape[1]
+    d_period = d.shape[0] if d_period is None else int(d_period)
+    k = {"absmax": ABSMAX, "pooled": POOLED_WMSE}[which] if isinstance(which, str) else int(which)
+    dev = w.device
+    out = {
+        "scales": torch.empty(n, dtype=torch.int16, device=dev),
+        "codes": torch.empty((n, GROUP), dtype=torch.int8, device=dev) if codes else None,
+        "objective": torch.empty(n, dtype=torch.float64, device=dev) if objective else None,
+    }
+    if k == POOLED_WMSE and workspace is None:
+        workspace = _workspace(cq_workspace_size(EXHAUSTIVE, E, n), dev)
+    cq_baseline_scales(w, d, d_period, E, n, k, out["scales"], out["codes"], out["objective"], workspace,
+                       stream)
+    return out
+
+
+def pack_gptq_v1(codes, grp_scales, out: int, inp: int, stream=None):
+    """GPTQ-v1 (qweight int32 [in/8, out], scales int16-stored fp16 bits [in/128, out])."""
+    qweight = torch.empty((inp // 8, out), dtype=torch.int32, device=codes.device)
+    scales = torch.empty((inp // GROUP, out), dtype=torch.int16, device=codes.device)
+    cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream)
+    return qweight, scales
+
+
+def proxy_worst_env_wmse(w, d_eval, scales, module_offsets, d_period=None, per_group=True, stream=None):
+    """(per_group or None, module_mean [n_modules], macro [1]) as float64 device tensors."""
+    _shape_check(w, d_eval)
+    n, E = w.shape[0], d_eval.shape[1]
+    d_period = d_eval.shape[0] if d_period is None else int(d_period)
+    n_modules = module_offsets.numel() - 1
+    dev = w.device
+    mm = torch.empty(n_modules, dtype=torch.float64, device=dev)
+    macro = torch.empty(1, dtype=torch.float64, device=dev)
+    pg = torch.empty(n, dtype=torch.float64, device=dev) if per_group else None
+    ws = None if per_group else _workspace(cq_proxy_workspace_size(n), dev)
+    cq_proxy_worst_env_wmse(w, d_eval, d_period, E, n, scales, module_offsets, n_modules, mm, macro, pg, ws,
+                            stream)
+    return pg, mm, macro
+
+
+def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax: int = 7, method="candidate",
+                           device="cuda"):
+    """One group, in the shape of the pages' solver call (CliffQuant README, "Use the solver").
+
+    ``weights`` has at most 128 entries, ``environment_diagonals`` is [E][len(weights)].
+    The group is zero-padded to 128 (a zero weight adds nothing at any scale).  Returns
+    (scale as float, objective, codes list).  Only qmin=-8, qmax=7 is served.
+    """
+    if (qmin, qmax) != (-8, 7):
+        raise NotImplementedError("only the signed 4-bit range [-8, 7] is implemented")
+    n = len(weights)
+    if not 1 <= n <= GROUP:
+        raise ValueError("1..128 weights")
+    E = len(environment_diagonals)
+    w = torch.zeros((1, GROUP), dtype=torch.float32)
+    w[0, :n] = torch.tensor(weights, dtype=torch.float32)
+    d = torch.zeros((1, E, GROUP), dtype=torch.float32)
+    d[0, :, :n] = torch.tensor(environment_diagonals, dtype=torch.float32)
+    r = quantize_groups(w.to(device), d.to(device), method=method)
+    torch.cuda.current_stream().synchronize()
+    bits = int(r["scales"].cpu().view(torch.uint16)[0]) if hasattr(torch, "uint16") else \
+        int(r["scales"].cpu()[0]) & 0xFFFF
+    scale = float(torch.tensor([bits], dtype=torch.int16).view(torch.float16)[0])
+    return scale, float(r["objective"].cpu()[0]), r["codes"].cpu()[0, :n].tolist()

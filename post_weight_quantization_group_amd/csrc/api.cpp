@@ -1,0 +1,161 @@
+// C ABI of the scale-selection library: argument checks, workspace carving,
+// and kernel launches on the caller's stream.  Declared in include/cq.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "cq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? CQ_OK : CQ_EHIP; }
+
+// Exhaustive-sweep workspace: [counter | pad][int32 queue of n_groups]
+size_t sweep_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u); }
+// Candidate workspace: [tie counter | pad][int32 tie list][sweep workspace]
+size_t cand_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u) + sweep_ws(n); }
+
+bool groups_ok(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups) {
+    if (n_groups < 0 || E < 1 || E > CQ_MAX_ENVS) return false;
+    if (n_groups == 0) return true;
+    if (!w || !d || d_period < 1) return false;
+    return aligned(w, 16) && aligned(d, 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cq_abi_version(void) { return CQ_ABI_VERSION; }
+
+const char* cq_status_string(int32_t s) {
+    switch (s) {
+        case CQ_OK: return "ok";
+        case CQ_EINVAL: return "invalid argument";
+        case CQ_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case CQ_EHIP: return "HIP launch failed";
+        case CQ_EUNSUPPORTED: return "not supported by this entry point";
+        default: return "unknown status";
+    }
+}
+
+size_t cq_workspace_size(int32_t method, int32_t E, int64_t n_groups) {
+    if (E < 1 || E > CQ_MAX_ENVS || n_groups < 0) return 0;
+    if (method == CQ_EXHAUSTIVE) return sweep_ws(n_groups);
+    if (method == CQ_CANDIDATE) return cand_ws(n_groups);
+    return 0;
+}
+
+int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups,
+                           int32_t method, uint16_t* scales, int8_t* codes, double* objective, uint8_t* flags,
+                           uint16_t* pooled_scales, double* pooled_objective, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
+    if (method != CQ_EXHAUSTIVE && method != CQ_CANDIDATE) return CQ_EINVAL;
+    if (n_groups > 0 && !scales) return CQ_EINVAL;
+    if (n_groups > INT32_MAX) return CQ_EINVAL;
+    if (method == CQ_CANDIDATE && (pooled_scales || pooled_objective)) return CQ_EUNSUPPORTED;
+    if (n_groups == 0) return CQ_OK;
+    const size_t need = cq_workspace_size(method, E, n_groups);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return CQ_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    if (method == CQ_EXHAUSTIVE) {
+        cqk::SweepArgs a{};
+        a.w = w; a.d = d; a.d_period = d_period;
+        a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
+        a.pscales = pooled_scales; a.pobjective = pooled_objective;
+        a.fb_count = (int32_t*)ws;
+        a.fb_list = (int32_t*)(ws + ALIGN);
+        a.want_minimax = 1;
+        a.want_pooled = (pooled_scales || pooled_objective) ? 1 : 0;
+        return hip_status(cqk::launch_sweep(a, E, n_groups, st));
+    }
+    cqk::CandArgs c{};
+    c.w = w; c.d = d; c.d_period = d_period; c.n_groups = n_groups;
+    c.scales = scales; c.codes = codes; c.objective = objective; c.flags = flags;
+    c.tie_count = (int32_t*)ws;
+    c.tie_list = (int32_t*)(ws + ALIGN);
+    hipError_t e = cqk::launch_candidate(c, E, st);
+    if (e != hipSuccess) return CQ_EHIP;
+    // groups whose direct candidates tied are decided by the exhaustive sweep
+    uint8_t* sws = ws + ALIGN + round_up((size_t)n_groups * 4u);
+    cqk::SweepArgs a{};
+    a.w = w; a.d = d; a.d_period = d_period;
+    a.list = c.tie_list; a.list_count = c.tie_count;
+    a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
+    a.fb_count = (int32_t*)sws;
+    a.fb_list = (int32_t*)(sws + ALIGN);
+    a.want_minimax = 1;
+    a.want_pooled = 0;
+    a.mark_fallback = 1;
+    return hip_status(cqk::launch_sweep(a, E, n_groups, st));
+}
+
+int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups,
+                           int32_t which, uint16_t* scales, int8_t* codes, double* objective, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (n_groups < 0 || n_groups > INT32_MAX) return CQ_EINVAL;
+    if (which == CQ_ABSMAX) {
+        if (n_groups == 0) return CQ_OK;
+        if (!w || !scales || !aligned(w, 16)) return CQ_EINVAL;
+        if (objective && !groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
+        return hip_status(cqk::launch_absmax(w, d, d_period, E, n_groups, scales, codes, objective, st));
+    }
+    if (which != CQ_POOLED_WMSE) return CQ_EINVAL;
+    if (!groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
+    if (n_groups == 0) return CQ_OK;
+    if (!scales) return CQ_EINVAL;
+    const size_t need = cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return CQ_EWORKSPACE;
+    uint8_t* ws = (uint8_t*)workspace;
+    cqk::SweepArgs a{};
+    a.w = w; a.d = d; a.d_period = d_period;
+    a.codes = codes; a.pscales = scales; a.pobjective = objective;
+    a.fb_count = (int32_t*)ws;
+    a.fb_list = (int32_t*)(ws + ALIGN);
+    a.want_minimax = 0;
+    a.want_pooled = 1;
+    return hip_status(cqk::launch_sweep(a, E, n_groups, st));
+}
+
+int32_t cq_pack_gptq_v1(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
+                        int32_t* qweight, uint16_t* scales, void* stream) {
+    if (out < 0 || in < 0 || in % CQ_GROUP != 0) return CQ_EINVAL;
+    if (out == 0 || in == 0) return CQ_OK;
+    if (!codes || !grp_scales || !qweight || !scales) return CQ_EINVAL;
+    if (!aligned(codes, 16) || !aligned(grp_scales, 2) || !aligned(qweight, 4) || !aligned(scales, 2))
+        return CQ_EINVAL;
+    if (in / CQ_GROUP > 65535 || (out + 63) / 64 > INT32_MAX) return CQ_EINVAL;
+    return hip_status(cqk::launch_pack(codes, grp_scales, out, in, qweight, scales, (hipStream_t)stream));
+}
+
+size_t cq_proxy_workspace_size(int64_t n_groups) {
+    return n_groups < 0 ? 0 : round_up((size_t)n_groups * 8u);
+}
+
+int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_period, int32_t E, int64_t n_groups,
+                                const uint16_t* scales, const int64_t* module_offsets, int32_t n_modules,
+                                double* module_mean, double* macro, double* per_group, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!groups_ok(w, d_eval, d_period, E, n_groups)) return CQ_EINVAL;
+    if (n_modules < 1 || !module_offsets || !module_mean || !macro) return CQ_EINVAL;
+    if (n_groups > 0 && !scales) return CQ_EINVAL;
+    if (n_groups / 4 + 1 > INT32_MAX) return CQ_EINVAL;
+    if (!per_group) {
+        if (!workspace || workspace_bytes < cq_proxy_workspace_size(n_groups) || !aligned(workspace, ALIGN))
+            return CQ_EWORKSPACE;
+        per_group = (double*)workspace;
+    } else if (!aligned(per_group, 8)) {
+        return CQ_EINVAL;
+    }
+    return hip_status(cqk::launch_proxy(w, d_eval, d_period, E, n_groups, scales, module_offsets, n_modules,
+                                        module_mean, macro, per_group, (hipStream_t)stream));
+}
+
+}  // extern "C"

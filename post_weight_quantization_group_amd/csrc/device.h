@@ -1,0 +1,122 @@
+// Device helpers shared by the gfx950 kernels of the scale-selection library.
+//
+// Definitions followed (CliffQuant repository README, "What CliffQuant
+// changes"): the admissible scales are the positive finite IEEE binary16
+// values, the code of a weight is its quotient by the scale rounded half to
+// even and then clipped to [-8, 7], the objective is the worst environment's
+// diagonal-weighted squared error, and an exact tie goes to the lower bit
+// pattern.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cqk {
+
+constexpr int G = 128;                  // weights per group
+constexpr uint32_t BITS_FIRST = 0x0001u; // 2^-24
+constexpr uint32_t BITS_LAST = 0x7BFFu;  // 65504
+constexpr uint32_t N_SCALES = 31743u;
+constexpr int BLOCK = 256;
+
+constexpr uint8_t FLAG_BAD_INPUT = 1u, FLAG_NEAR_TIE = 2u, FLAG_EXACT_TIE = 4u,
+                  FLAG_FALLBACK = 8u, FLAG_FP64_SWEEP = 16u;
+
+// Exact binary32 value of a positive binary16 bit pattern (no reliance on the
+// device's half-precision denormal mode).
+__device__ __forceinline__ float half_bits_value(uint32_t b) {
+    const uint32_t ex = b >> 10, man = b & 0x3FFu;
+    if (ex == 0u) return (float)man * 5.9604644775390625e-08f;  // man * 2^-24
+    return __uint_as_float(((ex + 112u) << 23) | (man << 13));   // rebias 15 -> 127
+}
+
+// The code rule with the quotient as one correctly rounded binary32 division.
+__device__ __forceinline__ float exact_code(float w, float s) {
+    const float x = w / s;
+    const float r = __builtin_rintf(x);
+    return __builtin_amdgcn_fmed3f(r, -8.0f, 7.0f);
+}
+
+// Per-environment error of one group at one scale in binary64, summed
+// i = 0..127 in order with every operation rounded on its own.  The code
+// decision uses the binary64 product w * (1/s): its relative error (2^-52) is
+// far below the smallest distance (2^-25 relative) at which a binary32 weight
+// over a binary16 scale can sit from a half-integer without being on it, so
+// every decision equals the exact one except at exact half-integers, where
+// both neighbouring codes give the same |w - s q| = s/2.
+__device__ __forceinline__ double env_error_f64(const float* w, const float* d, int dstride,
+                                                double s, double inv) {
+    double F = 0.0;
+    for (int i = 0; i < G; ++i) {
+        const double wi = (double)w[i];
+        double r = __builtin_rint(wi * inv);
+        r = r < -8.0 ? -8.0 : (r > 7.0 ? 7.0 : r);
+        const double sq = s * r;
+        const double t = wi - sq;
+        const double t2 = t * t;
+        const double term = (double)d[i * dstride] * t2;
+        F = F + term;
+    }
+    return F;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(v, o, 64);
+        v = u < v ? u : v;
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Block-wide reductions for 256 threads; `red` is caller LDS of >= 4 slots.
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
+    v = wave_min_u64(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = red[0];
+#pragma unroll
+    for (int k = 1; k < BLOCK / 64; ++k) r = red[k] < r ? red[k] : r;
+    return r;
+}
+__device__ __forceinline__ float block_max_f(float v, float* red) {
+    v = wave_max_f(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < BLOCK / 64; ++k) r = fmaxf(r, red[k]);
+    return r;
+}
+__device__ __forceinline__ float block_min_f(float v, float* red) {
+    v = wave_min_f(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < BLOCK / 64; ++k) r = fminf(r, red[k]);
+    return r;
+}
+
+// Key ordering (value, bit pattern) lexicographically for non-negative floats.
+__device__ __forceinline__ uint64_t key_of(float v, uint32_t b) {
+    return ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)b;
+}
+__device__ __forceinline__ float key_value(uint64_t k) { return __uint_as_float((uint32_t)(k >> 32)); }
+__device__ __forceinline__ uint32_t key_bits(uint64_t k) { return (uint32_t)(k & 0xFFFFFFFFu); }
+constexpr uint64_t KEY_NONE = ~0ull;
+
+}  // namespace cqk

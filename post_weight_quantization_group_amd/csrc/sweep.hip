@@ -1,0 +1,509 @@
+// Exhaustive FP16 scale sweep for gfx950.
+//
+// For every group the kernel evaluates all 31,743 positive finite binary16
+// scales (CliffQuant repository README, "What CliffQuant changes": the
+// independent reference enumerates every one of them; model card
+// "Verification").  Work split: one 256-thread workgroup per group; weights
+// and diagonals are staged in LDS; each wave takes chunks of 256 consecutive
+// scale patterns, four per lane, and every lane runs the 128 weights against
+// its four scales with per-environment accumulators in registers.
+//
+// Exactness.  The sweep runs in binary32 with a proven error bound and is a
+// screen only:
+//   * weights are pre-scaled by 2^k (max |w'| in [1,2)) and scales by the same
+//     2^k -- the quotient and the codes are unchanged and every error term
+//     stays in the normal binary32 range (groups for which that cannot be
+//     guaranteed go to the binary64 sweep);
+//   * the code uses x = w' * RN(1/s'); it can differ from the exact code only
+//     when the quotient is within 17 binary32 ulps of a half-integer, which
+//     raises that term by at most 137 u (u = 2^-24) and never lowers it;
+//   * e = fma(-s', q, w') is exact unless clipped (then one rounding), and
+//     e^2 plus 128 fused multiply-adds put the sum within (1 +- u)^131 of the
+//     exact value.
+//   So the binary32 value F~ satisfies (1-131u) F <= F~ <= (1+268u) F, and
+//   every scale whose F~ is within the factor 1.00004 of the smallest F~ is
+//   rescored in binary64 (same summation order as the definition's plain
+//   sequential sum), which decides the winner and the lower-bit-pattern tie.
+//   When the smallest F~ is 0 the group's zero-error scales are exact and the
+//   lowest such pattern wins directly.  A lane keeps its best three scales; if
+//   its third is inside the bound (it may have dropped a fourth), or more than
+//   256 scales survive, the group is queued for the binary64 sweep.
+#include "device.h"
+#include "launch.h"
+
+namespace cqk {
+
+constexpr int NS = 4;                        // scales per lane per chunk
+constexpr int CHUNK = 64 * NS;               // scales per wave per chunk
+constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;  // 124
+constexpr int CAP = 256;                     // shortlist capacity per group
+constexpr float SCREEN_RATIO = 1.00004f;
+constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
+
+template <int E>
+struct SweepSmem {
+    float w[G];
+    float wp[G];
+    float dt[G * E];  // [i][e]
+    float redf[4];
+    uint64_t redk[4];
+    uint32_t cand_b[CAP];
+    uint8_t cand_tag[CAP];
+    double cand_F[CAP];
+    double cand_P[CAP];
+    double pairF[BLOCK];
+    int n_cand;
+    int overflow;
+    uint32_t win_b[2];
+    double win_F[2];
+    uint8_t win_flags[2];
+};
+
+__device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
+    if (v < k[2]) {
+        if (v < k[1]) {
+            k[2] = k[1];
+            if (v < k[0]) { k[1] = k[0]; k[0] = v; }
+            else k[1] = v;
+        } else {
+            k[2] = v;
+        }
+    }
+}
+
+template <int E, bool CLIP>
+__device__ __forceinline__ void sweep_chunk_inner(const float* __restrict__ wp, const float* __restrict__ dt,
+                                                  const float (&nsv)[NS], const float (&inv)[NS],
+                                                  float (&acc)[NS][E]) {
+#pragma unroll 2
+    for (int i = 0; i < G; ++i) {
+        const float wi = wp[i];
+        float di[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) di[e] = dt[i * E + e];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const float x = wi * inv[t];
+            float r = __builtin_rintf(x);
+            if (CLIP) r = __builtin_amdgcn_fmed3f(r, -8.0f, 7.0f);
+            const float ev = __builtin_fmaf(nsv[t], r, wi);
+            const float e2 = ev * ev;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
+        }
+    }
+}
+
+// binary64 rescoring of the first n shortlist entries: cand_F = max_e F_e,
+// cand_P = (sum_e F_e)/E, each F_e summed in the definition's order.
+template <int E>
+__device__ void rescore(SweepSmem<E>& sm, int n) {
+    constexpr int PER = BLOCK / E;
+    const int t = threadIdx.x;
+    for (int base = 0; base < n; base += PER) {
+        const int nb = min(PER, n - base);
+        if (t < nb * E) {
+            const int j = base + t / E, e = t % E;
+            const double s = (double)half_bits_value(sm.cand_b[j]);
+            sm.pairF[t] = env_error_f64(sm.w, sm.dt + e, E, s, 1.0 / s);
+        }
+        __syncthreads();
+        if (t < nb) {
+            double F = sm.pairF[t * E], P = sm.pairF[t * E];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                const double v = sm.pairF[t * E + e];
+                F = v > F ? v : F;
+                P = P + v;
+            }
+            sm.cand_F[base + t] = F;
+            sm.cand_P[base + t] = P / (double)E;
+        }
+        __syncthreads();
+    }
+}
+
+// Thread 0: lexicographic (value, bits) winner among shortlist entries with `tag`.
+template <int E>
+__device__ void pick_winner(SweepSmem<E>& sm, int n, uint8_t tag, int slot) {
+    uint32_t bb = 0xFFFFFFFFu;
+    double bF = __builtin_inf();
+    int count = 0;
+    for (int j = 0; j < n; ++j) {
+        if (!(sm.cand_tag[j] & tag)) continue;
+        const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
+        const uint32_t b = sm.cand_b[j];
+        ++count;
+        if (v < bF || (v == bF && b < bb)) { bF = v; bb = b; }
+    }
+    bool tie = false;
+    for (int j = 0; j < n; ++j) {
+        if (!(sm.cand_tag[j] & tag)) continue;
+        const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
+        if (v == bF && sm.cand_b[j] != bb) tie = true;
+    }
+    sm.win_b[slot] = bb;
+    sm.win_F[slot] = bF;
+    sm.win_flags[slot] = (uint8_t)((count > 1 ? FLAG_NEAR_TIE : 0) | (tie ? FLAG_EXACT_TIE : 0));
+}
+
+__device__ __forceinline__ void append_cand(uint32_t* cb, uint8_t* ct, int* n, uint32_t b, uint8_t tag) {
+    const int j = atomicAdd(n, 1);
+    if (j < CAP) { cb[j] = b; ct[j] = tag; }
+}
+
+template <int E>
+__device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
+    const int tid = threadIdx.x;
+    const float* wg = a.w + g * G;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(E * G);
+
+    // ---- staging and group checks
+    if (tid < G) sm.w[tid] = wg[tid];
+    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = dg[j];
+    __syncthreads();
+    float bad = 0.0f, aw = 0.0f, wnz = __builtin_inff(), dmx = 0.0f, dnz = __builtin_inff();
+    if (tid < G) {
+        const float v = sm.w[tid];
+        if (!__builtin_isfinite(v)) bad = 1.0f;
+        aw = fabsf(v);
+        if (aw > 0.0f) wnz = aw;
+    }
+    for (int j = tid; j < E * G; j += BLOCK) {
+        const float v = sm.dt[j];
+        if (!(v >= 0.0f) || !__builtin_isfinite(v)) bad = 1.0f;
+        else {
+            dmx = fmaxf(dmx, v);
+            if (v > 0.0f) dnz = fminf(dnz, v);
+        }
+    }
+    bad = block_max_f(bad, sm.redf);
+    if (bad != 0.0f) aw = 0.0f;
+    const float wmax = block_max_f(aw, sm.redf);
+    const float wmin_nz = block_min_f(wnz, sm.redf);
+    const float dmax = block_max_f(dmx, sm.redf);
+    const float dmin_nz = block_min_f(dnz, sm.redf);
+
+    if (bad != 0.0f) {
+        if (tid < G && a.codes) a.codes[g * G + tid] = 0;
+        if (tid == 0) {
+            if (a.scales) a.scales[g] = 0;
+            if (a.objective) a.objective[g] = __builtin_nan("");
+            if (a.pscales) a.pscales[g] = 0;
+            if (a.pobjective) a.pobjective[g] = __builtin_nan("");
+            if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
+        }
+        return;
+    }
+
+    // ---- power-of-two pre-scaling and the no-underflow / no-overflow guarantee
+    int k = 0;
+    if (wmax > 0.0f) {
+        int ex;
+        frexpf(wmax, &ex);
+        k = min(100, max(-100, 1 - ex));
+    }
+    bool safe = dmax <= 0x1p100f;
+    if (wmin_nz < __builtin_inff()) {
+        const double elb = fmin(ldexp(1.0, k - 24), (double)wmin_nz * ldexp(1.0, k - 24));
+        const double e2 = elb * elb;
+        safe = safe && e2 >= 0x1p-120 && (dmin_nz == __builtin_inff() || (double)dmin_nz * e2 >= 0x1p-120);
+    }
+    if (!safe) {
+        if (tid == 0) {
+            const int j = atomicAdd(a.fb_count, 1);
+            a.fb_list[j] = (int32_t)g;
+        }
+        return;
+    }
+    const float pk = ldexpf(1.0f, k);
+    if (tid < G) sm.wp[tid] = sm.w[tid] * pk;
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    __syncthreads();
+
+    // ---- binary32 screen over all 31,743 scales
+    const int lane = tid & 63, wave = tid >> 6;
+    const float wmaxp = wmax * pk;
+    uint64_t mk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
+    uint64_t qk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
+    for (int c = wave; c < NCHUNK; c += BLOCK / 64) {
+        float nsv[NS], inv[NS];
+        float acc[NS][E];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + lane + 64 * t), BITS_LAST);
+            const float s = half_bits_value(b) * pk;
+            nsv[t] = -s;
+            inv[t] = 1.0f / s;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+        }
+        // wave-uniform: can any weight clip at the chunk's smallest scale?
+        const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        if (wmaxp <= 7.25f * s0)
+            sweep_chunk_inner<E, false>(sm.wp, sm.dt, nsv, inv, acc);
+        else
+            sweep_chunk_inner<E, true>(sm.wp, sm.dt, nsv, inv, acc);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + lane + 64 * t);
+            if (b > BITS_LAST) continue;
+            float Fm = acc[t][0], Ps = acc[t][0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                Fm = fmaxf(Fm, acc[t][e]);
+                Ps = Ps + acc[t][e];
+            }
+            if (a.want_minimax) top3_insert(mk, key_of(Fm, b));
+            if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
+        }
+    }
+
+    // ---- global best, runner-up and shortlist
+    for (int pol = 0; pol < 2; ++pol) {
+        const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+        if (!want) continue;
+        const uint64_t* kk = pol == 0 ? mk : qk;
+        const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
+        const uint64_t M1 = block_min_u64(kk[0], sm.redk);
+        const uint64_t S2 = block_min_u64(kk[0] == M1 ? kk[1] : kk[0], sm.redk);
+        const float m = key_value(M1);
+        if (m == 0.0f) {
+            // zero binary32 error is exact here: the lowest such pattern wins
+            if (tid == 0) {
+                append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(M1), tag);
+                sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
+                sm.win_b[pol] = key_bits(M1);
+            }
+        } else {
+            const float T = m * SCREEN_RATIO;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
+                    if (r == 2) sm.overflow = 1;
+                    else append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(kk[r]), tag);
+                }
+            }
+            if (tid == 0) sm.win_b[pol] = 0xFFFFFFFFu;  // decided by rescoring
+        }
+        __syncthreads();
+    }
+    __syncthreads();
+    const int n = sm.n_cand;
+    if (sm.overflow || n > CAP) {
+        if (tid == 0) {
+            const int j = atomicAdd(a.fb_count, 1);
+            a.fb_list[j] = (int32_t)g;
+        }
+        return;
+    }
+
+    // ---- binary64 rescoring and the lower-bit-pattern rule
+    rescore<E>(sm, n);
+    if (tid == 0) {
+        for (int pol = 0; pol < 2; ++pol) {
+            const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+            if (!want) continue;
+            const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
+            if (sm.win_b[pol] != 0xFFFFFFFFu) {  // zero rule: value from rescoring
+                const uint32_t b = sm.win_b[pol];
+                const uint8_t f = sm.win_flags[pol];
+                pick_winner<E>(sm, n, tag, pol);
+                sm.win_b[pol] = b;
+                sm.win_flags[pol] = f;
+            } else {
+                pick_winner<E>(sm, n, tag, pol);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- outputs
+    if (a.want_minimax) {
+        const uint32_t b = sm.win_b[0];
+        if (tid < G && a.codes) a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(b));
+        if (tid == 0) {
+            a.scales[g] = (uint16_t)b;
+            if (a.objective) a.objective[g] = sm.win_F[0];
+            if (a.flags) a.flags[g] = sm.win_flags[0] | (a.mark_fallback ? FLAG_FALLBACK : 0);
+        }
+    }
+    if (a.want_pooled && tid == 0) {
+        if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
+        if (a.pobjective) a.pobjective[g] = sm.win_F[1];
+        if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+    }
+    if (a.want_pooled && !a.want_minimax && tid < G && a.codes)
+        a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(sm.win_b[1]));
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK) void sweep_f32_kernel(SweepArgs a) {
+    __shared__ SweepSmem<E> sm;
+    if (a.list) {
+        const int cnt = *a.list_count;
+        for (int k = blockIdx.x; k < cnt; k += gridDim.x) {
+            sweep_group<E>(a, (int64_t)a.list[k], sm);
+            __syncthreads();
+        }
+    } else {
+        sweep_group<E>(a, (int64_t)blockIdx.x + a.group_offset, sm);
+    }
+}
+
+// ------------------------------------------------------------------ binary64 sweep
+// Every scale in binary64, each environment summed in the definition's order;
+// the lexicographic (value, bits) minimum is the answer with no screen at all.
+// Used for groups the binary32 screen could not settle.
+template <int E>
+struct F64Smem {
+    float w[G];
+    float dt[G * E];
+    double rv[BLOCK];
+    uint32_t rb[BLOCK];
+    double rv2[BLOCK];
+    uint32_t rb2[BLOCK];
+};
+
+__device__ __forceinline__ bool lex_less(double v, uint32_t b, double v2, uint32_t b2) {
+    return v < v2 || (v == v2 && b < b2);
+}
+
+template <int E>
+__device__ void f64_reduce(F64Smem<E>& sm, double v1, uint32_t b1, double v2, uint32_t b2,
+                           double& outv, uint32_t& outb, double& outv2) {
+    const int t = threadIdx.x;
+    sm.rv[t] = v1; sm.rb[t] = b1; sm.rv2[t] = v2; sm.rb2[t] = b2;
+    __syncthreads();
+    for (int s = BLOCK / 2; s > 0; s >>= 1) {
+        if (t < s) {
+            // merge two (best, second) pairs
+            double av = sm.rv[t], av2 = sm.rv2[t], bv = sm.rv[t + s], bv2 = sm.rv2[t + s];
+            uint32_t ab = sm.rb[t], ab2 = sm.rb2[t], bb = sm.rb[t + s], bb2 = sm.rb2[t + s];
+            if (lex_less(bv, bb, av, ab)) {
+                // b is best; second = min(a, b2)
+                sm.rv[t] = bv; sm.rb[t] = bb;
+                if (lex_less(av, ab, bv2, bb2)) { sm.rv2[t] = av; sm.rb2[t] = ab; }
+                else { sm.rv2[t] = bv2; sm.rb2[t] = bb2; }
+            } else {
+                if (lex_less(bv, bb, av2, ab2)) { sm.rv2[t] = bv; sm.rb2[t] = bb; }
+            }
+        }
+        __syncthreads();
+    }
+    outv = sm.rv[0]; outb = sm.rb[0]; outv2 = sm.rv2[0];
+    __syncthreads();
+}
+
+template <int E>
+__device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
+    const int tid = threadIdx.x;
+    const float* wg = a.w + g * G;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(E * G);
+    if (tid < G) sm.w[tid] = wg[tid];
+    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = dg[j];
+    __syncthreads();
+    const double INF = __builtin_inf();
+    double mv1 = INF, mv2 = INF, pv1 = INF, pv2 = INF;
+    uint32_t mb1 = 0xFFFFFFFFu, mb2 = 0xFFFFFFFFu, pb1 = 0xFFFFFFFFu, pb2 = 0xFFFFFFFFu;
+    for (uint32_t b = BITS_FIRST + tid; b <= BITS_LAST; b += BLOCK) {
+        const double s = (double)half_bits_value(b), inv = 1.0 / s;
+        double Fe[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) Fe[e] = 0.0;
+        for (int i = 0; i < G; ++i) {
+            const double wi = (double)sm.w[i];
+            double r = __builtin_rint(wi * inv);
+            r = r < -8.0 ? -8.0 : (r > 7.0 ? 7.0 : r);
+            const double sq = s * r;
+            const double t = wi - sq;
+            const double t2 = t * t;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const double term = (double)sm.dt[i * E + e] * t2;
+                Fe[e] = Fe[e] + term;
+            }
+        }
+        double F = Fe[0], P = Fe[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) { F = Fe[e] > F ? Fe[e] : F; P = P + Fe[e]; }
+        P = P / (double)E;
+        // ascending b within a thread: strict '<' keeps the lower pattern
+        if (F < mv1) { mv2 = mv1; mb2 = mb1; mv1 = F; mb1 = b; }
+        else if (F < mv2) { mv2 = F; mb2 = b; }
+        if (P < pv1) { pv2 = pv1; pb2 = pb1; pv1 = P; pb1 = b; }
+        else if (P < pv2) { pv2 = P; pb2 = b; }
+    }
+    double bestF, secF, bestP, secP;
+    uint32_t bm, bp;
+    f64_reduce<E>(sm, mv1, mb1, mv2, mb2, bestF, bm, secF);
+    f64_reduce<E>(sm, pv1, pb1, pv2, pb2, bestP, bp, secP);
+    if (a.want_minimax) {
+        if (tid < G && a.codes) a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(bm));
+        if (tid == 0) {
+            a.scales[g] = (uint16_t)bm;
+            if (a.objective) a.objective[g] = bestF;
+            if (a.flags)
+                a.flags[g] = FLAG_FP64_SWEEP | (secF == bestF ? (FLAG_EXACT_TIE | FLAG_NEAR_TIE) : 0) |
+                             (a.mark_fallback ? FLAG_FALLBACK : 0);
+        }
+    }
+    if (a.want_pooled) {
+        if (tid == 0) {
+            if (a.pscales) a.pscales[g] = (uint16_t)bp;
+            if (a.pobjective) a.pobjective[g] = bestP;
+            if (!a.want_minimax && a.flags)
+                a.flags[g] = FLAG_FP64_SWEEP | (secP == bestP ? (FLAG_EXACT_TIE | FLAG_NEAR_TIE) : 0);
+        }
+        if (!a.want_minimax && tid < G && a.codes)
+            a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(bp));
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK) void sweep_f64_kernel(SweepArgs a) {
+    __shared__ F64Smem<E> sm;
+    const int cnt = *a.fb_count;
+    for (int k = blockIdx.x; k < cnt; k += gridDim.x) {
+        f64_sweep_group<E>(a, (int64_t)a.fb_list[k], sm);
+        __syncthreads();
+    }
+}
+
+__global__ void zero_counter_kernel(int32_t* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
+}
+
+template <int E>
+static hipError_t launch_e(const SweepArgs& a, int64_t n_groups, int fb_blocks, hipStream_t st) {
+    hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
+    if (a.list) {
+        hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
+    } else {
+        // grid.x is limited to 2^31-1 blocks: split very large batches
+        const int64_t step = 1ll << 30;
+        for (int64_t off = 0; off < n_groups; off += step) {
+            SweepArgs b = a;
+            b.group_offset = off;
+            const int64_t n = n_groups - off < step ? n_groups - off : step;
+            hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+        }
+    }
+    hipLaunchKernelGGL(sweep_f64_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sweep(const SweepArgs& a, int E, int64_t n_groups, hipStream_t st) {
+    const int fb_blocks = (int)(n_groups < 2048 ? (n_groups > 0 ? n_groups : 1) : 2048);
+    switch (E) {
+#define CQ_CASE(N) case N: return launch_e<N>(a, n_groups, fb_blocks, st);
+        CQ_CASE(1) CQ_CASE(2) CQ_CASE(3) CQ_CASE(4) CQ_CASE(5) CQ_CASE(6) CQ_CASE(7) CQ_CASE(8)
+        CQ_CASE(9) CQ_CASE(10) CQ_CASE(11) CQ_CASE(12) CQ_CASE(13) CQ_CASE(14) CQ_CASE(15) CQ_CASE(16)
+        CQ_CASE(17) CQ_CASE(18) CQ_CASE(19) CQ_CASE(20) CQ_CASE(21) CQ_CASE(22) CQ_CASE(23) CQ_CASE(24)
+        CQ_CASE(25) CQ_CASE(26) CQ_CASE(27) CQ_CASE(28) CQ_CASE(29) CQ_CASE(30) CQ_CASE(31) CQ_CASE(32)
+#undef CQ_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace cqk

@@ -1,0 +1,87 @@
+"""The C ABI library without a GPU: it loads, exports every declared entry point, and rejects
+bad arguments before enqueueing anything (these calls never reach a HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_group_amd as cq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_names():
+    assert sorted(cq.EXPORTED_SYMBOLS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(cq.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert cq.cq_abi_version() == 1
+    assert cq.cq_status_string(0) == "ok"
+    assert "workspace" in cq.cq_status_string(-2)
+    assert cq.cq_status_string(123) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert cq.cq_workspace_size(cq.EXHAUSTIVE, 4, 0) >= 256
+    assert cq.cq_workspace_size(cq.EXHAUSTIVE, 4, 1000) >= 4000
+    assert cq.cq_workspace_size(cq.CANDIDATE, 4, 1000) > cq.cq_workspace_size(cq.EXHAUSTIVE, 4, 1000)
+    assert cq.cq_workspace_size(cq.EXHAUSTIVE, 0, 10) == 0
+    assert cq.cq_workspace_size(cq.EXHAUSTIVE, 33, 10) == 0
+    assert cq.cq_workspace_size(7, 4, 10) == 0
+    assert cq.cq_proxy_workspace_size(10) >= 80
+
+
+FAKE = 1 << 20  # a 16-byte-aligned address that is never dereferenced: every call below fails its checks
+
+
+def _quant(**kw):
+    lib = cq.load()
+    a = dict(w=FAKE, d=FAKE, d_period=1, E=4, n=10, method=0, scales=FAKE, codes=None, obj=None, flags=None,
+             ps=None, po=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.cq_quantize_groups(a["w"], a["d"], a["d_period"], a["E"], a["n"], a["method"], a["scales"],
+                                  a["codes"], a["obj"], a["flags"], a["ps"], a["po"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), -1), (dict(E=33), -1), (dict(n=-1), -1), (dict(d_period=0), -1), (dict(w=None), -1),
+    (dict(d=None), -1), (dict(scales=None), -1), (dict(method=5), -1), (dict(w=FAKE + 4), -1),
+    (dict(method=1, ps=FAKE), -4), (dict(ws=None), -2), (dict(ws=FAKE, wsb=16), -2),
+    (dict(ws=FAKE + 16, wsb=1 << 20), -2),
+])
+def test_quantize_rejects_before_launch(kw, status):
+    assert _quant(**kw) == status
+
+
+def test_zero_groups_is_a_no_op():
+    assert _quant(n=0, w=None, d=None, scales=None) == 0
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = cq.load()
+    assert lib.cq_pack_gptq_v1(FAKE, FAKE, 4, 100, FAKE, FAKE, None) == -1          # in % 128
+    assert lib.cq_pack_gptq_v1(FAKE + 1, FAKE, 4, 128, FAKE, FAKE, None) == -1      # codes alignment
+    assert lib.cq_pack_gptq_v1(None, FAKE, 4, 128, FAKE, FAKE, None) == -1
+    assert lib.cq_pack_gptq_v1(None, None, 0, 128, None, None, None) == 0           # empty
+    assert lib.cq_baseline_scales(FAKE, FAKE, 1, 4, 10, 9, FAKE, None, None, None, 0, None) == -1
+    assert lib.cq_baseline_scales(FAKE, FAKE, 1, 4, 10, 1, FAKE, None, None, None, 0, None) == -2
+    assert lib.cq_baseline_scales(FAKE, None, 1, 4, 10, 0, FAKE, None, FAKE, None, 0, None) == -1
+    assert lib.cq_proxy_worst_env_wmse(FAKE, FAKE, 1, 4, 10, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0,
+                                       None) == -1
+    assert lib.cq_proxy_worst_env_wmse(FAKE, FAKE, 1, 4, 10, FAKE, FAKE, 2, FAKE, FAKE, None, None, 0,
+                                       None) == -2
