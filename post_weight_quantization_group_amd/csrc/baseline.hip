@@ -13,22 +13,6 @@
 
 namespace cqk {
 
-// binary32 x >= 0 to the nearest binary16 pattern, ties to even; 0x7C00 on overflow.
-__device__ __forceinline__ uint32_t f32_to_half_bits_rne(float x) {
-    if (!(x < 65520.0f)) return 0x7C00u;
-    if (x < 0x1p-14f) {
-        // subnormal range: the pattern is x / 2^-24 rounded half to even (1024 = smallest normal)
-        return (uint32_t)__builtin_rintf(x * 16777216.0f);
-    }
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t ex = (u >> 23) - 127u + 15u;  // in 1..30
-    const uint32_t man = u & 0x7FFFFFu;
-    uint32_t r = man >> 13;
-    const uint32_t rem = man & 0x1FFFu;
-    if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
-    return (ex << 10) + r;  // a carry out of the fraction bumps the exponent, as it should
-}
-
 __global__ __launch_bounds__(128) void absmax_kernel(const float* __restrict__ w, const float* __restrict__ d,
                                                      int64_t d_period, int E, int64_t group_offset,
                                                      uint16_t* scales, int8_t* codes, double* objective) {

@@ -18,6 +18,14 @@ constexpr uint32_t BITS_LAST = 0x7BFFu;  // 65504
 constexpr uint32_t N_SCALES = 31743u;
 constexpr int BLOCK = 256;
 
+// Kernels are instantiated for 1, 2, 4, 8, 16 and 32 environments; other counts run the
+// next size up with zero diagonals, which add 0 to every sum and never win a maximum.
+inline int pad_envs(int E) {
+    int p = 1;
+    while (p < E) p <<= 1;
+    return p;
+}
+
 constexpr uint8_t FLAG_BAD_INPUT = 1u, FLAG_NEAR_TIE = 2u, FLAG_EXACT_TIE = 4u,
                   FLAG_FALLBACK = 8u, FLAG_FP64_SWEEP = 16u;
 
@@ -38,11 +46,13 @@ __device__ __forceinline__ float exact_code(float w, float s) {
 
 // Per-environment error of one group at one scale in binary64, summed
 // i = 0..127 in order with every operation rounded on its own.  The code
-// decision uses the binary64 product w * (1/s): its relative error (2^-52) is
-// far below the smallest distance (2^-25 relative) at which a binary32 weight
-// over a binary16 scale can sit from a half-integer without being on it, so
-// every decision equals the exact one except at exact half-integers, where
-// both neighbouring codes give the same |w - s q| = s/2.
+// decision uses the binary64 product w * (1/s).  A binary32 weight that is not
+// exactly (m + 1/2) s differs from that binary32 number by at least half a
+// binary32 spacing, so its quotient sits at least a quarter binary32 ulp of
+// m + 1/2 (about 2^-26 relative) away from the half-integer; the product's
+// relative error (2^-52) cannot cross it.  Every decision therefore equals the
+// exact one -- and the binary32-division one -- except at exact half-integers,
+// where both neighbouring codes give the same |w - s q| = s/2.
 __device__ __forceinline__ double env_error_f64(const float* w, const float* d, int dstride,
                                                 double s, double inv) {
     double F = 0.0;
@@ -57,6 +67,22 @@ __device__ __forceinline__ double env_error_f64(const float* w, const float* d, 
         F = F + term;
     }
     return F;
+}
+
+// binary32 x >= 0 to the nearest binary16 pattern, ties to even; 0x7C00 on overflow.
+__device__ __forceinline__ uint32_t f32_to_half_bits_rne(float x) {
+    if (!(x < 65520.0f)) return 0x7C00u;
+    if (x < 0x1p-14f) {
+        // subnormal range: the pattern is x / 2^-24 rounded half to even (1024 = smallest normal)
+        return (uint32_t)__builtin_rintf(x * 16777216.0f);
+    }
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t ex = (u >> 23) - 127u + 15u;  // in 1..30
+    const uint32_t man = u & 0x7FFFFFu;
+    uint32_t r = man >> 13;
+    const uint32_t rem = man & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+    return (ex << 10) + r;  // a carry out of the fraction bumps the exponent, as it should
 }
 
 // ---------------------------------------------------------------- reductions

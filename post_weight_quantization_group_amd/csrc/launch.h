@@ -9,6 +9,8 @@ struct SweepArgs {
     const float* w;
     const float* d;
     int64_t d_period;
+    int E;                     // environments in d; kernels run the next power of two, padded
+                               // with zero diagonals (which change no maximum and no sum)
     int64_t group_offset;      // direct mode: first group of this launch
     const int32_t* list;       // indirect mode: group ids (nullable)
     const int32_t* list_count; // indirect mode: device count of `list`
@@ -34,6 +36,7 @@ struct CandArgs {
     const float* w;
     const float* d;
     int64_t d_period;
+    int E;
     int64_t n_groups;
     uint16_t* scales;
     int8_t* codes;

@@ -21,15 +21,14 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-template <int E>
 __global__ __launch_bounds__(256) void proxy_group_kernel(const float* __restrict__ w, const float* __restrict__ d,
-                                                          int64_t d_period, int64_t n_groups,
+                                                          int64_t d_period, int E, int64_t n_groups,
                                                           const uint16_t* __restrict__ scales,
                                                           double* __restrict__ per_group) {
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (g >= n_groups) return;
-    const float* dg = d + (g % d_period) * (int64_t)(E * G);
+    const float* dg = d + (g % d_period) * (int64_t)E * G;
     const float2 wv = ((const float2*)(w + g * G))[lane];
     const double s = (double)half_bits_value(scales[g]);
     const double inv = 1.0 / s;
@@ -44,7 +43,6 @@ __global__ __launch_bounds__(256) void proxy_group_kernel(const float* __restric
         t2[h] = t * t;
     }
     double worst = 0.0;
-#pragma unroll
     for (int e = 0; e < E; ++e) {
         const float2 dv = ((const float2*)(dg + e * G))[lane];
         double part = (double)dv.x * t2[0] + (double)dv.y * t2[1];
@@ -87,27 +85,13 @@ __global__ __launch_bounds__(256) void proxy_macro_kernel(const double* __restri
     if (threadIdx.x == 0) *macro = red[0] / (double)n_modules;
 }
 
-template <int E>
-static void launch_groups(const float* w, const float* d, int64_t d_period, int64_t n_groups,
-                          const uint16_t* scales, double* per_group, hipStream_t st) {
-    const int64_t blocks = (n_groups + 3) / 4;
-    hipLaunchKernelGGL(proxy_group_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st, w, d, d_period, n_groups,
-                       scales, per_group);
-}
-
 hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,
                         double* module_mean, double* macro, double* per_group, hipStream_t st) {
     if (n_groups > 0) {
-        switch (E) {
-#define CQ_CASE(N) case N: launch_groups<N>(w, d, d_period, n_groups, scales, per_group, st); break;
-            CQ_CASE(1) CQ_CASE(2) CQ_CASE(3) CQ_CASE(4) CQ_CASE(5) CQ_CASE(6) CQ_CASE(7) CQ_CASE(8)
-            CQ_CASE(9) CQ_CASE(10) CQ_CASE(11) CQ_CASE(12) CQ_CASE(13) CQ_CASE(14) CQ_CASE(15) CQ_CASE(16)
-            CQ_CASE(17) CQ_CASE(18) CQ_CASE(19) CQ_CASE(20) CQ_CASE(21) CQ_CASE(22) CQ_CASE(23) CQ_CASE(24)
-            CQ_CASE(25) CQ_CASE(26) CQ_CASE(27) CQ_CASE(28) CQ_CASE(29) CQ_CASE(30) CQ_CASE(31) CQ_CASE(32)
-#undef CQ_CASE
-            default: return hipErrorInvalidValue;
-        }
+        const int64_t blocks = (n_groups + 3) / 4;
+        hipLaunchKernelGGL(proxy_group_kernel, dim3((unsigned)blocks), dim3(256), 0, st, w, d, d_period, E,
+                           n_groups, scales, per_group);
     }
     hipLaunchKernelGGL(proxy_module_kernel, dim3((unsigned)n_modules), dim3(256), 0, st, per_group,
                        module_offsets, n_groups, module_mean);

@@ -97,7 +97,7 @@ __device__ __forceinline__ void sweep_chunk_inner(const float* __restrict__ wp, 
 // binary64 rescoring of the first n shortlist entries: cand_F = max_e F_e,
 // cand_P = (sum_e F_e)/E, each F_e summed in the definition's order.
 template <int E>
-__device__ void rescore(SweepSmem<E>& sm, int n) {
+__device__ void rescore(SweepSmem<E>& sm, int n, int E_real) {
     constexpr int PER = BLOCK / E;
     const int t = threadIdx.x;
     for (int base = 0; base < n; base += PER) {
@@ -117,7 +117,7 @@ __device__ void rescore(SweepSmem<E>& sm, int n) {
                 P = P + v;
             }
             sm.cand_F[base + t] = F;
-            sm.cand_P[base + t] = P / (double)E;
+            sm.cand_P[base + t] = P / (double)E_real;
         }
         __syncthreads();
     }
@@ -156,11 +156,11 @@ template <int E>
 __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     const int tid = threadIdx.x;
     const float* wg = a.w + g * G;
-    const float* dg = a.d + (g % a.d_period) * (int64_t)(E * G);
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
 
-    // ---- staging and group checks
+    // ---- staging and group checks (environments a.E..E-1 are zero padding)
     if (tid < G) sm.w[tid] = wg[tid];
-    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = dg[j];
+    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
     __syncthreads();
     float bad = 0.0f, aw = 0.0f, wnz = __builtin_inff(), dmx = 0.0f, dnz = __builtin_inff();
     if (tid < G) {
@@ -299,7 +299,7 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     }
 
     // ---- binary64 rescoring and the lower-bit-pattern rule
-    rescore<E>(sm, n);
+    rescore<E>(sm, n, a.E);
     if (tid == 0) {
         for (int pol = 0; pol < 2; ++pol) {
             const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
@@ -399,9 +399,9 @@ template <int E>
 __device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
     const int tid = threadIdx.x;
     const float* wg = a.w + g * G;
-    const float* dg = a.d + (g % a.d_period) * (int64_t)(E * G);
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
     if (tid < G) sm.w[tid] = wg[tid];
-    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = dg[j];
+    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
     __syncthreads();
     const double INF = __builtin_inf();
     double mv1 = INF, mv2 = INF, pv1 = INF, pv2 = INF;
@@ -427,7 +427,7 @@ __device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
         double F = Fe[0], P = Fe[0];
 #pragma unroll
         for (int e = 1; e < E; ++e) { F = Fe[e] > F ? Fe[e] : F; P = P + Fe[e]; }
-        P = P / (double)E;
+        P = P / (double)a.E;
         // ascending b within a thread: strict '<' keeps the lower pattern
         if (F < mv1) { mv2 = mv1; mb2 = mb1; mv1 = F; mb1 = b; }
         else if (F < mv2) { mv2 = F; mb2 = b; }
@@ -493,15 +493,17 @@ static hipError_t launch_e(const SweepArgs& a, int64_t n_groups, int fb_blocks, 
     return hipGetLastError();
 }
 
-hipError_t launch_sweep(const SweepArgs& a, int E, int64_t n_groups, hipStream_t st) {
+hipError_t launch_sweep(const SweepArgs& a_in, int E, int64_t n_groups, hipStream_t st) {
     const int fb_blocks = (int)(n_groups < 2048 ? (n_groups > 0 ? n_groups : 1) : 2048);
-    switch (E) {
-#define CQ_CASE(N) case N: return launch_e<N>(a, n_groups, fb_blocks, st);
-        CQ_CASE(1) CQ_CASE(2) CQ_CASE(3) CQ_CASE(4) CQ_CASE(5) CQ_CASE(6) CQ_CASE(7) CQ_CASE(8)
-        CQ_CASE(9) CQ_CASE(10) CQ_CASE(11) CQ_CASE(12) CQ_CASE(13) CQ_CASE(14) CQ_CASE(15) CQ_CASE(16)
-        CQ_CASE(17) CQ_CASE(18) CQ_CASE(19) CQ_CASE(20) CQ_CASE(21) CQ_CASE(22) CQ_CASE(23) CQ_CASE(24)
-        CQ_CASE(25) CQ_CASE(26) CQ_CASE(27) CQ_CASE(28) CQ_CASE(29) CQ_CASE(30) CQ_CASE(31) CQ_CASE(32)
-#undef CQ_CASE
+    SweepArgs a = a_in;
+    a.E = E;
+    switch (pad_envs(E)) {
+        case 1: return launch_e<1>(a, n_groups, fb_blocks, st);
+        case 2: return launch_e<2>(a, n_groups, fb_blocks, st);
+        case 4: return launch_e<4>(a, n_groups, fb_blocks, st);
+        case 8: return launch_e<8>(a, n_groups, fb_blocks, st);
+        case 16: return launch_e<16>(a, n_groups, fb_blocks, st);
+        case 32: return launch_e<32>(a, n_groups, fb_blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -338,3 +338,21 @@ def test_minimax_proxy_not_worse_than_baselines_on_calibration_diagonals():
     pa = oracle.proxy(w, d, oracle.absmax_bits(w), mods, 1, p)[0]
     pp = oracle.proxy(w, d, r.pl_bits, mods, 1, p)[0]
     assert np.all(pm <= pa) and np.all(pm <= pp)
+
+
+def test_binary32_quotient_decides_like_exact_rational_near_every_half_integer():
+    """For every binary16 scale s and half-integer h in 0.5..8.5, weights 1-3 binary32 ulps either
+    side of h*s: round-half-even of the binary32 quotient equals the exact decision."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    s = bits.view(np.float16).astype(np.float32)
+    for h2 in range(1, 18, 2):
+        hs = (s * np.float32(h2 / 2)).astype(np.float32)
+        for k in (1, 2, 3):
+            for direction in (np.inf, -np.inf):
+                w = hs.copy()
+                for _ in range(k):
+                    w = np.nextafter(w, np.float32(direction))
+                got = np.array([oracle.codes_at(w[j:j + 1], int(bits[j]))[0] for j in range(0, w.size, 997)])
+                below = (w.astype(np.float64) < hs.astype(np.float64))[::997]
+                want = np.clip(np.where(below, h2 // 2, h2 // 2 + 1), -8, 7)
+                np.testing.assert_array_equal(got, want)
