@@ -4,8 +4,8 @@
 // scales (CliffQuant repository README, "What CliffQuant changes": the
 // independent reference enumerates every one of them; model card
 // "Verification").  Work split: one 256-thread workgroup per group; weights
-// and diagonals are staged in LDS; each wave takes chunks of 256 consecutive
-// scale patterns, four per lane, and every lane runs the 128 weights against
+// and diagonals are staged in LDS; each wave takes chunks of 512 consecutive
+// scale patterns, eight per lane, and every lane runs the 128 weights against
 // its four scales with per-environment accumulators in registers.
 //
 // Exactness.  The sweep runs in binary32 with a proven error bound and is a
@@ -33,9 +33,9 @@
 
 namespace cqk {
 
-constexpr int NS = 4;                        // scales per lane per chunk
+constexpr int NS = 8;                        // scales per lane per chunk
 constexpr int CHUNK = 64 * NS;               // scales per wave per chunk
-constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;  // 124
+constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;  // 62
 constexpr int CAP = 256;                     // shortlist capacity per group
 constexpr float SCREEN_RATIO = 1.00004f;
 constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
@@ -43,7 +43,7 @@ constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
 template <int E>
 struct SweepSmem {
     float w[G];
-    float wp[G];
+    __align__(16) float wp[G];
     float dt[G * E];  // [i][e]
     float redf[4];
     uint64_t redk[4];
@@ -71,6 +71,10 @@ __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
     }
 }
 
+// One chunk: every lane runs the 128 weights against its NS scales with the per-environment
+// sums in registers: q = rne(w' * RN(1/s')) (clipped when needed), e = fma(-s', q, w'),
+// e^2, then one fma per environment.  The weight and its E diagonals are LDS broadcasts
+// shared by all NS scales of the lane.
 template <int E, bool CLIP>
 __device__ __forceinline__ void sweep_chunk_inner(const float* __restrict__ wp, const float* __restrict__ dt,
                                                   const float (&nsv)[NS], const float (&inv)[NS],
@@ -229,9 +233,13 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     for (int c = wave; c < NCHUNK; c += BLOCK / 64) {
         float nsv[NS], inv[NS];
         float acc[NS][E];
+        // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
+        // otherwise share a lane; exact ties at power-of-two spacing (an outlier alone carrying a
+        // code) then fill one lane's top three.  Rotating by 5 per chunk spreads them out.
+        const int rot = (lane + 5 * c) & 63;
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + lane + 64 * t), BITS_LAST);
+            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
             const float s = half_bits_value(b) * pk;
             nsv[t] = -s;
             inv[t] = 1.0f / s;
@@ -246,13 +254,14 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
             sweep_chunk_inner<E, true>(sm.wp, sm.dt, nsv, inv, acc);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-            const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + lane + 64 * t);
+            const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
             if (b > BITS_LAST) continue;
             float Fm = acc[t][0], Ps = acc[t][0];
 #pragma unroll
             for (int e = 1; e < E; ++e) {
-                Fm = fmaxf(Fm, acc[t][e]);
-                Ps = Ps + acc[t][e];
+                const float v = acc[t][e];
+                Fm = fmaxf(Fm, v);
+                Ps = Ps + v;
             }
             if (a.want_minimax) top3_insert(mk, key_of(Fm, b));
             if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
