@@ -63,6 +63,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-candidate", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel of known "
+                         "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): every group is independent, "
@@ -114,6 +117,13 @@ def main():
         }
         mats.append(t)
     n_total = sum(t["n"] for t in mats)
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     use_candidate = not args.no_candidate
     if use_candidate:
         try:

@@ -10,8 +10,9 @@
 //  1. Code transitions.  For w_i != 0 and each c with |q_i| able to fall from
 //     c+1 to c, the first grid pattern t where |q_i(s_t)| <= c.  The test
 //     |q| <= c  <=>  |w| < (c+1/2) s  or  (|w| == (c+1/2) s and c even)  is
-//     exact in binary32 ((c+1/2) s has at most 15 significant bits), and it is
-//     monotone in s, so t is found by bisection over the 31,743 patterns.
+//     exact in binary32 ((c+1/2) s has at most 15 significant bits) and monotone
+//     in s; t is the binary16 rounding of |w|/(c+1/2) confirmed by a short walk
+//     on that predicate (bisection if the walk does not settle).
 //  2. Runs.  The events are sorted by t (bitonic sort in LDS); between two
 //     consecutive event patterns every code is constant, so each environment
 //     error is the quadratic f_e(s) = A_e - 2 B_e s + C_e s^2 with
@@ -21,21 +22,25 @@
 //     next to the run's continuous minimiser: a run end, the vertex B_e/C_e
 //     of an environment on top, or the crossing of two environments on top.
 //     Runs whose lower bound max_e min f_e already exceeds the best end-point
-//     value are skipped; in the rest every vertex and crossing on the upper
-//     envelope is mapped to its grid neighbours (+-2 patterns of slack).
+//     value are skipped; the rest are compacted into LDS and every vertex and
+//     crossing on their upper envelope is mapped to its grid neighbours (+-2
+//     patterns of slack).
 //  4. Reduction.  Every candidate within the proven error of the quadratic
 //     form of the best one is rescored directly in binary64 in the same
 //     summation order as the definition's plain sequential sum.  The lowest
-//     value wins; if two distinct patterns tie bit for bit, or the shortlist
-//     overflows, the group is handed to the exhaustive sweep (flag FALLBACK).
+//     value wins; if two distinct patterns tie bit for bit, or a list overflows
+//     (kept runs, candidates, shortlist), the group is handed to the exhaustive
+//     sweep (flag FALLBACK).
 #include "device.h"
 #include "launch.h"
 
 namespace cqk {
 namespace {
 
-constexpr int MAX_EV = 1024;  // at most 7 (w > 0) or 8 (w < 0) transitions per weight
-constexpr int CCAP = 256;
+constexpr int MAX_EV = 1024;  // 8 slots per weight: at most 7 (w > 0) or 8 (w < 0) transitions
+constexpr int QCAP = 512;     // quadratic-form candidates per group
+constexpr int CCAP = 256;     // direct-rescoring shortlist per group
+constexpr int rcap_for(int E) { return E <= 8 ? 64 : (E == 16 ? 32 : 16); }  // surviving runs
 // |error of a quadratic-form value| <= ERR_REL * max_e (A_e + 2 B0_e s + C0_e s^2): the prefix
 // sums run over <= 1024 events with partial sums in [0, B0_e] / [0, C0_e], plus the 128-term
 // initial sums and the evaluation itself, i.e. < 1200 roundings of 2^-53 each.
@@ -44,24 +49,29 @@ constexpr double SEL_SLACK = 1e-12;
 
 template <int E>
 struct CandSmem {
+    static constexpr int RCAP = rcap_for(E);
     float w[G];
     float d[E * G];  // [e][i]
     uint32_t ev[MAX_EV];
-    uint8_t mag0[G];
+    uint8_t magp[BLOCK];
+    double part[3][4 * E];
     double A[E], B0[E], C0[E];
     double wtot[BLOCK / 64][8];
     double redd[BLOCK / 64];
     float redf[BLOCK / 64];
+    int redi[BLOCK / 64];
+    uint32_t run_lo[RCAP], run_hi[RCAP];
+    uint8_t qbuf[RCAP][G];
+    double run_B[RCAP][E], run_C[RCAP][E];
+    uint32_t q_b[QCAP];
+    double q_lo[QCAP];
     uint32_t cand_b[CCAP];
     double cand_F[CCAP];
     double pairF[BLOCK];
-    int n_ev;
-    int n_cand;
-    int overflow;
+    int n_runs, n_q, n_cand;
     uint32_t win_b;
     double win_F;
-    int win_state;  // 0 ok, 1 tie or overflow -> exhaustive
-    int win_count;
+    int win_state, win_count;
 };
 
 __device__ __forceinline__ double wave_min_d(double v) {
@@ -82,6 +92,17 @@ __device__ __forceinline__ double block_min_d(double v, double* red) {
     for (int k = 1; k < BLOCK / 64; ++k) r = red[k] < r ? red[k] : r;
     return r;
 }
+__device__ __forceinline__ int block_sum_i(int v, int* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int k = 0; k < BLOCK / 64; ++k) r += red[k];
+    return r;
+}
 
 // |q(w, s_b)| <= c  (exact, see the file comment)
 __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
@@ -89,18 +110,33 @@ __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
     return a < hs || (a == hs && (c & 1) == 0);
 }
 
-template <int E>
-struct Run {
-    double B[E], C[E];
-};
+// First pattern b with mag_at_most(a, c, b), given that it is false at the first pattern and
+// true at the last.  The boundary a/(c+1/2) rounded to binary16 lands within a pattern of it;
+// a short walk confirms the first true pattern and bisection covers anything else.
+__device__ __forceinline__ uint32_t first_at_most(float a, int c) {
+    const float tau = a / ((float)(2 * c + 1) * 0.5f);
+    uint32_t b = f32_to_half_bits_rne(tau);
+    b = b < BITS_FIRST + 1 ? BITS_FIRST + 1 : (b > BITS_LAST ? BITS_LAST : b);
+    for (int k = 0; k < 4; ++k) {
+        const bool here = mag_at_most(a, c, b), before = mag_at_most(a, c, b - 1);
+        if (here && !before) return b;
+        if (here) --b;   // b > BITS_FIRST + 0 always: the first pattern is false
+        else ++b;        // b < BITS_LAST always: the last pattern is true
+    }
+    uint32_t lo = BITS_FIRST, hi = BITS_LAST;  // false at lo, true at hi
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (mag_at_most(a, c, mid)) hi = mid;
+        else lo = mid;
+    }
+    return hi;
+}
 
 template <int E>
-__device__ __forceinline__ double quad_at(const CandSmem<E>& sm, const double (&B)[E], const double (&C)[E],
-                                          double s, double& err) {
-    double F = sm.A[0] + s * (C[0] * s - 2.0 * B[0]), mag = 0.0;
-#pragma unroll
+__device__ __forceinline__ double quad_run(const CandSmem<E>& sm, int r, double s, double& err) {
+    double F = sm.A[0] + s * (sm.run_C[r][0] * s - 2.0 * sm.run_B[r][0]), mag = 0.0;
     for (int e = 0; e < E; ++e) {
-        const double f = sm.A[e] + s * (C[e] * s - 2.0 * B[e]);
+        const double f = sm.A[e] + s * (sm.run_C[r][e] * s - 2.0 * sm.run_B[r][e]);
         F = f > F ? f : F;
         const double m = sm.A[e] + s * (sm.C0[e] * s + 2.0 * sm.B0[e]);
         mag = m > mag ? m : mag;
@@ -109,37 +145,16 @@ __device__ __forceinline__ double quad_at(const CandSmem<E>& sm, const double (&
     return F;
 }
 
-// lower bound of F over the continuous run [slo, shi] (before the error allowance)
-template <int E>
-__device__ __forceinline__ double run_lower_bound(const CandSmem<E>& sm, const double (&B)[E], const double (&C)[E],
-                                                  double slo, double shi) {
-    double lb = -__builtin_inf();
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        double s;
-        if (C[e] > 0.0) {
-            s = B[e] / C[e];
-            s = s < slo ? slo : (s > shi ? shi : s);
-        } else {
-            s = B[e] > 0.0 ? shi : slo;  // linear (C = 0): B >= 0 decreases towards shi
-        }
-        const double f = sm.A[e] + s * (C[e] * s - 2.0 * B[e]);
-        lb = f > lb ? f : lb;
-    }
-    return lb;
-}
-
-// Calls fn(b) for every candidate pattern of the run [blo, bhi]: the two ends, and the grid
+// Calls fn(b) for every candidate pattern of surviving run r: its two ends, and the grid
 // neighbours (+-2) of each vertex and each pairwise crossing that lies on the upper envelope.
 template <int E, typename Fn>
-__device__ __forceinline__ void run_candidates(const CandSmem<E>& sm, const double (&B)[E], const double (&C)[E],
-                                               uint32_t blo, uint32_t bhi, Fn&& fn) {
+__device__ void run_candidates(const CandSmem<E>& sm, int r, Fn&& fn) {
+    const uint32_t blo = sm.run_lo[r], bhi = sm.run_hi[r];
     fn(blo);
     if (bhi != blo) fn(bhi);
     if (bhi - blo < 2) return;
     const double slo = (double)half_bits_value(blo), shi = (double)half_bits_value(bhi);
     auto near = [&](double s) {
-        if (!(s >= slo && s <= shi)) return;
         const uint32_t b0 = f32_to_half_bits_rne((float)s);
         const uint32_t lo = b0 >= blo + 2 ? b0 - 2 : blo;
         const uint32_t hi = b0 + 2 <= bhi ? b0 + 2 : bhi;
@@ -148,47 +163,49 @@ __device__ __forceinline__ void run_candidates(const CandSmem<E>& sm, const doub
     };
     auto on_top = [&](double s, int e1, int e2) {
         double err;
-        const double F = quad_at<E>(sm, B, C, s, err);
+        const double F = quad_run<E>(sm, r, s, err);
         const double tol = 2.0 * err + SEL_SLACK * (F > 0.0 ? F : 0.0);
-        const double f1 = sm.A[e1] + s * (C[e1] * s - 2.0 * B[e1]);
-        const double f2 = sm.A[e2] + s * (C[e2] * s - 2.0 * B[e2]);
+        const double f1 = sm.A[e1] + s * (sm.run_C[r][e1] * s - 2.0 * sm.run_B[r][e1]);
+        const double f2 = sm.A[e2] + s * (sm.run_C[r][e2] * s - 2.0 * sm.run_B[r][e2]);
         return f1 >= F - tol && f2 >= F - tol;
     };
-#pragma unroll
     for (int e = 0; e < E; ++e) {
-        if (C[e] > 0.0) {
-            const double v = B[e] / C[e];
+        const double C = sm.run_C[r][e];
+        if (C > 0.0) {
+            const double v = sm.run_B[r][e] / C;
             if (v >= slo && v <= shi && on_top(v, e, e)) near(v);
         }
     }
     for (int e1 = 0; e1 < E; ++e1) {
         for (int e2 = e1 + 1; e2 < E; ++e2) {
-            const double a = C[e1] - C[e2], hb = B[e1] - B[e2], cc = sm.A[e1] - sm.A[e2];
-            double r[2];
-            int nr = 0;
+            const double a = sm.run_C[r][e1] - sm.run_C[r][e2];
+            const double hb = sm.run_B[r][e1] - sm.run_B[r][e2];
+            const double cc = sm.A[e1] - sm.A[e2];
+            double r0 = -1.0, r1 = -1.0;
             if (a == 0.0) {
-                if (hb != 0.0) r[nr++] = cc / (2.0 * hb);
+                if (hb != 0.0) r0 = cc / (2.0 * hb);
             } else {
                 const double disc = hb * hb - a * cc;
                 if (disc >= 0.0) {
                     const double sq = __builtin_sqrt(disc);
                     const double qq = hb + (hb >= 0.0 ? sq : -sq);
                     if (qq != 0.0) {
-                        r[nr++] = qq / a;
-                        r[nr++] = cc / qq;
+                        r0 = qq / a;
+                        r1 = cc / qq;
                     } else {
-                        r[nr++] = hb / a;
+                        r0 = hb / a;
                     }
                 }
             }
-            for (int k = 0; k < nr; ++k)
-                if (r[k] >= slo && r[k] <= shi && on_top(r[k], e1, e2)) near(r[k]);
+            if (r0 >= slo && r0 <= shi && on_top(r0, e1, e2)) near(r0);
+            if (r1 >= slo && r1 <= shi && on_top(r1, e1, e2)) near(r1);
         }
     }
 }
 
 template <int E>
 __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
+    constexpr int RCAP = CandSmem<E>::RCAP;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* wg = a.w + g * G;
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
@@ -196,7 +213,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     // ---- staging and input checks (environments a.E..E-1 are zero padding)
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.d[j] = j / G < a.E ? dg[j] : 0.0f;
-    if (tid == 0) { sm.n_ev = 0; sm.n_cand = 0; sm.overflow = 0; }
+    if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; }
     __syncthreads();
     float bad = 0.0f;
     if (tid < G && !__builtin_isfinite(sm.w[tid])) bad = 1.0f;
@@ -214,44 +231,37 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         return;
     }
 
-    // ---- 1. code transitions
-    for (int j = tid; j < MAX_EV; j += BLOCK) sm.ev[j] = 0xFFFFFFFFu;
-    __syncthreads();
-    if (tid < G) {
-        const float wi = sm.w[tid];
+    // ---- 1. code transitions: thread t handles weight t/2, thresholds c = 4(t&1) .. 4(t&1)+3,
+    //         into the fixed slots 8i + c (unused slots hold the padding key)
+    int nvalid = 0;
+    {
+        const int i = tid >> 1, c0 = 4 * (tid & 1);
+        const float wi = sm.w[i];
         const float aw = fabsf(wi);
-        uint32_t keys[8];
-        int nk = 0, m0 = 0;
-        if (wi != 0.0f) {
-            const int cmax = wi > 0.0f ? 6 : 7;
-            for (int c = 0; c <= cmax; ++c) {
-                if (mag_at_most(aw, c, BITS_FIRST)) continue;
+        const int cmax = wi > 0.0f ? 6 : 7;
+        int m0 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + k;
+            uint32_t key = 0xFFFFFFFFu;
+            if (wi != 0.0f && c <= cmax && !mag_at_most(aw, c, BITS_FIRST)) {
                 ++m0;  // the magnitude at the first pattern exceeds c
-                if (!mag_at_most(aw, c, BITS_LAST)) continue;
-                uint32_t lo = BITS_FIRST, hi = BITS_LAST;  // false at lo, true at hi
-                while (hi - lo > 1) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if (mag_at_most(aw, c, mid)) hi = mid;
-                    else lo = mid;
+                if (mag_at_most(aw, c, BITS_LAST)) {
+                    key = (first_at_most(aw, c) << 11) | ((uint32_t)i << 4) | (uint32_t)c;
+                    ++nvalid;
                 }
-                keys[nk++] = (hi << 11) | ((uint32_t)tid << 4) | (uint32_t)c;
             }
+            sm.ev[8 * i + c] = key;
         }
-        sm.mag0[tid] = (uint8_t)m0;
-        if (nk) {
-            const int base = atomicAdd(&sm.n_ev, nk);
-            for (int k = 0; k < nk; ++k) sm.ev[base + k] = keys[k];
-        }
+        sm.magp[tid] = (uint8_t)m0;
     }
-    __syncthreads();
-    const int n_ev = sm.n_ev;
+    const int n_ev = block_sum_i(nvalid, sm.redi);  // includes the barrier after the slots
 
-    // ---- 2a. sort the events (bitonic, ascending; padding sorts last)
-    int N = 2;
-    while (N < n_ev) N <<= 1;
-    for (int k = 2; k <= N; k <<= 1) {
+    // ---- 2a. sort the events (bitonic over all 1024 slots, ascending; padding sorts last)
+    for (int k = 2; k <= MAX_EV; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int idx = tid; idx < N / 2; idx += BLOCK) {
+#pragma unroll
+            for (int idx = tid; idx < MAX_EV / 2; idx += BLOCK) {
                 const int p = 2 * idx - (idx & (j - 1));
                 const int q = p + j;
                 const uint32_t x = sm.ev[p], y = sm.ev[q];
@@ -262,18 +272,28 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
     }
 
-    // ---- 2b. initial coefficients at the first pattern
-    if (tid < E) {
+    // ---- 2b. coefficients at the first pattern: A = sum d w^2, B0 = sum d |w| |q|, C0 = sum d q^2
+    if (tid < 4 * E) {
+        const int e = tid >> 2, q4 = tid & 3;
         double A = 0.0, B = 0.0, C = 0.0;
-        for (int i = 0; i < G; ++i) {
-            const double dv = (double)sm.d[tid * G + i];
+        for (int i = 32 * q4; i < 32 * q4 + 32; ++i) {
+            const double dv = (double)sm.d[e * G + i];
             const double wv = (double)sm.w[i];
-            const double m = (double)sm.mag0[i];
+            const double m = (double)(sm.magp[2 * i] + sm.magp[2 * i + 1]);
             A += dv * (wv * wv);
             B += dv * (fabs(wv) * m);
             C += dv * (m * m);
         }
-        sm.A[tid] = A; sm.B0[tid] = B; sm.C0[tid] = C;
+        sm.part[0][tid] = A; sm.part[1][tid] = B; sm.part[2][tid] = C;
+    }
+    __syncthreads();
+    if (tid < E) {
+        const double* p0 = sm.part[0] + 4 * tid;
+        const double* p1 = sm.part[1] + 4 * tid;
+        const double* p2 = sm.part[2] + 4 * tid;
+        sm.A[tid] = ((p0[0] + p0[1]) + p0[2]) + p0[3];
+        sm.B0[tid] = ((p1[0] + p1[1]) + p1[2]) + p1[3];
+        sm.C0[tid] = ((p2[0] + p2[1]) + p2[2]) + p2[3];
     }
     __syncthreads();
 
@@ -332,16 +352,46 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
     }
 
-    // Walk this thread's runs: run k starts at event k (after applying it) and ends one pattern
-    // before the next event; thread 0 also owns the run before the first event.
-    auto walk = [&](auto&& on_run) {
-        double B[E], C[E];
+    // ---- 3a. one walk over this thread's runs (run k starts at event k, after applying it, and
+    //          ends one pattern before the next event; thread 0 also owns the run before the
+    //          first event): the best end value (upper bound U) and each run's lower bound
+    //          max_e min f_e over the run, minus the error allowance
+    double U = __builtin_inf();
+    double my_lb[5];
+    uint32_t my_lo[5], my_hi[5];
+    int my_n = 0;
+    {
+        auto on_run = [&](uint32_t blo, uint32_t bhi) {
+            const double slo = (double)half_bits_value(blo), shi = (double)half_bits_value(bhi);
+            double Flo = -__builtin_inf(), Fhi = -__builtin_inf(), lb = -__builtin_inf();
+            double mlo = 0.0, mhi = 0.0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) { B[e] = curB[e]; C[e] = curC[e]; }
-        if (tid == 0) {
-            const uint32_t t0 = n_ev > 0 ? (sm.ev[0] >> 11) : (BITS_LAST + 1);
-            on_run(B, C, BITS_FIRST, t0 - 1);
-        }
+            for (int e = 0; e < E; ++e) {
+                const double fl = sm.A[e] + slo * (curC[e] * slo - 2.0 * curB[e]);
+                const double fh = sm.A[e] + shi * (curC[e] * shi - 2.0 * curB[e]);
+                Flo = fl > Flo ? fl : Flo;
+                Fhi = fh > Fhi ? fh : Fhi;
+                double sv;
+                if (curC[e] > 0.0) {
+                    sv = curB[e] / curC[e];
+                    sv = sv < slo ? slo : (sv > shi ? shi : sv);
+                } else {
+                    sv = curB[e] > 0.0 ? shi : slo;  // linear (C = 0): B >= 0 decreases towards shi
+                }
+                const double fv = sm.A[e] + sv * (curC[e] * sv - 2.0 * curB[e]);
+                lb = fv > lb ? fv : lb;
+                const double ml = sm.A[e] + slo * (sm.C0[e] * slo + 2.0 * sm.B0[e]);
+                const double mh = sm.A[e] + shi * (sm.C0[e] * shi + 2.0 * sm.B0[e]);
+                mlo = ml > mlo ? ml : mlo;
+                mhi = mh > mhi ? mh : mhi;
+            }
+            U = fmin(U, fmin(Flo + ERR_REL * mlo, Fhi + ERR_REL * mhi));
+            my_lb[my_n] = lb - 2.0 * ERR_REL * mhi;  // the magnitude bound grows with s
+            my_lo[my_n] = blo;
+            my_hi[my_n] = bhi;
+            ++my_n;
+        };
+        if (tid == 0) on_run(BITS_FIRST, (n_ev > 0 ? (sm.ev[0] >> 11) : (BITS_LAST + 1)) - 1);
         for (int k = e0; k < e0 + 4 && k < n_ev; ++k) {
             const uint32_t key = sm.ev[k];
             const int i = (key >> 4) & 127, c = key & 15;
@@ -349,60 +399,76 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const double dv = (double)sm.d[e * G + i];
-                B[e] -= dv * aw;
-                C[e] -= dv * (double)(2 * c + 1);
+                curB[e] -= dv * aw;
+                curC[e] -= dv * (double)(2 * c + 1);
             }
             const uint32_t t = key >> 11;
             const uint32_t tn = k + 1 < n_ev ? (sm.ev[k + 1] >> 11) : (BITS_LAST + 1);
-            if (tn > t) on_run(B, C, t, tn - 1);
+            if (tn > t) on_run(t, tn - 1);
         }
-    };
-
-    // ---- 3a. upper bound U from the run ends
-    double U = __builtin_inf();
-    walk([&](const double (&B)[E], const double (&C)[E], uint32_t blo, uint32_t bhi) {
-        double err;
-        const double f0 = quad_at<E>(sm, B, C, (double)half_bits_value(blo), err);
-        U = fmin(U, f0 + err);
-        const double f1 = quad_at<E>(sm, B, C, (double)half_bits_value(bhi), err);
-        U = fmin(U, f1 + err);
-    });
+    }
     U = block_min_d(U, sm.redd);
 
-    // ---- 3b. candidates of the runs that can hold the minimum: their best upper bound
-    auto survives = [&](const double (&B)[E], const double (&C)[E], uint32_t blo, uint32_t bhi) {
-        const double slo = (double)half_bits_value(blo), shi = (double)half_bits_value(bhi);
-        double err;
-        quad_at<E>(sm, B, C, shi, err);  // the magnitude bound grows with s
-        return run_lower_bound<E>(sm, B, C, slo, shi) - 2.0 * err <= U;
-    };
+    // ---- 3b. keep the runs whose lower bound can reach U, and recompute their coefficients
+    //          directly from the codes at the run's first pattern
+    for (int k = 0; k < my_n; ++k) {
+        if (my_lb[k] <= U) {
+            const int r = atomicAdd(&sm.n_runs, 1);
+            if (r < RCAP) { sm.run_lo[r] = my_lo[k]; sm.run_hi[r] = my_hi[k]; }
+        }
+    }
+    __syncthreads();
+    const int n_runs = sm.n_runs;
+    if (n_runs <= RCAP) {
+        for (int j = tid; j < n_runs * G; j += BLOCK) {
+            const int r = j / G, i = j % G;
+            sm.qbuf[r][i] = (uint8_t)fabsf(exact_code(sm.w[i], half_bits_value(sm.run_lo[r])));
+        }
+        __syncthreads();
+        for (int j = tid; j < n_runs * E; j += BLOCK) {
+            const int r = j / E, e = j % E;
+            double B = 0.0, C = 0.0;
+            for (int i = 0; i < G; ++i) {
+                const double dv = (double)sm.d[e * G + i];
+                const double q = (double)sm.qbuf[r][i];
+                B += dv * (fabs((double)sm.w[i]) * q);
+                C += dv * (q * q);
+            }
+            sm.run_B[r][e] = B;
+            sm.run_C[r][e] = C;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3c. candidates of the kept runs: ends, vertices and crossings on the upper envelope
     double M = __builtin_inf();
-    walk([&](const double (&B)[E], const double (&C)[E], uint32_t blo, uint32_t bhi) {
-        if (!survives(B, C, blo, bhi)) return;
-        run_candidates<E>(sm, B, C, blo, bhi, [&](uint32_t b) {
-            double err;
-            const double f = quad_at<E>(sm, B, C, (double)half_bits_value(b), err);
-            M = fmin(M, f + err);
-        });
-    });
+    if (n_runs <= RCAP) {
+        for (int r = tid; r < n_runs; r += BLOCK) {
+            run_candidates<E>(sm, r, [&](uint32_t b) {
+                double err;
+                const double f = quad_run<E>(sm, r, (double)half_bits_value(b), err);
+                M = fmin(M, f + err);
+                const int j = atomicAdd(&sm.n_q, 1);
+                if (j < QCAP) { sm.q_b[j] = b; sm.q_lo[j] = f - err; }
+            });
+        }
+    }
     M = block_min_d(M, sm.redd);
+    const int n_q = sm.n_q;
     const double Msel = M * (1.0 + SEL_SLACK);
 
-    // ---- 3c. shortlist: every candidate whose lower bound reaches the best upper bound
-    walk([&](const double (&B)[E], const double (&C)[E], uint32_t blo, uint32_t bhi) {
-        if (!survives(B, C, blo, bhi)) return;
-        run_candidates<E>(sm, B, C, blo, bhi, [&](uint32_t b) {
-            double err;
-            const double f = quad_at<E>(sm, B, C, (double)half_bits_value(b), err);
-            if (f - err <= Msel) {
-                const int j = atomicAdd(&sm.n_cand, 1);
-                if (j < CCAP) sm.cand_b[j] = b;
+    // ---- 3d. shortlist: every candidate whose lower bound reaches the best upper bound
+    if (n_runs <= RCAP && n_q <= QCAP) {
+        for (int j = tid; j < n_q; j += BLOCK) {
+            if (sm.q_lo[j] <= Msel) {
+                const int k = atomicAdd(&sm.n_cand, 1);
+                if (k < CCAP) sm.cand_b[k] = sm.q_b[j];
             }
-        });
-    });
+        }
+    }
     __syncthreads();
     const int n = sm.n_cand;
-    if (n > CCAP || n == 0) {
+    if (n_runs > RCAP || n_q > QCAP || n > CCAP || n == 0) {
         if (tid == 0) {
             const int j = atomicAdd(a.tie_count, 1);
             a.tie_list[j] = (int32_t)g;

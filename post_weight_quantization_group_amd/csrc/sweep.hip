@@ -4,8 +4,8 @@
 // scales (CliffQuant repository README, "What CliffQuant changes": the
 // independent reference enumerates every one of them; model card
 // "Verification").  Work split: one 256-thread workgroup per group; weights
-// and diagonals are staged in LDS; each wave takes chunks of 512 consecutive
-// scale patterns, eight per lane, and every lane runs the 128 weights against
+// and diagonals are staged in LDS; each wave takes chunks of 64*NS consecutive
+// scale patterns, NS per lane (8 up to E = 8), and every lane runs the 128 weights against
 // its four scales with per-environment accumulators in registers.
 //
 // Exactness.  The sweep runs in binary32 with a proven error bound and is a
@@ -14,14 +14,15 @@
 //     2^k -- the quotient and the codes are unchanged and every error term
 //     stays in the normal binary32 range (groups for which that cannot be
 //     guaranteed go to the binary64 sweep);
-//   * the code uses x = w' * RN(1/s'); it can differ from the exact code only
-//     when the quotient is within 17 binary32 ulps of a half-integer, which
-//     raises that term by at most 137 u (u = 2^-24) and never lowers it;
+//   * the code uses x = w' * inv with inv within 1 ulp of 1/s' (hardware
+//     reciprocal plus a Newton step), so |x~ - x| <= 3u|x|; it can differ from
+//     the exact code only within 26 u of a half-integer (|x| <= 8.5), which
+//     raises that term by at most 208 u (u = 2^-24) and never lowers it;
 //   * e = fma(-s', q, w') is exact unless clipped (then one rounding), and
 //     e^2 plus 128 fused multiply-adds put the sum within (1 +- u)^131 of the
 //     exact value.
-//   So the binary32 value F~ satisfies (1-131u) F <= F~ <= (1+268u) F, and
-//   every scale whose F~ is within the factor 1.00004 of the smallest F~ is
+//   So the binary32 value F~ satisfies (1-131u) F <= F~ <= (1+340u) F, and
+//   every scale whose F~ is within the factor 1.00004 (> 1 + 472u) of the smallest F~ is
 //   rescored in binary64 (same summation order as the definition's plain
 //   sequential sum), which decides the winner and the lower-bit-pattern tie.
 //   When the smallest F~ is 0 the group's zero-error scales are exact and the
@@ -33,9 +34,10 @@
 
 namespace cqk {
 
-constexpr int NS = 8;                        // scales per lane per chunk
-constexpr int CHUNK = 64 * NS;               // scales per wave per chunk
-constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;  // 62
+// Scales per lane per chunk: 8 keeps the E accumulators of every scale in registers up to
+// E = 8 at four waves per SIMD; larger E trades scales for accumulators.
+constexpr int ns_for(int E) { return E <= 8 ? 8 : (E == 16 ? 4 : 2); }
+constexpr int min_blocks_for(int E) { return E <= 4 ? 4 : (E <= 16 ? 3 : 2); }
 constexpr int CAP = 256;                     // shortlist capacity per group
 constexpr float SCREEN_RATIO = 1.00004f;
 constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
@@ -43,8 +45,8 @@ constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
 template <int E>
 struct SweepSmem {
     float w[G];
-    __align__(16) float wp[G];
-    float dt[G * E];  // [i][e]
+    __align__(16) float wp[G];        // pre-scaled weights (screen)
+    __align__(16) float dt[G * E];    // [i][e]
     float redf[4];
     uint64_t redk[4];
     uint32_t cand_b[CAP];
@@ -72,10 +74,10 @@ __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
 }
 
 // One chunk: every lane runs the 128 weights against its NS scales with the per-environment
-// sums in registers: q = rne(w' * RN(1/s')) (clipped when needed), e = fma(-s', q, w'),
-// e^2, then one fma per environment.  The weight and its E diagonals are LDS broadcasts
-// shared by all NS scales of the lane.
-template <int E, bool CLIP>
+// sums in registers: q = rne(w' * (1/s')) (clipped when CLIP), e = fma(-s', q, w'), e^2, then
+// one fma per environment.  The weight and its E diagonals are LDS broadcasts shared by all NS
+// scales of the lane.
+template <int E, int NS, bool CLIP>
 __device__ __forceinline__ void sweep_chunk_inner(const float* __restrict__ wp, const float* __restrict__ dt,
                                                   const float (&nsv)[NS], const float (&inv)[NS],
                                                   float (&acc)[NS][E]) {
@@ -226,6 +228,9 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     __syncthreads();
 
     // ---- binary32 screen over all 31,743 scales
+    constexpr int NS = ns_for(E);
+    constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
+    constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;
     const int lane = tid & 63, wave = tid >> 6;
     const float wmaxp = wmax * pk;
     uint64_t mk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
@@ -242,16 +247,18 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
             const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
             const float s = half_bits_value(b) * pk;
             nsv[t] = -s;
-            inv[t] = 1.0f / s;
+            // reciprocal within 1 binary32 ulp: hardware estimate plus one Newton step
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
         }
         // wave-uniform: can any weight clip at the chunk's smallest scale?
         const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
         if (wmaxp <= 7.25f * s0)
-            sweep_chunk_inner<E, false>(sm.wp, sm.dt, nsv, inv, acc);
+            sweep_chunk_inner<E, NS, false>(sm.wp, sm.dt, nsv, inv, acc);
         else
-            sweep_chunk_inner<E, true>(sm.wp, sm.dt, nsv, inv, acc);
+            sweep_chunk_inner<E, NS, true>(sm.wp, sm.dt, nsv, inv, acc);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
@@ -263,8 +270,9 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
                 Fm = fmaxf(Fm, v);
                 Ps = Ps + v;
             }
-            if (a.want_minimax) top3_insert(mk, key_of(Fm, b));
-            if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
+            const uint64_t km = key_of(Fm, b), kq = key_of(Ps, b);
+            if (a.want_minimax && km < mk[2]) top3_insert(mk, km);
+            if (a.want_pooled && kq < qk[2]) top3_insert(qk, kq);
         }
     }
 
@@ -347,7 +355,7 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
 }
 
 template <int E>
-__global__ __launch_bounds__(BLOCK) void sweep_f32_kernel(SweepArgs a) {
+__global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void sweep_f32_kernel(SweepArgs a) {
     __shared__ SweepSmem<E> sm;
     if (a.list) {
         const int cnt = *a.list_count;
