@@ -14,8 +14,10 @@ inline size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? CQ_OK : CQ_EHIP; }
 
-// Exhaustive-sweep workspace: [counter | pad][int32 queue of n_groups]
-size_t sweep_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u); }
+// Exhaustive-sweep workspace: [counter | pad][int32 queue of n_groups][slice parts]
+size_t sweep_ws(int64_t n) {
+    return ALIGN + round_up((size_t)n * 4u) + round_up(sizeof(cqk::SlicePart) * cqk::SLICE_PARTS);
+}
 // Candidate workspace: [tie counter | pad][int32 tie list][sweep workspace]
 size_t cand_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u) + sweep_ws(n); }
 
@@ -71,6 +73,7 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
         a.pscales = pooled_scales; a.pobjective = pooled_objective;
         a.fb_count = (int32_t*)ws;
         a.fb_list = (int32_t*)(ws + ALIGN);
+        a.parts = (cqk::SlicePart*)(ws + ALIGN + round_up((size_t)n_groups * 4u));
         a.want_minimax = 1;
         a.want_pooled = (pooled_scales || pooled_objective) ? 1 : 0;
         return hip_status(cqk::launch_sweep(a, E, n_groups, st));
@@ -90,6 +93,7 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
     a.fb_count = (int32_t*)sws;
     a.fb_list = (int32_t*)(sws + ALIGN);
+    a.parts = (cqk::SlicePart*)(sws + ALIGN + round_up((size_t)n_groups * 4u));
     a.want_minimax = 1;
     a.want_pooled = 0;
     a.mark_fallback = 1;
@@ -119,6 +123,7 @@ int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int
     a.codes = codes; a.pscales = scales; a.pobjective = objective;
     a.fb_count = (int32_t*)ws;
     a.fb_list = (int32_t*)(ws + ALIGN);
+    a.parts = (cqk::SlicePart*)(ws + ALIGN + round_up((size_t)n_groups * 4u));
     a.want_minimax = 0;
     a.want_pooled = 1;
     return hip_status(cqk::launch_sweep(a, E, n_groups, st));

@@ -5,6 +5,22 @@
 
 namespace cqk {
 
+// One slice's share of a group's binary32 screen when several workgroups split the scale range:
+// per policy (0 minimax, 1 pooled) the slice's best and second keys (value bits << 32 | pattern),
+// the keys within the screen ratio of the slice's best, and the smallest value it could not keep.
+constexpr int SLICE_KEYS = 128;
+struct SlicePart {
+    uint32_t status;  // 0 screened, 1 bad input, 2 outside the screen's range
+    uint32_t n[2];
+    uint32_t ov[2];   // binary32 bits of the smallest value not stored (0xFFFFFFFF: none)
+    uint32_t pad;
+    uint64_t m1[2], s2[2];
+    uint64_t keys[2][SLICE_KEYS];
+};
+constexpr int SLICE_PARTS = 2048;  // parts in a sweep workspace
+constexpr int LIST_SLICES = 8;     // slices per listed group
+constexpr int LIST_SLICED = SLICE_PARTS / LIST_SLICES;  // listed groups handled by slices
+
 struct SweepArgs {
     const float* w;
     const float* d;
@@ -25,6 +41,9 @@ struct SweepArgs {
     int want_minimax;
     int want_pooled;
     int mark_fallback;         // OR CQ_FLAG_FALLBACK into the flags written
+    SlicePart* parts;          // SLICE_PARTS entries of workspace
+    int slices;                // workgroups per group (set by the launcher)
+    int list_begin;            // indirect mode: first list entry this launch serves
 };
 
 // Exhaustive sweep (binary32 screen + binary64 rescoring + binary64 sweep of

@@ -59,6 +59,8 @@ struct SweepSmem {
     uint32_t win_b[2];
     double win_F[2];
     uint8_t win_flags[2];
+    uint32_t ovbits;
+    uint64_t mrg_m1[2];
 };
 
 __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
@@ -158,13 +160,16 @@ __device__ __forceinline__ void append_cand(uint32_t* cb, uint8_t* ct, int* n, u
     if (j < CAP) { cb[j] = b; ct[j] = tag; }
 }
 
+// ------------------------------------------------------------------ stages of one group
+// Stage w (definition order), the pre-scaled copy and d; check the inputs.  Returns 0 when the
+// binary32 screen can run, 1 for bad input, 2 when the group lies outside the screen's
+// guaranteed range.  The result is the same in every workgroup that stages the same group.
 template <int E>
-__device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
+__device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, float& pk_out, float& wmax_out) {
     const int tid = threadIdx.x;
     const float* wg = a.w + g * G;
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
-
-    // ---- staging and group checks (environments a.E..E-1 are zero padding)
+    // environments a.E..E-1 are zero padding
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
     __syncthreads();
@@ -189,20 +194,9 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     const float wmin_nz = block_min_f(wnz, sm.redf);
     const float dmax = block_max_f(dmx, sm.redf);
     const float dmin_nz = block_min_f(dnz, sm.redf);
+    if (bad != 0.0f) return 1;
 
-    if (bad != 0.0f) {
-        if (tid < G && a.codes) a.codes[g * G + tid] = 0;
-        if (tid == 0) {
-            if (a.scales) a.scales[g] = 0;
-            if (a.objective) a.objective[g] = __builtin_nan("");
-            if (a.pscales) a.pscales[g] = 0;
-            if (a.pobjective) a.pobjective[g] = __builtin_nan("");
-            if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
-        }
-        return;
-    }
-
-    // ---- power-of-two pre-scaling and the no-underflow / no-overflow guarantee
+    // power-of-two pre-scaling and the no-underflow / no-overflow guarantee
     int k = 0;
     if (wmax > 0.0f) {
         int ex;
@@ -215,27 +209,48 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
         const double e2 = elb * elb;
         safe = safe && e2 >= 0x1p-120 && (dmin_nz == __builtin_inff() || (double)dmin_nz * e2 >= 0x1p-120);
     }
-    if (!safe) {
-        if (tid == 0) {
-            const int j = atomicAdd(a.fb_count, 1);
-            a.fb_list[j] = (int32_t)g;
-        }
-        return;
-    }
+    if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
     if (tid < G) sm.wp[tid] = sm.w[tid] * pk;
     if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
     __syncthreads();
+    pk_out = pk;
+    wmax_out = wmax;
+    return 0;
+}
 
-    // ---- binary32 screen over all 31,743 scales
+__device__ __forceinline__ void write_bad(const SweepArgs& a, int64_t g) {
+    const int tid = threadIdx.x;
+    if (tid < G && a.codes) a.codes[g * G + tid] = 0;
+    if (tid == 0) {
+        if (a.scales) a.scales[g] = 0;
+        if (a.objective) a.objective[g] = __builtin_nan("");
+        if (a.pscales) a.pscales[g] = 0;
+        if (a.pobjective) a.pobjective[g] = __builtin_nan("");
+        if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
+    }
+}
+
+__device__ __forceinline__ void queue_fp64(const SweepArgs& a, int64_t g) {
+    if (threadIdx.x == 0) {
+        const int j = atomicAdd(a.fb_count, 1);
+        a.fb_list[j] = (int32_t)g;
+    }
+}
+
+// The binary32 screen over the chunks of one slice (chunk c belongs to wave c % 4 of slice
+// (c / 4) % S): each lane's best three (value, pattern) keys for minimax and for pooled.
+template <int E>
+__device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk, float wmax, int slice, int S,
+                            uint64_t (&mk)[3], uint64_t (&qk)[3]) {
     constexpr int NS = ns_for(E);
     constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
     constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float wmaxp = wmax * pk;
-    uint64_t mk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
-    uint64_t qk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
-    for (int c = wave; c < NCHUNK; c += BLOCK / 64) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
+    for (int c = wave + 4 * slice; c < NCHUNK; c += 4 * S) {
         float nsv[NS], inv[NS];
         float acc[NS][E];
         // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
@@ -275,8 +290,65 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
             if (a.want_pooled && kq < qk[2]) top3_insert(qk, kq);
         }
     }
+}
 
-    // ---- global best, runner-up and shortlist
+// Rescoring, the lower-bit-pattern rule and the outputs, once sm holds the shortlist
+// (sm.cand_*, sm.n_cand, sm.overflow) and, for the zero rule, sm.win_b / sm.win_flags.
+template <int E>
+__device__ void finish_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
+    const int tid = threadIdx.x;
+    __syncthreads();
+    const int n = sm.n_cand;
+    if (sm.overflow || n > CAP) {
+        queue_fp64(a, g);
+        return;
+    }
+    rescore<E>(sm, n, a.E);
+    if (tid == 0) {
+        for (int pol = 0; pol < 2; ++pol) {
+            const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+            if (!want) continue;
+            const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
+            if (sm.win_b[pol] != 0xFFFFFFFFu) {  // zero rule: value from rescoring
+                const uint32_t b = sm.win_b[pol];
+                const uint8_t f = sm.win_flags[pol];
+                pick_winner<E>(sm, n, tag, pol);
+                sm.win_b[pol] = b;
+                sm.win_flags[pol] = f;
+            } else {
+                pick_winner<E>(sm, n, tag, pol);
+            }
+        }
+    }
+    __syncthreads();
+    if (a.want_minimax) {
+        const uint32_t b = sm.win_b[0];
+        if (tid < G && a.codes) a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(b));
+        if (tid == 0) {
+            a.scales[g] = (uint16_t)b;
+            if (a.objective) a.objective[g] = sm.win_F[0];
+            if (a.flags) a.flags[g] = sm.win_flags[0] | (a.mark_fallback ? FLAG_FALLBACK : 0);
+        }
+    }
+    if (a.want_pooled && tid == 0) {
+        if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
+        if (a.pobjective) a.pobjective[g] = sm.win_F[1];
+        if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+    }
+    if (a.want_pooled && !a.want_minimax && tid < G && a.codes)
+        a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(sm.win_b[1]));
+}
+
+// One workgroup per group: screen everything, shortlist, finish.
+template <int E>
+__device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
+    const int tid = threadIdx.x;
+    float pk, wmax;
+    const int status = stage_group<E>(a, g, sm, pk, wmax);
+    if (status == 1) { write_bad(a, g); return; }
+    if (status == 2) { queue_fp64(a, g); return; }
+    uint64_t mk[3], qk[3];
+    screen_keys<E>(a, sm, pk, wmax, 0, 1, mk, qk);
     for (int pol = 0; pol < 2; ++pol) {
         const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
         if (!want) continue;
@@ -305,66 +377,153 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
         }
         __syncthreads();
     }
-    __syncthreads();
-    const int n = sm.n_cand;
-    if (sm.overflow || n > CAP) {
-        if (tid == 0) {
-            const int j = atomicAdd(a.fb_count, 1);
-            a.fb_list[j] = (int32_t)g;
-        }
+    finish_group<E>(a, g, sm);
+}
+
+// Slice `slice` of S of one group: screen its chunks and record, per policy, its best and
+// second keys and every key within the screen ratio of its own best (a superset of its share of
+// the group's shortlist, since the group's best is no larger).  A lane whose third key is inside
+// that bound may have dropped a fourth: its third value is recorded as the smallest value not kept.
+template <int E>
+__device__ void sweep_slice(const SweepArgs& a, int64_t g, int slice, int S, SlicePart* part, SweepSmem<E>& sm) {
+    const int tid = threadIdx.x;
+    float pk, wmax;
+    const int status = stage_group<E>(a, g, sm, pk, wmax);
+    if (status != 0) {
+        if (tid == 0) part->status = (uint32_t)status;
         return;
     }
-
-    // ---- binary64 rescoring and the lower-bit-pattern rule
-    rescore<E>(sm, n, a.E);
-    if (tid == 0) {
-        for (int pol = 0; pol < 2; ++pol) {
-            const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
-            if (!want) continue;
-            const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
-            if (sm.win_b[pol] != 0xFFFFFFFFu) {  // zero rule: value from rescoring
-                const uint32_t b = sm.win_b[pol];
-                const uint8_t f = sm.win_flags[pol];
-                pick_winner<E>(sm, n, tag, pol);
-                sm.win_b[pol] = b;
-                sm.win_flags[pol] = f;
-            } else {
-                pick_winner<E>(sm, n, tag, pol);
+    uint64_t mk[3], qk[3];
+    screen_keys<E>(a, sm, pk, wmax, slice, S, mk, qk);
+    for (int pol = 0; pol < 2; ++pol) {
+        const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+        if (!want) continue;
+        const uint64_t* kk = pol == 0 ? mk : qk;
+        const uint64_t M1 = block_min_u64(kk[0], sm.redk);
+        const uint64_t S2 = block_min_u64(kk[0] == M1 ? kk[1] : kk[0], sm.redk);
+        if (tid == 0) { sm.n_cand = 0; sm.ovbits = 0xFFFFFFFFu; }
+        __syncthreads();
+        const float m = key_value(M1);
+        const float T = m * SCREEN_RATIO;  // 0 when m == 0: only exact zeros are kept
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
+                if (r == 2) atomicMin(&sm.ovbits, (uint32_t)(kk[r] >> 32));
+                const int j = atomicAdd(&sm.n_cand, 1);
+                if (j < SLICE_KEYS) part->keys[pol][j] = kk[r];
+                else atomicMin(&sm.ovbits, (uint32_t)(kk[r] >> 32));
             }
         }
-    }
-    __syncthreads();
-
-    // ---- outputs
-    if (a.want_minimax) {
-        const uint32_t b = sm.win_b[0];
-        if (tid < G && a.codes) a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(b));
+        __syncthreads();
         if (tid == 0) {
-            a.scales[g] = (uint16_t)b;
-            if (a.objective) a.objective[g] = sm.win_F[0];
-            if (a.flags) a.flags[g] = sm.win_flags[0] | (a.mark_fallback ? FLAG_FALLBACK : 0);
+            part->m1[pol] = M1;
+            part->s2[pol] = S2;
+            part->n[pol] = (uint32_t)min(sm.n_cand, SLICE_KEYS);
+            part->ov[pol] = sm.ovbits;
         }
+        __syncthreads();
     }
-    if (a.want_pooled && tid == 0) {
-        if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
-        if (a.pobjective) a.pobjective[g] = sm.win_F[1];
-        if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+    if (tid == 0) part->status = 0;
+}
+
+// Merge the S parts of one group into its shortlist, then finish it.
+template <int E>
+__device__ void merge_group(const SweepArgs& a, int64_t g, int S, const SlicePart* parts, SweepSmem<E>& sm) {
+    const int tid = threadIdx.x;
+    const uint32_t status = parts[0].status;  // identical in every slice
+    if (status == 1) { write_bad(a, g); return; }
+    if (status == 2) { queue_fp64(a, g); return; }
+    const float* wg = a.w + g * G;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
+    if (tid < G) sm.w[tid] = wg[tid];
+    for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    __syncthreads();
+    for (int pol = 0; pol < 2; ++pol) {
+        const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+        if (!want) continue;
+        const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
+        if (tid == 0) {
+            uint64_t M1 = KEY_NONE, S2 = KEY_NONE;
+            uint32_t ov = 0xFFFFFFFFu;
+            for (int q = 0; q < S; ++q) {
+                const uint64_t x = parts[q].m1[pol], y = parts[q].s2[pol];
+                // keep the two smallest of all slices' best and second keys
+                if (x < M1) { S2 = M1 < y ? M1 : y; M1 = x; }
+                else if (x < S2) S2 = x;
+                if (y < S2 && y != M1) S2 = y;
+                ov = parts[q].ov[pol] < ov ? parts[q].ov[pol] : ov;
+            }
+            sm.mrg_m1[pol] = M1;
+            const float m = key_value(M1);
+            if (m == 0.0f) {
+                sm.win_b[pol] = key_bits(M1);
+                sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
+                append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(M1), tag);
+            } else {
+                sm.win_b[pol] = 0xFFFFFFFFu;
+                if (__uint_as_float(ov) <= m * SCREEN_RATIO) sm.overflow = 1;
+            }
+        }
+        __syncthreads();
+        const float m = key_value(sm.mrg_m1[pol]);
+        if (m != 0.0f) {
+            const float T = m * SCREEN_RATIO;
+            for (int j = tid; j < S * SLICE_KEYS; j += BLOCK) {
+                const int q = j / SLICE_KEYS, r = j % SLICE_KEYS;
+                if (r < (int)parts[q].n[pol]) {
+                    const uint64_t k = parts[q].keys[pol][r];
+                    if (key_value(k) <= T) append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(k), tag);
+                }
+            }
+        }
+        __syncthreads();
     }
-    if (a.want_pooled && !a.want_minimax && tid < G && a.codes)
-        a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(sm.win_b[1]));
+    finish_group<E>(a, g, sm);
 }
 
 template <int E>
 __global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void sweep_f32_kernel(SweepArgs a) {
     __shared__ SweepSmem<E> sm;
+    const int S = a.slices;
     if (a.list) {
+        // Listed groups (the count is on the device).  Sliced launch: entries below LIST_SLICED,
+        // each split over S workgroups (entry k, slice j on workgroup (k % lanes) * S + j, lanes =
+        // grid / S).  Unsliced launch: entries from list_begin on, one workgroup each.
         const int cnt = *a.list_count;
-        for (int k = blockIdx.x; k < cnt; k += gridDim.x) {
-            sweep_group<E>(a, (int64_t)a.list[k], sm);
-            __syncthreads();
+        const int lanes = gridDim.x / S;
+        const int sl = blockIdx.x % S;
+        if (S > 1) {
+            for (int k = blockIdx.x / S; k < min(cnt, LIST_SLICED); k += lanes) {
+                sweep_slice<E>(a, (int64_t)a.list[k], sl, S, a.parts + (int64_t)k * S + sl, sm);
+                __syncthreads();
+            }
+        } else {
+            for (int k = a.list_begin + blockIdx.x; k < cnt; k += gridDim.x) {
+                sweep_group<E>(a, (int64_t)a.list[k], sm);
+                __syncthreads();
+            }
         }
+    } else if (S > 1) {
+        const int64_t k = blockIdx.x / S;
+        sweep_slice<E>(a, k + a.group_offset, blockIdx.x % S, S, a.parts + blockIdx.x, sm);
     } else {
         sweep_group<E>(a, (int64_t)blockIdx.x + a.group_offset, sm);
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK) void sweep_merge_kernel(SweepArgs a, int n_direct) {
+    __shared__ SweepSmem<E> sm;
+    const int S = a.slices;
+    if (a.list) {
+        const int end = min(*a.list_count, LIST_SLICED);
+        for (int k = blockIdx.x; k < end; k += gridDim.x) {
+            merge_group<E>(a, (int64_t)a.list[k], S, a.parts + (int64_t)k * S, sm);
+            __syncthreads();
+        }
+    } else if ((int)blockIdx.x < n_direct) {
+        merge_group<E>(a, (int64_t)blockIdx.x + a.group_offset, S, a.parts + (int64_t)blockIdx.x * S, sm);
     }
 }
 
@@ -492,18 +651,47 @@ __global__ void zero_counter_kernel(int32_t* p) {
 }
 
 template <int E>
-static hipError_t launch_e(const SweepArgs& a, int64_t n_groups, int fb_blocks, hipStream_t st) {
+static hipError_t launch_e(const SweepArgs& a_in, int64_t n_groups, hipStream_t st) {
+    constexpr int NCHUNK = (N_SCALES + 64 * ns_for(E) - 1) / (64 * ns_for(E));
+    constexpr int S_MAX = NCHUNK / 4 < 15 ? NCHUNK / 4 : 15;  // every slice gets chunks for 4 waves
+    SweepArgs a = a_in;
+    const int fb_blocks = (int)(n_groups < 64 ? (n_groups > 0 ? n_groups : 1) : 64);
     hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
     if (a.list) {
-        hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
-    } else {
-        // grid.x is limited to 2^31-1 blocks: split very large batches
-        const int64_t step = 1ll << 30;
-        for (int64_t off = 0; off < n_groups; off += step) {
+        // listed groups (few, count unknown on the host): small looping grids
+        a.slices = LIST_SLICES;
+        const int lanes = (int)(n_groups < 32 ? n_groups : 32);
+        hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3(lanes * LIST_SLICES), dim3(BLOCK), 0, st, a);
+        hipLaunchKernelGGL(sweep_merge_kernel<E>, dim3(lanes), dim3(BLOCK), 0, st, a, 0);
+        if (n_groups > LIST_SLICED) {  // a long list: the rest one workgroup each
             SweepArgs b = a;
-            b.group_offset = off;
-            const int64_t n = n_groups - off < step ? n_groups - off : step;
-            hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+            b.slices = 1;
+            b.list_begin = LIST_SLICED;
+            const int64_t rest = n_groups - LIST_SLICED;
+            hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)(rest < 2048 ? rest : 2048)), dim3(BLOCK), 0, st, b);
+        }
+    } else {
+        // few groups: split each over S workgroups so that the whole GPU works on them
+        int S = 1;
+        if (n_groups < 1024) {
+            S = (int)((2048 + n_groups - 1) / n_groups);
+            S = S > S_MAX ? S_MAX : S;
+            while (S > 1 && n_groups * S > SLICE_PARTS) --S;
+        }
+        a.slices = S;
+        if (S > 1) {
+            hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)(n_groups * S)), dim3(BLOCK), 0, st, a);
+            hipLaunchKernelGGL(sweep_merge_kernel<E>, dim3((unsigned)n_groups), dim3(BLOCK), 0, st, a,
+                               (int)n_groups);
+        } else {
+            // grid.x is limited to 2^31-1 blocks: split very large batches
+            const int64_t step = 1ll << 30;
+            for (int64_t off = 0; off < n_groups; off += step) {
+                SweepArgs b = a;
+                b.group_offset = off;
+                const int64_t n = n_groups - off < step ? n_groups - off : step;
+                hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+            }
         }
     }
     hipLaunchKernelGGL(sweep_f64_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
@@ -511,16 +699,15 @@ static hipError_t launch_e(const SweepArgs& a, int64_t n_groups, int fb_blocks, 
 }
 
 hipError_t launch_sweep(const SweepArgs& a_in, int E, int64_t n_groups, hipStream_t st) {
-    const int fb_blocks = (int)(n_groups < 2048 ? (n_groups > 0 ? n_groups : 1) : 2048);
     SweepArgs a = a_in;
     a.E = E;
     switch (pad_envs(E)) {
-        case 1: return launch_e<1>(a, n_groups, fb_blocks, st);
-        case 2: return launch_e<2>(a, n_groups, fb_blocks, st);
-        case 4: return launch_e<4>(a, n_groups, fb_blocks, st);
-        case 8: return launch_e<8>(a, n_groups, fb_blocks, st);
-        case 16: return launch_e<16>(a, n_groups, fb_blocks, st);
-        case 32: return launch_e<32>(a, n_groups, fb_blocks, st);
+        case 1: return launch_e<1>(a, n_groups, st);
+        case 2: return launch_e<2>(a, n_groups, st);
+        case 4: return launch_e<4>(a, n_groups, st);
+        case 8: return launch_e<8>(a, n_groups, st);
+        case 16: return launch_e<16>(a, n_groups, st);
+        case 32: return launch_e<32>(a, n_groups, st);
         default: return hipErrorInvalidValue;
     }
 }

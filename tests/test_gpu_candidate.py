@@ -117,3 +117,29 @@ def test_candidate_odd_env_counts():
         sol = oracle.solve(w, d, 24, n_threads=threads())
         check_minimax(w, d, 24, c, sol)
         check_minimax(w, d, 24, x, sol)
+
+
+def test_many_fallbacks_take_both_list_paths():
+    """More tie groups than the sliced list path serves (256): all-zero and symmetric-pair
+    groups mixed with ordinary ones; every group must still match the exhaustive sweep."""
+    rng = np.random.default_rng(21)
+    n = 900
+    w = W.round_bf16(rng.normal(0, 0.02, (n, 128)).astype(np.float32))
+    d = rng.lognormal(0, 1, (n, 4, 128)).astype(np.float32)
+    zero = rng.random(n) < 0.4
+    w[zero] = 0.0
+    pairs = (~zero) & (rng.random(n) < 0.3)
+    for j in np.nonzero(pairs)[0]:
+        c = 2.0 ** -int(rng.integers(5, 11))
+        mult = np.array([1, 2, 3] + list(rng.integers(1, 4, 61)), np.float64)
+        w[j] = rng.permutation(np.concatenate([mult * c, -mult * c])).astype(np.float32)
+        d[j, 1] = d[j, 0]
+    c, x = _both(w, d, n)
+    flags = _agree(c, x, "fallback mix")
+    assert np.count_nonzero(flags & cq.FLAG_FALLBACK) > 256
+    bits = bits_np(c["scales"])
+    assert np.all(bits[zero] == 1)
+    sel = np.nonzero(~zero)[0][:40]
+    sol = oracle.solve(w[sel], d[sel], sel.size, n_threads=threads())
+    sub = {k: (v[torch.from_numpy(sel).cuda()] if v is not None else None) for k, v in c.items()}
+    check_minimax(w[sel], d[sel], sel.size, sub, sol)
