@@ -39,8 +39,8 @@ def cpu_baseline(k: int, budget_s: float) -> dict:
     import workloads as W
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     threads = max(1, min(cores, 256))
-    gids = W.sample_groups(k, 86016, salt=99)
-    w, d, _ = W.gather_matrix_groups(k, gids[: max(threads, 1) * 64])
+    gids = W.sample_groups(k, W.config(k).n_groups, salt=99)
+    w, d, _ = W.gather_matrix_groups(k, gids)
     # calibrate on one group per thread, then size the sample to the time budget
     t0 = time.perf_counter()
     oracle.solve(w[:threads], d[:threads], threads, n_threads=threads)
@@ -54,6 +54,138 @@ def cpu_baseline(k: int, budget_s: float) -> dict:
                       f"(minimax and pooled), {dt:.1f} s wall"}
 
 
+def _timed(fn, reps=1):
+    """(result of the last call, average ms) of fn() on the current stream, after one warm-up."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        out = fn()
+    b.record()
+    torch.cuda.synchronize()
+    return out, a.elapsed_time(b) / reps
+
+
+def measure_all_configs() -> dict:
+    """Throughput of every kernel on the five synthetic configs (reported beside the headline).
+
+    config 0/1/4: exhaustive (minimax + pooled in one sweep), candidate, AbsMax, pack, proxies;
+    config 2: candidate, pack and proxy on all 150 matrices, exhaustive on the seeded
+    10,000-group sample; config 3: exhaustive and candidate on all 262,144 groups.
+    """
+    import torch
+
+    import post_weight_quantization_group_amd as cq
+    import workloads as W
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def matrix_pass(k, mats_idx=None):
+        spec = W.config(k)
+        E = spec.E
+        idx = range(len(spec.matrices)) if mats_idx is None else mats_idx
+        tot = {"exhaustive_ms": 0.0, "candidate_ms": 0.0, "absmax_ms": 0.0, "pack_ms": 0.0, "proxy_ms": 0.0,
+               "groups": 0, "fallback": 0, "fp64_sweep": 0, "mismatch": 0}
+        module_means = {"minimax": [], "pooled": [], "absmax": []}
+        for m in idx:
+            mat = spec.matrices[m]
+            w, d, p = W.matrix_groups(*W.make_matrix(k, m))
+            n = w.shape[0]
+            wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
+            r, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="exhaustive", pooled=True))
+            tot["exhaustive_ms"] += ms
+            c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
+            tot["candidate_ms"] += ms
+            ab, ms = _timed(lambda: cq.baseline_scales(wt, dt, p, "absmax", objective=False))
+            tot["absmax_ms"] += ms
+            codes = r["codes"].reshape(mat.out, mat.inp)
+            sc = r["scales"].reshape(mat.out, mat.inp // 128)
+            _, ms = _timed(lambda: cq.pack_gptq_v1(codes, sc, mat.out, mat.inp))
+            tot["pack_ms"] += ms
+            off = torch.tensor([0, n], dtype=torch.int64, device=dev)
+            for name, sv in (("minimax", r["scales"]), ("pooled", r["pooled_scales"]), ("absmax", ab["scales"])):
+                (_, mm, _), ms = _timed(lambda: cq.proxy_worst_env_wmse(wt, dt, sv, off, p, per_group=False))
+                tot["proxy_ms"] += ms
+                module_means[name].append(float(mm.cpu()[0]))
+            f = c["flags"].cpu().numpy()
+            tot["fallback"] += int(np.count_nonzero(f & cq.FLAG_FALLBACK))
+            tot["fp64_sweep"] += int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP))
+            tot["mismatch"] += int(torch.count_nonzero(r["scales"] != c["scales"]).item())
+            tot["groups"] += n
+        out = {"groups": tot["groups"], "E": E,
+               "exhaustive_groups_per_s": tot["groups"] / tot["exhaustive_ms"] * 1e3,
+               "exhaustive_frac_fp32_peak": tot["groups"] / tot["exhaustive_ms"] * 1e3 * flops_per_group(E)
+               / (PEAK_FP32_TFLOPS * 1e12),
+               "candidate_groups_per_s": tot["groups"] / tot["candidate_ms"] * 1e3,
+               "candidate_hbm_frac": tot["groups"] * 642 / (tot["candidate_ms"] / 1e3) / 8e12,
+               "absmax_groups_per_s": tot["groups"] / tot["absmax_ms"] * 1e3,
+               "pack_ms": tot["pack_ms"], "pack_hbm_frac": tot["groups"] * 196 / (tot["pack_ms"] / 1e3) / 8e12,
+               "proxy_ms": tot["proxy_ms"],
+               "candidate_fallback_groups": tot["fallback"], "exhaustive_fp64_sweep_groups": tot["fp64_sweep"],
+               "candidate_vs_exhaustive_scale_mismatches": tot["mismatch"],
+               "proxy_module_macro": {k2: float(np.mean(v)) for k2, v in module_means.items()}}
+        return out
+
+    res["config0"] = matrix_pass(0)
+    res["config1"] = matrix_pass(1)
+    res["config4"] = matrix_pass(4)
+    # config 2: candidate + pack + proxy on every matrix, exhaustive on the 10,000-group sample
+    spec = W.config(2)
+    cand_ms = pack_ms = proxy_ms = 0.0
+    fb = n_all = 0
+    means = []
+    for m, mat in enumerate(spec.matrices):
+        w, d, p = W.matrix_groups(*W.make_matrix(2, m))
+        n = w.shape[0]
+        wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
+        c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
+        cand_ms += ms
+        codes = c["codes"].reshape(mat.out, mat.inp)
+        sc = c["scales"].reshape(mat.out, mat.inp // 128)
+        _, ms = _timed(lambda: cq.pack_gptq_v1(codes, sc, mat.out, mat.inp))
+        pack_ms += ms
+        off = torch.tensor([0, n], dtype=torch.int64, device=dev)
+        (_, mm, _), ms = _timed(lambda: cq.proxy_worst_env_wmse(wt, dt, c["scales"], off, p, per_group=False))
+        proxy_ms += ms
+        means.append(float(mm.cpu()[0]))
+        fb += int(np.count_nonzero(c["flags"].cpu().numpy() & cq.FLAG_FALLBACK))
+        n_all += n
+    gids = W.sample_groups(2, 10000)
+    ws_, ds_, _ = W.gather_matrix_groups(2, gids)
+    wt, dt = torch.from_numpy(ws_).to(dev), torch.from_numpy(ds_).to(dev)
+    r, ms_x = _timed(lambda: cq.quantize_groups(wt, dt, ws_.shape[0], method="exhaustive"))
+    c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, ws_.shape[0], method="candidate"))
+    res["config2"] = {"groups": n_all, "E": 4, "candidate_groups_per_s": n_all / cand_ms * 1e3,
+                      "candidate_hbm_frac": n_all * 642 / (cand_ms / 1e3) / 8e12,
+                      "candidate_ms": cand_ms, "candidate_fallback_groups": fb,
+                      "pack_ms": pack_ms, "pack_hbm_frac": n_all * 196 / (pack_ms / 1e3) / 8e12,
+                      "proxy_ms": proxy_ms, "proxy_module_macro_minimax": float(np.mean(means)),
+                      "sample_groups": int(ws_.shape[0]),
+                      "sample_exhaustive_groups_per_s": ws_.shape[0] / ms_x * 1e3,
+                      "sample_exhaustive_frac_fp32_peak": ws_.shape[0] / ms_x * 1e3 * flops_per_group(4)
+                      / (PEAK_FP32_TFLOPS * 1e12),
+                      "sample_candidate_vs_exhaustive_scale_mismatches":
+                          int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
+    # config 3: per-group diagonals
+    w3, d3, cat3, _ = W.make_groups(3)
+    n3 = w3.shape[0]
+    wt, dt = torch.from_numpy(w3).to(dev), torch.from_numpy(d3).to(dev)
+    del d3
+    r, ms_x = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="exhaustive", pooled=False))
+    c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="candidate"))
+    fl = c["flags"].cpu().numpy()
+    res["config3"] = {"groups": n3, "E": 8, "exhaustive_groups_per_s": n3 / ms_x * 1e3,
+                      "exhaustive_frac_fp32_peak": n3 / ms_x * 1e3 * flops_per_group(8) / (PEAK_FP32_TFLOPS * 1e12),
+                      "candidate_groups_per_s": n3 / ms_c * 1e3,
+                      "candidate_fallback_groups": int(np.count_nonzero(fl & cq.FLAG_FALLBACK)),
+                      "exhaustive_fp64_sweep_groups": int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)),
+                      "candidate_vs_exhaustive_scale_mismatches":
+                          int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +195,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-candidate", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also measure every kernel on the five synthetic configs (adds 'per_config')")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -206,6 +340,8 @@ def main():
                         "fp64_sweep": int(np.count_nonzero(flags & 16))},
         "wall_s": wall,
     }
+    if args.all_configs:
+        line["per_config"] = measure_all_configs()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
     print(json.dumps(line), flush=True)
