@@ -169,6 +169,7 @@ __device__ void run_candidates(const CandSmem<E>& sm, int r, Fn&& fn) {
         const double f2 = sm.A[e2] + s * (sm.run_C[r][e2] * s - 2.0 * sm.run_B[r][e2]);
         return f1 >= F - tol && f2 >= F - tol;
     };
+#pragma unroll 1
     for (int e = 0; e < E; ++e) {
         const double C = sm.run_C[r][e];
         if (C > 0.0) {
@@ -176,7 +177,9 @@ __device__ void run_candidates(const CandSmem<E>& sm, int r, Fn&& fn) {
             if (v >= slo && v <= shi && on_top(v, e, e)) near(v);
         }
     }
+#pragma unroll 1
     for (int e1 = 0; e1 < E; ++e1) {
+#pragma unroll 1
         for (int e2 = e1 + 1; e2 < E; ++e2) {
             const double a = sm.run_C[r][e1] - sm.run_C[r][e2];
             const double hb = sm.run_B[r][e1] - sm.run_B[r][e2];
@@ -297,22 +300,49 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
     __syncthreads();
 
-    // ---- 2c. block prefix sum of the coefficient changes; thread t owns events 4t..4t+3
-    double curB[E], curC[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) { curB[e] = sm.B0[e]; curC[e] = sm.C0[e]; }
+    // ---- 2c/3a. per batch of 4 environments: block prefix sum of the coefficient changes
+    //          (thread t owns events 4t..4t+3), then a walk over the thread's runs that folds
+    //          the batch into each run's end values, lower bound and magnitude bound.  Run k
+    //          starts at event k (after applying it) and ends one pattern before the next event;
+    //          thread 0 also owns the run before the first event.  Only 8 coefficients and the
+    //          per-run maxima stay in registers, whatever E is.
     const int e0 = 4 * tid;
+    // Fixed run slots of this thread: slot 0 is the run before the first event (thread 0 only),
+    // slot 1+k the run that starts at event e0+k (empty when the next event has the same pattern).
+    uint32_t r_lo[5], r_hi[5];
+    bool r_ok[5];
+    double r_flo[5], r_fhi[5], r_lb[5], r_mlo[5], r_mhi[5];
+    r_ok[0] = tid == 0;
+    r_lo[0] = BITS_FIRST;
+    r_hi[0] = (n_ev > 0 ? (sm.ev[0] >> 11) : (BITS_LAST + 1)) - 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int ev_k = e0 + k;
+        const uint32_t t = ev_k < n_ev ? (sm.ev[ev_k] >> 11) : 0u;
+        const uint32_t tn = ev_k + 1 < n_ev ? (sm.ev[ev_k + 1] >> 11) : (BITS_LAST + 1);
+        r_ok[k + 1] = ev_k < n_ev && tn > t;
+        r_lo[k + 1] = t;
+        r_hi[k + 1] = tn - 1;
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        r_flo[j] = -__builtin_inf(); r_fhi[j] = -__builtin_inf(); r_lb[j] = -__builtin_inf();
+        r_mlo[j] = 0.0; r_mhi[j] = 0.0;
+    }
+#pragma unroll 1
     for (int eb = 0; eb < E; eb += 4) {
+        constexpr int NB = E < 4 ? E : 4;  // environments in this batch
         double loc[8];
 #pragma unroll
         for (int v = 0; v < 8; ++v) loc[v] = 0.0;
-        for (int k = e0; k < e0 + 4 && k < n_ev; ++k) {
-            const uint32_t key = sm.ev[k];
-            const int i = (key >> 4) & 127, c = key & 15;
-            const double aw = fabs((double)sm.w[i]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                if (eb + v < E) {
+        for (int k = 0; k < 4; ++k) {
+            if (e0 + k < n_ev) {
+                const uint32_t key = sm.ev[e0 + k];
+                const int i = (key >> 4) & 127, c = key & 15;
+                const double aw = fabs((double)sm.w[i]);
+#pragma unroll
+                for (int v = 0; v < NB; ++v) {
                     const double dv = (double)sm.d[(eb + v) * G + i];
                     loc[v] -= dv * aw;
                     loc[4 + v] -= dv * (double)(2 * c + 1);
@@ -336,85 +366,71 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             for (int v = 0; v < 8; ++v) sm.wtot[wave][v] = inc[v];
         }
         __syncthreads();
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            double ex = __shfl_up(inc[v], 1, 64);
-            if (lane == 0) ex = 0.0;
-            for (int w2 = 0; w2 < wave; ++w2) ex += sm.wtot[w2][v];
-            inc[v] = ex;  // exclusive prefix at this thread's first event
-        }
+        double cB[4], cC[4];  // coefficients at this thread's first run
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            if (eb + v < E) {
-                curB[eb + v] += inc[v];
-                curC[eb + v] += inc[4 + v];
-            }
+            double exB = __shfl_up(inc[v], 1, 64), exC = __shfl_up(inc[4 + v], 1, 64);
+            if (lane == 0) { exB = 0.0; exC = 0.0; }
+            for (int w2 = 0; w2 < wave; ++w2) { exB += sm.wtot[w2][v]; exC += sm.wtot[w2][4 + v]; }
+            cB[v] = v < NB ? sm.B0[eb + v] + exB : 0.0;
+            cC[v] = v < NB ? sm.C0[eb + v] + exC : 0.0;
         }
-    }
-
-    // ---- 3a. one walk over this thread's runs (run k starts at event k, after applying it, and
-    //          ends one pattern before the next event; thread 0 also owns the run before the
-    //          first event): the best end value (upper bound U) and each run's lower bound
-    //          max_e min f_e over the run, minus the error allowance
-    double U = __builtin_inf();
-    double my_lb[5];
-    uint32_t my_lo[5], my_hi[5];
-    int my_n = 0;
-    {
-        auto on_run = [&](uint32_t blo, uint32_t bhi) {
-            const double slo = (double)half_bits_value(blo), shi = (double)half_bits_value(bhi);
-            double Flo = -__builtin_inf(), Fhi = -__builtin_inf(), lb = -__builtin_inf();
-            double mlo = 0.0, mhi = 0.0;
+        // fold this batch into run slot j with the current coefficients
+        auto fold = [&](int j) {
+            const double slo = (double)half_bits_value(r_lo[j]), shi = (double)half_bits_value(r_hi[j]);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const double fl = sm.A[e] + slo * (curC[e] * slo - 2.0 * curB[e]);
-                const double fh = sm.A[e] + shi * (curC[e] * shi - 2.0 * curB[e]);
-                Flo = fl > Flo ? fl : Flo;
-                Fhi = fh > Fhi ? fh : Fhi;
+            for (int v = 0; v < NB; ++v) {
+                const double A = sm.A[eb + v], B = cB[v], C = cC[v];
+                const double fl = A + slo * (C * slo - 2.0 * B);
+                const double fh = A + shi * (C * shi - 2.0 * B);
                 double sv;
-                if (curC[e] > 0.0) {
-                    sv = curB[e] / curC[e];
+                if (C > 0.0) {
+                    sv = B / C;
                     sv = sv < slo ? slo : (sv > shi ? shi : sv);
                 } else {
-                    sv = curB[e] > 0.0 ? shi : slo;  // linear (C = 0): B >= 0 decreases towards shi
+                    sv = B > 0.0 ? shi : slo;  // linear (C = 0): B >= 0 decreases towards shi
                 }
-                const double fv = sm.A[e] + sv * (curC[e] * sv - 2.0 * curB[e]);
-                lb = fv > lb ? fv : lb;
-                const double ml = sm.A[e] + slo * (sm.C0[e] * slo + 2.0 * sm.B0[e]);
-                const double mh = sm.A[e] + shi * (sm.C0[e] * shi + 2.0 * sm.B0[e]);
-                mlo = ml > mlo ? ml : mlo;
-                mhi = mh > mhi ? mh : mhi;
+                const double fv = A + sv * (C * sv - 2.0 * B);
+                const double ml = A + slo * (sm.C0[eb + v] * slo + 2.0 * sm.B0[eb + v]);
+                const double mh = A + shi * (sm.C0[eb + v] * shi + 2.0 * sm.B0[eb + v]);
+                r_flo[j] = fl > r_flo[j] ? fl : r_flo[j];
+                r_fhi[j] = fh > r_fhi[j] ? fh : r_fhi[j];
+                r_lb[j] = fv > r_lb[j] ? fv : r_lb[j];
+                r_mlo[j] = ml > r_mlo[j] ? ml : r_mlo[j];
+                r_mhi[j] = mh > r_mhi[j] ? mh : r_mhi[j];
             }
-            U = fmin(U, fmin(Flo + ERR_REL * mlo, Fhi + ERR_REL * mhi));
-            my_lb[my_n] = lb - 2.0 * ERR_REL * mhi;  // the magnitude bound grows with s
-            my_lo[my_n] = blo;
-            my_hi[my_n] = bhi;
-            ++my_n;
         };
-        if (tid == 0) on_run(BITS_FIRST, (n_ev > 0 ? (sm.ev[0] >> 11) : (BITS_LAST + 1)) - 1);
-        for (int k = e0; k < e0 + 4 && k < n_ev; ++k) {
-            const uint32_t key = sm.ev[k];
-            const int i = (key >> 4) & 127, c = key & 15;
-            const double aw = fabs((double)sm.w[i]);
+        if (r_ok[0]) fold(0);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const double dv = (double)sm.d[e * G + i];
-                curB[e] -= dv * aw;
-                curC[e] -= dv * (double)(2 * c + 1);
+        for (int k = 0; k < 4; ++k) {
+            if (e0 + k < n_ev) {
+                const uint32_t key = sm.ev[e0 + k];
+                const int i = (key >> 4) & 127, c = key & 15;
+                const double aw = fabs((double)sm.w[i]);
+#pragma unroll
+                for (int v = 0; v < NB; ++v) {
+                    const double dv = (double)sm.d[(eb + v) * G + i];
+                    cB[v] -= dv * aw;
+                    cC[v] -= dv * (double)(2 * c + 1);
+                }
             }
-            const uint32_t t = key >> 11;
-            const uint32_t tn = k + 1 < n_ev ? (sm.ev[k + 1] >> 11) : (BITS_LAST + 1);
-            if (tn > t) on_run(t, tn - 1);
+            if (r_ok[k + 1]) fold(k + 1);
         }
     }
+    // upper bound U from the run ends, and each run's lower bound minus its error allowance
+    double U = __builtin_inf();
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+        if (r_ok[j]) U = fmin(U, fmin(r_flo[j] + ERR_REL * r_mlo[j], r_fhi[j] + ERR_REL * r_mhi[j]));
     U = block_min_d(U, sm.redd);
 
     // ---- 3b. keep the runs whose lower bound can reach U, and recompute their coefficients
     //          directly from the codes at the run's first pattern
-    for (int k = 0; k < my_n; ++k) {
-        if (my_lb[k] <= U) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        if (r_ok[j] && r_lb[j] - 2.0 * ERR_REL * r_mhi[j] <= U) {  // the magnitude bound grows with s
             const int r = atomicAdd(&sm.n_runs, 1);
-            if (r < RCAP) { sm.run_lo[r] = my_lo[k]; sm.run_hi[r] = my_hi[k]; }
+            if (r < RCAP) { sm.run_lo[r] = r_lo[j]; sm.run_hi[r] = r_hi[j]; }
         }
     }
     __syncthreads();
@@ -532,8 +548,10 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
 }
 
+constexpr int cand_min_blocks(int E) { return E <= 4 ? 4 : (E == 8 ? 3 : (E == 16 ? 2 : 1)); }
+
 template <int E>
-__global__ __launch_bounds__(BLOCK) void candidate_kernel(CandArgs a, int64_t group_offset) {
+__global__ __launch_bounds__(BLOCK, cand_min_blocks(E)) void candidate_kernel(CandArgs a, int64_t group_offset) {
     __shared__ CandSmem<E> sm;
     candidate_group<E>(a, (int64_t)blockIdx.x + group_offset, sm);
 }

@@ -655,7 +655,7 @@ static hipError_t launch_e(const SweepArgs& a_in, int64_t n_groups, hipStream_t 
     constexpr int NCHUNK = (N_SCALES + 64 * ns_for(E) - 1) / (64 * ns_for(E));
     constexpr int S_MAX = NCHUNK / 4 < 15 ? NCHUNK / 4 : 15;  // every slice gets chunks for 4 waves
     SweepArgs a = a_in;
-    const int fb_blocks = (int)(n_groups < 64 ? (n_groups > 0 ? n_groups : 1) : 64);
+    const int fb_blocks = (int)(n_groups < 1024 ? (n_groups > 0 ? n_groups : 1) : 1024);
     hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
     if (a.list) {
         // listed groups (few, count unknown on the host): small looping grids
