@@ -260,19 +260,57 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
     const int n_ev = block_sum_i(nvalid, sm.redi);  // includes the barrier after the slots
 
-    // ---- 2a. sort the events (bitonic over all 1024 slots, ascending; padding sorts last)
-    for (int k = 2; k <= MAX_EV; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
+    // ---- 2a. sort the events (bitonic over all 1024 slots, ascending; padding sorts last).
+    //          Thread t holds positions 4t..4t+3 in registers: partners closer than 4 are in
+    //          the same thread, closer than 256 in the same wave (lane shuffles); only the
+    //          three stages with partners in another wave go through LDS.
+    {
+        uint32_t key[4];
 #pragma unroll
-            for (int idx = tid; idx < MAX_EV / 2; idx += BLOCK) {
-                const int p = 2 * idx - (idx & (j - 1));
-                const int q = p + j;
-                const uint32_t x = sm.ev[p], y = sm.ev[q];
-                const bool up = (p & k) == 0;
-                if ((x > y) == up) { sm.ev[p] = y; sm.ev[q] = x; }
+        for (int r = 0; r < 4; ++r) key[r] = sm.ev[4 * tid + r];
+#pragma unroll
+        for (int kk = 1; kk <= 10; ++kk) {
+            const int k = 1 << kk;
+#pragma unroll
+            for (int jj = kk - 1; jj >= 0; --jj) {
+                const int j = 1 << jj;
+                if (j < 4) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if ((r & j) == 0) {
+                            const bool up = ((4 * tid + r) & k) == 0;
+                            const uint32_t x = key[r], y = key[r + j];
+                            if ((x > y) == up) { key[r] = y; key[r + j] = x; }
+                        }
+                    }
+                } else {
+                    const int m = j >> 2;  // partner thread: tid ^ m
+                    const bool up = ((4 * tid) & k) == 0, lower = (tid & m) == 0;
+                    uint32_t other[4];
+                    if (j < 256) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) other[r] = __shfl_xor(key[r], m, 64);
+                    } else {
+                        __syncthreads();
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sm.ev[4 * tid + r] = key[r];
+                        __syncthreads();
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) other[r] = sm.ev[4 * (tid ^ m) + r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t lo = key[r] < other[r] ? key[r] : other[r];
+                        const uint32_t hi = key[r] < other[r] ? other[r] : key[r];
+                        key[r] = lower == up ? lo : hi;
+                    }
+                }
             }
-            __syncthreads();
         }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.ev[4 * tid + r] = key[r];
+        __syncthreads();
     }
 
     // ---- 2b. coefficients at the first pattern: A = sum d w^2, B0 = sum d |w| |q|, C0 = sum d q^2
