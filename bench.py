@@ -28,10 +28,24 @@ SCALES = 31743
 PEAK_FP32_TFLOPS = 157.3  # 256 CU x 4 SIMD x 16 lanes x 2 (dual fp32) x 2 (fma) x 2.4 GHz
 
 
-def flops_per_group(E: int) -> int:
-    """Algorithmic flops of one group's sweep: per scale and weight one quotient multiply,
+def flops_per_pattern(E: int) -> int:
+    """Algorithmic flops of one scale of one group's sweep: per weight one quotient multiply,
     a residual fma (2), a square (1) and E weighted fmas (2E)."""
-    return SCALES * 128 * (2 * E + 4)
+    return 128 * (2 * E + 4)
+
+
+def screened_patterns(w: np.ndarray) -> np.ndarray:
+    """Scale patterns the exhaustive sweep evaluates per group: 1 up to the first binary16 scale
+    >= 2 max|w| (every one when 2 max|w| > 65504).  From there on every code is 0 and the
+    objective is the same value at every pattern, so the lowest of them stands for all."""
+    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    t = 2.0 * np.abs(w.astype(np.float64)).max(axis=1)
+    return np.minimum(np.searchsorted(grid, t, side="left") + 1, SCALES)
+
+
+def sweep_flops(w: np.ndarray, E: int) -> float:
+    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]."""
+    return float(screened_patterns(w).sum()) * flops_per_pattern(E)
 
 
 def cpu_baseline(k: int, budget_s: float) -> dict:
@@ -87,12 +101,13 @@ def measure_all_configs() -> dict:
         E = spec.E
         idx = range(len(spec.matrices)) if mats_idx is None else mats_idx
         tot = {"exhaustive_ms": 0.0, "candidate_ms": 0.0, "absmax_ms": 0.0, "pack_ms": 0.0, "proxy_ms": 0.0,
-               "groups": 0, "fallback": 0, "fp64_sweep": 0, "mismatch": 0}
+               "groups": 0, "fallback": 0, "fp64_sweep": 0, "mismatch": 0, "flops": 0.0}
         module_means = {"minimax": [], "pooled": [], "absmax": []}
         for m in idx:
             mat = spec.matrices[m]
             w, d, p = W.matrix_groups(*W.make_matrix(k, m))
             n = w.shape[0]
+            tot["flops"] += sweep_flops(w, E)
             wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
             r, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="exhaustive", pooled=True))
             tot["exhaustive_ms"] += ms
@@ -116,8 +131,7 @@ def measure_all_configs() -> dict:
             tot["groups"] += n
         out = {"groups": tot["groups"], "E": E,
                "exhaustive_groups_per_s": tot["groups"] / tot["exhaustive_ms"] * 1e3,
-               "exhaustive_frac_fp32_peak": tot["groups"] / tot["exhaustive_ms"] * 1e3 * flops_per_group(E)
-               / (PEAK_FP32_TFLOPS * 1e12),
+               "exhaustive_frac_fp32_peak": tot["flops"] / (tot["exhaustive_ms"] / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
                "candidate_groups_per_s": tot["groups"] / tot["candidate_ms"] * 1e3,
                "candidate_hbm_frac": tot["groups"] * 642 / (tot["candidate_ms"] / 1e3) / 8e12,
                "absmax_groups_per_s": tot["groups"] / tot["absmax_ms"] * 1e3,
@@ -164,7 +178,7 @@ def measure_all_configs() -> dict:
                       "proxy_ms": proxy_ms, "proxy_module_macro_minimax": float(np.mean(means)),
                       "sample_groups": int(ws_.shape[0]),
                       "sample_exhaustive_groups_per_s": ws_.shape[0] / ms_x * 1e3,
-                      "sample_exhaustive_frac_fp32_peak": ws_.shape[0] / ms_x * 1e3 * flops_per_group(4)
+                      "sample_exhaustive_frac_fp32_peak": sweep_flops(ws_, 4) / (ms_x / 1e3)
                       / (PEAK_FP32_TFLOPS * 1e12),
                       "sample_candidate_vs_exhaustive_scale_mismatches":
                           int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
@@ -177,7 +191,7 @@ def measure_all_configs() -> dict:
     c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="candidate"))
     fl = c["flags"].cpu().numpy()
     res["config3"] = {"groups": n3, "E": 8, "exhaustive_groups_per_s": n3 / ms_x * 1e3,
-                      "exhaustive_frac_fp32_peak": n3 / ms_x * 1e3 * flops_per_group(8) / (PEAK_FP32_TFLOPS * 1e12),
+                      "exhaustive_frac_fp32_peak": sweep_flops(w3, 8) / (ms_x / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
                       "candidate_groups_per_s": n3 / ms_c * 1e3,
                       "candidate_fallback_groups": int(np.count_nonzero(fl & cq.FLAG_FALLBACK)),
                       "exhaustive_fp64_sweep_groups": int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)),
@@ -226,6 +240,7 @@ def main():
         n = w.shape[0]
         t = {
             "name": mat.name, "out": mat.out, "inp": mat.inp, "n": n, "p": p,
+            "flops": sweep_flops(w, E), "patterns": float(screened_patterns(w).mean()),
             "w": torch.from_numpy(w).to(dev), "d": torch.from_numpy(d).to(dev),
             "scales": torch.empty(n, dtype=torch.int16, device=dev),
             "codes": torch.empty((n, 128), dtype=torch.int8, device=dev),
@@ -279,7 +294,7 @@ def main():
                                   t["obj"], t["flags"], t["pscales"], t["pobj"], t["ws"])
             if record:
                 b.record(stream)
-                sweep_ev.append((a, b, t["n"]))
+                sweep_ev.append((a, b, t["n"], t["flops"]))
             if use_candidate:
                 cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.CANDIDATE, t["cscales"],
                                       t["ccodes"], t["cobj"], t["cflags"], None, None, t["cws"])
@@ -307,11 +322,12 @@ def main():
     value = n_total / (ms_step / 1e3)
 
     # dominant kernel: the exhaustive sweep call, per launch (one launch per matrix)
-    durs = [a.elapsed_time(b) for a, b, _ in sweep_ev]
-    groups = [n for _, _, n in sweep_ev]
+    durs = [a.elapsed_time(b) for a, b, _, _ in sweep_ev]
     avg_ms = float(np.mean(durs))
-    avg_groups = float(np.mean(groups))
-    achieved = flops_per_group(E) * avg_groups / (avg_ms / 1e3) / 1e12
+    avg_groups = float(np.mean([n for _, _, n, _ in sweep_ev]))
+    avg_flops = float(np.mean([f for _, _, _, f in sweep_ev]))
+    achieved = avg_flops / (avg_ms / 1e3) / 1e12
+    patterns = float(np.mean([t["patterns"] for t in mats]))
     flags = torch.cat([t["flags"] for t in mats]).cpu().numpy()
 
     line = {
@@ -334,7 +350,8 @@ def main():
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
                      "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
                      "launch_ms": avg_ms, "groups_per_launch": avg_groups,
-                     "flops_per_group": flops_per_group(E)},
+                     "flops_per_launch": avg_flops, "flops_per_pattern": flops_per_pattern(E),
+                     "patterns_per_group": patterns},
         "sweep_groups_per_s": avg_groups / (avg_ms / 1e3),
         "flag_counts": {"near_tie": int(np.count_nonzero(flags & 2)), "exact_tie": int(np.count_nonzero(flags & 4)),
                         "fp64_sweep": int(np.count_nonzero(flags & 16))},

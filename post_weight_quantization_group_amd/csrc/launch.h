@@ -13,7 +13,7 @@ struct SlicePart {
     uint32_t status;  // 0 screened, 1 bad input, 2 outside the screen's range
     uint32_t n[2];
     uint32_t ov[2];   // binary32 bits of the smallest value not stored (0xFFFFFFFF: none)
-    uint32_t pad;
+    uint32_t b_top;   // last pattern screened (the same in every slice)
     uint64_t m1[2], s2[2];
     uint64_t keys[2][SLICE_KEYS];
 };

@@ -1,12 +1,16 @@
 // Exhaustive FP16 scale sweep for gfx950.
 //
-// For every group the kernel evaluates all 31,743 positive finite binary16
+// For every group the kernel decides among all 31,743 positive finite binary16
 // scales (CliffQuant repository README, "What CliffQuant changes": the
 // independent reference enumerates every one of them; model card
-// "Verification").  Work split: one 256-thread workgroup per group; weights
-// and diagonals are staged in LDS; each wave takes chunks of 64*NS consecutive
-// scale patterns, NS per lane (8 up to E = 8), and every lane runs the 128 weights against
-// its four scales with per-environment accumulators in registers.
+// "Verification").  It evaluates every pattern up to the top pattern b_top, the
+// smallest scale >= 2 max|w|: from there on every code is 0, the objective is
+// the same binary64 value at every pattern, and b_top wins all those exact ties
+// by the lower-bit-pattern rule (about 40% of the grid on typical weights).
+// Work split: one 256-thread workgroup per group; weights and diagonals are
+// staged in LDS; each wave takes chunks of 64*NS consecutive scale patterns,
+// NS per lane (8 up to E = 8), and every lane runs the 128 weights against its
+// NS scales with per-environment accumulators in registers.
 //
 // Exactness.  The sweep runs in binary32 with a proven error bound and is a
 // screen only:
@@ -61,6 +65,7 @@ struct SweepSmem {
     uint8_t win_flags[2];
     uint32_t ovbits;
     uint64_t mrg_m1[2];
+    uint32_t b_top;                   // last pattern screened (top_pattern)
 };
 
 __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
@@ -155,6 +160,25 @@ __device__ void pick_winner(SweepSmem<E>& sm, int n, uint8_t tag, int slot) {
     sm.win_flags[slot] = (uint8_t)((count > 1 ? FLAG_NEAR_TIE : 0) | (tie ? FLAG_EXACT_TIE : 0));
 }
 
+// The smallest pattern whose scale is at least 2 max|w| (BITS_LAST when there is none).  From
+// there on every code is 0 (|w/s| <= 1/2 rounds to 0), so every residual is w itself and the
+// objective is the same binary64 value at every larger pattern: those patterns tie with this one
+// and lose to it by the lower-bit-pattern rule.  The sweep stops here.
+__device__ __forceinline__ uint32_t top_pattern(float wmax) {
+    const float t = 2.0f * wmax;
+    if (!(t <= 65504.0f)) return BITS_LAST;
+    uint32_t b = f32_to_half_bits_rne(t);
+    b = b < BITS_FIRST ? BITS_FIRST : (b > BITS_LAST ? BITS_LAST : b);
+    while (b > BITS_FIRST && half_bits_value(b - 1) >= t) --b;
+    while (b < BITS_LAST && half_bits_value(b) < t) ++b;
+    return b;
+}
+
+// Flags of a winner at the top pattern: every larger pattern ties with it exactly.
+__device__ __forceinline__ uint8_t top_tie_flags(uint32_t win, uint32_t b_top) {
+    return (win == b_top && b_top < BITS_LAST) ? (uint8_t)(FLAG_NEAR_TIE | FLAG_EXACT_TIE) : (uint8_t)0;
+}
+
 __device__ __forceinline__ void append_cand(uint32_t* cb, uint8_t* ct, int* n, uint32_t b, uint8_t tag) {
     const int j = atomicAdd(n, 1);
     if (j < CAP) { cb[j] = b; ct[j] = tag; }
@@ -212,7 +236,7 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
     if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
     if (tid < G) sm.wp[tid] = sm.w[tid] * pk;
-    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.b_top = top_pattern(wmax); }
     __syncthreads();
     pk_out = pk;
     wmax_out = wmax;
@@ -245,12 +269,13 @@ __device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk
                             uint64_t (&mk)[3], uint64_t (&qk)[3]) {
     constexpr int NS = ns_for(E);
     constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
-    constexpr int NCHUNK = (N_SCALES + CHUNK - 1) / CHUNK;
+    const uint32_t b_top = sm.b_top;
+    const int nchunk = (int)((b_top - BITS_FIRST) / CHUNK) + 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float wmaxp = wmax * pk;
 #pragma unroll
     for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
-    for (int c = wave + 4 * slice; c < NCHUNK; c += 4 * S) {
+    for (int c = wave + 4 * slice; c < nchunk; c += 4 * S) {
         float nsv[NS], inv[NS];
         float acc[NS][E];
         // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
@@ -259,7 +284,7 @@ __device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk
         const int rot = (lane + 5 * c) & 63;
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
+            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), b_top);
             const float s = half_bits_value(b) * pk;
             nsv[t] = -s;
             // reciprocal within 1 binary32 ulp: hardware estimate plus one Newton step
@@ -277,7 +302,7 @@ __device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
-            if (b > BITS_LAST) continue;
+            if (b > b_top) continue;
             float Fm = acc[t][0], Ps = acc[t][0];
 #pragma unroll
             for (int e = 1; e < E; ++e) {
@@ -327,13 +352,14 @@ __device__ void finish_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
         if (tid == 0) {
             a.scales[g] = (uint16_t)b;
             if (a.objective) a.objective[g] = sm.win_F[0];
-            if (a.flags) a.flags[g] = sm.win_flags[0] | (a.mark_fallback ? FLAG_FALLBACK : 0);
+            if (a.flags)
+                a.flags[g] = sm.win_flags[0] | top_tie_flags(b, sm.b_top) | (a.mark_fallback ? FLAG_FALLBACK : 0);
         }
     }
     if (a.want_pooled && tid == 0) {
         if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
         if (a.pobjective) a.pobjective[g] = sm.win_F[1];
-        if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+        if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1] | top_tie_flags(sm.win_b[1], sm.b_top);
     }
     if (a.want_pooled && !a.want_minimax && tid < G && a.codes)
         a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(sm.win_b[1]));
@@ -423,7 +449,10 @@ __device__ void sweep_slice(const SweepArgs& a, int64_t g, int slice, int S, Sli
         }
         __syncthreads();
     }
-    if (tid == 0) part->status = 0;
+    if (tid == 0) {
+        part->b_top = sm.b_top;
+        part->status = 0;
+    }
 }
 
 // Merge the S parts of one group into its shortlist, then finish it.
@@ -437,7 +466,7 @@ __device__ void merge_group(const SweepArgs& a, int64_t g, int S, const SlicePar
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
-    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.b_top = parts[0].b_top; }
     __syncthreads();
     for (int pol = 0; pol < 2; ++pol) {
         const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
@@ -579,10 +608,13 @@ __device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.dt[(j % G) * E + j / G] = j / G < a.E ? dg[j] : 0.0f;
     __syncthreads();
+    float wmax = 0.0f;
+    for (int i = 0; i < G; ++i) wmax = fmaxf(wmax, fabsf(sm.w[i]));
+    const uint32_t b_top = top_pattern(wmax);
     const double INF = __builtin_inf();
     double mv1 = INF, mv2 = INF, pv1 = INF, pv2 = INF;
     uint32_t mb1 = 0xFFFFFFFFu, mb2 = 0xFFFFFFFFu, pb1 = 0xFFFFFFFFu, pb2 = 0xFFFFFFFFu;
-    for (uint32_t b = BITS_FIRST + tid; b <= BITS_LAST; b += BLOCK) {
+    for (uint32_t b = BITS_FIRST + tid; b <= b_top; b += BLOCK) {
         const double s = (double)half_bits_value(b), inv = 1.0 / s;
         double Fe[E];
 #pragma unroll
@@ -621,7 +653,7 @@ __device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
             if (a.objective) a.objective[g] = bestF;
             if (a.flags)
                 a.flags[g] = FLAG_FP64_SWEEP | (secF == bestF ? (FLAG_EXACT_TIE | FLAG_NEAR_TIE) : 0) |
-                             (a.mark_fallback ? FLAG_FALLBACK : 0);
+                             top_tie_flags(bm, b_top) | (a.mark_fallback ? FLAG_FALLBACK : 0);
         }
     }
     if (a.want_pooled) {
@@ -629,7 +661,8 @@ __device__ void f64_sweep_group(const SweepArgs& a, int64_t g, F64Smem<E>& sm) {
             if (a.pscales) a.pscales[g] = (uint16_t)bp;
             if (a.pobjective) a.pobjective[g] = bestP;
             if (!a.want_minimax && a.flags)
-                a.flags[g] = FLAG_FP64_SWEEP | (secP == bestP ? (FLAG_EXACT_TIE | FLAG_NEAR_TIE) : 0);
+                a.flags[g] = FLAG_FP64_SWEEP | (secP == bestP ? (FLAG_EXACT_TIE | FLAG_NEAR_TIE) : 0) |
+                             top_tie_flags(bp, b_top);
         }
         if (!a.want_minimax && tid < G && a.codes)
             a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(bp));
@@ -653,7 +686,9 @@ __global__ void zero_counter_kernel(int32_t* p) {
 template <int E>
 static hipError_t launch_e(const SweepArgs& a_in, int64_t n_groups, hipStream_t st) {
     constexpr int NCHUNK = (N_SCALES + 64 * ns_for(E) - 1) / (64 * ns_for(E));
-    constexpr int S_MAX = NCHUNK / 4 < 15 ? NCHUNK / 4 : 15;  // every slice gets chunks for 4 waves
+    // Slices per group: the screen usually stops near 40% of the grid (the top pattern), so a
+    // group has about NCHUNK / 2 chunks; S_MAX gives each wave of each slice about one of them.
+    constexpr int S_MAX = NCHUNK / 8 < 15 ? NCHUNK / 8 : 15;
     SweepArgs a = a_in;
     const int fb_blocks = (int)(n_groups < 1024 ? (n_groups > 0 ? n_groups : 1) : 1024);
     hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);

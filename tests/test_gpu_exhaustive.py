@@ -80,6 +80,42 @@ def test_constructed_ties_and_edge_groups():
     assert np.all(flags[:4] & cq.FLAG_EXACT_TIE)
 
 
+def test_top_pattern_ranges_sliced_and_unsliced():
+    """Where the sweep stops (the first scale >= 2 max|w|): past the grid (2 max|w| > 65504,
+    every pattern screened), in the last binade, in the subnormal range, and after a lone
+    weight.  Twelve groups go through the sliced path; the same groups tiled to 1,200 go one
+    workgroup each and must give identical results."""
+    rng = np.random.default_rng(23)
+    ws = []
+    big = rng.normal(0, 3000, 128)
+    big[7] = 40000.0
+    ws.append(big)
+    mid = rng.normal(0, 2000, 128)
+    mid[3] = -15000.0
+    ws.append(mid)
+    ws.append(rng.uniform(-1, 1, 128) * 1e-6)
+    ws.append(rng.uniform(-1, 1, 128) * 3e-5)
+    lone = np.zeros(128)
+    lone[100] = 0.3
+    ws.append(lone)
+    for sd in (0.005, 0.02, 0.08, 0.5, 4.0, 100.0, 1000.0):
+        ws.append(rng.normal(0, sd, 128))
+    w = W.round_bf16(np.stack(ws).astype(np.float32))
+    n = w.shape[0]
+    d = rng.lognormal(0, 1, (n, 4, 128)).astype(np.float32)
+    r = _run(w, d, n)
+    sol = oracle.solve(w, d, n, n_threads=threads())
+    check_minimax(w, d, n, r, sol)
+    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
+    reps = 100
+    wt, dt = np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1))
+    rt = _run(wt, dt, n * reps)
+    for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
+        a = r[key].cpu().numpy()
+        b = rt[key].cpu().numpy().reshape((reps,) + a.shape)
+        assert np.all(b == a[None]), key
+
+
 def test_bad_inputs_are_flagged():
     rng = np.random.default_rng(3)
     w = rng.normal(0, 0.02, (4, 128)).astype(np.float32)

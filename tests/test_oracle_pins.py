@@ -5,6 +5,7 @@ formula: they use closed forms, library routines (numpy's float16), exact
 rational arithmetic, invariances and hand-computed values.
 """
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -231,6 +232,55 @@ def test_single_weight_takes_smallest_exact_scale(wv):
         if np.isfinite(h) and h > 0 and Fraction(float(h)) == s:
             exact.append(int(h.view(np.uint16)))
     assert int(r.mm_bits[0]) == min(exact) and r.mm_F1[0] == 0.0
+
+
+def _top_pattern(w):
+    """Smallest pattern whose binary16 value is >= 2 max|w|, or None when 2 max|w| > 65504."""
+    grid = _grid_values()
+    t = 2.0 * float(np.max(np.abs(w.astype(np.float64))))
+    j = int(np.searchsorted(grid, t, side="left"))
+    return None if j == grid.size else j + 1
+
+
+@pytest.mark.parametrize("case", ["config0", "large", "subnormal"])
+def test_scales_above_twice_max_weight_tie_exactly(case):
+    """From the first scale >= 2 max|w| on, |w/s| <= 1/2 rounds every code to 0, so the
+    objective is max_e sum_i d w^2 (the pooled one its mean) at every larger pattern, bitwise
+    the same value: the lower-bit-pattern rule never picks a pattern above that first one.
+    The exhaustive sweep stops there."""
+    if case == "config0":
+        w, d, p = workloads.matrix_groups(*workloads.make_matrix(0, 0))
+        groups = [(w[g], d[g % p]) for g in (0, 17, 100)]
+    elif case == "large":   # 2 max|w| = 3e4 lies inside the grid's last binade
+        rng = np.random.default_rng(4)
+        w = rng.normal(0, 2000, 128).astype(np.float32)
+        w[3] = 15000.0
+        groups = [(w, rng.lognormal(0, 1, (3, 128)).astype(np.float32))]
+    else:                   # 2 max|w| inside the subnormal range
+        rng = np.random.default_rng(5)
+        w = (rng.uniform(-1, 1, 128) * 1e-6).astype(np.float32)
+        groups = [(w, rng.lognormal(0, 1, (2, 128)).astype(np.float32))]
+    for wg, dg in groups:
+        bt = _top_pattern(wg)
+        assert bt is not None
+        F, P = oracle.curve(wg, dg)
+        assert np.all(F[bt - 1:] == F[bt - 1]) and np.all(P[bt - 1:] == P[bt - 1])
+        # closed form of the all-zero-code objective
+        w64 = wg.astype(np.float64)
+        Fe = [math.fsum(float(x) for x in dg[e].astype(np.float64) * w64 * w64) for e in range(dg.shape[0])]
+        assert F[bt - 1] == pytest.approx(max(Fe), rel=1e-13)
+        assert np.all(oracle.codes_at(wg, bt) == 0)
+        assert bt == 1 or np.any(oracle.codes_at(wg, bt - 1) != 0)
+        r = oracle.solve(wg[None, :], dg[None, :])
+        assert int(r.mm_bits[0]) <= bt and int(r.pl_bits[0]) <= bt
+
+
+def test_no_top_pattern_when_twice_max_weight_exceeds_the_grid():
+    """2 max|w| > 65504: no binary16 scale zeroes every code and the sweep covers the grid."""
+    w = np.zeros(128, np.float32)
+    w[0] = 40000.0
+    assert _top_pattern(w) is None
+    assert np.any(oracle.codes_at(w, 0x7BFF) != 0)
 
 
 # ---------------------------------------------------------------- P6: invariances
