@@ -43,9 +43,26 @@ def screened_patterns(w: np.ndarray) -> np.ndarray:
     return np.minimum(np.searchsorted(grid, t, side="left") + 1, SCALES)
 
 
+def nonzero_code_terms(w: np.ndarray) -> float:
+    """Terms (scale, weight) with a nonzero code over the screened patterns: weight i has a
+    nonzero code at scale s when s < 2|w_i|.  A code-0 term is d w^2 whatever the scale, so the
+    sweep sums those once; the others each take a quotient, a rounding, a residual, a square and
+    E weighted sums."""
+    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    per_w = np.searchsorted(grid, 2.0 * np.abs(w.astype(np.float64)), side="left")
+    top = screened_patterns(w)
+    return float(np.minimum(per_w, top[:, None]).sum())
+
+
 def sweep_flops(w: np.ndarray, E: int) -> float:
-    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]."""
-    return float(screened_patterns(w).sum()) * flops_per_pattern(E)
+    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]: 2E + 4 per term with
+    a nonzero code (a quotient multiply, a residual fma, a square and E weighted fmas)."""
+    return nonzero_code_terms(w) * (2 * E + 4)
+
+
+def full_grid_flops(n_groups: int, E: int) -> float:
+    """The same count for a plain sweep of every weight at every one of the 31,743 scales."""
+    return float(n_groups) * SCALES * flops_per_pattern(E)
 
 
 def cpu_baseline(k: int, budget_s: float) -> dict:
@@ -350,9 +367,10 @@ def main():
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
                      "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
                      "launch_ms": avg_ms, "groups_per_launch": avg_groups,
-                     "flops_per_launch": avg_flops, "flops_per_pattern": flops_per_pattern(E),
+                     "flops_per_launch": avg_flops, "flops_per_nonzero_code_term": 2 * E + 4,
                      "patterns_per_group": patterns},
         "sweep_groups_per_s": avg_groups / (avg_ms / 1e3),
+        "sweep_full_grid_equivalent_tflops": full_grid_flops(avg_groups, E) / (avg_ms / 1e3) / 1e12,
         "flag_counts": {"near_tie": int(np.count_nonzero(flags & 2)), "exact_tie": int(np.count_nonzero(flags & 4)),
                         "fp64_sweep": int(np.count_nonzero(flags & 16))},
         "wall_s": wall,

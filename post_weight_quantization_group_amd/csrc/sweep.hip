@@ -49,8 +49,13 @@ constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
 template <int E>
 struct SweepSmem {
     float w[G];
-    __align__(16) float wp[G];        // pre-scaled weights (screen)
-    __align__(16) float dt[G * E];    // [i][e]
+    __align__(16) float dt[G * E];    // [i][e], definition order (rescoring)
+    // screen order (sort by the clip key, see stage_group)
+    __align__(16) float ws[G];        // pre-scaled weights
+    __align__(16) float ds[G * E];    // their diagonals [r][e]
+    float ks[G];                      // clip keys, ascending
+    float qs[G];                      // the code a weight takes once it is clipped (7 or -8)
+    float kz[(G + 1) * E];            // kz[m][e]: binary32 sum of d w'^2 over the first m weights
     float redf[4];
     uint64_t redk[4];
     uint32_t cand_b[CAP];
@@ -80,26 +85,48 @@ __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
     }
 }
 
-// One chunk: every lane runs the 128 weights against its NS scales with the per-environment
+// Weights [i0, i1) of the screen order against the lane's NS scales, with the per-environment
 // sums in registers: q = rne(w' * (1/s')) (clipped when CLIP), e = fma(-s', q, w'), e^2, then
 // one fma per environment.  The weight and its E diagonals are LDS broadcasts shared by all NS
 // scales of the lane.
 template <int E, int NS, bool CLIP>
-__device__ __forceinline__ void sweep_chunk_inner(const float* __restrict__ wp, const float* __restrict__ dt,
-                                                  const float (&nsv)[NS], const float (&inv)[NS],
-                                                  float (&acc)[NS][E]) {
+__device__ __forceinline__ void sweep_range(const float* __restrict__ ws, const float* __restrict__ ds, int i0,
+                                            int i1, const float (&nsv)[NS], const float (&inv)[NS],
+                                            float (&acc)[NS][E]) {
 #pragma unroll 2
-    for (int i = 0; i < G; ++i) {
-        const float wi = wp[i];
+    for (int i = i0; i < i1; ++i) {
+        const float wi = ws[i];
         float di[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) di[e] = dt[i * E + e];
+        for (int e = 0; e < E; ++e) di[e] = ds[i * E + e];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const float x = wi * inv[t];
             float r = __builtin_rintf(x);
             if (CLIP) r = __builtin_amdgcn_fmed3f(r, -8.0f, 7.0f);
             const float ev = __builtin_fmaf(nsv[t], r, wi);
+            const float e2 = ev * ev;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
+        }
+    }
+}
+
+// Weights [i0, i1) whose code is the clipped one, qs (7 or -8), at every scale of the chunk:
+// e = fma(-s', q, w'), e^2, one fma per environment; no quotient.
+template <int E, int NS>
+__device__ __forceinline__ void sweep_range_clipped(const float* __restrict__ ws, const float* __restrict__ qs,
+                                                    const float* __restrict__ ds, int i0, int i1,
+                                                    const float (&nsv)[NS], float (&acc)[NS][E]) {
+#pragma unroll 2
+    for (int i = i0; i < i1; ++i) {
+        const float wi = ws[i], qi = qs[i];
+        float di[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) di[e] = ds[i * E + e];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const float ev = __builtin_fmaf(nsv[t], qi, wi);
             const float e2 = ev * ev;
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
@@ -235,8 +262,43 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
     }
     if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
-    if (tid < G) sm.wp[tid] = sm.w[tid] * pk;
     if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.b_top = top_pattern(wmax); }
+    // Screen order: ascending clip key K = w'/6.5 (w' > 0) or |w'|/7.5 (otherwise), ties by
+    // index.  For any chunk of scales [s_lo, s_hi], the weights whose code is 0 throughout, those
+    // that never clip, those that may clip and those whose code is 7 or -8 throughout are then
+    // four consecutive ranges of this order (screen_keys).
+    float wv = 0.0f, key = 0.0f;
+    if (tid < G) {
+        wv = sm.w[tid] * pk;
+        key = wv > 0.0f ? wv * (1.0f / 6.5f) : -wv * (1.0f / 7.5f);
+        sm.kz[tid] = key;  // scratch until the prefix sums
+    }
+    __syncthreads();
+    if (tid < G) {
+        int rank = 0;
+        for (int j = 0; j < G; ++j) {
+            const float kj = sm.kz[j];
+            rank += (kj < key || (kj == key && j < tid)) ? 1 : 0;
+        }
+        sm.ws[rank] = wv;
+        sm.ks[rank] = key;
+        sm.qs[rank] = wv > 0.0f ? 7.0f : -8.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) sm.ds[rank * E + e] = sm.dt[tid * E + e];
+    }
+    __syncthreads();
+    // kz[m][e]: the code-0 terms d e^2 = d w'^2 of the first m weights, e^2 rounded and then one
+    // fma each, as in the screen itself (a chunk starts its sums from kz of its code-0 range)
+    if (tid < E) {
+        float acc = 0.0f;
+        sm.kz[tid] = 0.0f;
+        for (int r = 0; r < G; ++r) {
+            const float v = sm.ws[r];
+            const float e2 = v * v;
+            acc = __builtin_fmaf(sm.ds[r * E + tid], e2, acc);
+            sm.kz[(r + 1) * E + tid] = acc;
+        }
+    }
     __syncthreads();
     pk_out = pk;
     wmax_out = wmax;
@@ -265,14 +327,14 @@ __device__ __forceinline__ void queue_fp64(const SweepArgs& a, int64_t g) {
 // The binary32 screen over the chunks of one slice (chunk c belongs to wave c % 4 of slice
 // (c / 4) % S): each lane's best three (value, pattern) keys for minimax and for pooled.
 template <int E>
-__device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk, float wmax, int slice, int S,
+__device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk, int slice, int S,
                             uint64_t (&mk)[3], uint64_t (&qk)[3]) {
     constexpr int NS = ns_for(E);
     constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
     const uint32_t b_top = sm.b_top;
     const int nchunk = (int)((b_top - BITS_FIRST) / CHUNK) + 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float wmaxp = wmax * pk;
+    const float k0 = sm.ks[lane], k1 = sm.ks[lane + 64];
 #pragma unroll
     for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
     for (int c = wave + 4 * slice; c < nchunk; c += 4 * S) {
@@ -290,15 +352,31 @@ __device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk
             // reciprocal within 1 binary32 ulp: hardware estimate plus one Newton step
             const float r0 = __builtin_amdgcn_rcpf(s);
             inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
         }
-        // wave-uniform: can any weight clip at the chunk's smallest scale?
-        const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
-        if (wmaxp <= 7.25f * s0)
-            sweep_chunk_inner<E, NS, false>(sm.wp, sm.dt, nsv, inv, acc);
-        else
-            sweep_chunk_inner<E, NS, true>(sm.wp, sm.dt, nsv, inv, acc);
+        // The chunk's weight ranges (wave-uniform).  With K~ within 2u of the exact key and
+        // 2^-20 margins on the thresholds:
+        //   K~ <= s_lo/15:       |w'| <= 7.5 K < s_lo/2, code 0 at every scale of the chunk;
+        //   K~ <  1.1333 s_lo:   x in (-8.5, 7.5) (7.367 s_lo or 8.5 s_lo bounds |w'|), never clipped;
+        //   K~ >  s_hi:          w' > 6.5 s_hi or w' < -7.5 s_hi, code 7 or -8 throughout;
+        //   otherwise:           the rounded code may clip.
+        const float s_lo = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        const float s_hi = half_bits_value(min(BITS_FIRST + (uint32_t)(c * CHUNK + CHUNK - 1), b_top)) * pk;
+        const float tz = s_lo * ((1.0f / 15.0f) * (1.0f - 0x1p-20f));
+        const float tu = s_lo * ((8.5f / 7.5f) * (1.0f - 0x1p-20f));
+        const float tc = s_hi * (1.0f + 0x1p-20f);
+        const int m_c = G - (int)(__popcll(__ballot(k0 > tc)) + __popcll(__ballot(k1 > tc)));
+        const int m_u = min(m_c, (int)(__popcll(__ballot(k0 < tu)) + __popcll(__ballot(k1 < tu))));
+        const int m_z = min(m_u, (int)(__popcll(__ballot(k0 <= tz)) + __popcll(__ballot(k1 <= tz))));
+        // code-0 weights: their terms are the same at every scale, summed once in kz
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float z = sm.kz[m_z * E + e];
+#pragma unroll
+            for (int t = 0; t < NS; ++t) acc[t][e] = z;
+        }
+        sweep_range<E, NS, false>(sm.ws, sm.ds, m_z, m_u, nsv, inv, acc);
+        sweep_range<E, NS, true>(sm.ws, sm.ds, m_u, m_c, nsv, inv, acc);
+        sweep_range_clipped<E, NS>(sm.ws, sm.qs, sm.ds, m_c, G, nsv, acc);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
@@ -374,7 +452,7 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     if (status == 1) { write_bad(a, g); return; }
     if (status == 2) { queue_fp64(a, g); return; }
     uint64_t mk[3], qk[3];
-    screen_keys<E>(a, sm, pk, wmax, 0, 1, mk, qk);
+    screen_keys<E>(a, sm, pk, 0, 1, mk, qk);
     for (int pol = 0; pol < 2; ++pol) {
         const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
         if (!want) continue;
@@ -420,7 +498,7 @@ __device__ void sweep_slice(const SweepArgs& a, int64_t g, int slice, int S, Sli
         return;
     }
     uint64_t mk[3], qk[3];
-    screen_keys<E>(a, sm, pk, wmax, slice, S, mk, qk);
+    screen_keys<E>(a, sm, pk, slice, S, mk, qk);
     for (int pol = 0; pol < 2; ++pol) {
         const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
         if (!want) continue;
