@@ -137,6 +137,29 @@ __device__ __forceinline__ float block_min_f(float v, float* red) {
     return r;
 }
 
+// Block-wide maxima of N values at once, in one barrier round; `red` holds >= 4 * N slots.
+template <int N>
+__device__ __forceinline__ void block_max_fn(float (&v)[N], float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] = fmaxf(v[k], __shfl_xor(v[k], o, 64));
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) red[(threadIdx.x >> 6) * N + k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        float r = red[k];
+#pragma unroll
+        for (int w = 1; w < BLOCK / 64; ++w) r = fmaxf(r, red[w * N + k]);
+        v[k] = r;
+    }
+}
+
 // Key ordering (value, bit pattern) lexicographically for non-negative floats.
 __device__ __forceinline__ uint64_t key_of(float v, uint32_t b) {
     return ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)b;

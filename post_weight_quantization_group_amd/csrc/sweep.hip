@@ -55,8 +55,8 @@ struct SweepSmem {
     __align__(16) float ds[G * E];    // their diagonals [r][e]
     float ks[G];                      // clip keys, ascending
     float qs[G];                      // the code a weight takes once it is clipped (7 or -8)
-    float kz[(G + 1) * E];            // kz[m][e]: binary32 sum of d w'^2 over the first m weights
-    float redf[4];
+    __align__(16) float kz[(G + 1) * E];  // kz[m][e]: binary32 sum of d w'^2 over the first m weights
+    float redf[4 * 5];
     uint64_t redk[4];
     uint32_t cand_b[CAP];
     uint8_t cand_tag[CAP];
@@ -65,6 +65,7 @@ struct SweepSmem {
     double pairF[BLOCK];
     int n_cand;
     int overflow;
+    int next_chunk;                   // the screen's work counter (chunks handed to waves)
     uint32_t win_b[2];
     double win_F[2];
     uint8_t win_flags[2];
@@ -239,13 +240,10 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
             if (v > 0.0f) dnz = fminf(dnz, v);
         }
     }
-    bad = block_max_f(bad, sm.redf);
-    if (bad != 0.0f) aw = 0.0f;
-    const float wmax = block_max_f(aw, sm.redf);
-    const float wmin_nz = block_min_f(wnz, sm.redf);
-    const float dmax = block_max_f(dmx, sm.redf);
-    const float dmin_nz = block_min_f(dnz, sm.redf);
-    if (bad != 0.0f) return 1;
+    float red[5] = {bad, aw, -wnz, dmx, -dnz};  // minima as maxima of negations
+    block_max_fn<5>(red, sm.redf);
+    if (red[0] != 0.0f) return 1;
+    const float wmax = red[1], wmin_nz = -red[2], dmax = red[3], dmin_nz = -red[4];
 
     // power-of-two pre-scaling and the no-underflow / no-overflow guarantee
     int k = 0;
@@ -262,7 +260,7 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
     }
     if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
-    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.b_top = top_pattern(wmax); }
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.next_chunk = 0; sm.b_top = top_pattern(wmax); }
     // Screen order: ascending clip key K = w'/6.5 (w' > 0) or |w'|/7.5 (otherwise), ties by
     // index.  For any chunk of scales [s_lo, s_hi], the weights whose code is 0 throughout, those
     // that never clip, those that may clip and those whose code is 7 or -8 throughout are then
@@ -274,12 +272,28 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
         sm.kz[tid] = key;  // scratch until the prefix sums
     }
     __syncthreads();
-    if (tid < G) {
-        int rank = 0;
-        for (int j = 0; j < G; ++j) {
-            const float kj = sm.kz[j];
-            rank += (kj < key || (kj == key && j < tid)) ? 1 : 0;
+    int* rk = reinterpret_cast<int*>(sm.pairF);  // scratch: partial ranks (rescoring comes later)
+    {
+        // rank = number of weights ordered before this one; each half of the block counts over
+        // one half of the keys
+        const int i = tid & (G - 1), h = tid >> 7;
+        const float ki = sm.kz[i];
+        const float4* k4 = reinterpret_cast<const float4*>(sm.kz + (G / 2) * h);
+        int cnt = 0;
+#pragma unroll 4
+        for (int q = 0; q < G / 8; ++q) {
+            const float4 v = k4[q];
+            const int j = (G / 2) * h + 4 * q;
+            cnt += (v.x < ki || (v.x == ki && j < i)) ? 1 : 0;
+            cnt += (v.y < ki || (v.y == ki && j + 1 < i)) ? 1 : 0;
+            cnt += (v.z < ki || (v.z == ki && j + 2 < i)) ? 1 : 0;
+            cnt += (v.w < ki || (v.w == ki && j + 3 < i)) ? 1 : 0;
         }
+        rk[tid] = cnt;
+    }
+    __syncthreads();
+    if (tid < G) {
+        const int rank = rk[tid] + rk[tid + G];
         sm.ws[rank] = wv;
         sm.ks[rank] = key;
         sm.qs[rank] = wv > 0.0f ? 7.0f : -8.0f;
@@ -290,13 +304,19 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
     // kz[m][e]: the code-0 terms d e^2 = d w'^2 of the first m weights, e^2 rounded and then one
     // fma each, as in the screen itself (a chunk starts its sums from kz of its code-0 range)
     if (tid < E) {
+        constexpr int PB = 8;
         float acc = 0.0f;
         sm.kz[tid] = 0.0f;
-        for (int r = 0; r < G; ++r) {
-            const float v = sm.ws[r];
-            const float e2 = v * v;
-            acc = __builtin_fmaf(sm.ds[r * E + tid], e2, acc);
-            sm.kz[(r + 1) * E + tid] = acc;
+        for (int r0 = 0; r0 < G; r0 += PB) {
+            float wb[PB], db[PB];  // loads first, so that they overlap
+#pragma unroll
+            for (int q = 0; q < PB; ++q) { wb[q] = sm.ws[r0 + q]; db[q] = sm.ds[(r0 + q) * E + tid]; }
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                const float e2 = wb[q] * wb[q];
+                acc = __builtin_fmaf(db[q], e2, acc);
+                sm.kz[(r0 + q + 1) * E + tid] = acc;
+            }
         }
     }
     __syncthreads();
@@ -324,20 +344,26 @@ __device__ __forceinline__ void queue_fp64(const SweepArgs& a, int64_t g) {
     }
 }
 
-// The binary32 screen over the chunks of one slice (chunk c belongs to wave c % 4 of slice
-// (c / 4) % S): each lane's best three (value, pattern) keys for minimax and for pooled.
+// The binary32 screen over the chunks of one slice (the chunks c with c % S == slice): each
+// lane's best three (value, pattern) keys for minimax and for pooled.  Waves take the slice's
+// chunks in ascending order from a counter in LDS: chunk costs differ (low scales keep every
+// weight busy, high ones are mostly code-0 sums), and the costly ones go first.
 template <int E>
-__device__ void screen_keys(const SweepArgs& a, const SweepSmem<E>& sm, float pk, int slice, int S,
+__device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int slice, int S,
                             uint64_t (&mk)[3], uint64_t (&qk)[3]) {
     constexpr int NS = ns_for(E);
     constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
     const uint32_t b_top = sm.b_top;
     const int nchunk = (int)((b_top - BITS_FIRST) / CHUNK) + 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const float k0 = sm.ks[lane], k1 = sm.ks[lane + 64];
 #pragma unroll
     for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
-    for (int c = wave + 4 * slice; c < nchunk; c += 4 * S) {
+    for (;;) {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&sm.next_chunk, 1);
+        const int c = slice + S * __builtin_amdgcn_readfirstlane(k);
+        if (c >= nchunk) break;
         float nsv[NS], inv[NS];
         float acc[NS][E];
         // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
