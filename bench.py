@@ -65,6 +65,36 @@ def full_grid_flops(n_groups: int, E: int) -> float:
     return float(n_groups) * SCALES * flops_per_pattern(E)
 
 
+def sweep_traffic(config: int):
+    """HBM bytes per sweep launch from the committed counter summary (FETCH_SIZE and WRITE_SIZE
+    passes, each scaled by a 256 MiB device copy), or None when that summary is missing, covers
+    another workload, or was taken on sweep sources other than the current ones."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "sweep_f32_config1_hbm_counters.md")
+    if config != 1 or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    h = re.search(r"^sweep_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not t or not h:
+        return None
+    return int(t.group(1)) if sweep_sources_hash() == h.group(1) else None
+
+
+def sweep_sources_hash() -> str:
+    """sha256 of the sweep's sources (sweep.hip, device.h, launch.h) with comments and blank
+    space removed: a change of comments alone leaves the kernel, and its counters, as they were."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "post_weight_quantization_group_amd", "csrc")
+    text = "".join(open(os.path.join(csrc, f)).read() for f in ("sweep.hip", "device.h", "launch.h"))
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def cpu_baseline(k: int, budget_s: float) -> dict:
     import oracle
     import workloads as W
@@ -364,7 +394,7 @@ def main():
                    "matrices": [f"{t['name']} {t['out']}x{t['inp']}" for t in mats],
                    "candidate_solver_in_step": use_candidate},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": sweep_traffic(args.config),
                      "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
                      "launch_ms": avg_ms, "groups_per_launch": avg_groups,
                      "flops_per_launch": avg_flops, "flops_per_nonzero_code_term": 2 * E + 4,

@@ -8,9 +8,12 @@
 // the same binary64 value at every pattern, and b_top wins all those exact ties
 // by the lower-bit-pattern rule (about 40% of the grid on typical weights).
 // Work split: one 256-thread workgroup per group; weights and diagonals are
-// staged in LDS; each wave takes chunks of 64*NS consecutive scale patterns,
-// NS per lane (8 up to E = 8), and every lane runs the 128 weights against its
-// NS scales with per-environment accumulators in registers.
+// staged in LDS, sorted by a clip key; each wave takes chunks of 64*NS
+// consecutive scale patterns, NS per lane (8 up to E = 8), with the
+// per-environment sums in registers.  Within a chunk the sorted weights fall
+// into four consecutive ranges: code 0 at every scale of the chunk (their
+// terms d w^2 enter as one prefix sum), never clipped, possibly clipped, and
+// code 7 or -8 throughout (no quotient needed).
 //
 // Exactness.  The sweep runs in binary32 with a proven error bound and is a
 // screen only:
@@ -23,8 +26,9 @@
 //     the exact code only within 26 u of a half-integer (|x| <= 8.5), which
 //     raises that term by at most 208 u (u = 2^-24) and never lowers it;
 //   * e = fma(-s', q, w') is exact unless clipped (then one rounding), and
-//     e^2 plus 128 fused multiply-adds put the sum within (1 +- u)^131 of the
-//     exact value.
+//     every term meets at most 129 more roundings on its way into the sum
+//     (e^2, then one fma per later weight, the code-0 prefix sums included),
+//     which puts the sum within (1 +- u)^131 of the exact value.
 //   So the binary32 value F~ satisfies (1-131u) F <= F~ <= (1+340u) F, and
 //   every scale whose F~ is within the factor 1.00004 (> 1 + 472u) of the smallest F~ is
 //   rescored in binary64 (same summation order as the definition's plain
