@@ -13,7 +13,8 @@
 //     exact in binary32 ((c+1/2) s has at most 15 significant bits) and monotone
 //     in s; t is the binary16 rounding of |w|/(c+1/2) confirmed by a short walk
 //     on that predicate (bisection if the walk does not settle).
-//  2. Runs.  The events are sorted by t (bitonic sort in LDS); between two
+//  2. Runs.  The events are sorted by t (a bitonic sort held in registers:
+//     lane shuffles, with 3 of its 55 stages through LDS); between two
 //     consecutive event patterns every code is constant, so each environment
 //     error is the quadratic f_e(s) = A_e - 2 B_e s + C_e s^2 with
 //     B_e = sum d w q, C_e = sum d q^2.  A block-wide prefix sum over the
