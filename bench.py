@@ -43,21 +43,27 @@ def screened_patterns(w: np.ndarray) -> np.ndarray:
     return np.minimum(np.searchsorted(grid, t, side="left") + 1, SCALES)
 
 
-def nonzero_code_terms(w: np.ndarray) -> float:
-    """Terms (scale, weight) with a nonzero code over the screened patterns: weight i has a
-    nonzero code at scale s when s < 2|w_i|.  A code-0 term is d w^2 whatever the scale, so the
-    sweep sums those once; the others each take a quotient, a rounding, a residual, a square and
-    E weighted sums."""
+def active_terms(w: np.ndarray) -> float:
+    """Terms (scale, weight) over the screened patterns whose code is neither 0 nor held at the
+    clip end.  Weight i has code 0 at scale s when s >= 2|w_i|, and its code is held at 7 (w > 0)
+    or -8 (w < 0) for every scale below w/6.5 (w > 0) or up to |w|/7.5 (w < 0).  Both kinds of
+    term have a closed form at every scale (d w^2, and a quadratic in s with fixed coefficients),
+    so the sweep sums them once per chunk of scales; the active ones each take a quotient, a
+    rounding, a residual, a square and E weighted sums."""
     grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
-    per_w = np.searchsorted(grid, 2.0 * np.abs(w.astype(np.float64)), side="left")
-    top = screened_patterns(w)
-    return float(np.minimum(per_w, top[:, None]).sum())
+    a = np.abs(w.astype(np.float64))
+    top = screened_patterns(w)[:, None]
+    nonzero = np.minimum(np.searchsorted(grid, 2.0 * a, side="left"), top)
+    held = np.where(w > 0, np.searchsorted(grid, a / 6.5, side="left"),
+                    np.searchsorted(grid, a / 7.5, side="right"))
+    held = np.minimum(np.where(w == 0, 0, held), top)
+    return float((nonzero - held).sum())
 
 
 def sweep_flops(w: np.ndarray, E: int) -> float:
-    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]: 2E + 4 per term with
-    a nonzero code (a quotient multiply, a residual fma, a square and E weighted fmas)."""
-    return nonzero_code_terms(w) * (2 * E + 4)
+    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]: 2E + 4 per active
+    term (a quotient multiply, a residual fma, a square and E weighted fmas)."""
+    return active_terms(w) * (2 * E + 4)
 
 
 def full_grid_flops(n_groups: int, E: int) -> float:
@@ -397,7 +403,7 @@ def main():
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": sweep_traffic(args.config),
                      "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
                      "launch_ms": avg_ms, "groups_per_launch": avg_groups,
-                     "flops_per_launch": avg_flops, "flops_per_nonzero_code_term": 2 * E + 4,
+                     "flops_per_launch": avg_flops, "flops_per_active_term": 2 * E + 4,
                      "patterns_per_group": patterns},
         "sweep_groups_per_s": avg_groups / (avg_ms / 1e3),
         "sweep_full_grid_equivalent_tflops": full_grid_flops(avg_groups, E) / (avg_ms / 1e3) / 1e12,

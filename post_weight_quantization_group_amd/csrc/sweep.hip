@@ -139,6 +139,52 @@ __device__ __forceinline__ void sweep_range_clipped(const float* __restrict__ ws
     }
 }
 
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The fixed-code range [m_c, G) of a chunk in closed form.  Every weight there has code q = 7 or
+// -8 at every scale of the chunk, so the range adds Q_e(s) = A_e - 2 B_e s + C_e s^2 with
+// A = sum d w'^2, B = sum d w' q, C = sum d q^2 (all terms >= 0: w' and q share their sign).
+// The sums run in binary64, 64/E lanes per environment and a butterfly over those lanes; each
+// lane returns the sums of environment lane % E.  Q is used only when its binary64 error, at
+// most 2^-45 (A + 2 B s + C s^2) (fewer than 140 roundings of 2^-53 along any path), is below
+// 2^-31 of min Q over the chunk [s_lo, s_hi]: then Q~ = Q (1 +- 2^-31) at every scale of the
+// chunk and the screen's bound is unchanged.  Otherwise the range is summed term by term.
+template <int E>
+__device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int m_c, float s_lo, float s_hi,
+                                                double& A, double& B, double& C) {
+    constexpr int P = 64 / E;  // lanes per environment
+    const int lane = threadIdx.x & 63, e = lane % E;
+    A = 0.0; B = 0.0; C = 0.0;
+    for (int r = m_c + lane / E; r < G; r += P) {
+        const double wv = (double)sm.ws[r], q = (double)sm.qs[r], dv = (double)sm.ds[r * E + e];
+        const double dw = dv * wv;  // exact (24 + 24 bits)
+        A = __builtin_fma(dw, wv, A);
+        B = __builtin_fma(dw, q, B);
+        C = __builtin_fma(dv, q * q, C);
+    }
+#pragma unroll
+    for (int o = E; o < 64; o <<= 1) {
+        A += __shfl_xor(A, o, 64);
+        B += __shfl_xor(B, o, 64);
+        C += __shfl_xor(C, o, 64);
+    }
+    bool ok = true;
+    if (C > 0.0) {
+        const double lo = (double)s_lo, hi = (double)s_hi;
+        const double M = __builtin_fma(hi, __builtin_fma(hi, C, 2.0 * B), A);
+        double v = B / C;
+        v = v < lo ? lo : (v > hi ? hi : v);
+        const double qmin = __builtin_fma(v, __builtin_fma(v, C, -2.0 * B), A);
+        ok = M * 0x1p-13 <= qmin;  // 2^-45 M <= 2^-32 qmin, with room for the rounded vertex
+    }
+    return __ballot(!ok) == 0;
+}
+
 // binary64 rescoring of the first n shortlist entries: cand_F = max_e F_e,
 // cand_P = (sum_e F_e)/E, each F_e summed in the definition's order.
 template <int E>
@@ -397,16 +443,30 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
         const int m_c = G - (int)(__popcll(__ballot(k0 > tc)) + __popcll(__ballot(k1 > tc)));
         const int m_u = min(m_c, (int)(__popcll(__ballot(k0 < tu)) + __popcll(__ballot(k1 < tu))));
         const int m_z = min(m_u, (int)(__popcll(__ballot(k0 <= tz)) + __popcll(__ballot(k1 <= tz))));
-        // code-0 weights: their terms are the same at every scale, summed once in kz
+        // The sums start from the terms that need no per-scale work: the code-0 ones (the same at
+        // every scale, summed once in kz) and, when its closed form is accurate enough, the
+        // fixed-code range: acc = fl32(kz + Q_e(s)), one rounding, which the screen's count of
+        // at most 129 roundings per term covers.
+        double fa = 0.0, fb = 0.0, fc = 0.0;
+        const bool closed = m_c < G && fixed_code_sums<E>(sm, m_c, s_lo, s_hi, fa, fb, fc);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float z = sm.kz[m_z * E + e];
+            if (closed) {
+                const double A = readlane_f64(fa, e), B2 = -2.0 * readlane_f64(fb, e), C = readlane_f64(fc, e);
 #pragma unroll
-            for (int t = 0; t < NS; ++t) acc[t][e] = z;
+                for (int t = 0; t < NS; ++t) {
+                    const double sv = -(double)nsv[t];
+                    acc[t][e] = (float)((double)z + __builtin_fma(sv, __builtin_fma(sv, C, B2), A));
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < NS; ++t) acc[t][e] = z;
+            }
         }
         sweep_range<E, NS, false>(sm.ws, sm.ds, m_z, m_u, nsv, inv, acc);
         sweep_range<E, NS, true>(sm.ws, sm.ds, m_u, m_c, nsv, inv, acc);
-        sweep_range_clipped<E, NS>(sm.ws, sm.qs, sm.ds, m_c, G, nsv, acc);
+        if (!closed) sweep_range_clipped<E, NS>(sm.ws, sm.qs, sm.ds, m_c, G, nsv, acc);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
