@@ -59,6 +59,10 @@ struct SweepSmem {
     __align__(16) float ds[G * E];    // their diagonals [r][e]
     float ks[G];                      // clip keys, ascending
     float qs[G];                      // the code a weight takes once it is clipped (7 or -8)
+    // per wave, per chunk (screen_keys): the code a weight keeps over the chunk (127 if it
+    // changes), and the list of weights whose code changes, never-clipped ones first
+    int8_t qc[4][G];
+    uint8_t vlist[4][G];
     __align__(16) float kz[(G + 1) * E];  // kz[m][e]: binary32 sum of d w'^2 over the first m weights
     float redf[4 * 5];
     uint64_t redk[4];
@@ -86,33 +90,6 @@ __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
             else k[1] = v;
         } else {
             k[2] = v;
-        }
-    }
-}
-
-// Weights [i0, i1) of the screen order against the lane's NS scales, with the per-environment
-// sums in registers: q = rne(w' * (1/s')) (clipped when CLIP), e = fma(-s', q, w'), e^2, then
-// one fma per environment.  The weight and its E diagonals are LDS broadcasts shared by all NS
-// scales of the lane.
-template <int E, int NS, bool CLIP>
-__device__ __forceinline__ void sweep_range(const float* __restrict__ ws, const float* __restrict__ ds, int i0,
-                                            int i1, const float (&nsv)[NS], const float (&inv)[NS],
-                                            float (&acc)[NS][E]) {
-#pragma unroll 2
-    for (int i = i0; i < i1; ++i) {
-        const float wi = ws[i];
-        float di[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) di[e] = ds[i * E + e];
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-            const float x = wi * inv[t];
-            float r = __builtin_rintf(x);
-            if (CLIP) r = __builtin_amdgcn_fmed3f(r, -8.0f, 7.0f);
-            const float ev = __builtin_fmaf(nsv[t], r, wi);
-            const float e2 = ev * ev;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
         }
     }
 }
@@ -146,22 +123,26 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// The fixed-code range [m_c, G) of a chunk in closed form.  Every weight there has code q = 7 or
-// -8 at every scale of the chunk, so the range adds Q_e(s) = A_e - 2 B_e s + C_e s^2 with
-// A = sum d w'^2, B = sum d w' q, C = sum d q^2 (all terms >= 0: w' and q share their sign).
+// The weights of [r0, G) that keep one code q over the chunk in closed form: the fixed-code
+// range [m_c, G) (q = 7 or -8) and, below m_c, those with qc != 127.  They add
+// Q_e(s) = A_e - 2 B_e s + C_e s^2 with A = sum d w'^2, B = sum d w' q, C = sum d q^2 (all
+// terms >= 0: q is 0 or has the sign of w').
 // The sums run in binary64, 64/E lanes per environment and a butterfly over those lanes; each
 // lane returns the sums of environment lane % E.  Q is used only when its binary64 error, at
 // most 2^-45 (A + 2 B s + C s^2) (fewer than 140 roundings of 2^-53 along any path), is below
 // 2^-31 of min Q over the chunk [s_lo, s_hi]: then Q~ = Q (1 +- 2^-31) at every scale of the
 // chunk and the screen's bound is unchanged.  Otherwise the range is summed term by term.
 template <int E>
-__device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int m_c, float s_lo, float s_hi,
+__device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, int m_c, float s_lo, float s_hi,
                                                 double& A, double& B, double& C) {
     constexpr int P = 64 / E;  // lanes per environment
-    const int lane = threadIdx.x & 63, e = lane % E;
+    const int lane = threadIdx.x & 63, e = lane % E, wave = threadIdx.x >> 6;
     A = 0.0; B = 0.0; C = 0.0;
-    for (int r = m_c + lane / E; r < G; r += P) {
-        const double wv = (double)sm.ws[r], q = (double)sm.qs[r], dv = (double)sm.ds[r * E + e];
+    for (int r = r0 + lane / E; r < G; r += P) {
+        const int qcode = r < m_c ? (int)sm.qc[wave][r] : 0;
+        if (qcode == 127) continue;  // its code changes within the chunk: summed term by term
+        const double wv = (double)sm.ws[r], dv = (double)sm.ds[r * E + e];
+        const double q = r < m_c ? (double)qcode : (double)sm.qs[r];
         const double dw = dv * wv;  // exact (24 + 24 bits)
         A = __builtin_fma(dw, wv, A);
         B = __builtin_fma(dw, q, B);
@@ -183,6 +164,73 @@ __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int m_c,
         ok = M * 0x1p-13 <= qmin;  // 2^-45 M <= 2^-32 qmin, with room for the rounded vertex
     }
     return __ballot(!ok) == 0;
+}
+
+// The listed weights vl[i0..i1) of the screen order against the lane's NS scales, with the
+// per-environment sums in registers: q = rne(w' * (1/s')) (clipped when CLIP), e = fma(-s', q, w'),
+// e^2, then one fma per environment.  The weight and its E diagonals are LDS broadcasts shared by
+// all NS scales of the lane.
+template <int E, int NS, bool CLIP>
+__device__ __forceinline__ void sweep_list(const float* __restrict__ ws, const float* __restrict__ ds,
+                                           const uint8_t* __restrict__ vl, int i0, int i1,
+                                           const float (&nsv)[NS], const float (&inv)[NS], float (&acc)[NS][E]) {
+#pragma unroll 2
+    for (int i = i0; i < i1; ++i) {
+        const int r = vl[i];
+        const float wi = ws[r];
+        float di[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) di[e] = ds[r * E + e];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const float x = wi * inv[t];
+            float q = __builtin_rintf(x);
+            if (CLIP) q = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f);
+            const float ev = __builtin_fmaf(nsv[t], q, wi);
+            const float e2 = ev * ev;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
+        }
+    }
+}
+
+// Which weights of [m_z, m_c) keep one code over the chunk's scales [s_lo, s_hi]: the codes at
+// both ends agree (codes are monotone in s).  The quotients use reciprocals within 1 ulp, so
+// x~ = x (1 +- 3u); a code is taken only when x~ is farther than 2^-20 max(1, |x~|) from a
+// half-integer, where it equals the exact code.  Anything closer counts as changing, which is
+// always safe.  Writes the kept code to qc (127 when it changes) and lists the weights whose code
+// changes (all of them when `all`), in screen order, so that the never-clipped ones (r < m_u)
+// come first; returns the list length and their number in n_u.
+template <int E>
+__device__ __forceinline__ int classify_chunk(SweepSmem<E>& sm, int m_z, int m_u, int m_c, float inv_lo, float inv_hi,
+                                              bool all, int& n_u) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int n = 0;
+    n_u = 0;
+    for (int base = m_z; base < m_c; base += 64) {
+        const int r = base + lane;
+        bool var = false;
+        if (r < m_c) {
+            var = all;
+            if (!all) {
+                const float w = sm.ws[r];
+                const float xl = w * inv_lo, xh = w * inv_hi;
+                const float rl = __builtin_rintf(xl), rh = __builtin_rintf(xh);
+                const float ml = 0.5f - 0x1p-20f * fmaxf(1.0f, fabsf(xl));
+                const float mh = 0.5f - 0x1p-20f * fmaxf(1.0f, fabsf(xh));
+                const float ql = __builtin_amdgcn_fmed3f(rl, -8.0f, 7.0f), qh = __builtin_amdgcn_fmed3f(rh, -8.0f, 7.0f);
+                var = ql != qh || fabsf(xl - rl) >= ml || fabsf(xh - rh) >= mh;
+                sm.qc[wave][r] = var ? (int8_t)127 : (int8_t)ql;
+            }
+        }
+        const uint64_t m = __ballot(var);
+        if (var) sm.vlist[wave][n + __popcll(m & below)] = (uint8_t)r;
+        n += (int)__popcll(m);
+        n_u += (int)__popcll(__ballot(var && r < m_u));
+    }
+    __builtin_amdgcn_wave_barrier();
+    return n;
 }
 
 // binary64 rescoring of the first n shortlist entries: cand_F = max_e F_e,
@@ -447,8 +495,14 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
         // every scale, summed once in kz) and, when its closed form is accurate enough, the
         // fixed-code range: acc = fl32(kz + Q_e(s)), one rounding, which the screen's count of
         // at most 129 roundings per term covers.
+        const float rl0 = __builtin_amdgcn_rcpf(s_lo), rh0 = __builtin_amdgcn_rcpf(s_hi);
+        const float inv_lo = __builtin_fmaf(rl0, __builtin_fmaf(-s_lo, rl0, 1.0f), rl0);
+        const float inv_hi = __builtin_fmaf(rh0, __builtin_fmaf(-s_hi, rh0, 1.0f), rh0);
+        int n_u = 0;
+        int n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, false, n_u);
         double fa = 0.0, fb = 0.0, fc = 0.0;
-        const bool closed = m_c < G && fixed_code_sums<E>(sm, m_c, s_lo, s_hi, fa, fb, fc);
+        const bool closed = fixed_code_sums<E>(sm, m_z, m_c, s_lo, s_hi, fa, fb, fc);
+        if (!closed) n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, true, n_u);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float z = sm.kz[m_z * E + e];
@@ -464,8 +518,11 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
                 for (int t = 0; t < NS; ++t) acc[t][e] = z;
             }
         }
-        sweep_range<E, NS, false>(sm.ws, sm.ds, m_z, m_u, nsv, inv, acc);
-        sweep_range<E, NS, true>(sm.ws, sm.ds, m_u, m_c, nsv, inv, acc);
+        // the listed weights term by term: those whose code changes within the chunk, or all of
+        // [m_z, m_c) and then the fixed-code range when the closed form is not accurate enough
+        const uint8_t* vl = sm.vlist[threadIdx.x >> 6];
+        sweep_list<E, NS, false>(sm.ws, sm.ds, vl, 0, n_u, nsv, inv, acc);
+        sweep_list<E, NS, true>(sm.ws, sm.ds, vl, n_u, n_var, nsv, inv, acc);
         if (!closed) sweep_range_clipped<E, NS>(sm.ws, sm.qs, sm.ds, m_c, G, nsv, acc);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
