@@ -106,6 +106,27 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
 }
 
 // |q(w, s_b)| <= c  (exact, see the file comment)
+// Inclusive prefix sum over the 64 lanes of a wave through DPP: row_shr 1, 2, 4, 8 within each
+// row of 16 lanes (lanes with no source add 0), then row_bcast15 and row_bcast31 carry the
+// totals of the earlier rows.  Both 32-bit halves of a double move together.
+__device__ __forceinline__ double wave_inclusive_sum_f64(double x) {
+#define CQ_SCAN_STEP(ctrl, rmask)                                                                      \
+    {                                                                                                  \
+        const uint64_t u_ = __builtin_bit_cast(uint64_t, x);                                           \
+        const uint32_t lo_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u_, ctrl, rmask, 0xF, true); \
+        const uint32_t hi_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u_ >> 32), ctrl, rmask, 0xF, true); \
+        x += __builtin_bit_cast(double, ((uint64_t)hi_ << 32) | lo_);                                  \
+    }
+    CQ_SCAN_STEP(0x111, 0xF)
+    CQ_SCAN_STEP(0x112, 0xF)
+    CQ_SCAN_STEP(0x114, 0xF)
+    CQ_SCAN_STEP(0x118, 0xF)
+    CQ_SCAN_STEP(0x142, 0xA)
+    CQ_SCAN_STEP(0x143, 0xC)
+#undef CQ_SCAN_STEP
+    return x;
+}
+
 __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
     const float hs = (float)(2 * c + 1) * 0.5f * half_bits_value(b);
     return a < hs || (a == hs && (c & 1) == 0);
@@ -383,22 +404,14 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 #pragma unroll
                 for (int v = 0; v < NB; ++v) {
                     const double dv = (double)sm.d[(eb + v) * G + i];
-                    loc[v] -= dv * aw;
-                    loc[4 + v] -= dv * (double)(2 * c + 1);
+                    loc[v] = __builtin_fma(-dv, aw, loc[v]);
+                    loc[4 + v] = __builtin_fma(-dv, (double)(2 * c + 1), loc[4 + v]);
                 }
             }
         }
         double inc[8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            double x = loc[v];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
-            }
-            inc[v] = x;
-        }
+        for (int v = 0; v < 8; ++v) inc[v] = wave_inclusive_sum_f64(loc[v]);
         __syncthreads();
         if (lane == 63) {
 #pragma unroll
@@ -419,24 +432,25 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             const double slo = (double)half_bits_value(r_lo[j]), shi = (double)half_bits_value(r_hi[j]);
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
-                const double A = sm.A[eb + v], B = cB[v], C = cC[v];
-                const double fl = A + slo * (C * slo - 2.0 * B);
-                const double fh = A + shi * (C * shi - 2.0 * B);
+                const double A = sm.A[eb + v], B = cB[v], C = cC[v], B2 = -2.0 * B;
+                const double fl = __builtin_fma(slo, __builtin_fma(C, slo, B2), A);
+                const double fh = __builtin_fma(shi, __builtin_fma(C, shi, B2), A);
                 double sv;
                 if (C > 0.0) {
-                    sv = B / C;
+                    // The vertex B/C need not be exact: an error d moves f(sv) by C d^2, and a
+                    // relative error of 2^-40 in sv keeps that below 2^-80 of the magnitude bound,
+                    // far inside the 2^-40 allowance.  Hardware reciprocal plus one Newton step.
+                    const double r0 = __builtin_amdgcn_rcp(C);
+                    const double r1 = __builtin_fma(r0, __builtin_fma(-C, r0, 1.0), r0);
+                    sv = B * r1;
                     sv = sv < slo ? slo : (sv > shi ? shi : sv);
                 } else {
                     sv = B > 0.0 ? shi : slo;  // linear (C = 0): B >= 0 decreases towards shi
                 }
-                const double fv = A + sv * (C * sv - 2.0 * B);
-                const double ml = A + slo * (sm.C0[eb + v] * slo + 2.0 * sm.B0[eb + v]);
-                const double mh = A + shi * (sm.C0[eb + v] * shi + 2.0 * sm.B0[eb + v]);
-                r_flo[j] = fl > r_flo[j] ? fl : r_flo[j];
-                r_fhi[j] = fh > r_fhi[j] ? fh : r_fhi[j];
-                r_lb[j] = fv > r_lb[j] ? fv : r_lb[j];
-                r_mlo[j] = ml > r_mlo[j] ? ml : r_mlo[j];
-                r_mhi[j] = mh > r_mhi[j] ? mh : r_mhi[j];
+                const double fv = __builtin_fma(sv, __builtin_fma(C, sv, B2), A);
+                r_flo[j] = fmax(r_flo[j], fl);
+                r_fhi[j] = fmax(r_fhi[j], fh);
+                r_lb[j] = fmax(r_lb[j], fv);
             }
         };
         if (r_ok[0]) fold(0);
@@ -449,11 +463,24 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 #pragma unroll
                 for (int v = 0; v < NB; ++v) {
                     const double dv = (double)sm.d[(eb + v) * G + i];
-                    cB[v] -= dv * aw;
-                    cC[v] -= dv * (double)(2 * c + 1);
+                    cB[v] = __builtin_fma(-dv, aw, cB[v]);
+                    cC[v] = __builtin_fma(-dv, (double)(2 * c + 1), cC[v]);
                 }
             }
             if (r_ok[k + 1]) fold(k + 1);
+        }
+    }
+    // Magnitude bound of each run end, max_e (A_e + 2 B0_e s + C0_e s^2), taken from the maxima
+    // of A, B0 and C0 over the environments: never smaller, so the allowances only grow.
+    {
+        double am = 0.0, bm = 0.0, cm = 0.0;
+        for (int e = 0; e < E; ++e) { am = fmax(am, sm.A[e]); bm = fmax(bm, sm.B0[e]); cm = fmax(cm, sm.C0[e]); }
+        const double b2 = 2.0 * bm;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const double slo = (double)half_bits_value(r_lo[j]), shi = (double)half_bits_value(r_hi[j]);
+            r_mlo[j] = __builtin_fma(slo, __builtin_fma(cm, slo, b2), am);
+            r_mhi[j] = __builtin_fma(shi, __builtin_fma(cm, shi, b2), am);
         }
     }
     // upper bound U from the run ends, and each run's lower bound minus its error allowance
