@@ -167,13 +167,21 @@ __device__ __forceinline__ double quad_run(const CandSmem<E>& sm, int r, double 
     return F;
 }
 
-// Calls fn(b) for every candidate pattern of surviving run r: its two ends, and the grid
-// neighbours (+-2) of each vertex and each pairwise crossing that lies on the upper envelope.
+// Items of the candidate search of a surviving run: k = 0 its two ends, k = 1..E the vertex of
+// environment k-1, then one item per pair of environments for their crossings.
+template <int E>
+constexpr int cand_items() { return 1 + E + E * (E - 1) / 2; }
+
+// Calls fn(b) for every candidate pattern of item k of surviving run r: the run's ends, or the
+// grid neighbours (+-2) of a vertex or of a pairwise crossing that lies on the upper envelope.
 template <int E, typename Fn>
-__device__ void run_candidates(const CandSmem<E>& sm, int r, Fn&& fn) {
+__device__ void run_candidate_item(const CandSmem<E>& sm, int r, int k, Fn&& fn) {
     const uint32_t blo = sm.run_lo[r], bhi = sm.run_hi[r];
-    fn(blo);
-    if (bhi != blo) fn(bhi);
+    if (k == 0) {
+        fn(blo);
+        if (bhi != blo) fn(bhi);
+        return;
+    }
     if (bhi - blo < 2) return;
     const double slo = (double)half_bits_value(blo), shi = (double)half_bits_value(bhi);
     auto near = [&](double s) {
@@ -191,41 +199,39 @@ __device__ void run_candidates(const CandSmem<E>& sm, int r, Fn&& fn) {
         const double f2 = sm.A[e2] + s * (sm.run_C[r][e2] * s - 2.0 * sm.run_B[r][e2]);
         return f1 >= F - tol && f2 >= F - tol;
     };
-#pragma unroll 1
-    for (int e = 0; e < E; ++e) {
+    if (k <= E) {
+        const int e = k - 1;
         const double C = sm.run_C[r][e];
         if (C > 0.0) {
             const double v = sm.run_B[r][e] / C;
             if (v >= slo && v <= shi && on_top(v, e, e)) near(v);
         }
+        return;
     }
-#pragma unroll 1
-    for (int e1 = 0; e1 < E; ++e1) {
-#pragma unroll 1
-        for (int e2 = e1 + 1; e2 < E; ++e2) {
-            const double a = sm.run_C[r][e1] - sm.run_C[r][e2];
-            const double hb = sm.run_B[r][e1] - sm.run_B[r][e2];
-            const double cc = sm.A[e1] - sm.A[e2];
-            double r0 = -1.0, r1 = -1.0;
-            if (a == 0.0) {
-                if (hb != 0.0) r0 = cc / (2.0 * hb);
+    int p = k - 1 - E, e1 = 0;
+    while (p >= E - 1 - e1) { p -= E - 1 - e1; ++e1; }
+    const int e2 = e1 + 1 + p;
+    const double a = sm.run_C[r][e1] - sm.run_C[r][e2];
+    const double hb = sm.run_B[r][e1] - sm.run_B[r][e2];
+    const double cc = sm.A[e1] - sm.A[e2];
+    double r0 = -1.0, r1 = -1.0;
+    if (a == 0.0) {
+        if (hb != 0.0) r0 = cc / (2.0 * hb);
+    } else {
+        const double disc = hb * hb - a * cc;
+        if (disc >= 0.0) {
+            const double sq = __builtin_sqrt(disc);
+            const double qq = hb + (hb >= 0.0 ? sq : -sq);
+            if (qq != 0.0) {
+                r0 = qq / a;
+                r1 = cc / qq;
             } else {
-                const double disc = hb * hb - a * cc;
-                if (disc >= 0.0) {
-                    const double sq = __builtin_sqrt(disc);
-                    const double qq = hb + (hb >= 0.0 ? sq : -sq);
-                    if (qq != 0.0) {
-                        r0 = qq / a;
-                        r1 = cc / qq;
-                    } else {
-                        r0 = hb / a;
-                    }
-                }
+                r0 = hb / a;
             }
-            if (r0 >= slo && r0 <= shi && on_top(r0, e1, e2)) near(r0);
-            if (r1 >= slo && r1 <= shi && on_top(r1, e1, e2)) near(r1);
         }
     }
+    if (r0 >= slo && r0 <= shi && on_top(r0, e1, e2)) near(r0);
+    if (r1 >= slo && r1 <= shi && on_top(r1, e1, e2)) near(r1);
 }
 
 template <int E>
@@ -507,17 +513,28 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             sm.qbuf[r][i] = (uint8_t)fabsf(exact_code(sm.w[i], half_bits_value(sm.run_lo[r])));
         }
         __syncthreads();
-        for (int j = tid; j < n_runs * E; j += BLOCK) {
-            const int r = j / E, e = j % E;
+        // four consecutive threads per (run, environment), 32 weights each
+        for (int j0 = 0; j0 < n_runs * E * 4; j0 += BLOCK) {
+            const int j = j0 + tid;
+            const bool live = j < n_runs * E * 4;
+            const int r = j / (4 * E), e = (j / 4) % E, part = j % 4;
             double B = 0.0, C = 0.0;
-            for (int i = 0; i < G; ++i) {
-                const double dv = (double)sm.d[e * G + i];
-                const double q = (double)sm.qbuf[r][i];
-                B += dv * (fabs((double)sm.w[i]) * q);
-                C += dv * (q * q);
+            if (live) {
+                for (int i = 32 * part; i < 32 * part + 32; ++i) {
+                    const double dv = (double)sm.d[e * G + i];
+                    const double q = (double)sm.qbuf[r][i];
+                    B = __builtin_fma(dv, fabs((double)sm.w[i]) * q, B);
+                    C = __builtin_fma(dv, q * q, C);
+                }
             }
-            sm.run_B[r][e] = B;
-            sm.run_C[r][e] = C;
+            B += __shfl_xor(B, 1, 64);
+            C += __shfl_xor(C, 1, 64);
+            B += __shfl_xor(B, 2, 64);
+            C += __shfl_xor(C, 2, 64);
+            if (live && part == 0) {
+                sm.run_B[r][e] = B;
+                sm.run_C[r][e] = C;
+            }
         }
     }
     __syncthreads();
@@ -525,8 +542,10 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     // ---- 3c. candidates of the kept runs: ends, vertices and crossings on the upper envelope
     double M = __builtin_inf();
     if (n_runs <= RCAP) {
-        for (int r = tid; r < n_runs; r += BLOCK) {
-            run_candidates<E>(sm, r, [&](uint32_t b) {
+        constexpr int K = cand_items<E>();
+        for (int j = tid; j < n_runs * K; j += BLOCK) {
+            const int r = j / K;
+            run_candidate_item<E>(sm, r, j % K, [&](uint32_t b) {
                 double err;
                 const double f = quad_run<E>(sm, r, (double)half_bits_value(b), err);
                 M = fmin(M, f + err);
