@@ -578,13 +578,20 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
 
     // ---- 4. direct binary64 rescoring (definition order) and the reduction
-    constexpr int PER = BLOCK / E;
+    // The codes of a batch of shortlisted scales come first, from all threads, into qbuf (free by
+    // now); each (scale, environment) sum then runs in the definition's order.
+    constexpr int PER = BLOCK / E < CandSmem<E>::RCAP ? BLOCK / E : CandSmem<E>::RCAP;
     for (int base = 0; base < n; base += PER) {
         const int nb = min(PER, n - base);
+        for (int j = tid; j < nb * G; j += BLOCK) {
+            const int c = j / G, i = j % G;
+            sm.qbuf[c][i] = (uint8_t)(int8_t)exact_code(sm.w[i], half_bits_value(sm.cand_b[base + c]));
+        }
+        __syncthreads();
         if (tid < nb * E) {
-            const int j = base + tid / E, e = tid % E;
-            const double s = (double)half_bits_value(sm.cand_b[j]);
-            sm.pairF[tid] = env_error_f64(sm.w, sm.d + e * G, 1, s, 1.0 / s);
+            const int c = tid / E, e = tid % E;
+            const double s = (double)half_bits_value(sm.cand_b[base + c]);
+            sm.pairF[tid] = env_error_codes_f64(sm.w, sm.d + e * G, 1, reinterpret_cast<const int8_t*>(sm.qbuf[c]), s);
         }
         __syncthreads();
         if (tid < nb) {

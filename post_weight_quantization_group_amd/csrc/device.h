@@ -69,6 +69,22 @@ __device__ __forceinline__ double env_error_f64(const float* w, const float* d, 
     return F;
 }
 
+// env_error_f64 with the codes given: q[i] is the exact code of w[i] at s.  Same operations in the
+// same order, so the same value.
+__device__ __forceinline__ double env_error_codes_f64(const float* w, const float* d, int dstride,
+                                                      const int8_t* q, double s) {
+    double F = 0.0;
+    for (int i = 0; i < G; ++i) {
+        const double wi = (double)w[i];
+        const double sq = s * (double)q[i];
+        const double t = wi - sq;
+        const double t2 = t * t;
+        const double term = (double)d[i * dstride] * t2;
+        F = F + term;
+    }
+    return F;
+}
+
 // binary32 x >= 0 to the nearest binary16 pattern, ties to even; 0x7C00 on overflow.
 __device__ __forceinline__ uint32_t f32_to_half_bits_rne(float x) {
     if (!(x < 65520.0f)) return 0x7C00u;
