@@ -63,6 +63,7 @@ struct SweepSmem {
     // changes), and the list of weights whose code changes, never-clipped ones first
     int8_t qc[4][G];
     uint8_t vlist[4][G];
+    int8_t rq[32][G];                 // rescoring: the codes of a batch of shortlisted scales
     __align__(16) float kz[(G + 1) * E];  // kz[m][e]: binary32 sum of d w'^2 over the first m weights
     float redf[4 * 5];
     uint64_t redk[4];
@@ -158,7 +159,8 @@ __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, 
     if (C > 0.0) {
         const double lo = (double)s_lo, hi = (double)s_hi;
         const double M = __builtin_fma(hi, __builtin_fma(hi, C, 2.0 * B), A);
-        double v = B / C;
+        const double r0 = __builtin_amdgcn_rcp(C);
+        double v = B * __builtin_fma(r0, __builtin_fma(-C, r0, 1.0), r0);  // the vertex, to ~2^-50
         v = v < lo ? lo : (v > hi ? hi : v);
         const double qmin = __builtin_fma(v, __builtin_fma(v, C, -2.0 * B), A);
         ok = M * 0x1p-13 <= qmin;  // 2^-45 M <= 2^-32 qmin, with room for the rounded vertex
@@ -237,14 +239,21 @@ __device__ __forceinline__ int classify_chunk(SweepSmem<E>& sm, int m_z, int m_u
 // cand_P = (sum_e F_e)/E, each F_e summed in the definition's order.
 template <int E>
 __device__ void rescore(SweepSmem<E>& sm, int n, int E_real) {
-    constexpr int PER = BLOCK / E;
+    constexpr int PER = BLOCK / E < 32 ? BLOCK / E : 32;
     const int t = threadIdx.x;
     for (int base = 0; base < n; base += PER) {
         const int nb = min(PER, n - base);
+        // the batch's codes from all threads first; each (scale, environment) sum then runs the
+        // definition's operations in its order
+        for (int j = t; j < nb * G; j += BLOCK) {
+            const int c = j / G, i = j % G;
+            sm.rq[c][i] = (int8_t)exact_code(sm.w[i], half_bits_value(sm.cand_b[base + c]));
+        }
+        __syncthreads();
         if (t < nb * E) {
-            const int j = base + t / E, e = t % E;
-            const double s = (double)half_bits_value(sm.cand_b[j]);
-            sm.pairF[t] = env_error_f64(sm.w, sm.dt + e, E, s, 1.0 / s);
+            const int c = t / E, e = t % E;
+            const double s = (double)half_bits_value(sm.cand_b[base + c]);
+            sm.pairF[t] = env_error_codes_f64(sm.w, sm.dt + e, E, sm.rq[c], s);
         }
         __syncthreads();
         if (t < nb) {
@@ -507,11 +516,13 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
         for (int e = 0; e < E; ++e) {
             const float z = sm.kz[m_z * E + e];
             if (closed) {
-                const double A = readlane_f64(fa, e), B2 = -2.0 * readlane_f64(fb, e), C = readlane_f64(fc, e);
+                // fl32(z + Q(s)) with z added to A first (binary64, far inside the 2^-31)
+                const double A = readlane_f64(fa, e) + (double)z;
+                const double B2 = -2.0 * readlane_f64(fb, e), C = readlane_f64(fc, e);
 #pragma unroll
                 for (int t = 0; t < NS; ++t) {
                     const double sv = -(double)nsv[t];
-                    acc[t][e] = (float)((double)z + __builtin_fma(sv, __builtin_fma(sv, C, B2), A));
+                    acc[t][e] = (float)__builtin_fma(sv, __builtin_fma(sv, C, B2), A);
                 }
             } else {
 #pragma unroll
