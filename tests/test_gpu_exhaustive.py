@@ -116,6 +116,36 @@ def test_top_pattern_ranges_sliced_and_unsliced():
         assert np.all(b == a[None]), key
 
 
+def test_thirty_two_environments_both_methods():
+    """E = 32, the largest environment count: exhaustive (minimax and pooled) and candidate
+    against the oracle on 16 groups with per-group diagonals."""
+    rng = np.random.default_rng(31)
+    n = 16
+    w = W.round_bf16(rng.normal(0, 0.03, (n, 128)).astype(np.float32))
+    w[::5, 7] *= 8.0
+    d = rng.lognormal(0, 1.2, (n, 32, 128)).astype(np.float32)
+    sol = oracle.solve(w, d, n, n_threads=threads())
+    r = _run(w, d, n)
+    check_minimax(w, d, n, r, sol)
+    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
+    c = _run(w, d, n, method="candidate", pooled=False)
+    check_minimax(w, d, n, c, sol)
+
+
+def test_batch_sizes_around_the_slicing_switch():
+    """1,023 groups run sliced, 1,024 and 1,025 one workgroup each: every batch gives bit for bit
+    what the same groups give inside one full-matrix run."""
+    w, d, p = W.matrix_groups(*W.make_matrix(1, 0))
+    full = _run(w, d, p)
+    for n in (1023, 1024, 1025):
+        # keep whole d periods so that every group sees its own diagonal slice
+        r = _run(w[:n], d, p)
+        for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
+            a = r[key].cpu().numpy()
+            b = full[key].cpu().numpy()[:n]
+            assert np.array_equal(a, b), (n, key)
+
+
 def test_bad_inputs_are_flagged():
     rng = np.random.default_rng(3)
     w = rng.normal(0, 0.02, (4, 128)).astype(np.float32)
