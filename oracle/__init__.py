@@ -28,7 +28,9 @@ N_SCALES = LAST_BITS - FIRST_BITS + 1  # 31,743
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cq_oracle.c")
-_LIB = os.path.join(_HERE, "libcq_oracle.so")
+# CQ_ORACLE_LIB names another build of cq_oracle.c to load instead; the mutation test uses it
+# to run the pins against copies with a planted mistake.
+_LIB = os.environ.get("CQ_ORACLE_LIB") or os.path.join(_HERE, "libcq_oracle.so")
 _lib = None
 
 
