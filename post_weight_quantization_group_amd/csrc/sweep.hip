@@ -9,8 +9,8 @@
 // by the lower-bit-pattern rule (about 40% of the grid on typical weights).
 // Work split: one 256-thread workgroup per group; weights and diagonals are
 // staged in LDS, sorted by a clip key; each wave takes chunks of 64*NS
-// consecutive scale patterns, NS per lane (8 up to E = 8), with the
-// per-environment sums in registers.  Within a chunk the sorted weights fall
+// consecutive scale patterns, NS = 4 per lane, with the per-environment sums
+// in registers.  Within a chunk the sorted weights fall
 // into four consecutive ranges: code 0 at every scale of the chunk (their
 // terms d w^2 enter as one prefix sum), never clipped, possibly clipped, and
 // code 7 or -8 throughout (no quotient needed).
@@ -42,10 +42,13 @@
 
 namespace cqk {
 
-// Scales per lane per chunk: 8 keeps the E accumulators of every scale in registers up to
-// E = 8 at four waves per SIMD; larger E trades scales for accumulators.
-constexpr int ns_for(int E) { return E <= 8 ? 8 : (E == 16 ? 4 : 2); }
-constexpr int min_blocks_for(int E) { return E <= 4 ? 4 : (E <= 16 ? 3 : 2); }
+// Scales per lane per chunk, and workgroups per CU.  Four scales per lane (chunks of 256
+// patterns) keep the chunks narrow, so fewer weights change code within one, and leave room for
+// many waves per SIMD: the screen's dependent LDS loads and binary64 chains need the latency
+// hiding more than they suffer from the few spills this costs.  Measured on gfx950 against 8
+// scales at 4 workgroups: E = 1, 2, 4, 8, 16, 32 run 23-26% faster (E = 16 15%).
+constexpr int ns_for(int E) { return 4; }
+constexpr int min_blocks_for(int E) { return E == 1 ? 8 : (E <= 4 ? 7 : (E == 8 ? 5 : (E == 16 ? 4 : 2))); }
 constexpr int CAP = 256;                     // shortlist capacity per group
 constexpr float SCREEN_RATIO = 1.00004f;
 constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
