@@ -60,6 +60,59 @@ def active_terms(w: np.ndarray) -> float:
     return float((nonzero - held).sum())
 
 
+def necessary_terms(w: np.ndarray, d: np.ndarray, opt_m: np.ndarray, opt_p: np.ndarray, chunk: int = 128):
+    """Active terms (see active_terms) of the chunks of `chunk` consecutive patterns that the
+    binary32 screen cannot skip, per group, and the number of those chunks.  The screen skips a
+    chunk when a lower bound on the objective over it exceeds 1.001 times the best value screened
+    so far, for minimax and for pooled; the bound is the code-0 prefix sum (weights with clip key
+    <= s_lo/15) plus, for weights clipped throughout (clip key > s_hi), d (|w| - |q| s_hi)^2 when
+    positive.  The best value screened is never below the optimum, so every chunk whose bound is
+    at most 1.0009 times the optimum (binary64 here, a margin for the screen's binary32) is
+    screened: the count is a lower bound on the work done.  w [n, 128], d [n, E, 128], opt_m the
+    minimax optimum and opt_p the pooled optimum times E (a sum over environments)."""
+    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    top = screened_patterns(w)
+    w64, d64 = w.astype(np.float64), d.astype(np.float64)
+    a = np.abs(w64)
+    nonzero = np.minimum(np.searchsorted(grid, 2.0 * a, side="left"), top[:, None])
+    held = np.where(w64 > 0, np.searchsorted(grid, a / 6.5, side="left"), np.searchsorted(grid, a / 7.5, side="right"))
+    held = np.minimum(np.where(w64 == 0, 0, held), top[:, None])
+    key = np.where(w64 > 0, w64 / 6.5, a / 7.5)
+    qa = np.where(w64 > 0, 7.0, 8.0)
+    terms = np.zeros(w.shape[0])
+    chunks = np.zeros(w.shape[0])
+    for j in range(w.shape[0]):
+        nch = (int(top[j]) - 1) // chunk + 1
+        c0 = np.arange(nch) * chunk                        # first pattern index (0-based) of each chunk
+        c1 = np.minimum(c0 + chunk, int(top[j]))           # one past the last
+        lo, hi = grid[c0], grid[c1 - 1]
+        zmask = key[j][None, :] <= lo[:, None] / 15.0      # [nch, 128]
+        cmask = key[j][None, :] > hi[:, None]
+        t = np.maximum(0.0, a[j][None, :] - qa[j][None, :] * hi[:, None]) * cmask
+        zt = np.where(zmask, a[j][None, :] ** 2, 0.0)
+        lb = np.einsum("ce,ke->kc", d64[j], t * t + zt)   # [nch, E]
+        need = lb.max(axis=1) <= 1.0009 * opt_m[j]
+        if opt_p is not None:
+            need |= lb.sum(axis=1) <= 1.0009 * opt_p[j]
+        ov = np.minimum(nonzero[j][None, :], c1[:, None]) - np.maximum(held[j][None, :], c0[:, None])
+        terms[j] = np.clip(ov, 0, None)[need].sum()
+        chunks[j] = need.sum()
+    return terms, chunks
+
+
+def sampled_sweep_flops(w: np.ndarray, d: np.ndarray, d_period: int, r: dict, E: int, pooled: bool,
+                        n_sample: int = 512, seed: int = 2024) -> float:
+    """The sweep's work over all groups of w (2E + 4 flops per unskippable active term, see
+    necessary_terms), from a seeded sample of its groups and the optima in r (quantize_groups)."""
+    rng = np.random.default_rng(seed)
+    n = w.shape[0]
+    idx = np.sort(rng.choice(n, size=min(n_sample, n), replace=False))
+    om = r["objective"].cpu().numpy()[idx]
+    op = r["pooled_objective"].cpu().numpy()[idx] * E if pooled else None
+    terms, _ = necessary_terms(w[idx], d[idx % d_period], om, op, chunk=128)
+    return float(terms.mean()) * n * (2 * E + 4)
+
+
 def sweep_flops(w: np.ndarray, E: int) -> float:
     """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]: 2E + 4 per active
     term (a quotient multiply, a residual fma, a square and E weighted fmas)."""
@@ -160,10 +213,10 @@ def measure_all_configs() -> dict:
             mat = spec.matrices[m]
             w, d, p = W.matrix_groups(*W.make_matrix(k, m))
             n = w.shape[0]
-            tot["flops"] += sweep_flops(w, E)
             wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
             r, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="exhaustive", pooled=True))
             tot["exhaustive_ms"] += ms
+            tot["flops"] += sampled_sweep_flops(w, d, p, r, E, True)
             c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
             tot["candidate_ms"] += ms
             ab, ms = _timed(lambda: cq.baseline_scales(wt, dt, p, "absmax", objective=False))
@@ -231,20 +284,22 @@ def measure_all_configs() -> dict:
                       "proxy_ms": proxy_ms, "proxy_module_macro_minimax": float(np.mean(means)),
                       "sample_groups": int(ws_.shape[0]),
                       "sample_exhaustive_groups_per_s": ws_.shape[0] / ms_x * 1e3,
-                      "sample_exhaustive_frac_fp32_peak": sweep_flops(ws_, 4) / (ms_x / 1e3)
-                      / (PEAK_FP32_TFLOPS * 1e12),
+                      "sample_exhaustive_frac_fp32_peak":
+                          sampled_sweep_flops(ws_, ds_, ws_.shape[0], r, 4, False) / (ms_x / 1e3)
+                          / (PEAK_FP32_TFLOPS * 1e12),
                       "sample_candidate_vs_exhaustive_scale_mismatches":
                           int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
     # config 3: per-group diagonals
     w3, d3, cat3, _ = W.make_groups(3)
     n3 = w3.shape[0]
     wt, dt = torch.from_numpy(w3).to(dev), torch.from_numpy(d3).to(dev)
-    del d3
     r, ms_x = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="exhaustive", pooled=False))
+    flops3 = sampled_sweep_flops(w3, d3, n3, r, 8, False)
+    del d3
     c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="candidate"))
     fl = c["flags"].cpu().numpy()
     res["config3"] = {"groups": n3, "E": 8, "exhaustive_groups_per_s": n3 / ms_x * 1e3,
-                      "exhaustive_frac_fp32_peak": sweep_flops(w3, 8) / (ms_x / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
+                      "exhaustive_frac_fp32_peak": flops3 / (ms_x / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
                       "candidate_groups_per_s": n3 / ms_c * 1e3,
                       "candidate_fallback_groups": int(np.count_nonzero(fl & cq.FLAG_FALLBACK)),
                       "exhaustive_fp64_sweep_groups": int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)),
@@ -293,7 +348,7 @@ def main():
         n = w.shape[0]
         t = {
             "name": mat.name, "out": mat.out, "inp": mat.inp, "n": n, "p": p,
-            "flops": sweep_flops(w, E), "patterns": float(screened_patterns(w).mean()),
+            "w_np": w, "d_np": d, "patterns": float(screened_patterns(w).mean()),
             "w": torch.from_numpy(w).to(dev), "d": torch.from_numpy(d).to(dev),
             "scales": torch.empty(n, dtype=torch.int16, device=dev),
             "codes": torch.empty((n, 128), dtype=torch.int8, device=dev),
@@ -347,7 +402,7 @@ def main():
                                   t["obj"], t["flags"], t["pscales"], t["pobj"], t["ws"])
             if record:
                 b.record(stream)
-                sweep_ev.append((a, b, t["n"], t["flops"]))
+                sweep_ev.append((a, b, t))
             if use_candidate:
                 cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.CANDIDATE, t["cscales"],
                                       t["ccodes"], t["cobj"], t["cflags"], None, None, t["cws"])
@@ -374,11 +429,24 @@ def main():
     ms_step = ms_total / args.steps
     value = n_total / (ms_step / 1e3)
 
-    # dominant kernel: the exhaustive sweep call, per launch (one launch per matrix)
-    durs = [a.elapsed_time(b) for a, b, _, _ in sweep_ev]
+    # dominant kernel: the exhaustive sweep call, per launch (one launch per matrix).  Its work:
+    # the active terms of the chunks no exact screen with its lower bound can skip, per group from
+    # a seeded sample of 1,024 groups per matrix (against the optima the sweep returned), times
+    # 2E + 4 flops; chunks of 128 patterns as in the kernel.
+    rng = np.random.default_rng(2024)
+    nec_chunks, all_terms = [], []
+    for t in mats:
+        idx = np.sort(rng.choice(t["n"], size=min(1024, t["n"]), replace=False))
+        om = t["obj"].cpu().numpy()[idx]
+        op = t["pobj"].cpu().numpy()[idx] * E
+        terms, chunks = necessary_terms(t["w_np"][idx], t["d_np"][idx % t["p"]], om, op, chunk=128)
+        t["flops"] = float(terms.mean()) * t["n"] * (2 * E + 4)
+        nec_chunks.append(float(chunks.mean()))
+        all_terms.append(active_terms(t["w_np"][idx]) / idx.size)
+    durs = [a.elapsed_time(b) for a, b, _ in sweep_ev]
     avg_ms = float(np.mean(durs))
-    avg_groups = float(np.mean([n for _, _, n, _ in sweep_ev]))
-    avg_flops = float(np.mean([f for _, _, _, f in sweep_ev]))
+    avg_groups = float(np.mean([t["n"] for _, _, t in sweep_ev]))
+    avg_flops = float(np.mean([t["flops"] for _, _, t in sweep_ev]))
     achieved = avg_flops / (avg_ms / 1e3) / 1e12
     patterns = float(np.mean([t["patterns"] for t in mats]))
     flags = torch.cat([t["flags"] for t in mats]).cpu().numpy()
@@ -404,7 +472,11 @@ def main():
                      "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
                      "launch_ms": avg_ms, "groups_per_launch": avg_groups,
                      "flops_per_launch": avg_flops, "flops_per_active_term": 2 * E + 4,
-                     "patterns_per_group": patterns},
+                     "patterns_per_group": patterns,
+                     "chunks_per_group": float(np.mean([(t["patterns"] - 1) // 128 + 1 for t in mats])),
+                     "unskippable_chunks_per_group": float(np.mean(nec_chunks)),
+                     "active_terms_per_group_unskippable": avg_flops / avg_groups / (2 * E + 4),
+                     "active_terms_per_group_all_chunks": float(np.mean(all_terms))},
         "sweep_groups_per_s": avg_groups / (avg_ms / 1e3),
         "sweep_full_grid_equivalent_tflops": full_grid_flops(avg_groups, E) / (avg_ms / 1e3) / 1e12,
         "flag_counts": {"near_tie": int(np.count_nonzero(flags & 2)), "exact_tie": int(np.count_nonzero(flags & 4)),

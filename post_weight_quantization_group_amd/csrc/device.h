@@ -56,6 +56,7 @@ __device__ __forceinline__ float exact_code(float w, float s) {
 __device__ __forceinline__ double env_error_f64(const float* w, const float* d, int dstride,
                                                 double s, double inv) {
     double F = 0.0;
+#pragma unroll 8
     for (int i = 0; i < G; ++i) {
         const double wi = (double)w[i];
         double r = __builtin_rint(wi * inv);
@@ -74,6 +75,7 @@ __device__ __forceinline__ double env_error_f64(const float* w, const float* d, 
 __device__ __forceinline__ double env_error_codes_f64(const float* w, const float* d, int dstride,
                                                       const int8_t* q, double s) {
     double F = 0.0;
+#pragma unroll 8
     for (int i = 0; i < G; ++i) {
         const double wi = (double)w[i];
         const double sq = s * (double)q[i];

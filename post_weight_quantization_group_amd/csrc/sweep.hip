@@ -47,7 +47,7 @@ namespace cqk {
 // many waves per SIMD: the screen's dependent LDS loads and binary64 chains need the latency
 // hiding more than they suffer from the few spills this costs.  Measured on gfx950 against 8
 // scales at 4 workgroups: E = 1, 2, 4, 8, 16, 32 run 23-26% faster (E = 16 15%).
-constexpr int ns_for(int E) { return 4; }
+constexpr int ns_for(int E) { return 2; }
 constexpr int min_blocks_for(int E) { return E == 1 ? 8 : (E <= 4 ? 7 : (E == 8 ? 5 : (E == 16 ? 4 : 2))); }
 constexpr int CAP = 256;                     // shortlist capacity per group
 constexpr float SCREEN_RATIO = 1.00004f;
@@ -72,18 +72,23 @@ struct SweepSmem {
     uint64_t redk[4];
     uint32_t cand_b[CAP];
     uint8_t cand_tag[CAP];
-    double cand_F[CAP];
+    __align__(16) double cand_F[CAP];
     double cand_P[CAP];
-    double pairF[BLOCK];
+    __align__(16) double pairF[BLOCK];
     int n_cand;
     int overflow;
-    int next_chunk;                   // the screen's work counter (chunks handed to waves)
+    // the screen's work counters: chunks handed out upwards from c_start and downwards from
+    // c_start - 1, and the limits beyond which every chunk is known to be skippable
+    int next_up, next_down;
+    int lim_up, lim_down;
     uint32_t win_b[2];
     double win_F[2];
     uint8_t win_flags[2];
     uint32_t ovbits;
     uint64_t mrg_m1[2];
     uint32_t b_top;                   // last pattern screened (top_pattern)
+    int c_start;                      // the chunk screened first (around max|w|/7)
+    uint32_t u_bits[2];               // smallest minimax / pooled binary32 value screened so far
 };
 
 __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
@@ -370,34 +375,49 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
     }
     if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
-    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; sm.next_chunk = 0; sm.b_top = top_pattern(wmax); }
+    if (tid == 0) {
+        sm.n_cand = 0;
+        sm.overflow = 0;
+        sm.next_up = 0;
+        sm.next_down = 0;
+        sm.lim_up = 0x7FFFFFFF;
+        sm.lim_down = -1;
+        const uint32_t b_top = top_pattern(wmax);
+        sm.b_top = b_top;
+        // the screen starts at the AbsMax scale's chunk, where the optimum usually lies
+        uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 7.0f));
+        b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > b_top ? b_top : b_a);
+        sm.c_start = (int)((b_a - BITS_FIRST) / (uint32_t)(64 * ns_for(E)));
+        sm.u_bits[0] = 0x7F800000u;
+        sm.u_bits[1] = 0x7F800000u;
+    }
     // Screen order: ascending clip key K = w'/6.5 (w' > 0) or |w'|/7.5 (otherwise), ties by
     // index.  For any chunk of scales [s_lo, s_hi], the weights whose code is 0 throughout, those
     // that never clip, those that may clip and those whose code is 7 or -8 throughout are then
     // four consecutive ranges of this order (screen_keys).
+    // Scratch until the shortlist: the keys made unique as (key bits, index), which order as
+    // (key, index) since keys are >= 0, and the partial ranks.
+    uint64_t* ck = reinterpret_cast<uint64_t*>(sm.pairF);
+    int* rk = reinterpret_cast<int*>(sm.cand_F);
     float wv = 0.0f, key = 0.0f;
     if (tid < G) {
         wv = sm.w[tid] * pk;
-        key = wv > 0.0f ? wv * (1.0f / 6.5f) : -wv * (1.0f / 7.5f);
-        sm.kz[tid] = key;  // scratch until the prefix sums
+        key = wv > 0.0f ? wv * (1.0f / 6.5f) : fabsf(wv) * (1.0f / 7.5f);  // +0 for a zero weight
+        ck[tid] = ((uint64_t)__float_as_uint(key) << 7) | (uint64_t)tid;
     }
     __syncthreads();
-    int* rk = reinterpret_cast<int*>(sm.pairF);  // scratch: partial ranks (rescoring comes later)
     {
         // rank = number of weights ordered before this one; each half of the block counts over
         // one half of the keys
         const int i = tid & (G - 1), h = tid >> 7;
-        const float ki = sm.kz[i];
-        const float4* k4 = reinterpret_cast<const float4*>(sm.kz + (G / 2) * h);
+        const uint64_t ki = ck[i];
+        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(ck + (G / 2) * h);
         int cnt = 0;
-#pragma unroll 4
-        for (int q = 0; q < G / 8; ++q) {
-            const float4 v = k4[q];
-            const int j = (G / 2) * h + 4 * q;
-            cnt += (v.x < ki || (v.x == ki && j < i)) ? 1 : 0;
-            cnt += (v.y < ki || (v.y == ki && j + 1 < i)) ? 1 : 0;
-            cnt += (v.z < ki || (v.z == ki && j + 2 < i)) ? 1 : 0;
-            cnt += (v.w < ki || (v.w == ki && j + 3 < i)) ? 1 : 0;
+#pragma unroll 8
+        for (int q = 0; q < G / 4; ++q) {
+            const ulonglong2 v = k2[q];
+            cnt += v.x < ki ? 1 : 0;
+            cnt += v.y < ki ? 1 : 0;
         }
         rk[tid] = cnt;
     }
@@ -411,23 +431,25 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
         for (int e = 0; e < E; ++e) sm.ds[rank * E + e] = sm.dt[tid * E + e];
     }
     __syncthreads();
-    // kz[m][e]: the code-0 terms d e^2 = d w'^2 of the first m weights, e^2 rounded and then one
-    // fma each, as in the screen itself (a chunk starts its sums from kz of its code-0 range)
-    if (tid < E) {
-        constexpr int PB = 8;
-        float acc = 0.0f;
-        sm.kz[tid] = 0.0f;
-        for (int r0 = 0; r0 < G; r0 += PB) {
-            float wb[PB], db[PB];  // loads first, so that they overlap
+    // kz[m][e]: the code-0 terms d w'^2 (w'^2 rounded, then the product) of the first m weights
+    // of the screen order, one wave per environment: lane l adds the terms of weights 2l and
+    // 2l + 1, then an inclusive scan over the lanes.  Every term meets at most 10 roundings (a
+    // chunk starts its sums from kz of its code-0 range).
+    for (int e = tid >> 6; e < E; e += BLOCK / 64) {
+        const int l = tid & 63;
+        const float w0 = sm.ws[2 * l], w1 = sm.ws[2 * l + 1];
+        const float t0 = sm.ds[(2 * l) * E + e] * (w0 * w0);
+        const float t1 = sm.ds[(2 * l + 1) * E + e] * (w1 * w1);
+        float x = t0 + t1;
 #pragma unroll
-            for (int q = 0; q < PB; ++q) { wb[q] = sm.ws[r0 + q]; db[q] = sm.ds[(r0 + q) * E + tid]; }
-#pragma unroll
-            for (int q = 0; q < PB; ++q) {
-                const float e2 = wb[q] * wb[q];
-                acc = __builtin_fmaf(db[q], e2, acc);
-                sm.kz[(r0 + q + 1) * E + tid] = acc;
-            }
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(x, o, 64);
+            if (l >= o) x += y;
         }
+        const float below = __shfl_up(x, 1, 64);
+        sm.kz[(2 * l + 1) * E + e] = (l == 0 ? 0.0f : below) + t0;
+        sm.kz[(2 * l + 2) * E + e] = x;
+        if (l == 0) sm.kz[e] = 0.0f;
     }
     __syncthreads();
     pk_out = pk;
@@ -454,26 +476,123 @@ __device__ __forceinline__ void queue_fp64(const SweepArgs& a, int64_t g) {
     }
 }
 
-// The binary32 screen over the chunks of one slice (the chunks c with c % S == slice): each
-// lane's best three (value, pattern) keys for minimax and for pooled.  Waves take the slice's
-// chunks in ascending order from a counter in LDS: chunk costs differ (low scales keep every
-// weight busy, high ones are mostly code-0 sums), and the costly ones go first.
+// Lower bounds on each environment's objective at every scale of a chunk, summed in binary32
+// from non-negative terms.  Z: the code-0 range [0, m_z) contributes its prefix sum kz (a
+// non-decreasing function of the chunk's s_lo).  C: a weight that is clipped (code 7 or -8) at
+// every scale of the chunk contributes d (|w'| - |q| s_hi)^2 when |w'| > |q| s_hi (its residual
+// |w'| - |q| s only grows as s falls below s_hi): a non-increasing function of s_hi.  Every other
+// term counts as 0, so Z + C bounds the chunk, Z bounds every chunk above it and C every chunk
+// below it.  Any weight with |w'| > |q| s_hi has a clip key above the chunk's C threshold, so the
+// range [m_c, G) holds all of them.  The lanes of environment lane % E split the weights; returns
+// per lane the environment's C and Z.
+template <int E>
+__device__ __forceinline__ void chunk_lower_bounds(const SweepSmem<E>& sm, int m_z, int m_c, float s_hi,
+                                                   float& lb_c, float& lb_z) {
+    constexpr int P = 64 / E;
+    const int lane = threadIdx.x & 63, e = lane % E;
+    float v = 0.0f;
+    for (int r = m_c + lane / E; r < G; r += P) {
+        const float w = sm.ws[r];
+        // |q| s_hi is exact (an 11-bit scale times 7 or 8): one rounding, the sign exact
+        const float t = fmaxf(__builtin_fmaf(w > 0.0f ? -7.0f : -8.0f, s_hi, fabsf(w)), 0.0f);
+        v = __builtin_fmaf(sm.ds[r * E + e], t * t, v);
+    }
+#pragma unroll
+    for (int o = E; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    lb_c = v;
+    lb_z = sm.kz[m_z * E + e];
+}
+
+// Maximum (minimax) and sum (pooled) over the environments of a per-lane value of environment
+// lane % E; the same in all lanes.
+template <int E>
+__device__ __forceinline__ void env_max_sum(float v, float& mx, float& su) {
+    mx = v;
+    su = v;
+#pragma unroll
+    for (int o = 1; o < E; o <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        su += __shfl_xor(su, o, 64);
+    }
+}
+
+// The binary32 screen over the chunks of one slice: each lane's best three (value, pattern) keys
+// for minimax and for pooled.  The slice's chunks are c_start + slice + S v upwards and
+// c_start - 1 - slice - S v downwards (v = 0, 1, ...); waves take them from two counters in LDS,
+// each time from the side that has handed out fewer, so the chunks near the optimum come first.
+// A chunk whose lower bound Z + C (chunk_lower_bounds) exceeds 1.001 times the smallest value
+// screened so far (for each policy wanted) is skipped: all its binary32 values would exceed the
+// shortlist threshold.  When C alone does on the way down (Z alone on the way up), so does every
+// further chunk on that side, and that side stops.  With u = 2^-24: the computed bound is at most (1 + 150u) times an exact lower bound
+// of F (at most 143 roundings of non-negative terms along any path), the screen's values are at
+// least (1 - 131u) F (pooled: (1 - 131u)(1 - Eu)), and the threshold is at most 1.00004 (1 + u)
+// times a value already screened, which is below 1.001 (1 - 350u).  Skipped
+// scales are neither the minimum nor in the shortlist, nor can they push a shortlisted key out of
+// a lane's best three, so the outputs are those of the full screen.
 template <int E>
 __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int slice, int S,
                             uint64_t (&mk)[3], uint64_t (&qk)[3]) {
     constexpr int NS = ns_for(E);
     constexpr int CHUNK = 64 * NS;                          // scales per wave per chunk
-    const uint32_t b_top = sm.b_top;
+    // wave-uniform values read from LDS, held in scalar registers
+    const uint32_t b_top = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.b_top);
+    pk = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pk)));
     const int nchunk = (int)((b_top - BITS_FIRST) / CHUNK) + 1;
     const int lane = threadIdx.x & 63;
     const float k0 = sm.ks[lane], k1 = sm.ks[lane + 64];
 #pragma unroll
     for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
+    const int c_start = __builtin_amdgcn_readfirstlane(sm.c_start);
+    volatile uint32_t* u_bits = sm.u_bits;
     for (;;) {
-        int k = 0;
-        if (lane == 0) k = atomicAdd(&sm.next_chunk, 1);
-        const int c = slice + S * __builtin_amdgcn_readfirstlane(k);
-        if (c >= nchunk) break;
+        int cl = -1, down = 0;
+        if (lane == 0) {
+            const int first = *(volatile int*)&sm.next_up <= *(volatile int*)&sm.next_down ? 0 : 1;
+            for (int j = 0; j < 2 && cl < 0; ++j) {
+                if ((first ^ j) == 0) {
+                    const int cc = c_start + slice + S * atomicAdd(&sm.next_up, 1);
+                    if (cc < nchunk && cc < *(volatile int*)&sm.lim_up) cl = cc;
+                } else {
+                    const int cc = c_start - 1 - slice - S * atomicAdd(&sm.next_down, 1);
+                    if (cc >= 0 && cc > *(volatile int*)&sm.lim_down) { cl = cc; down = 1; }
+                }
+            }
+        }
+        const int c = __builtin_amdgcn_readfirstlane(cl);
+        if (c < 0) break;
+        const bool going_down = __builtin_amdgcn_readfirstlane(down) != 0;
+        // The chunk's weight ranges (wave-uniform).  With K~ within 2u of the exact key and
+        // 2^-20 margins on the thresholds:
+        //   K~ <= s_lo/15:       |w'| <= 7.5 K < s_lo/2, code 0 at every scale of the chunk;
+        //   K~ <  1.1333 s_lo:   x in (-8.5, 7.5) (7.367 s_lo or 8.5 s_lo bounds |w'|), never clipped;
+        //   K~ >  s_hi:          w' > 6.5 s_hi or w' < -7.5 s_hi, code 7 or -8 throughout;
+        //   otherwise:           the rounded code may clip.
+        const float s_lo = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        const float s_hi = half_bits_value(min(BITS_FIRST + (uint32_t)(c * CHUNK + CHUNK - 1), b_top)) * pk;
+        const float tz = s_lo * ((1.0f / 15.0f) * (1.0f - 0x1p-20f));
+        const float tu = s_lo * ((8.5f / 7.5f) * (1.0f - 0x1p-20f));
+        const float tc = s_hi * (1.0f + 0x1p-20f);
+        const int m_c = G - (int)(__popcll(__ballot(k0 > tc)) + __popcll(__ballot(k1 > tc)));
+        const int m_u = min(m_c, (int)(__popcll(__ballot(k0 < tu)) + __popcll(__ballot(k1 < tu))));
+        const int m_z = min(m_u, (int)(__popcll(__ballot(k0 <= tz)) + __popcll(__ballot(k1 <= tz))));
+        {
+            float lb_c, lb_z;
+            chunk_lower_bounds<E>(sm, m_z, m_c, s_hi, lb_c, lb_z);
+            float t_max, t_sum, o_max, o_sum;
+            env_max_sum<E>(lb_c + lb_z, t_max, t_sum);
+            env_max_sum<E>(going_down ? lb_c : lb_z, o_max, o_sum);
+            const float um = 1.001f * __uint_as_float(u_bits[0]), up = 1.001f * __uint_as_float(u_bits[1]);
+            const bool side = (!a.want_minimax || o_max > um) && (!a.want_pooled || o_sum > up);
+            const bool skip = (!a.want_minimax || t_max > um) && (!a.want_pooled || t_sum > up);
+            if (__builtin_amdgcn_readfirstlane((int)side)) {
+                if (lane == 0) {
+                    if (going_down) atomicMax(&sm.lim_down, c);
+                    else atomicMin(&sm.lim_up, c);
+                }
+                continue;
+            }
+            if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+        }
         float nsv[NS], inv[NS];
         float acc[NS][E];
         // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
@@ -489,20 +608,6 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
             const float r0 = __builtin_amdgcn_rcpf(s);
             inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
         }
-        // The chunk's weight ranges (wave-uniform).  With K~ within 2u of the exact key and
-        // 2^-20 margins on the thresholds:
-        //   K~ <= s_lo/15:       |w'| <= 7.5 K < s_lo/2, code 0 at every scale of the chunk;
-        //   K~ <  1.1333 s_lo:   x in (-8.5, 7.5) (7.367 s_lo or 8.5 s_lo bounds |w'|), never clipped;
-        //   K~ >  s_hi:          w' > 6.5 s_hi or w' < -7.5 s_hi, code 7 or -8 throughout;
-        //   otherwise:           the rounded code may clip.
-        const float s_lo = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
-        const float s_hi = half_bits_value(min(BITS_FIRST + (uint32_t)(c * CHUNK + CHUNK - 1), b_top)) * pk;
-        const float tz = s_lo * ((1.0f / 15.0f) * (1.0f - 0x1p-20f));
-        const float tu = s_lo * ((8.5f / 7.5f) * (1.0f - 0x1p-20f));
-        const float tc = s_hi * (1.0f + 0x1p-20f);
-        const int m_c = G - (int)(__popcll(__ballot(k0 > tc)) + __popcll(__ballot(k1 > tc)));
-        const int m_u = min(m_c, (int)(__popcll(__ballot(k0 < tu)) + __popcll(__ballot(k1 < tu))));
-        const int m_z = min(m_u, (int)(__popcll(__ballot(k0 <= tz)) + __popcll(__ballot(k1 <= tz))));
         // The sums start from the terms that need no per-scale work: the code-0 ones (the same at
         // every scale, summed once in kz) and, when its closed form is accurate enough, the
         // fixed-code range: acc = fl32(kz + Q_e(s)), one rounding, which the screen's count of
@@ -538,6 +643,7 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
         sweep_list<E, NS, false>(sm.ws, sm.ds, vl, 0, n_u, nsv, inv, acc);
         sweep_list<E, NS, true>(sm.ws, sm.ds, vl, n_u, n_var, nsv, inv, acc);
         if (!closed) sweep_range_clipped<E, NS>(sm.ws, sm.qs, sm.ds, m_c, G, nsv, acc);
+        float bm = __builtin_inff(), bp = __builtin_inff();
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
@@ -549,10 +655,15 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
                 Fm = fmaxf(Fm, v);
                 Ps = Ps + v;
             }
+            bm = fminf(bm, Fm);
+            bp = fminf(bp, Ps);
             const uint64_t km = key_of(Fm, b), kq = key_of(Ps, b);
             if (a.want_minimax && km < mk[2]) top3_insert(mk, km);
             if (a.want_pooled && kq < qk[2]) top3_insert(qk, kq);
         }
+        // values are >= 0, so their bit patterns order as the values do
+        if (a.want_minimax) atomicMin(&sm.u_bits[0], __float_as_uint(bm));
+        if (a.want_pooled) atomicMin(&sm.u_bits[1], __float_as_uint(bp));
     }
 }
 

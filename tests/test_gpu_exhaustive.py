@@ -116,6 +116,50 @@ def test_top_pattern_ranges_sliced_and_unsliced():
         assert np.all(b == a[None]), key
 
 
+def test_optimum_far_from_the_absmax_scale():
+    """The screen starts at the chunk of max|w|/7 and skips chunks whose lower bound exceeds the
+    best value seen.  Groups whose optimum lies far from there: a large weight whose diagonal is
+    tiny (the optimum clips it, several binades below), diagonals that weigh the largest weight
+    only (codes 1..7 of it all fit exactly; the small weights decide, possibly far above), one
+    environment on a few small weights.  Sliced (12 groups) and one workgroup each (tiled)."""
+    rng = np.random.default_rng(31)
+    ws, ds = [], []
+    for big, dbig in ((1.0, 1e-6), (0.5, 1e-4), (8.0, 1e-7), (0.25, 1e-3)):
+        x = rng.normal(0, 0.01, 128)
+        x[9] = big
+        dd = rng.lognormal(0, 0.5, (4, 128))
+        dd[:, 9] = dbig
+        ws.append(x); ds.append(dd)
+    for big in (0.75, 0.0625, 3.0, 0.4):
+        x = rng.normal(0, 0.02, 128)
+        x[50] = big
+        dd = np.full((4, 128), 1e-6) * rng.lognormal(0, 0.3, (4, 128))
+        dd[:, 50] = 1.0
+        ws.append(x); ds.append(dd)
+    for sd in (0.01, 0.03, 0.1, 1.0):
+        x = rng.normal(0, sd, 128)
+        dd = rng.lognormal(0, 1, (4, 128))
+        dd[2] = 1e-5
+        dd[2, :4] = 50.0
+        ws.append(x); ds.append(dd)
+    w = W.round_bf16(np.stack(ws).astype(np.float32))
+    d = np.stack(ds).astype(np.float32)
+    n = w.shape[0]
+    say(f"optimum far from max|w|/7: {n} groups, sliced and tiled")
+    r = _run(w, d, n)
+    sol = oracle.solve(w, d, n, n_threads=threads())
+    check_minimax(w, d, n, r, sol)
+    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
+    start = np.array([int(np.float16(np.abs(w[j]).max() / 7).view(np.uint16)) for j in range(n)])
+    say(f"  winner minus start pattern: {bits_np(r['scales']).astype(np.int64) - start}")
+    reps = 100
+    rt = _run(np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1)), n * reps)
+    for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
+        a = r[key].cpu().numpy()
+        b = rt[key].cpu().numpy().reshape((reps,) + a.shape)
+        assert np.all(b == a[None]), key
+
+
 def test_thirty_two_environments_both_methods():
     """E = 32, the largest environment count: exhaustive (minimax and pooled) and candidate
     against the oracle on 16 groups with per-group diagonals."""
