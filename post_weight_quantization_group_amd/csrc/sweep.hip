@@ -141,9 +141,11 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // most 2^-45 (A + 2 B s + C s^2) (fewer than 140 roundings of 2^-53 along any path), is below
 // 2^-31 of min Q over the chunk [s_lo, s_hi]: then Q~ = Q (1 +- 2^-31) at every scale of the
 // chunk and the screen's bound is unchanged.  Otherwise the range is summed term by term.
+// qlo is the computed min of Q over the chunk (Q at the clamped vertex; A when C = 0); when Q is
+// used, every exact Q over the chunk is at least qlo (1 - 2^-31).
 template <int E>
 __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, int m_c, float s_lo, float s_hi,
-                                                double& A, double& B, double& C) {
+                                                double& A, double& B, double& C, double& qlo) {
     constexpr int P = 64 / E;  // lanes per environment
     const int lane = threadIdx.x & 63, e = lane % E, wave = threadIdx.x >> 6;
     A = 0.0; B = 0.0; C = 0.0;
@@ -164,6 +166,7 @@ __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, 
         C += __shfl_xor(C, o, 64);
     }
     bool ok = true;
+    qlo = A;
     if (C > 0.0) {
         const double lo = (double)s_lo, hi = (double)s_hi;
         const double M = __builtin_fma(hi, __builtin_fma(hi, C, 2.0 * B), A);
@@ -172,6 +175,7 @@ __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, 
         v = v < lo ? lo : (v > hi ? hi : v);
         const double qmin = __builtin_fma(v, __builtin_fma(v, C, -2.0 * B), A);
         ok = M * 0x1p-13 <= qmin;  // 2^-45 M <= 2^-32 qmin, with room for the rounded vertex
+        qlo = qmin;
     }
     return __ballot(!ok) == 0;
 }
@@ -617,9 +621,19 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
         const float inv_hi = __builtin_fmaf(rh0, __builtin_fmaf(-s_hi, rh0, 1.0f), rh0);
         int n_u = 0;
         int n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, false, n_u);
-        double fa = 0.0, fb = 0.0, fc = 0.0;
-        const bool closed = fixed_code_sums<E>(sm, m_z, m_c, s_lo, s_hi, fa, fb, fc);
-        if (!closed) n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, true, n_u);
+        double fa = 0.0, fb = 0.0, fc = 0.0, fq = 0.0;
+        const bool closed = fixed_code_sums<E>(sm, m_z, m_c, s_lo, s_hi, fa, fb, fc, fq);
+        if (closed) {
+            // A second lower bound, now that the fixed codes are summed: kz + min over the chunk
+            // of Q (every other term counts as 0).  Same margins as the first.
+            float t_max, t_sum;
+            env_max_sum<E>((float)(fq + (double)sm.kz[m_z * E + lane % E]), t_max, t_sum);
+            const bool skip = (!a.want_minimax || t_max > 1.001f * __uint_as_float(u_bits[0])) &&
+                              (!a.want_pooled || t_sum > 1.001f * __uint_as_float(u_bits[1]));
+            if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+        } else {
+            n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, true, n_u);
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float z = sm.kz[m_z * E + e];
