@@ -59,10 +59,19 @@ __global__ __launch_bounds__(256) void proxy_module_kernel(const double* __restr
     const int m = blockIdx.x;
     const int64_t lo = off[m], hi = off[m + 1];
     const bool valid = lo >= 0 && hi <= n_groups && lo < hi;
-    double acc = 0.0;
-    if (valid)
-        for (int64_t g = lo + threadIdx.x; g < hi; g += 256) acc += per_group[g];
-    red[threadIdx.x] = acc;
+    // eight accumulators per thread (thread t, slot k: groups lo + t + 256 (8j + k)), added in a
+    // fixed order, so the loads of a pass overlap and repeated runs stay bit-identical
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if (valid) {
+        for (int64_t g0 = lo + threadIdx.x; g0 < hi; g0 += 8 * 256) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int64_t g = g0 + 256 * k;
+                if (g < hi) acc[k] += per_group[g];
+            }
+        }
+    }
+    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
