@@ -59,19 +59,24 @@ __global__ __launch_bounds__(256) void proxy_module_kernel(const double* __restr
     const int m = blockIdx.x;
     const int64_t lo = off[m], hi = off[m + 1];
     const bool valid = lo >= 0 && hi <= n_groups && lo < hi;
-    // eight accumulators per thread (thread t, slot k: groups lo + t + 256 (8j + k)), added in a
-    // fixed order, so the loads of a pass overlap and repeated runs stay bit-identical
-    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    // each thread sums a contiguous run of the module's groups (four interleaved accumulators,
+    // the loads independent of the adds), then a fixed tree: repeated runs are bit-identical
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if (valid) {
-        for (int64_t g0 = lo + threadIdx.x; g0 < hi; g0 += 8 * 256) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int64_t g = g0 + 256 * k;
-                if (g < hi) acc[k] += per_group[g];
-            }
+        const int64_t per = (hi - lo + 255) / 256;
+        const int64_t b = lo + (int64_t)threadIdx.x * per;
+        const int64_t e = b + per < hi ? b + per : hi;
+        int64_t g = b;
+#pragma unroll 4
+        for (; g + 4 <= e; g += 4) {
+            acc[0] += per_group[g];
+            acc[1] += per_group[g + 1];
+            acc[2] += per_group[g + 2];
+            acc[3] += per_group[g + 3];
         }
+        for (; g < e; ++g) acc[0] += per_group[g];
     }
-    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    red[threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
