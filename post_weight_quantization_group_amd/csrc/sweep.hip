@@ -3,17 +3,20 @@
 // For every group the kernel decides among all 31,743 positive finite binary16
 // scales (CliffQuant repository README, "What CliffQuant changes": the
 // independent reference enumerates every one of them; model card
-// "Verification").  It evaluates every pattern up to the top pattern b_top, the
+// "Verification").  It considers every pattern up to the top pattern b_top, the
 // smallest scale >= 2 max|w|: from there on every code is 0, the objective is
 // the same binary64 value at every pattern, and b_top wins all those exact ties
 // by the lower-bit-pattern rule (about 40% of the grid on typical weights).
 // Work split: one 256-thread workgroup per group; weights and diagonals are
 // staged in LDS, sorted by a clip key; each wave takes chunks of 64*NS
-// consecutive scale patterns, NS = 4 per lane, with the per-environment sums
+// consecutive scale patterns, NS = 2 per lane, with the per-environment sums
 // in registers.  Within a chunk the sorted weights fall
 // into four consecutive ranges: code 0 at every scale of the chunk (their
 // terms d w^2 enter as one prefix sum), never clipped, possibly clipped, and
-// code 7 or -8 throughout (no quotient needed).
+// code 7 or -8 throughout (no quotient needed).  Chunks are taken outward from
+// the AbsMax scale's chunk, and a chunk whose proven lower bound exceeds the
+// best value already screened is skipped (screen_keys): branch and bound, with
+// the outputs of the full screen.
 //
 // Exactness.  The sweep runs in binary32 with a proven error bound and is a
 // screen only:
@@ -42,11 +45,12 @@
 
 namespace cqk {
 
-// Scales per lane per chunk, and workgroups per CU.  Four scales per lane (chunks of 256
-// patterns) keep the chunks narrow, so fewer weights change code within one, and leave room for
-// many waves per SIMD: the screen's dependent LDS loads and binary64 chains need the latency
-// hiding more than they suffer from the few spills this costs.  Measured on gfx950 against 8
-// scales at 4 workgroups: E = 1, 2, 4, 8, 16, 32 run 23-26% faster (E = 16 15%).
+// Scales per lane per chunk, and workgroups per CU.  Two scales per lane (chunks of 128
+// patterns) keep the chunks narrow, so fewer weights change code within one and the chunk bounds
+// are tight, and leave room for many waves per SIMD: the screen's dependent LDS loads and
+// binary64 chains need the latency hiding more than they suffer from the few spills this costs.
+// Measured on gfx950 with chunk skipping: 128-pattern chunks beat 256 by 7-8% at E = 4, 64
+// (one scale per lane) lose 30%.
 constexpr int ns_for(int E) { return 2; }
 constexpr int min_blocks_for(int E) { return E == 1 ? 8 : (E <= 4 ? 7 : (E == 8 ? 5 : (E == 16 ? 4 : 2))); }
 constexpr int CAP = 256;                     // shortlist capacity per group
