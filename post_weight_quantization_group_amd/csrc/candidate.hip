@@ -51,8 +51,8 @@ constexpr double SEL_SLACK = 1e-12;
 template <int E>
 struct CandSmem {
     static constexpr int RCAP = rcap_for(E);
-    float w[G];
-    float d[E * G];  // [e][i]
+    __align__(16) float w[G];
+    __align__(16) float d[E * G];  // [e][i]
     uint32_t ev[MAX_EV];
     uint8_t magp[BLOCK];
     double part[3][4 * E];
@@ -69,7 +69,9 @@ struct CandSmem {
     uint32_t cand_b[CCAP];
     double cand_F[CCAP];
     double pairF[BLOCK];
-    int n_runs, n_q, n_cand;
+    int n_runs, n_q, n_cand, n_ev;
+    uint32_t win_lo, win_hi;          // the window of patterns that can hold the optimum
+    double u_probe;                   // F at the AbsMax scale
     uint32_t win_b;
     double win_F;
     int win_state, win_count;
@@ -244,7 +246,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     // ---- staging and input checks (environments a.E..E-1 are zero padding)
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.d[j] = j / G < a.E ? dg[j] : 0.0f;
-    if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; }
+    if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; sm.win_lo = BITS_FIRST; sm.win_hi = BITS_LAST; }
     __syncthreads();
     float bad = 0.0f;
     if (tid < G && !__builtin_isfinite(sm.w[tid])) bad = 1.0f;
@@ -261,10 +263,62 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
         return;
     }
+    const float wmax = block_max_f(tid < G ? fabsf(sm.w[tid]) : 0.0f, sm.redf);
 
-    // ---- 1. code transitions: thread t handles weight t/2, thresholds c = 4(t&1) .. 4(t&1)+3,
-    //         into the fixed slots 8i + c (unused slots hold the padding key)
-    int nvalid = 0;
+    // ---- 0. where the optimum can lie.  U = F at the AbsMax scale s_a (binary64) bounds the
+    //         optimum from above.  Below y_i = |w_i|/|q_i| (q_i = 7 for w_i > 0, -8 otherwise)
+    //         weight i is clipped and its residual is |w_i| - |q_i| s, so every scale with
+    //         s <= (|w_i| - sqrt(1.0001 U / max_e d_ei)) / |q_i| has max_e F_e(s) > U: it is
+    //         neither the answer nor a tie with it.  The largest such bound over the weights (less
+    //         2^-40 for the binary64 roundings) gives the first pattern that can hold the optimum;
+    //         only transitions above it matter.  Thread i < G takes weight i: its residual at s_a
+    //         (waves 0 and 1 sum each environment by a butterfly) and then its bound.
+    uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 7.0f));
+    b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > BITS_LAST ? BITS_LAST : b_a);
+    {
+        const float sa = half_bits_value(b_a);
+        double dmax = 0.0;
+        if (wave < 2) {
+            const double r = __builtin_fma(-(double)sa, (double)exact_code(sm.w[tid], sa), (double)sm.w[tid]);
+            const double r2 = r * r;
+            for (int e = 0; e < E; ++e) {
+                const double dv = (double)sm.d[e * G + tid];
+                dmax = fmax(dmax, dv);
+                double v = dv * r2;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+                if (lane == 0) sm.part[wave][e] = v;
+            }
+        }
+        __syncthreads();
+        double U = 0.0;
+        for (int e = 0; e < E; ++e) U = fmax(U, sm.part[0][e] + sm.part[1][e]);
+        double lo = -1.0;
+        if (wave < 2 && dmax > 0.0 && wmax > 0.0f) {
+            const double aw = fabs((double)sm.w[tid]), qa = sm.w[tid] > 0.0f ? 7.0 : 8.0;
+            lo = (aw - __builtin_sqrt(1.0001 * U / dmax)) / qa * (1.0 - 0x1p-40);
+        }
+        lo = -block_min_d(-lo, sm.redd);  // the largest bound over the weights
+        if (tid == 0) {
+            // the first pattern above lo (never above b_a: F(s_a) <= U)
+            uint32_t b = BITS_FIRST;
+            if (lo >= (double)half_bits_value(BITS_FIRST)) {
+                b = f32_to_half_bits_rne((float)lo);
+                b = b < BITS_FIRST ? BITS_FIRST : (b > b_a ? b_a : b);
+                while (b > BITS_FIRST && (double)half_bits_value(b - 1) > lo) --b;
+                while (b < b_a && (double)half_bits_value(b) <= lo) ++b;
+            }
+            sm.win_lo = b;
+            sm.win_hi = BITS_LAST;
+        }
+        __syncthreads();
+    }
+    const uint32_t win_lo = sm.win_lo, win_hi = sm.win_hi;
+
+    // ---- 1. code transitions inside the window: thread t handles weight t/2, thresholds
+    //         c = 4(t&1) .. 4(t&1)+3; the events are appended in any order (the sort orders them)
+    if (tid == 0) sm.n_ev = 0;
+    __syncthreads();
     {
         const int i = tid >> 1, c0 = 4 * (tid & 1);
         const float wi = sm.w[i];
@@ -274,25 +328,29 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = c0 + k;
-            uint32_t key = 0xFFFFFFFFu;
-            if (wi != 0.0f && c <= cmax && !mag_at_most(aw, c, BITS_FIRST)) {
-                ++m0;  // the magnitude at the first pattern exceeds c
-                if (mag_at_most(aw, c, BITS_LAST)) {
-                    key = (first_at_most(aw, c) << 11) | ((uint32_t)i << 4) | (uint32_t)c;
-                    ++nvalid;
+            if (wi != 0.0f && c <= cmax && !mag_at_most(aw, c, win_lo)) {
+                ++m0;  // the magnitude at the window's first pattern exceeds c
+                if (mag_at_most(aw, c, win_hi)) {
+                    const int j = atomicAdd(&sm.n_ev, 1);
+                    sm.ev[j] = (first_at_most(aw, c) << 11) | ((uint32_t)i << 4) | (uint32_t)c;
                 }
             }
-            sm.ev[8 * i + c] = key;
         }
         sm.magp[tid] = (uint8_t)m0;
     }
-    const int n_ev = block_sum_i(nvalid, sm.redi);  // includes the barrier after the slots
+    __syncthreads();
+    const int n_ev = sm.n_ev;
+    // the sort's size: the next power of two >= n_ev (at least 4), padding keys sort last
+    const int log_n = n_ev <= 4 ? 2 : 32 - __builtin_clz((uint32_t)(n_ev - 1));
+    for (int j = n_ev + tid; j < (1 << log_n); j += BLOCK) sm.ev[j] = 0xFFFFFFFFu;
+    __syncthreads();
 
-    // ---- 2a. sort the events (bitonic over all 1024 slots, ascending; padding sorts last).
-    //          Thread t holds positions 4t..4t+3 in registers: partners closer than 4 are in
-    //          the same thread, closer than 256 in the same wave (lane shuffles); only the
-    //          three stages with partners in another wave go through LDS.
-    {
+    // ---- 2a. sort the events (bitonic, ascending): the first log_n merge phases of the network
+    //          over 1024 positions sort positions 0 .. 2^log_n - 1.  Thread t holds positions
+    //          4t..4t+3 in registers: partners closer than 4 are in the same thread, closer than
+    //          256 in the same wave (lane shuffles); only stages with partners in another wave
+    //          (2^log_n > 256) go through LDS.  Up to 256 events, wave 0 sorts alone.
+    if (log_n > 8 || wave == 0) {
         uint32_t key[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) key[r] = sm.ev[4 * tid + r];
@@ -301,6 +359,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             const int k = 1 << kk;
 #pragma unroll
             for (int jj = kk - 1; jj >= 0; --jj) {
+                if (kk > log_n) continue;  // uniform: the phases past the sort's size
                 const int j = 1 << jj;
                 if (j < 4) {
 #pragma unroll
@@ -335,13 +394,14 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
                 }
             }
         }
-        __syncthreads();
+        if (log_n > 8) __syncthreads();
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm.ev[4 * tid + r] = key[r];
-        __syncthreads();
     }
+    __syncthreads();
 
-    // ---- 2b. coefficients at the first pattern: A = sum d w^2, B0 = sum d |w| |q|, C0 = sum d q^2
+    // ---- 2b. coefficients at the window's first pattern: A = sum d w^2, B0 = sum d |w| |q|,
+    //          C0 = sum d q^2
     if (tid < 4 * E) {
         const int e = tid >> 2, q4 = tid & 3;
         double A = 0.0, B = 0.0, C = 0.0;
@@ -379,13 +439,13 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     bool r_ok[5];
     double r_flo[5], r_fhi[5], r_lb[5], r_mlo[5], r_mhi[5];
     r_ok[0] = tid == 0;
-    r_lo[0] = BITS_FIRST;
-    r_hi[0] = (n_ev > 0 ? (sm.ev[0] >> 11) : (BITS_LAST + 1)) - 1;
+    r_lo[0] = win_lo;
+    r_hi[0] = (n_ev > 0 ? (sm.ev[0] >> 11) : (win_hi + 1)) - 1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int ev_k = e0 + k;
         const uint32_t t = ev_k < n_ev ? (sm.ev[ev_k] >> 11) : 0u;
-        const uint32_t tn = ev_k + 1 < n_ev ? (sm.ev[ev_k + 1] >> 11) : (BITS_LAST + 1);
+        const uint32_t tn = ev_k + 1 < n_ev ? (sm.ev[ev_k + 1] >> 11) : (win_hi + 1);
         r_ok[k + 1] = ev_k < n_ev && tn > t;
         r_lo[k + 1] = t;
         r_hi[k + 1] = tn - 1;
