@@ -129,6 +129,47 @@ __device__ __forceinline__ double wave_inclusive_sum_f64(double x) {
     return x;
 }
 
+// Bitonic sort (ascending) of positions 0 .. 2^log_n - 1 of ev by one wave, 64 KPT >= 2^log_n:
+// lane l holds positions KPT l .. KPT l + KPT - 1 in registers, so partners closer than KPT are in
+// the same lane and the others one lane shuffle away; no barrier is needed.
+template <int KPT>
+__device__ __forceinline__ void wave_sort(uint32_t* ev, int log_n, int lane) {
+    constexpr int LOGMAX = KPT == 4 ? 8 : (KPT == 8 ? 9 : 10);
+    uint32_t key[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) key[r] = ev[KPT * lane + r];
+#pragma unroll
+    for (int kk = 1; kk <= LOGMAX; ++kk) {
+        const int k = 1 << kk;
+#pragma unroll
+        for (int jj = kk - 1; jj >= 0; --jj) {
+            if (kk > log_n) continue;  // uniform: the phases past the sort's size
+            const int j = 1 << jj;
+            if (j < KPT) {
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    if ((r & j) == 0) {
+                        const bool up = ((KPT * lane + r) & k) == 0;
+                        const uint32_t x = key[r], y = key[r + j];
+                        if ((x > y) == up) { key[r] = y; key[r + j] = x; }
+                    }
+                }
+            } else {
+                const int m = j / KPT;  // partner lane: lane ^ m
+                const bool up = ((KPT * lane) & k) == 0, lower = (lane & m) == 0;
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    const uint32_t o = __shfl_xor(key[r], m, 64);
+                    const uint32_t lo = key[r] < o ? key[r] : o, hi = key[r] < o ? o : key[r];
+                    key[r] = lower == up ? lo : hi;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) ev[KPT * lane + r] = key[r];
+}
+
 __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
     const float hs = (float)(2 * c + 1) * 0.5f * half_bits_value(b);
     return a < hs || (a == hs && (c & 1) == 0);
@@ -272,7 +313,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     //         neither the answer nor a tie with it.  The largest such bound over the weights (less
     //         2^-40 for the binary64 roundings) gives the first pattern that can hold the optimum;
     //         only transitions above it matter.  Thread i < G takes weight i: its residual at s_a
-    //         (waves 0 and 1 sum each environment by a butterfly) and then its bound.
+    //         (waves 0 and 1 sum each environment by a DPP scan) and then its bound.
     uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 7.0f));
     b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > BITS_LAST ? BITS_LAST : b_a);
     {
@@ -281,13 +322,13 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         if (wave < 2) {
             const double r = __builtin_fma(-(double)sa, (double)exact_code(sm.w[tid], sa), (double)sm.w[tid]);
             const double r2 = r * r;
+            // the environments' wave sums side by side (DPP scans; lane 63 holds each total)
+#pragma unroll
             for (int e = 0; e < E; ++e) {
                 const double dv = (double)sm.d[e * G + tid];
                 dmax = fmax(dmax, dv);
-                double v = dv * r2;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-                if (lane == 0) sm.part[wave][e] = v;
+                const double v = wave_inclusive_sum_f64(dv * r2);
+                if (lane == 63) sm.part[wave][e] = v;
             }
         }
         __syncthreads();
@@ -349,8 +390,12 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     //          over 1024 positions sort positions 0 .. 2^log_n - 1.  Thread t holds positions
     //          4t..4t+3 in registers: partners closer than 4 are in the same thread, closer than
     //          256 in the same wave (lane shuffles); only stages with partners in another wave
-    //          (2^log_n > 256) go through LDS.  Up to 256 events, wave 0 sorts alone.
-    if (log_n > 8 || wave == 0) {
+    //          (2^log_n > 256) go through LDS.  Up to 512 events, wave 0 sorts alone (wave_sort).
+    if (log_n <= 8) {
+        if (wave == 0) wave_sort<4>(sm.ev, log_n, lane);
+    } else if (log_n == 9) {
+        if (wave == 0) wave_sort<8>(sm.ev, log_n, lane);
+    } else {
         uint32_t key[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) key[r] = sm.ev[4 * tid + r];
