@@ -71,7 +71,6 @@ struct CandSmem {
     double pairF[BLOCK];
     int n_runs, n_q, n_cand, n_ev;
     uint32_t win_lo, win_hi;          // the window of patterns that can hold the optimum
-    double u_probe;                   // F at the AbsMax scale
     uint32_t win_b;
     double win_F;
     int win_state, win_count;
@@ -306,15 +305,17 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
     const float wmax = block_max_f(tid < G ? fabsf(sm.w[tid]) : 0.0f, sm.redf);
 
-    // ---- 0. where the optimum can lie.  U = F at the AbsMax scale s_a (binary64) bounds the
-    //         optimum from above.  Below y_i = |w_i|/|q_i| (q_i = 7 for w_i > 0, -8 otherwise)
-    //         weight i is clipped and its residual is |w_i| - |q_i| s, so every scale with
-    //         s <= (|w_i| - sqrt(1.0001 U / max_e d_ei)) / |q_i| has max_e F_e(s) > U: it is
-    //         neither the answer nor a tie with it.  The largest such bound over the weights (less
-    //         2^-40 for the binary64 roundings) gives the first pattern that can hold the optimum;
-    //         only transitions above it matter.  Thread i < G takes weight i: its residual at s_a
-    //         (waves 0 and 1 sum each environment by a DPP scan) and then its bound.
-    uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 7.0f));
+    // ---- 0. where the optimum can lie.  U = F at s_a = binary16(max|w|/9) (binary64) bounds
+    //         the optimum from above; the minimax optimum usually lies near there, below the
+    //         AbsMax scale, so U is tighter than at max|w|/7.  Below y_i = |w_i|/|q_i| (q_i = 7
+    //         for w_i > 0, -8 otherwise) weight i is clipped and its residual is |w_i| - |q_i| s,
+    //         so every scale with s <= (|w_i| - sqrt(1.0001 U / max_e d_ei)) / |q_i| has
+    //         max_e F_e(s) > U: it is neither the answer nor a tie with it.  The largest such
+    //         bound over the weights (less 2^-40 for the binary64 roundings) gives the first
+    //         pattern that can hold the optimum; only transitions above it matter.  Thread i < G
+    //         takes weight i: its residual at s_a (waves 0 and 1 sum each environment by a DPP
+    //         scan) and then its bound.
+    uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 9.0f));
     b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > BITS_LAST ? BITS_LAST : b_a);
     {
         const float sa = half_bits_value(b_a);
