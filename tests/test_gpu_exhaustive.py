@@ -117,11 +117,13 @@ def test_top_pattern_ranges_sliced_and_unsliced():
 
 
 def test_optimum_far_from_the_absmax_scale():
-    """The screen starts at the chunk of max|w|/7 and skips chunks whose lower bound exceeds the
-    best value seen.  Groups whose optimum lies far from there: a large weight whose diagonal is
-    tiny (the optimum clips it, several binades below), diagonals that weigh the largest weight
-    only (codes 1..7 of it all fit exactly; the small weights decide, possibly far above), one
-    environment on a few small weights.  Sliced (12 groups) and one workgroup each (tiled)."""
+    """The screen starts at the chunk of max|w|/9 and skips chunks whose lower bound exceeds the
+    best value seen; the candidate solver drops transitions below a bound from its probe there.
+    Groups whose optimum lies far from there (8,010 patterns below to 683 above): a large weight
+    whose diagonal is tiny (the optimum clips it, several binades below), diagonals that weigh
+    the largest weight only (codes 1..7 of it all fit exactly; the small weights decide, above),
+    one environment on a few small weights.  Exhaustive sliced (12 groups) and one workgroup each
+    (tiled), and the candidate solver, against the oracle."""
     rng = np.random.default_rng(31)
     ws, ds = [], []
     for big, dbig in ((1.0, 1e-6), (0.5, 1e-4), (8.0, 1e-7), (0.25, 1e-3)):
@@ -150,8 +152,12 @@ def test_optimum_far_from_the_absmax_scale():
     sol = oracle.solve(w, d, n, n_threads=threads())
     check_minimax(w, d, n, r, sol)
     check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
-    start = np.array([int(np.float16(np.abs(w[j]).max() / 7).view(np.uint16)) for j in range(n)])
+    start = np.array([int(np.float16(np.abs(w[j]).max() / 9).view(np.uint16)) for j in range(n)])
     say(f"  winner minus start pattern: {bits_np(r['scales']).astype(np.int64) - start}")
+    # the candidate solver's window (from its probe at max|w|/9) must keep these optima too
+    c = cq.quantize_groups(dev(w), dev(d), n, method="candidate")
+    torch.cuda.synchronize()
+    check_minimax(w, d, n, c, sol)
     reps = 100
     rt = _run(np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1)), n * reps)
     for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
