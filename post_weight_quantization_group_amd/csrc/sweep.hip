@@ -52,7 +52,7 @@ namespace cqk {
 // Measured on gfx950 with chunk skipping: 128-pattern chunks beat 256 by 7-8% at E = 4, 64
 // (one scale per lane) lose 30%.
 constexpr int ns_for(int E) { return 2; }
-constexpr int min_blocks_for(int E) { return E == 1 ? 8 : (E <= 4 ? 7 : (E == 8 ? 5 : (E == 16 ? 4 : 2))); }
+constexpr int min_blocks_for(int E) { return E <= 2 ? 8 : (E == 4 ? 7 : (E == 8 ? 5 : (E == 16 ? 4 : 2))); }
 constexpr int CAP = 256;                     // shortlist capacity per group
 constexpr float SCREEN_RATIO = 1.00004f;
 constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
