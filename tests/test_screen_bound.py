@@ -103,3 +103,29 @@ def test_unskippable_count_is_a_subset_of_the_grid():
     assert np.all(chunks >= 1)
     assert np.all(terms > 0)
     assert terms.sum() <= bench.active_terms(w)
+
+
+@pytest.mark.parametrize("j", range(10))
+def test_candidate_window_drops_only_scales_above_the_probe(j):
+    """The candidate solver ignores every scale s <= lo, lo = max_i (|w_i| - sqrt(1.0001 U /
+    max_e d_ei)) / |q_i| (q_i = 7 for w_i > 0, else -8), with U = max_e F_e at s_a = binary16(
+    max|w|/9).  Below |w_i|/|q_i| weight i is clipped with residual |w_i| - |q_i| s, so every such
+    scale has max_e F_e > 1.0001 U (checked exactly here at every pattern), and the optimum, at
+    most U, lies above lo."""
+    w, d = _groups()[j]
+    a = np.abs(w)
+    if a.max() == 0:
+        return
+    top = int(np.searchsorted(GRID, 2.0 * a.max(), side="left")) + 1
+    F = _objectives(w, d, top).max(axis=0)
+    sa = float(np.float16(a.max() / 9))
+    qa_code = np.clip(np.rint(w / sa), -8, 7)
+    U = (d @ ((w - sa * qa_code) ** 2)).max()
+    qa = np.where(w > 0, 7.0, 8.0)
+    dm = d.max(axis=0)
+    lo = np.where(dm > 0, (a - np.sqrt(1.0001 * U / np.where(dm > 0, dm, 1.0))) / qa, -np.inf).max()
+    below = GRID[:top] <= lo
+    assert np.all(F[below] > 1.0001 * U * (1 - 1e-12))
+    assert GRID[int(np.argmin(F))] > lo
+    if j < 6:
+        assert below.sum() > 0.4 * top  # on typical groups most of the grid is ruled out
