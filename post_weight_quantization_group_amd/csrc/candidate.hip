@@ -1,12 +1,15 @@
 // Candidate-set solver for gfx950.
 //
-// The pages' production solver "enumerates the analytically sufficient
-// candidates induced by code transitions, quadratic vertices, and environment
-// intersections" and sends a tie between direct-candidate objectives to an
-// exhaustive-grid check (CliffQuant repository README, "What CliffQuant
-// changes" and "Verification"; model card "Verification").  The steps here
-// are our own design of that idea on the binary16 grid:
+// The pages' production solver lists the scales that can be optimal -- those
+// where a code changes, the vertices of the quadratic pieces, and the points
+// where two environments' errors cross -- and hands a tie between directly
+// scored candidates to an exhaustive check of the grid (CliffQuant repository
+// README, "What CliffQuant changes" and "Verification"; model card
+// "Verification").  The steps here are our own design of that idea on the
+// binary16 grid:
 //
+//  0. Window.  Scales below a bound from the best single clipped weight
+//     against F at max|w|/9 cannot be optimal; no transition below it is kept.
 //  1. Code transitions.  For w_i != 0 and each c with |q_i| able to fall from
 //     c+1 to c, the first grid pattern t where |q_i(s_t)| <= c.  The test
 //     |q| <= c  <=>  |w| < (c+1/2) s  or  (|w| == (c+1/2) s and c even)  is
@@ -14,7 +17,8 @@
 //     in s; t is the binary16 rounding of |w|/(c+1/2) confirmed by a short walk
 //     on that predicate (bisection if the walk does not settle).
 //  2. Runs.  The events are sorted by t (a bitonic sort held in registers:
-//     lane shuffles, with 3 of its 55 stages through LDS); between two
+//     lane shuffles; one wave up to 512 events, else four waves with 3 stages
+//     through LDS); between two
 //     consecutive event patterns every code is constant, so each environment
 //     error is the quadratic f_e(s) = A_e - 2 B_e s + C_e s^2 with
 //     B_e = sum d w q, C_e = sum d q^2.  A block-wide prefix sum over the
