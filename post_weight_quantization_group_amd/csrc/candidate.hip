@@ -132,21 +132,6 @@ __device__ __forceinline__ double wave_inclusive_sum_f64(double x) {
     return x;
 }
 
-// The value of lane (lane ^ m) for m = 1, 2, 4, 8 through DPP (quad_perm [1,0,3,2] and
-// [2,3,0,1]; half-row mirror, i.e. xor 7, then quad_perm [3,2,1,0], i.e. xor 3; row rotate by 8),
-// with no LDS round trip; a lane shuffle for larger m.  m is a constant once the callers' loops
-// are unrolled.
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int m) {
-    switch (m) {
-        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-        case 4: return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false),
-                                                          0x1B, 0xF, 0xF, false);
-        case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
-        default: return (uint32_t)__shfl_xor((int)v, m, 64);
-    }
-}
-
 // Bitonic sort (ascending) of positions 0 .. 2^log_n - 1 of ev by one wave, 64 KPT >= 2^log_n:
 // lane l holds positions KPT l .. KPT l + KPT - 1 in registers, so partners closer than KPT are in
 // the same lane and the others one lane shuffle away; no barrier is needed.

@@ -103,23 +103,47 @@ __device__ __forceinline__ uint32_t f32_to_half_bits_rne(float x) {
     return (ex << 10) + r;  // a carry out of the fraction bumps the exponent, as it should
 }
 
+// ---------------------------------------------------------------- lane exchange
+// The value of lane (lane ^ m) for m = 1, 2, 4, 8 through DPP moves (quad_perm [1,0,3,2] and
+// [2,3,0,1]; half-row mirror, i.e. xor 7, then quad_perm [3,2,1,0], i.e. xor 3; row rotate by 8),
+// with no LDS round trip; a lane shuffle for larger m.  m is a constant once the callers' loops
+// are unrolled.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int m) {
+    switch (m) {
+        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+        case 4: return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false),
+                                                          0x1B, 0xF, 0xF, false);
+        case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+        default: return (uint32_t)__shfl_xor((int)v, m, 64);
+    }
+}
+__device__ __forceinline__ float lane_xor(float v, int m) { return __uint_as_float(lane_xor(__float_as_uint(v), m)); }
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v, int m) {
+    const uint32_t lo = lane_xor((uint32_t)v, m), hi = lane_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double lane_xor(double v, int m) {
+    return __builtin_bit_cast(double, lane_xor(__builtin_bit_cast(uint64_t, v), m));
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t u = __shfl_xor(v, o, 64);
+        const uint64_t u = lane_xor(v, o);
         v = u < v ? u : v;
     }
     return v;
 }
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, lane_xor(v, o));
     return v;
 }
 __device__ __forceinline__ float wave_min_f(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, lane_xor(v, o));
     return v;
 }
 
@@ -161,7 +185,7 @@ __device__ __forceinline__ void block_max_fn(float (&v)[N], float* red) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) v[k] = fmaxf(v[k], __shfl_xor(v[k], o, 64));
+        for (int k = 0; k < N; ++k) v[k] = fmaxf(v[k], lane_xor(v[k], o));
     }
     __syncthreads();
     if ((threadIdx.x & 63) == 0) {

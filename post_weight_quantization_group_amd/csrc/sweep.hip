@@ -165,9 +165,9 @@ __device__ __forceinline__ bool fixed_code_sums(const SweepSmem<E>& sm, int r0, 
     }
 #pragma unroll
     for (int o = E; o < 64; o <<= 1) {
-        A += __shfl_xor(A, o, 64);
-        B += __shfl_xor(B, o, 64);
-        C += __shfl_xor(C, o, 64);
+        A += lane_xor(A, o);
+        B += lane_xor(B, o);
+        C += lane_xor(C, o);
     }
     bool ok = true;
     qlo = A;
@@ -508,7 +508,7 @@ __device__ __forceinline__ void chunk_lower_bounds(const SweepSmem<E>& sm, int m
         v = __builtin_fmaf(sm.ds[r * E + e], t * t, v);
     }
 #pragma unroll
-    for (int o = E; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    for (int o = E; o < 64; o <<= 1) v += lane_xor(v, o);
     lb_c = v;
     lb_z = sm.kz[m_z * E + e];
 }
@@ -521,8 +521,8 @@ __device__ __forceinline__ void env_max_sum(float v, float& mx, float& su) {
     su = v;
 #pragma unroll
     for (int o = 1; o < E; o <<= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        su += __shfl_xor(su, o, 64);
+        mx = fmaxf(mx, lane_xor(mx, o));
+        su += lane_xor(su, o);
     }
 }
 
