@@ -83,7 +83,7 @@ struct CandSmem {
 __device__ __forceinline__ double wave_min_d(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const double u = __shfl_xor(v, o, 64);
+        const double u = lane_xor(v, o);
         v = u < v ? u : v;
     }
     return v;
@@ -100,7 +100,7 @@ __device__ __forceinline__ double block_min_d(double v, double* red) {
 }
 __device__ __forceinline__ int block_sum_i(int v, int* red) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    for (int o = 32; o > 0; o >>= 1) v += (int)lane_xor((uint32_t)v, o);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -537,7 +537,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         double cB[4], cC[4];  // coefficients at this thread's first run
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            double exB = __shfl_up(inc[v], 1, 64), exC = __shfl_up(inc[4 + v], 1, 64);
+            double exB = lane_prev(inc[v]), exC = lane_prev(inc[4 + v]);
             if (lane == 0) { exB = 0.0; exC = 0.0; }
             for (int w2 = 0; w2 < wave; ++w2) { exB += sm.wtot[w2][v]; exC += sm.wtot[w2][4 + v]; }
             cB[v] = v < NB ? sm.B0[eb + v] + exB : 0.0;
@@ -637,10 +637,10 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
                     C = __builtin_fma(dv, q * q, C);
                 }
             }
-            B += __shfl_xor(B, 1, 64);
-            C += __shfl_xor(C, 1, 64);
-            B += __shfl_xor(B, 2, 64);
-            C += __shfl_xor(C, 2, 64);
+            B += lane_xor(B, 1);
+            C += lane_xor(C, 1);
+            B += lane_xor(B, 2);
+            C += lane_xor(C, 2);
             if (live && part == 0) {
                 sm.run_B[r][e] = B;
                 sm.run_C[r][e] = C;

@@ -126,6 +126,31 @@ __device__ __forceinline__ uint64_t lane_xor(uint64_t v, int m) {
 __device__ __forceinline__ double lane_xor(double v, int m) {
     return __builtin_bit_cast(double, lane_xor(__builtin_bit_cast(uint64_t, v), m));
 }
+// The value of lane (lane - 1), 0 in lane 0 (DPP wave shift right by one).
+__device__ __forceinline__ uint32_t lane_prev(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float lane_prev(float v) { return __uint_as_float(lane_prev(__float_as_uint(v))); }
+__device__ __forceinline__ double lane_prev(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = ((uint64_t)lane_prev((uint32_t)(u >> 32)) << 32) | lane_prev((uint32_t)u);
+    return __builtin_bit_cast(double, r);
+}
+// Inclusive prefix sum over the 64 lanes of a wave through DPP: row_shr 1, 2, 4, 8 within each
+// row of 16 lanes (lanes with no source add 0), then row_bcast15 and row_bcast31 carry the
+// totals of the earlier rows.
+__device__ __forceinline__ float wave_inclusive_sum_f32(float x) {
+#define CQ_SCAN_STEP32(ctrl, rmask) \
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xF, true));
+    CQ_SCAN_STEP32(0x111, 0xF)
+    CQ_SCAN_STEP32(0x112, 0xF)
+    CQ_SCAN_STEP32(0x114, 0xF)
+    CQ_SCAN_STEP32(0x118, 0xF)
+    CQ_SCAN_STEP32(0x142, 0xA)
+    CQ_SCAN_STEP32(0x143, 0xC)
+#undef CQ_SCAN_STEP32
+    return x;
+}
 
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {

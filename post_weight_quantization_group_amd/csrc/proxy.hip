@@ -17,7 +17,7 @@ namespace cqk {
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    for (int o = 32; o > 0; o >>= 1) v += lane_xor(v, o);
     return v;
 }
 

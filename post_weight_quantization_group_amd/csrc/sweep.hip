@@ -450,14 +450,8 @@ __device__ int stage_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm, floa
         const float w0 = sm.ws[2 * l], w1 = sm.ws[2 * l + 1];
         const float t0 = sm.ds[(2 * l) * E + e] * (w0 * w0);
         const float t1 = sm.ds[(2 * l + 1) * E + e] * (w1 * w1);
-        float x = t0 + t1;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(x, o, 64);
-            if (l >= o) x += y;
-        }
-        const float below = __shfl_up(x, 1, 64);
-        sm.kz[(2 * l + 1) * E + e] = (l == 0 ? 0.0f : below) + t0;
+        const float x = wave_inclusive_sum_f32(t0 + t1);
+        sm.kz[(2 * l + 1) * E + e] = lane_prev(x) + t0;  // lane 0 adds 0
         sm.kz[(2 * l + 2) * E + e] = x;
         if (l == 0) sm.kz[e] = 0.0f;
     }
