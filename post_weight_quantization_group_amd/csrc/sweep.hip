@@ -597,21 +597,6 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
             }
             if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
         }
-        float nsv[NS], inv[NS];
-        float acc[NS][E];
-        // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
-        // otherwise share a lane; exact ties at power-of-two spacing (an outlier alone carrying a
-        // code) then fill one lane's top three.  Rotating by 5 per chunk spreads them out.
-        const int rot = (lane + 5 * c) & 63;
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), b_top);
-            const float s = half_bits_value(b) * pk;
-            nsv[t] = -s;
-            // reciprocal within 1 binary32 ulp: hardware estimate plus one Newton step
-            const float r0 = __builtin_amdgcn_rcpf(s);
-            inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
-        }
         // The sums start from the terms that need no per-scale work: the code-0 ones (the same at
         // every scale, summed once in kz) and, when its closed form is accurate enough, the
         // fixed-code range: acc = fl32(kz + Q_e(s)), one rounding, which the screen's count of
@@ -633,6 +618,21 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
             if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
         } else {
             n_var = classify_chunk<E>(sm, m_z, m_u, m_c, inv_lo, inv_hi, true, n_u);
+        }
+        float nsv[NS], inv[NS];
+        float acc[NS][E];
+        // Lane rotation: pattern b and b + 0x400k (the same fraction, 2^k times larger) would
+        // otherwise share a lane; exact ties at power-of-two spacing (an outlier alone carrying a
+        // code) then fill one lane's top three.  Rotating by 5 per chunk spreads them out.
+        const int rot = (lane + 5 * c) & 63;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), b_top);
+            const float s = half_bits_value(b) * pk;
+            nsv[t] = -s;
+            // reciprocal within 1 binary32 ulp: hardware estimate plus one Newton step
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
