@@ -226,10 +226,11 @@ def measure_all_configs() -> dict:
             _, ms = _timed(lambda: cq.pack_gptq_v1(codes, sc, mat.out, mat.inp))
             tot["pack_ms"] += ms
             off = torch.tensor([0, n], dtype=torch.int64, device=dev)
-            for name, sv in (("minimax", r["scales"]), ("pooled", r["pooled_scales"]), ("absmax", ab["scales"])):
-                (_, mm, _), ms = _timed(lambda: cq.proxy_worst_env_wmse(wt, dt, sv, off, p, per_group=False))
-                tot["proxy_ms"] += ms
-                module_means[name].append(float(mm.cpu()[0]))
+            sv = torch.stack((r["scales"], r["pooled_scales"], ab["scales"]))
+            (_, mm, _), ms = _timed(lambda: cq.proxy_worst_env_wmse_multi(wt, dt, sv, off, p, per_group=False))
+            tot["proxy_ms"] += ms
+            for j, name in enumerate(("minimax", "pooled", "absmax")):
+                module_means[name].append(float(mm.cpu()[j, 0]))
             f = c["flags"].cpu().numpy()
             tot["fallback"] += int(np.count_nonzero(f & cq.FLAG_FALLBACK))
             tot["fp64_sweep"] += int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP))
@@ -350,17 +351,15 @@ def main():
             "name": mat.name, "out": mat.out, "inp": mat.inp, "n": n, "p": p,
             "w_np": w, "d_np": d, "patterns": float(screened_patterns(w).mean()),
             "w": torch.from_numpy(w).to(dev), "d": torch.from_numpy(d).to(dev),
-            "scales": torch.empty(n, dtype=torch.int16, device=dev),
+            "sc3": torch.empty((3, n), dtype=torch.int16, device=dev),
             "codes": torch.empty((n, 128), dtype=torch.int8, device=dev),
             "obj": torch.empty(n, dtype=torch.float64, device=dev),
             "flags": torch.empty(n, dtype=torch.uint8, device=dev),
-            "pscales": torch.empty(n, dtype=torch.int16, device=dev),
             "pobj": torch.empty(n, dtype=torch.float64, device=dev),
             "cscales": torch.empty(n, dtype=torch.int16, device=dev),
             "ccodes": torch.empty((n, 128), dtype=torch.int8, device=dev),
             "cobj": torch.empty(n, dtype=torch.float64, device=dev),
             "cflags": torch.empty(n, dtype=torch.uint8, device=dev),
-            "ascales": torch.empty(n, dtype=torch.int16, device=dev),
             "acodes": torch.empty((n, 128), dtype=torch.int8, device=dev),
             "aobj": torch.empty(n, dtype=torch.float64, device=dev),
             "qweight": torch.empty((mat.inp // 8, mat.out), dtype=torch.int32, device=dev),
@@ -372,6 +371,7 @@ def main():
             "macro": torch.empty((3, 1), dtype=torch.float64, device=dev),
             "pg": torch.empty((3, n), dtype=torch.float64, device=dev),
         }
+        t["scales"], t["pscales"], t["ascales"] = t["sc3"][0], t["sc3"][1], t["sc3"][2]
         mats.append(t)
     n_total = sum(t["n"] for t in mats)
     if args.copy_calibration_mib > 0:
@@ -409,9 +409,9 @@ def main():
             cq.cq_baseline_scales(t["w"], t["d"], t["p"], E, t["n"], cq.ABSMAX, t["ascales"], t["acodes"],
                                   t["aobj"])
             cq.cq_pack_gptq_v1(t["codes"], t["scales"], t["out"], t["inp"], t["qweight"], t["qscales"])
-            for j, sc in enumerate((t["scales"], t["pscales"], t["ascales"])):
-                cq.cq_proxy_worst_env_wmse(t["w"], t["d"], t["p"], E, t["n"], sc, t["off"], 1, t["mm"][j],
-                                           t["macro"][j], t["pg"][j])
+            # minimax, pooled and AbsMax scales are the rows of sc3: one proxy pass for all three
+            cq.cq_proxy_worst_env_wmse_multi(t["w"], t["d"], t["p"], E, t["n"], 3, t["sc3"], t["off"], 1, t["mm"],
+                                             t["macro"], t["pg"])
 
     for _ in range(args.warmup):
         step(False)

@@ -57,6 +57,7 @@ extern "C" {
 #define CQ_ABI_VERSION 1
 #define CQ_GROUP 128
 #define CQ_MAX_ENVS 32
+#define CQ_MAX_POLICIES 64
 
 /* Status codes. */
 #define CQ_OK 0
@@ -162,6 +163,26 @@ int32_t cq_proxy_worst_env_wmse(const float *w, const float *d_eval, int64_t d_p
                                 const int64_t *module_offsets, int32_t n_modules,
                                 double *module_mean, double *macro, double *per_group,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same proxy for n_policies scale policies of the same groups in one call
+ * (the model card compares the minimax scales with the AbsMax baseline on this
+ * proxy: Qwen3.5-0.8B-Base-CliffQuant-W4A16-G128 model card, "Held-out
+ * reconstruction proxy"); w and d_eval are read once for all of them, and each
+ * policy's results equal those of a cq_proxy_worst_env_wmse call on its own
+ * scales bit for bit.
+ *   scales       device uint16 [n_policies][n_groups].
+ *   module_mean  out, double [n_policies][n_modules].
+ *   macro        out, double [n_policies].
+ *   per_group    out, nullable, double [n_policies][n_groups].
+ * 1 <= n_policies <= CQ_MAX_POLICIES.  workspace (only when per_group is
+ * NULL): cq_proxy_workspace_size(n_policies * n_groups) bytes.
+ */
+int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64_t d_period, int32_t E,
+                                      int64_t n_groups, int32_t n_policies, const uint16_t *scales,
+                                      const int64_t *module_offsets, int32_t n_modules,
+                                      double *module_mean, double *macro, double *per_group,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,8 +28,9 @@ __all__ = [
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
     "cq_quantize_groups", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
-    "cq_proxy_worst_env_wmse", "quantize_groups", "baseline_scales", "pack_gptq_v1",
-    "proxy_worst_env_wmse", "solve_breakpoint_exact", "EXPORTED_SYMBOLS",
+    "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
+    "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
+    "EXPORTED_SYMBOLS",
 ]
 
 GROUP = 128
@@ -39,7 +40,7 @@ FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
-                    "cq_proxy_worst_env_wmse")
+                    "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -81,6 +82,8 @@ def load():
         lib.cq_proxy_workspace_size.argtypes = [I64]
         lib.cq_proxy_worst_env_wmse.restype = I32
         lib.cq_proxy_worst_env_wmse.argtypes = [P, P, I64, I32, I64, P, P, I32, P, P, P, P, SZ, P]
+        lib.cq_proxy_worst_env_wmse_multi.restype = I32
+        lib.cq_proxy_worst_env_wmse_multi.argtypes = [P, P, I64, I32, I64, I32, P, P, I32, P, P, P, P, SZ, P]
         _lib = lib
     return _lib
 
@@ -157,6 +160,15 @@ def cq_proxy_worst_env_wmse(w, d_eval, d_period, E, n_groups, scales, module_off
                                           _p(module_offsets), n_modules, _p(module_mean), _p(macro),
                                           _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
            "cq_proxy_worst_env_wmse")
+
+
+def cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, n_policies, scales, module_offsets, n_modules,
+                                  module_mean, macro, per_group=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_proxy_worst_env_wmse_multi(_p(w), _p(d_eval), d_period, E, n_groups, n_policies, _p(scales),
+                                                _p(module_offsets), n_modules, _p(module_mean), _p(macro),
+                                                _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
+           "cq_proxy_worst_env_wmse_multi")
 
 
 # ---------------------------------------------------------------- helpers
@@ -241,6 +253,26 @@ def proxy_worst_env_wmse(w, d_eval, scales, module_offsets, d_period=None, per_g
     ws = None if per_group else _workspace(cq_proxy_workspace_size(n), dev)
     cq_proxy_worst_env_wmse(w, d_eval, d_period, E, n, scales, module_offsets, n_modules, mm, macro, pg, ws,
                             stream)
+    return pg, mm, macro
+
+
+def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None, per_group=True, stream=None):
+    """The proxy for several policies at once: scales [P, n_groups] int16 on the device.
+    Returns (per_group [P, n] or None, module_mean [P, n_modules], macro [P]) as float64 device tensors."""
+    _shape_check(w, d_eval)
+    n, E = w.shape[0], d_eval.shape[1]
+    if scales.dim() != 2 or scales.shape[1] != n:
+        raise ValueError("scales must be [n_policies, n_groups]")
+    n_pol = scales.shape[0]
+    d_period = d_eval.shape[0] if d_period is None else int(d_period)
+    n_modules = module_offsets.numel() - 1
+    dev = w.device
+    mm = torch.empty((n_pol, n_modules), dtype=torch.float64, device=dev)
+    macro = torch.empty(n_pol, dtype=torch.float64, device=dev)
+    pg = torch.empty((n_pol, n), dtype=torch.float64, device=dev) if per_group else None
+    ws = None if per_group else _workspace(cq_proxy_workspace_size(n * n_pol), dev)
+    cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n, n_pol, scales, module_offsets, n_modules, mm, macro,
+                                  pg, ws, stream)
     return pg, mm, macro
 
 

@@ -107,7 +107,7 @@ int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int
     if (n_groups < 0 || n_groups > INT32_MAX) return CQ_EINVAL;
     if (which == CQ_ABSMAX) {
         if (n_groups == 0) return CQ_OK;
-        if (!w || !scales || !aligned(w, 16)) return CQ_EINVAL;
+        if (!w || !scales || !aligned(w, 16) || (codes && !aligned(codes, 16))) return CQ_EINVAL;
         if (objective && !groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
         return hip_status(cqk::launch_absmax(w, d, d_period, E, n_groups, scales, codes, objective, st));
     }
@@ -144,23 +144,34 @@ size_t cq_proxy_workspace_size(int64_t n_groups) {
     return n_groups < 0 ? 0 : round_up((size_t)n_groups * 8u);
 }
 
-int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_period, int32_t E, int64_t n_groups,
-                                const uint16_t* scales, const int64_t* module_offsets, int32_t n_modules,
-                                double* module_mean, double* macro, double* per_group, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+int32_t cq_proxy_worst_env_wmse_multi(const float* w, const float* d_eval, int64_t d_period, int32_t E,
+                                      int64_t n_groups, int32_t n_policies, const uint16_t* scales,
+                                      const int64_t* module_offsets, int32_t n_modules, double* module_mean,
+                                      double* macro, double* per_group, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
     if (!groups_ok(w, d_eval, d_period, E, n_groups)) return CQ_EINVAL;
+    if (n_policies < 1 || n_policies > CQ_MAX_POLICIES) return CQ_EINVAL;
     if (n_modules < 1 || !module_offsets || !module_mean || !macro) return CQ_EINVAL;
     if (n_groups > 0 && !scales) return CQ_EINVAL;
-    if (n_groups / 4 + 1 > INT32_MAX) return CQ_EINVAL;
+    if ((n_groups + 15) / 16 > INT32_MAX || n_groups > INT64_MAX / 8 / n_policies) return CQ_EINVAL;
     if (!per_group) {
-        if (!workspace || workspace_bytes < cq_proxy_workspace_size(n_groups) || !aligned(workspace, ALIGN))
+        if (!workspace || workspace_bytes < cq_proxy_workspace_size(n_groups * n_policies) ||
+            !aligned(workspace, ALIGN))
             return CQ_EWORKSPACE;
         per_group = (double*)workspace;
     } else if (!aligned(per_group, 8)) {
         return CQ_EINVAL;
     }
-    return hip_status(cqk::launch_proxy(w, d_eval, d_period, E, n_groups, scales, module_offsets, n_modules,
-                                        module_mean, macro, per_group, (hipStream_t)stream));
+    return hip_status(cqk::launch_proxy(w, d_eval, d_period, E, n_groups, n_policies, scales, module_offsets,
+                                        n_modules, module_mean, macro, per_group, (hipStream_t)stream));
+}
+
+int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_period, int32_t E, int64_t n_groups,
+                                const uint16_t* scales, const int64_t* module_offsets, int32_t n_modules,
+                                double* module_mean, double* macro, double* per_group, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, 1, scales, module_offsets, n_modules,
+                                         module_mean, macro, per_group, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -5,111 +5,152 @@
 //   p_g   = max_e (1/128) sum_i d_eval[e][i] (w_i - s_g q_i(s_g))^2   (binary64)
 //   mean over each module's groups, then the mean over modules.
 //
-// Stage 1: one wave per group, two weights per lane; each lane forms its two
-// squared residuals once and the E environment sums are wave-reduced in
-// binary64.  Stage 2: one workgroup per module sums its p_g in a fixed order.
-// Stage 3: one workgroup averages the module means in a fixed order.  Every
-// reduction order is fixed, so repeated runs are bit-identical.
+// Several scale policies are evaluated in one pass (scales [P][n_groups],
+// outputs [P][...]): the weights and diagonals are read once for all of them.
+// Stage 1: 16 lanes per group, four groups per wave, eight weights per lane.
+// Each lane forms its weights' squared residuals at each policy's scale once;
+// the E environment sums are reduced over the group's 16 lanes (one DPP row,
+// lane xor 1, 2, 4, 8) in binary64.  Stage 2: one workgroup per (module,
+// policy) sums its p_g in a fixed order.  Stage 3: one workgroup per policy
+// averages the module means in a fixed order.  Every reduction order is fixed,
+// so repeated runs are bit-identical, and a policy's results do not depend on
+// which other policies share the call.
 #include "device.h"
 #include "launch.h"
 
 namespace cqk {
 
+__device__ __forceinline__ double row_sum_f64(double v) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += lane_xor(v, o);
+    return v;
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += lane_xor(v, o);
     return v;
 }
 
+constexpr int PROXY_PCHUNK = 4;  // policies whose residuals a lane holds at once
+
 __global__ __launch_bounds__(256) void proxy_group_kernel(const float* __restrict__ w, const float* __restrict__ d,
-                                                          int64_t d_period, int E, int64_t n_groups,
+                                                          int64_t d_period, int E, int64_t n_groups, int P,
                                                           const uint16_t* __restrict__ scales,
                                                           double* __restrict__ per_group) {
-    const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int sub = threadIdx.x & 15;
+    const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    // a group owns one whole DPP row, so every lane of a row is live or none is
     if (g >= n_groups) return;
-    const float* dg = d + (g % d_period) * (int64_t)E * G;
-    const float2 wv = ((const float2*)(w + g * G))[lane];
-    const double s = (double)half_bits_value(scales[g]);
-    const double inv = 1.0 / s;
-    double t2[2];
-    const float wl[2] = {wv.x, wv.y};
+    const float4* wr = (const float4*)(w + g * G) + 2 * sub;
+    const float4 w0 = wr[0], w1 = wr[1];
+    const float wl[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const float* dg = d + (g % d_period) * (int64_t)E * G + 8 * sub;
+    for (int p0 = 0; p0 < P; p0 += PROXY_PCHUNK) {
+        const int np = P - p0 < PROXY_PCHUNK ? P - p0 : PROXY_PCHUNK;
+        double t2[PROXY_PCHUNK][8], worst[PROXY_PCHUNK];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const double wi = (double)wl[h];
-        double r = __builtin_rint(wi * inv);
-        r = r < -8.0 ? -8.0 : (r > 7.0 ? 7.0 : r);
-        const double t = wi - s * r;
-        t2[h] = t * t;
+        for (int k = 0; k < PROXY_PCHUNK; ++k) {
+            worst[k] = 0.0;
+            const double s = k < np ? (double)half_bits_value(scales[(int64_t)(p0 + k) * n_groups + g]) : 1.0;
+            const double inv = 1.0 / s;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double wi = (double)wl[j];
+                double r = __builtin_rint(wi * inv);
+                r = r < -8.0 ? -8.0 : (r > 7.0 ? 7.0 : r);
+                const double t = wi - s * r;
+                t2[k][j] = t * t;
+            }
+        }
+        for (int e = 0; e < E; ++e) {
+            const float4* dr = (const float4*)(dg + e * G);
+            const float4 d0 = dr[0], d1 = dr[1];
+            const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+            for (int k = 0; k < PROXY_PCHUNK; ++k) {
+                if (k < np) {
+                    double part = 0.0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) part += (double)dl[j] * t2[k][j];
+                    part = row_sum_f64(part);
+                    worst[k] = e == 0 ? part : (part > worst[k] ? part : worst[k]);
+                }
+            }
+        }
+        if (sub == 0) {
+#pragma unroll
+            for (int k = 0; k < PROXY_PCHUNK; ++k)
+                if (k < np) per_group[(int64_t)(p0 + k) * n_groups + g] = worst[k] / 128.0;
+        }
     }
-    double worst = 0.0;
-    for (int e = 0; e < E; ++e) {
-        const float2 dv = ((const float2*)(dg + e * G))[lane];
-        double part = (double)dv.x * t2[0] + (double)dv.y * t2[1];
-        part = wave_sum_f64(part);
-        worst = e == 0 ? part : (part > worst ? part : worst);
-    }
-    if (lane == 0) per_group[g] = worst / 128.0;
 }
 
-__global__ __launch_bounds__(256) void proxy_module_kernel(const double* __restrict__ per_group,
-                                                           const int64_t* __restrict__ off, int64_t n_groups,
-                                                           double* __restrict__ module_mean) {
-    __shared__ double red[256];
+constexpr int MODULE_THREADS = 1024;
+
+// grid (n_modules, P)
+__global__ __launch_bounds__(MODULE_THREADS) void proxy_module_kernel(const double* __restrict__ per_group,
+                                                                      const int64_t* __restrict__ off,
+                                                                      int64_t n_groups, int n_modules,
+                                                                      double* __restrict__ module_mean) {
+    __shared__ double red[MODULE_THREADS / 64];
     const int m = blockIdx.x;
+    const double* pg = per_group + (int64_t)blockIdx.y * n_groups;
     const int64_t lo = off[m], hi = off[m + 1];
     const bool valid = lo >= 0 && hi <= n_groups && lo < hi;
     // each thread sums a contiguous run of the module's groups (four interleaved accumulators,
     // the loads independent of the adds), then a fixed tree: repeated runs are bit-identical
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if (valid) {
-        const int64_t per = (hi - lo + 255) / 256;
+        const int64_t per = (hi - lo + MODULE_THREADS - 1) / MODULE_THREADS;
         const int64_t b = lo + (int64_t)threadIdx.x * per;
         const int64_t e = b + per < hi ? b + per : hi;
         int64_t g = b;
-#pragma unroll 4
+#pragma unroll 2
         for (; g + 4 <= e; g += 4) {
-            acc[0] += per_group[g];
-            acc[1] += per_group[g + 1];
-            acc[2] += per_group[g + 2];
-            acc[3] += per_group[g + 3];
+            acc[0] += pg[g];
+            acc[1] += pg[g + 1];
+            acc[2] += pg[g + 2];
+            acc[3] += pg[g + 3];
         }
-        for (; g < e; ++g) acc[0] += per_group[g];
+        for (; g < e; ++g) acc[0] += pg[g];
     }
-    red[threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const double v = wave_sum_f64((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = red[0];
+        for (int k = 1; k < MODULE_THREADS / 64; ++k) t += red[k];
+        module_mean[(int64_t)blockIdx.y * n_modules + m] = valid ? t / (double)(hi - lo) : __builtin_nan("");
     }
-    if (threadIdx.x == 0) module_mean[m] = valid ? red[0] / (double)(hi - lo) : __builtin_nan("");
 }
 
+// grid (P)
 __global__ __launch_bounds__(256) void proxy_macro_kernel(const double* __restrict__ module_mean, int n_modules,
                                                           double* __restrict__ macro) {
     __shared__ double red[256];
+    const double* mm = module_mean + (int64_t)blockIdx.x * n_modules;
     double acc = 0.0;
-    for (int m = threadIdx.x; m < n_modules; m += 256) acc += module_mean[m];
+    for (int m = threadIdx.x; m < n_modules; m += 256) acc += mm[m];
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
         if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *macro = red[0] / (double)n_modules;
+    if (threadIdx.x == 0) macro[blockIdx.x] = red[0] / (double)n_modules;
 }
 
-hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
+hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups, int P,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,
                         double* module_mean, double* macro, double* per_group, hipStream_t st) {
     if (n_groups > 0) {
-        const int64_t blocks = (n_groups + 3) / 4;
+        const int64_t blocks = (n_groups + 15) / 16;
         hipLaunchKernelGGL(proxy_group_kernel, dim3((unsigned)blocks), dim3(256), 0, st, w, d, d_period, E,
-                           n_groups, scales, per_group);
+                           n_groups, P, scales, per_group);
     }
-    hipLaunchKernelGGL(proxy_module_kernel, dim3((unsigned)n_modules), dim3(256), 0, st, per_group,
-                       module_offsets, n_groups, module_mean);
-    hipLaunchKernelGGL(proxy_macro_kernel, dim3(1), dim3(256), 0, st, module_mean, n_modules, macro);
+    hipLaunchKernelGGL(proxy_module_kernel, dim3((unsigned)n_modules, (unsigned)P), dim3(MODULE_THREADS), 0, st,
+                       per_group, module_offsets, n_groups, n_modules, module_mean);
+    hipLaunchKernelGGL(proxy_macro_kernel, dim3((unsigned)P), dim3(256), 0, st, module_mean, n_modules, macro);
     return hipGetLastError();
 }
 

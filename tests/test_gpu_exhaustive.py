@@ -282,6 +282,32 @@ def test_absmax_matches_oracle():
     np.testing.assert_array_equal(ab["objective"].cpu().numpy(), oracle.objective(w, d, bits, p))
 
 
+@pytest.mark.parametrize("E", [1, 3, 4, 8, 17, 32])
+def test_absmax_objective_every_env_count(E):
+    """The per-(group, environment) objective kernel at environment counts that fill a 256-thread
+    workgroup unevenly, a group count that leaves the last workgroup ragged, and d shared with a
+    period: scales, codes and the binary64 objective equal the oracle's bit for bit, and the
+    scales and codes equal those of the call without the objective."""
+    rng = np.random.default_rng(100 + E)
+    gpb = 256 // E
+    n = 3 * gpb + 5
+    w = (rng.standard_normal((n, 128)) * np.exp(rng.uniform(-6, 2, (n, 1)))).astype(np.float32)
+    w[0] = 0.0
+    w[1, 7] = 3.0e4
+    period = n - 2
+    d = rng.gamma(0.7, 1.0, (period, E, 128)).astype(np.float32)
+    say(f"AbsMax objective: E={E}, {n} groups, d period {period}")
+    ab = cq.baseline_scales(dev(w), dev(d), period, "absmax")
+    ab0 = cq.baseline_scales(dev(w), dev(d), period, "absmax", objective=False)
+    torch.cuda.synchronize()
+    bits = bits_np(ab["scales"])
+    np.testing.assert_array_equal(bits, oracle.absmax_bits(w))
+    np.testing.assert_array_equal(ab["codes"].cpu().numpy(), oracle.codes_for(w, bits))
+    np.testing.assert_array_equal(ab["objective"].cpu().numpy(), oracle.objective(w, d, bits, period))
+    np.testing.assert_array_equal(bits_np(ab0["scales"]), bits)
+    np.testing.assert_array_equal(ab0["codes"].cpu().numpy(), ab["codes"].cpu().numpy())
+
+
 def test_pooled_baseline_entry_matches_fused():
     w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
     wt, dt = dev(w), dev(d)
@@ -319,6 +345,37 @@ def test_proxy_matches_oracle():
     np.testing.assert_allclose(pg.cpu().numpy(), rp, rtol=1e-6, atol=0)
     np.testing.assert_allclose(mm.cpu().numpy(), rm, rtol=1e-6, atol=0)
     assert abs(macro.cpu().item() - rmac) <= 1e-6 * rmac
+
+
+@pytest.mark.parametrize("E,n_pol", [(4, 3), (3, 6), (32, 1)])
+def test_proxy_multi_matches_single_calls_and_oracle(E, n_pol):
+    """Several policies in one call: each policy's per-group values, module means and macro equal
+    those of a single-policy call bit for bit, and the oracle's within the proxy tolerance.  The
+    group count is not a multiple of the 16 groups of a workgroup, and one module is empty."""
+    rng = np.random.default_rng(200 + E)
+    n = 16 * 9 + 7
+    w = (rng.standard_normal((n, 128)) * 0.02).astype(np.float32)
+    d = rng.gamma(0.7, 1.0, (n, E, 128)).astype(np.float32)
+    bits = np.stack([rng.integers(0x1400, 0x2400, n) for _ in range(n_pol)]).astype(np.uint16)
+    bits[0] = oracle.absmax_bits(w)
+    off = np.array([0, 60, 60, 100, n], np.int64)
+    mods = np.repeat(np.arange(4), np.diff(off))
+    say(f"proxy multi: E={E}, {n_pol} policies, {n} groups")
+    wt, dt, ot = dev(w), dev(d), dev(off)
+    pg, mm, macro = cq.proxy_worst_env_wmse_multi(wt, dt, dev(bits.view(np.int16)), ot)
+    torch.cuda.synchronize()
+    pg, mm, macro = pg.cpu().numpy(), mm.cpu().numpy(), macro.cpu().numpy()
+    for k in range(n_pol):
+        p1, m1, mac1 = cq.proxy_worst_env_wmse(wt, dt, dev(bits[k].view(np.int16)), ot)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(pg[k], p1.cpu().numpy())
+        np.testing.assert_array_equal(mm[k], m1.cpu().numpy())
+        assert np.isnan(mm[k, 1])
+        rp, rm, _ = oracle.proxy(w, d, bits[k], mods, 4, n)
+        np.testing.assert_allclose(pg[k], rp, rtol=1e-6, atol=0)
+        keep = np.array([0, 2, 3])
+        np.testing.assert_allclose(mm[k, keep], rm[keep], rtol=1e-6, atol=0)
+        assert np.isnan(macro[k]) and np.isnan(mac1.cpu().item())
 
 
 def test_repeatable():
