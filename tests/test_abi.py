@@ -85,3 +85,17 @@ def test_other_entry_points_reject_bad_arguments():
                                        None) == -1
     assert lib.cq_proxy_worst_env_wmse(FAKE, FAKE, 1, 4, 10, FAKE, FAKE, 2, FAKE, FAKE, None, None, 0,
                                        None) == -2
+    assert lib.cq_baseline_scales(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE + 8, None, None, 0, None) == -1  # codes
+
+
+def test_multi_policy_proxy_rejects_bad_arguments():
+    lib = cq.load()
+    f = lib.cq_proxy_worst_env_wmse_multi
+    assert f(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1     # no policy
+    assert f(FAKE, FAKE, 1, 4, 10, 65, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1    # too many
+    assert f(FAKE, FAKE, 1, 4, 10, 3, None, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1     # no scales
+    assert f(FAKE, FAKE, 1, 4, 10, 3, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0, None) == -1     # no module
+    assert f(FAKE, FAKE, 1, 4, 10, 3, FAKE, FAKE, 1, FAKE, FAKE, FAKE + 4, None, 0, None) == -1  # per_group
+    # without per_group the workspace must hold n_policies * n_groups values
+    # (100 groups x 3 policies x 8 bytes = 2,400 > 2,048)
+    assert f(FAKE, FAKE, 1, 4, 100, 3, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 2048, None) == -2
