@@ -675,9 +675,17 @@ __device__ void screen_keys(const SweepArgs& a, SweepSmem<E>& sm, float pk, int 
             if (a.want_minimax && km < mk[2]) top3_insert(mk, km);
             if (a.want_pooled && kq < qk[2]) top3_insert(qk, kq);
         }
-        // values are >= 0, so their bit patterns order as the values do
-        if (a.want_minimax) atomicMin(&sm.u_bits[0], __float_as_uint(bm));
-        if (a.want_pooled) atomicMin(&sm.u_bits[1], __float_as_uint(bp));
+        // values are >= 0, so their bit patterns order as the values do; the wave's minimum goes
+        // in with one lane's atomic (64 lanes on one LDS word would serialise), and only when it
+        // improves on the running minimum
+        if (a.want_minimax) {
+            const float m = wave_min_f(bm);
+            if (lane == 0 && __float_as_uint(m) < u_bits[0]) atomicMin(&sm.u_bits[0], __float_as_uint(m));
+        }
+        if (a.want_pooled) {
+            const float m = wave_min_f(bp);
+            if (lane == 0 && __float_as_uint(m) < u_bits[1]) atomicMin(&sm.u_bits[1], __float_as_uint(m));
+        }
     }
 }
 
