@@ -83,10 +83,12 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     c.scales = scales; c.codes = codes; c.objective = objective; c.flags = flags;
     c.tie_count = (int32_t*)ws;
     c.tie_list = (int32_t*)(ws + ALIGN);
+    // groups whose direct candidates tied are decided by the exhaustive sweep, whose binary64
+    // queue counter is cleared together with the tie counter
+    uint8_t* sws = ws + ALIGN + round_up((size_t)n_groups * 4u);
+    c.zero_also = (int32_t*)sws;
     hipError_t e = cqk::launch_candidate(c, E, st);
     if (e != hipSuccess) return CQ_EHIP;
-    // groups whose direct candidates tied are decided by the exhaustive sweep
-    uint8_t* sws = ws + ALIGN + round_up((size_t)n_groups * 4u);
     cqk::SweepArgs a{};
     a.w = w; a.d = d; a.d_period = d_period;
     a.list = c.tie_list; a.list_count = c.tie_count;
@@ -97,6 +99,7 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     a.want_minimax = 1;
     a.want_pooled = 0;
     a.mark_fallback = 1;
+    a.fb_zeroed = 1;
     return hip_status(cqk::launch_sweep(a, E, n_groups, st));
 }
 

@@ -57,7 +57,14 @@ struct CandSmem {
     static constexpr int RCAP = rcap_for(E);
     __align__(16) float w[G];
     __align__(16) float d[E * G];  // [e][i]
-    uint32_t ev[MAX_EV];
+    union {
+        uint32_t ev[MAX_EV];   // transitions: read last by the run folds
+        struct {               // quadratic-form candidates: written first after the runs are kept
+            double q_lo[QCAP];
+            uint32_t q_b[QCAP];
+        };
+        double pairF[BLOCK];   // rescoring sums: written first after the shortlist is taken
+    };
     uint8_t magp[BLOCK];
     double part[3][4 * E];
     double A[E], B0[E], C0[E];
@@ -68,11 +75,8 @@ struct CandSmem {
     uint32_t run_lo[RCAP], run_hi[RCAP];
     uint8_t qbuf[RCAP][G];
     double run_B[RCAP][E], run_C[RCAP][E];
-    uint32_t q_b[QCAP];
-    double q_lo[QCAP];
     uint32_t cand_b[CCAP];
     double cand_F[CCAP];
-    double pairF[BLOCK];
     int n_runs, n_q, n_cand, n_ev;
     uint32_t win_lo, win_hi;          // the window of patterns that can hold the optimum
     uint32_t win_b;
@@ -752,7 +756,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 
 // Workgroups per CU.  Up to E = 4, five fit the LDS (31.8 KB each at E = 4) and run 11% faster
 // than four on gfx950; at E = 16 three (with some spills) beat two by 13%.
-constexpr int cand_min_blocks(int E) { return E <= 4 ? 5 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
+constexpr int cand_min_blocks(int E) { return E <= 4 ? 6 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
 
 template <int E>
 __global__ __launch_bounds__(BLOCK, cand_min_blocks(E)) void candidate_kernel(CandArgs a, int64_t group_offset) {
@@ -760,13 +764,16 @@ __global__ __launch_bounds__(BLOCK, cand_min_blocks(E)) void candidate_kernel(Ca
     candidate_group<E>(a, (int64_t)blockIdx.x + group_offset, sm);
 }
 
-__global__ void zero_tie_counter(int32_t* p) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
+__global__ void zero_tie_counter(int32_t* p, int32_t* q) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        *p = 0;
+        if (q) *q = 0;
+    }
 }
 
 template <int E>
 hipError_t launch_e(const CandArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(zero_tie_counter, dim3(1), dim3(64), 0, st, a.tie_count);
+    hipLaunchKernelGGL(zero_tie_counter, dim3(1), dim3(64), 0, st, a.tie_count, a.zero_also);
     const int64_t step = 1ll << 30;
     for (int64_t off = 0; off < a.n_groups; off += step) {
         const int64_t n = a.n_groups - off < step ? a.n_groups - off : step;

@@ -43,7 +43,9 @@ struct SweepArgs {
     int mark_fallback;         // OR CQ_FLAG_FALLBACK into the flags written
     SlicePart* parts;          // SLICE_PARTS entries of workspace
     int slices;                // workgroups per group (set by the launcher)
-    int list_begin;            // indirect mode: first list entry this launch serves
+    int list_split;            // indirect mode: workgroups below this serve the sliced entries,
+                               // the others one entry each (set by the launcher)
+    int fb_zeroed;             // the caller has zeroed fb_count earlier on the same stream
 };
 
 // Exhaustive sweep (binary32 screen + binary64 rescoring + binary64 sweep of
@@ -63,6 +65,7 @@ struct CandArgs {
     uint8_t* flags;
     int32_t* tie_count;   // groups handed to the exhaustive sweep
     int32_t* tie_list;
+    int32_t* zero_also;   // nullable: another counter to clear with tie_count (one launch)
 };
 hipError_t launch_candidate(const CandArgs& a, int E, hipStream_t st);
 

@@ -888,19 +888,21 @@ __global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void sweep_f32_kernel(Swe
     __shared__ SweepSmem<E> sm;
     const int S = a.slices;
     if (a.list) {
-        // Listed groups (the count is on the device).  Sliced launch: entries below LIST_SLICED,
-        // each split over S workgroups (entry k, slice j on workgroup (k % lanes) * S + j, lanes =
-        // grid / S).  Unsliced launch: entries from list_begin on, one workgroup each.
+        // Listed groups (the count is on the device).  Workgroups below list_split serve the
+        // entries below LIST_SLICED, each split over S workgroups (entry k, slice j on workgroup
+        // (k % lanes) * S + j, lanes = list_split / S); the others serve the entries from
+        // LIST_SLICED on, one workgroup each.
         const int cnt = *a.list_count;
-        const int lanes = gridDim.x / S;
-        const int sl = blockIdx.x % S;
-        if (S > 1) {
+        if ((int)blockIdx.x < a.list_split) {
+            const int lanes = a.list_split / S;
+            const int sl = blockIdx.x % S;
             for (int k = blockIdx.x / S; k < min(cnt, LIST_SLICED); k += lanes) {
                 sweep_slice<E>(a, (int64_t)a.list[k], sl, S, a.parts + (int64_t)k * S + sl, sm);
                 __syncthreads();
             }
         } else {
-            for (int k = a.list_begin + blockIdx.x; k < cnt; k += gridDim.x) {
+            const int nb = gridDim.x - a.list_split;
+            for (int k = LIST_SLICED + ((int)blockIdx.x - a.list_split); k < cnt; k += nb) {
                 sweep_group<E>(a, (int64_t)a.list[k], sm);
                 __syncthreads();
             }
@@ -1063,20 +1065,17 @@ static hipError_t launch_e(const SweepArgs& a_in, int64_t n_groups, hipStream_t 
     constexpr int S_MAX = NCHUNK / 8 < 15 ? NCHUNK / 8 : 15;
     SweepArgs a = a_in;
     const int fb_blocks = (int)(n_groups < 1024 ? (n_groups > 0 ? n_groups : 1) : 1024);
-    hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
+    if (!a.fb_zeroed) hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
     if (a.list) {
-        // listed groups (few, count unknown on the host): small looping grids
+        // listed groups (few, count unknown on the host): one small looping grid, the first
+        // LIST_SLICED entries sliced, a long list's rest one workgroup each
         a.slices = LIST_SLICES;
         const int lanes = (int)(n_groups < 32 ? n_groups : 32);
-        hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3(lanes * LIST_SLICES), dim3(BLOCK), 0, st, a);
+        a.list_split = lanes * LIST_SLICES;
+        const int64_t rest = n_groups > LIST_SLICED ? n_groups - LIST_SLICED : 0;
+        const int rest_blocks = (int)(rest < 2048 ? rest : 2048);
+        hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3(a.list_split + rest_blocks), dim3(BLOCK), 0, st, a);
         hipLaunchKernelGGL(sweep_merge_kernel<E>, dim3(lanes), dim3(BLOCK), 0, st, a, 0);
-        if (n_groups > LIST_SLICED) {  // a long list: the rest one workgroup each
-            SweepArgs b = a;
-            b.slices = 1;
-            b.list_begin = LIST_SLICED;
-            const int64_t rest = n_groups - LIST_SLICED;
-            hipLaunchKernelGGL(sweep_f32_kernel<E>, dim3((unsigned)(rest < 2048 ? rest : 2048)), dim3(BLOCK), 0, st, b);
-        }
     } else {
         // few groups: split each over S workgroups so that the whole GPU works on them
         int S = 1;
