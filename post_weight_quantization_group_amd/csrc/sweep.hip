@@ -287,28 +287,41 @@ __device__ void rescore(SweepSmem<E>& sm, int n, int E_real) {
     }
 }
 
-// Thread 0: lexicographic (value, bits) winner among shortlist entries with `tag`.
+// One wave: the lexicographic (value, bits) winner among shortlist entries with `tag`, the
+// number of such entries and whether another pattern has the same value.  Each lane takes every
+// 64th entry; the lanes' winners meet in a DPP reduction under the same order.  Lane 0 writes.
 template <int E>
 __device__ void pick_winner(SweepSmem<E>& sm, int n, uint8_t tag, int slot) {
+    const int lane = threadIdx.x & 63;
     uint32_t bb = 0xFFFFFFFFu;
     double bF = __builtin_inf();
     int count = 0;
-    for (int j = 0; j < n; ++j) {
+    for (int j = lane; j < n; j += 64) {
         if (!(sm.cand_tag[j] & tag)) continue;
         const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
         const uint32_t b = sm.cand_b[j];
         ++count;
         if (v < bF || (v == bF && b < bb)) { bF = v; bb = b; }
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double v = lane_xor(bF, o);
+        const uint32_t b = lane_xor(bb, o);
+        if (v < bF || (v == bF && b < bb)) { bF = v; bb = b; }
+        count += (int)lane_xor((uint32_t)count, o);
+    }
     bool tie = false;
-    for (int j = 0; j < n; ++j) {
+    for (int j = lane; j < n; j += 64) {
         if (!(sm.cand_tag[j] & tag)) continue;
         const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
         if (v == bF && sm.cand_b[j] != bb) tie = true;
     }
-    sm.win_b[slot] = bb;
-    sm.win_F[slot] = bF;
-    sm.win_flags[slot] = (uint8_t)((count > 1 ? FLAG_NEAR_TIE : 0) | (tie ? FLAG_EXACT_TIE : 0));
+    tie = __ballot(tie) != 0;
+    if (lane == 0) {
+        sm.win_b[slot] = bb;
+        sm.win_F[slot] = bF;
+        sm.win_flags[slot] = (uint8_t)((count > 1 ? FLAG_NEAR_TIE : 0) | (tie ? FLAG_EXACT_TIE : 0));
+    }
 }
 
 // The smallest pattern whose scale is at least 2 max|w| (BITS_LAST when there is none).  From
@@ -701,19 +714,18 @@ __device__ void finish_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
         return;
     }
     rescore<E>(sm, n, a.E);
-    if (tid == 0) {
-        for (int pol = 0; pol < 2; ++pol) {
-            const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
-            if (!want) continue;
+    {
+        // wave 0 picks the minimax winner, wave 1 the pooled one
+        const int pol = tid >> 6;
+        const bool want = pol == 0 ? a.want_minimax : (pol == 1 && a.want_pooled);
+        if (want) {
             const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
-            if (sm.win_b[pol] != 0xFFFFFFFFu) {  // zero rule: value from rescoring
-                const uint32_t b = sm.win_b[pol];
-                const uint8_t f = sm.win_flags[pol];
-                pick_winner<E>(sm, n, tag, pol);
+            const uint32_t b = sm.win_b[pol];
+            const uint8_t f = sm.win_flags[pol];
+            pick_winner<E>(sm, n, tag, pol);
+            if (b != 0xFFFFFFFFu && (tid & 63) == 0) {  // zero rule: only the value from rescoring
                 sm.win_b[pol] = b;
                 sm.win_flags[pol] = f;
-            } else {
-                pick_winner<E>(sm, n, tag, pol);
             }
         }
     }
