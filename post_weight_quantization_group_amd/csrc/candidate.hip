@@ -716,26 +716,46 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
         __syncthreads();
     }
-    if (tid == 0) {
+    if (tid < 64) {
+        // wave 0: the lexicographic (value, bits) minimum, each lane over every 64th entry and
+        // then a DPP reduction under the same order; the other patterns counted once each, and
+        // whether one of them has the same value
         uint32_t bb = 0xFFFFFFFFu;
         double bF = __builtin_inf();
-        for (int j = 0; j < n; ++j) {
+        for (int j = tid; j < n; j += 64) {
             const double v = sm.cand_F[j];
             const uint32_t b = sm.cand_b[j];
             if (v < bF || (v == bF && b < bb)) { bF = v; bb = b; }
         }
-        int tie = 0, distinct = 0;
-        for (int j = 0; j < n; ++j) {
-            if (sm.cand_b[j] == bb) continue;
-            bool first = true;  // count each other pattern once
-            for (int k = 0; k < j; ++k) if (sm.cand_b[k] == sm.cand_b[j]) { first = false; break; }
-            if (first) ++distinct;
-            if (sm.cand_F[j] == bF) tie = 1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double v = lane_xor(bF, o);
+            const uint32_t b = lane_xor(bb, o);
+            if (v < bF || (v == bF && b < bb)) { bF = v; bb = b; }
         }
-        sm.win_b = bb;
-        sm.win_F = bF;
-        sm.win_state = tie;
-        sm.win_count = distinct + 1;
+        int distinct = 0;
+        bool tie = false;
+        for (int j0 = 0; j0 < n; j0 += 64) {
+            const int j = j0 + tid;
+            bool first = false, same = false;
+            if (j < n) {
+                const uint32_t bj = sm.cand_b[j];
+                if (bj != bb) {
+                    first = true;  // the first entry with this pattern
+                    for (int k = 0; k < j; ++k)
+                        if (sm.cand_b[k] == bj) { first = false; break; }
+                    same = sm.cand_F[j] == bF;
+                }
+            }
+            distinct += (int)__popcll(__ballot(first));
+            tie = tie || __ballot(same) != 0;
+        }
+        if (tid == 0) {
+            sm.win_b = bb;
+            sm.win_F = bF;
+            sm.win_state = tie ? 1 : 0;
+            sm.win_count = distinct + 1;
+        }
     }
     __syncthreads();
     if (sm.win_state) {
@@ -754,8 +774,9 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
 }
 
-// Workgroups per CU.  Up to E = 4, five fit the LDS (31.8 KB each at E = 4) and run 11% faster
-// than four on gfx950; at E = 16 three (with some spills) beat two by 13%.
+// Workgroups per CU.  Up to E = 4, six fit the LDS (25.7 KB each at E = 4, with the unions in
+// CandSmem) and run 2% faster than five (five beat four by 11%) on gfx950; at E = 16 three (with
+// some spills) beat two by 13%.
 constexpr int cand_min_blocks(int E) { return E <= 4 ? 6 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
 
 template <int E>
