@@ -227,6 +227,26 @@ __device__ __forceinline__ void block_max_fn(float (&v)[N], float* red) {
     }
 }
 
+// Block-wide minima of N 64-bit values at once, in one barrier round; `red` holds >= 4 * N slots.
+template <int N>
+__device__ __forceinline__ void block_min_u64n(uint64_t (&v)[N], uint64_t* red) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = wave_min_u64(v[k]);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) red[(threadIdx.x >> 6) * N + k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        uint64_t r = red[k];
+#pragma unroll
+        for (int w = 1; w < BLOCK / 64; ++w) r = red[w * N + k] < r ? red[w * N + k] : r;
+        v[k] = r;
+    }
+}
+
 // Key ordering (value, bit pattern) lexicographically for non-negative floats.
 __device__ __forceinline__ uint64_t key_of(float v, uint32_t b) {
     return ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)b;

@@ -73,7 +73,7 @@ struct SweepSmem {
     int8_t rq[32][G];                 // rescoring: the codes of a batch of shortlisted scales
     __align__(16) float kz[(G + 1) * E];  // kz[m][e]: binary32 sum of d w'^2 over the first m weights
     float redf[4 * 5];
-    uint64_t redk[4];
+    uint64_t redk[8];
     uint32_t cand_b[CAP];
     uint8_t cand_tag[CAP];
     __align__(16) double cand_F[CAP];
@@ -759,16 +759,20 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
     if (status == 2) { queue_fp64(a, g); return; }
     uint64_t mk[3], qk[3];
     screen_keys<E>(a, sm, pk, 0, 1, mk, qk);
+    // both policies' smallest keys in one block reduction
+    uint64_t best[2] = {mk[0], qk[0]};
+    block_min_u64n<2>(best, sm.redk);
     for (int pol = 0; pol < 2; ++pol) {
         const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
         if (!want) continue;
         const uint64_t* kk = pol == 0 ? mk : qk;
         const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
-        const uint64_t M1 = block_min_u64(kk[0], sm.redk);
-        const uint64_t S2 = block_min_u64(kk[0] == M1 ? kk[1] : kk[0], sm.redk);
+        const uint64_t M1 = best[pol];
         const float m = key_value(M1);
         if (m == 0.0f) {
-            // zero binary32 error is exact here: the lowest such pattern wins
+            // zero binary32 error is exact here: the lowest such pattern wins; the second key
+            // tells whether another pattern is zero too
+            const uint64_t S2 = block_min_u64(kk[0] == M1 ? kk[1] : kk[0], sm.redk);
             if (tid == 0) {
                 append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(M1), tag);
                 sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
@@ -785,9 +789,8 @@ __device__ void sweep_group(const SweepArgs& a, int64_t g, SweepSmem<E>& sm) {
             }
             if (tid == 0) sm.win_b[pol] = 0xFFFFFFFFu;  // decided by rescoring
         }
-        __syncthreads();
     }
-    finish_group<E>(a, g, sm);
+    finish_group<E>(a, g, sm);  // starts with a barrier: the appends are in place
 }
 
 // Slice `slice` of S of one group: screen its chunks and record, per policy, its best and
