@@ -12,7 +12,10 @@ array reshuffles or means:
   "Quantization configuration": GPTQ v1, 4 bits, group 128, symmetric);
 * the module-macro worst-environment weighted-MSE proxy (same card,
   "Held-out reconstruction proxy"; CliffQuant README, "Held-out
-  reconstruction proxy").
+  reconstruction proxy");
+* the held-out comparison of two policies on that proxy: per-group wins, ties
+  and losses, the macro effect and its paired module-stratified bootstrap
+  interval (CliffQuant README, "Held-out reconstruction proxy").
 """
 from __future__ import annotations
 
@@ -251,3 +254,66 @@ def proxy(w, d_eval, bits, module_of_group, n_modules: int, d_period=None, n_thr
     for v in module_mean:
         acc = acc + float(v)
     return per_group, module_mean, acc / n_modules
+
+
+# ---------------------------------------------------------------- held-out comparison
+def _seq_sum_rows(x: np.ndarray) -> np.ndarray:
+    """Left-to-right binary64 sum of each row (numpy's cumsum adds in order; sum() would not)."""
+    if x.shape[-1] == 0:
+        return np.zeros(x.shape[:-1])
+    return np.cumsum(x, axis=-1)[..., -1]
+
+
+def heldout_compare(pa, pb, module_offsets, boot_idx, alpha: float = 0.05):
+    """Policy A against policy B on per-group proxy values (CliffQuant README, "Held-out
+    reconstruction proxy": CliffQuant's wins, ties and losses against Pooled-WMSE by group, and the
+    paired module-stratified bootstrap effect with its 95% interval).
+
+    Readings where the pages are silent:
+    * a win of A is p_A < p_B, a tie p_A == p_B, a loss p_A > p_B (exact comparisons);
+    * the effect is the mean over modules of each module's mean of (p_B - p_A), summed in order
+      (the paired form of macro_B - macro_A);
+    * replicate r resamples each module's groups with replacement, the same draw for both
+      policies: position j of module m takes group boot_idx[r, j] (drawn in m's range), and the
+      replicate effect is the effect formula on those groups;
+    * the interval is the linear-interpolation percentile at 100 alpha/2 and 100 (1 - alpha/2) of
+      the replicates sorted ascending: position q (B - 1), value v[lo] + (v[lo+1] - v[lo]) t.
+    A module whose range is empty, or a replicate with a draw outside its module, gives NaN.
+
+    Returns (counts [wins, ties, losses], effect, replicates sorted ascending, (lo, hi))."""
+    pa = np.asarray(pa, dtype=np.float64)
+    pb = np.asarray(pb, dtype=np.float64)
+    off = np.asarray(module_offsets, dtype=np.int64)
+    idx = np.asarray(boot_idx, dtype=np.int64)
+    counts = np.array([np.count_nonzero(pa < pb), np.count_nonzero(pa == pb), np.count_nonzero(pa > pb)],
+                      dtype=np.int64)
+    diff = pb - pa
+    M = off.size - 1
+    B = idx.shape[0]
+    # rows: the point estimate (identity draw) then the replicates
+    means = np.empty((B + 1, M))
+    for m in range(M):
+        lo, hi = int(off[m]), int(off[m + 1])
+        if hi <= lo:
+            means[:, m] = np.nan
+            continue
+        pos = np.arange(lo, hi)
+        draw = np.vstack([pos[None, :], idx[:, lo:hi]])
+        ok = np.all((draw >= lo) & (draw < hi), axis=1)
+        vals = diff[np.clip(draw, lo, hi - 1)]
+        means[:, m] = np.where(ok, _seq_sum_rows(vals) / float(hi - lo), np.nan)
+    effects = _seq_sum_rows(means) / float(M)
+    effect = float(effects[0])
+    reps = np.sort(effects[1:])  # NaN sorts last
+
+    def pct(q):
+        if B == 0 or np.isnan(reps[-1]):
+            return float("nan")
+        pos = q * (B - 1)
+        lo = int(np.floor(pos))
+        t = pos - lo
+        if lo + 1 >= B:
+            return float(reps[B - 1])
+        return float(reps[lo] + (reps[lo + 1] - reps[lo]) * t)
+
+    return counts, effect, reps, (pct(alpha / 2.0), pct(1.0 - alpha / 2.0))

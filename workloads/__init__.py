@@ -32,7 +32,7 @@ import numpy as np
 GROUP = 128
 
 # stream ids inside one unit (matrix or chunk)
-_S_WEIGHT, _S_OUTLIER, _S_DBASE, _S_DPERT, _S_PERM, _S_STD = range(6)
+_S_WEIGHT, _S_OUTLIER, _S_DBASE, _S_DPERT, _S_PERM, _S_STD, _S_DEVAL, _S_BOOT = range(8)
 
 
 def _rng(k: int, unit: int, stream: int) -> np.random.Generator:
@@ -280,6 +280,59 @@ def gather_matrix_groups(k: int, gids: np.ndarray):
         w[sel] = wg[local[sel]]
         d[sel] = dg[local[sel] % period]
     return w, d, m_idx
+
+
+# ---------------------------------------------------------------- held-out evaluation
+def heldout_matrix_diagonals(k: int, m: int) -> np.ndarray:
+    """Held-out diagonals [E, in] of matrix ``m`` (configs 0-2): the same per-channel base as the
+    calibration diagonals of make_matrix, times a fresh per-environment perturbation.  The stand-in
+    for diagonals estimated from held-out text windows disjoint from the calibration windows
+    (model card, "Calibration and evaluation data"): the same channels matter, the sampling noise
+    differs."""
+    spec = config(k)
+    if k not in (0, 1, 2):
+        raise ValueError("held-out diagonals are drawn for configs 0-2")
+    mat = spec.matrices[m]
+    return _diag_lognormal_pert(_rng(k, m, _S_DBASE), _rng(k, m, _S_DEVAL), spec.E, mat.inp)
+
+
+def heldout_sample(k: int, count: int, salt: int = 7):
+    """A seeded sample of ``count`` groups across all matrices of config ``k`` (sorted, so each
+    matrix's groups are contiguous) with calibration and held-out diagonals expanded per group.
+    Returns (w [n,128], d [n,E,128], d_eval [n,E,128], module_offsets [n_modules+1] int64) where
+    the modules are the matrices that have at least one sampled group."""
+    spec = config(k)
+    gids = sample_groups(k, count, salt)
+    m_idx, local = locate(k, gids)
+    w = np.empty((gids.size, GROUP), dtype=np.float32)
+    d = np.empty((gids.size, spec.E, GROUP), dtype=np.float32)
+    de = np.empty((gids.size, spec.E, GROUP), dtype=np.float32)
+    for m in np.unique(m_idx):
+        W, dmat = make_matrix(k, int(m))
+        wg, dg, period = matrix_groups(W, dmat)
+        _, dge, _ = matrix_groups(W, heldout_matrix_diagonals(k, int(m)))
+        sel = np.nonzero(m_idx == m)[0]
+        w[sel] = wg[local[sel]]
+        d[sel] = dg[local[sel] % period]
+        de[sel] = dge[local[sel] % period]
+    starts = np.searchsorted(m_idx, np.unique(m_idx), side="left")
+    off = np.concatenate([starts, [gids.size]]).astype(np.int64)
+    return w, d, de, off
+
+
+def bootstrap_indices(module_offsets, n_boot: int, seed: int = 0) -> np.ndarray:
+    """Resampling draws for a module-stratified bootstrap: int32 [n_boot, n_groups] where entry
+    [r, j] for j in module m's range [off[m], off[m+1]) is uniform on that range (with
+    replacement).  Only random numbers: the resampling arithmetic lives with the callers."""
+    off = np.asarray(module_offsets, dtype=np.int64)
+    n = int(off[-1])
+    rng = _rng(0, (1 << 22) + seed, _S_BOOT)
+    idx = np.empty((n_boot, n), dtype=np.int32)
+    for m in range(off.size - 1):
+        lo, hi = int(off[m]), int(off[m + 1])
+        if hi > lo:
+            idx[:, lo:hi] = rng.integers(lo, hi, size=(n_boot, hi - lo), dtype=np.int64)
+    return idx
 
 
 # ---------------------------------------------------------------- the pages' example
