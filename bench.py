@@ -290,6 +290,26 @@ def measure_all_configs() -> dict:
                           / (PEAK_FP32_TFLOPS * 1e12),
                       "sample_candidate_vs_exhaustive_scale_mismatches":
                           int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
+    # held-out evaluation on config 2: 4,096 groups sampled across all 150 matrices, scales from
+    # the calibration diagonals, the three policies' proxy on held-out diagonals, and minimax
+    # against pooled with a 10,000-replicate module-stratified bootstrap
+    wh, dh, deh, offh = W.heldout_sample(2, 4096)
+    nh = wh.shape[0]
+    idxh = W.bootstrap_indices(offh, 10000, seed=0)
+    wt, dt, det = (torch.from_numpy(x).to(dev) for x in (wh, dh, deh))
+    ot, it = torch.from_numpy(offh).to(dev), torch.from_numpy(idxh).to(dev)
+    r = cq.quantize_groups(wt, dt, nh, method="exhaustive", pooled=True)
+    ab = cq.baseline_scales(wt, dt, nh, "absmax", objective=False)
+    sv = torch.stack((r["scales"], r["pooled_scales"], ab["scales"]))
+    (pgh, mmh, mach), ms_p = _timed(lambda: cq.proxy_worst_env_wmse_multi(wt, det, sv, ot, nh))
+    (cnt, eff, _, ci), ms_h = _timed(lambda: cq.heldout_compare(pgh[0].contiguous(), pgh[1].contiguous(), ot, it))
+    macro = mach.cpu().numpy()
+    res["config2_heldout"] = {"groups": nh, "modules": int(offh.size - 1), "E": 4, "replicates": 10000,
+                              "proxy_macro_minimax_pooled_absmax": [float(x) for x in macro],
+                              "minimax_wins_ties_losses_vs_pooled": [int(x) for x in cnt.cpu().numpy()],
+                              "effect_pooled_minus_minimax": float(eff.cpu().item()),
+                              "effect_ci95": [float(x) for x in ci.cpu().numpy()],
+                              "proxy_ms": ms_p, "compare_ms": ms_h}
     # config 3: per-group diagonals
     w3, d3, cat3, _ = W.make_groups(3)
     n3 = w3.shape[0]

@@ -58,6 +58,7 @@ extern "C" {
 #define CQ_GROUP 128
 #define CQ_MAX_ENVS 32
 #define CQ_MAX_POLICIES 64
+#define CQ_MAX_BOOT (1 << 20)
 
 /* Status codes. */
 #define CQ_OK 0
@@ -183,6 +184,40 @@ int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64
                                       const int64_t *module_offsets, int32_t n_modules,
                                       double *module_mean, double *macro, double *per_group,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Held-out comparison of two scale policies on the proxy's per-group values
+ * (CliffQuant README, "Held-out reconstruction proxy": the minimax policy's
+ * wins, ties and losses against Pooled-WMSE by group, and the paired
+ * module-stratified bootstrap effect with its 95% interval).
+ *   pa, pb          device double [n_groups]: per-group proxy values p_g of
+ *                   policies A and B (e.g. two rows of the per_group output of
+ *                   cq_proxy_worst_env_wmse_multi on held-out diagonals).
+ *   module_offsets  device int64 [n_modules+1] as for the proxy; a module whose
+ *                   range is empty or out of bounds makes the effect NaN.
+ *   boot_idx        device int32 [n_boot][n_groups], drawn by the caller:
+ *                   replicate r takes, at position j of module m's range, group
+ *                   boot_idx[r][j], which must lie in m's range (else that
+ *                   replicate is NaN).  The same draw serves both policies.
+ *   alpha           0 < alpha < 1: the interval runs from the 100 alpha/2 to
+ *                   the 100 (1 - alpha/2) percentile.
+ *   counts          out, device int64 [3]: groups with p_A < p_B, ==, >.
+ *   effect          out, device double [1]: the mean over modules of each
+ *                   module's mean of (p_B - p_A), every sum left to right.
+ *   boot            out, device double [n_boot]: the replicate effects (the same
+ *                   formula on each draw), sorted ascending, NaN last.
+ *   ci              out, device double [2]: the percentiles of boot by linear
+ *                   interpolation at position q (n_boot - 1); NaN when n_boot is
+ *                   0 or a replicate is NaN.
+ * 0 <= n_boot <= CQ_MAX_BOOT; (n_boot + 1) * n_modules <= 2^31 - 1.
+ * workspace: cq_heldout_workspace_size(n_boot, n_modules) bytes.
+ */
+size_t cq_heldout_workspace_size(int32_t n_boot, int32_t n_modules);
+int32_t cq_heldout_compare(const double *pa, const double *pb, int64_t n_groups,
+                           const int64_t *module_offsets, int32_t n_modules,
+                           const int32_t *boot_idx, int32_t n_boot, double alpha,
+                           int64_t *counts, double *effect, double *boot, double *ci,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ __all__ = [
     "cq_quantize_groups", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
-    "EXPORTED_SYMBOLS",
+    "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "EXPORTED_SYMBOLS",
 ]
 
 GROUP = 128
@@ -40,7 +40,8 @@ FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
-                    "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi")
+                    "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
+                    "cq_heldout_compare")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -84,6 +85,10 @@ def load():
         lib.cq_proxy_worst_env_wmse.argtypes = [P, P, I64, I32, I64, P, P, I32, P, P, P, P, SZ, P]
         lib.cq_proxy_worst_env_wmse_multi.restype = I32
         lib.cq_proxy_worst_env_wmse_multi.argtypes = [P, P, I64, I32, I64, I32, P, P, I32, P, P, P, P, SZ, P]
+        lib.cq_heldout_workspace_size.restype = SZ
+        lib.cq_heldout_workspace_size.argtypes = [I32, I32]
+        lib.cq_heldout_compare.restype = I32
+        lib.cq_heldout_compare.argtypes = [P, P, I64, P, I32, P, I32, ctypes.c_double, P, P, P, P, P, SZ, P]
         _lib = lib
     return _lib
 
@@ -169,6 +174,18 @@ def cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, n_policies, 
                                                 _p(module_offsets), n_modules, _p(module_mean), _p(macro),
                                                 _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
            "cq_proxy_worst_env_wmse_multi")
+
+
+def cq_heldout_workspace_size(n_boot: int, n_modules: int) -> int:
+    return load().cq_heldout_workspace_size(n_boot, n_modules)
+
+
+def cq_heldout_compare(pa, pb, n_groups, module_offsets, n_modules, boot_idx, n_boot, alpha, counts, effect, boot,
+                       ci, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_heldout_compare(_p(pa), _p(pb), n_groups, _p(module_offsets), n_modules, _p(boot_idx), n_boot,
+                                     float(alpha), _p(counts), _p(effect), _p(boot), _p(ci), _p(workspace), ws_bytes,
+                                     _stream(stream)), "cq_heldout_compare")
 
 
 # ---------------------------------------------------------------- helpers
@@ -274,6 +291,24 @@ def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None,
     cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n, n_pol, scales, module_offsets, n_modules, mm, macro,
                                   pg, ws, stream)
     return pg, mm, macro
+
+
+def heldout_compare(pa, pb, module_offsets, boot_idx, alpha=0.05, stream=None):
+    """Policy A against policy B on per-group proxy values (float64 [n] device tensors), with the
+    bootstrap draws boot_idx (int32 [n_boot, n] device tensor).  Returns (counts int64 [3] =
+    wins/ties/losses of A, effect [1], replicates [n_boot] sorted, ci [2]) as device tensors."""
+    n = pa.numel()
+    n_modules = module_offsets.numel() - 1
+    n_boot = boot_idx.shape[0] if boot_idx is not None else 0
+    dev = pa.device
+    counts = torch.empty(3, dtype=torch.int64, device=dev)
+    effect = torch.empty(1, dtype=torch.float64, device=dev)
+    boot = torch.empty(max(n_boot, 1), dtype=torch.float64, device=dev)
+    ci = torch.empty(2, dtype=torch.float64, device=dev)
+    ws = _workspace(cq_heldout_workspace_size(n_boot, n_modules), dev)
+    cq_heldout_compare(pa, pb, n, module_offsets, n_modules, boot_idx if n_boot > 0 else None, n_boot, alpha, counts,
+                       effect, boot, ci, ws, stream)
+    return counts, effect, boot[:n_boot], ci
 
 
 def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax: int = 7, method="candidate",

@@ -177,4 +177,28 @@ int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_p
                                          module_mean, macro, per_group, workspace, workspace_bytes, stream);
 }
 
+size_t cq_heldout_workspace_size(int32_t n_boot, int32_t n_modules) {
+    if (n_boot < 0 || n_modules < 1) return 0;
+    return round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u) + round_up((size_t)n_boot * 8u);
+}
+
+int32_t cq_heldout_compare(const double* pa, const double* pb, int64_t n_groups, const int64_t* module_offsets,
+                           int32_t n_modules, const int32_t* boot_idx, int32_t n_boot, double alpha,
+                           int64_t* counts, double* effect, double* boot, double* ci, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (n_groups < 0 || n_modules < 1 || n_boot < 0 || n_boot > CQ_MAX_BOOT) return CQ_EINVAL;
+    if (!(alpha > 0.0 && alpha < 1.0)) return CQ_EINVAL;
+    if (n_groups > 0 && (!pa || !pb || !aligned(pa, 8) || !aligned(pb, 8))) return CQ_EINVAL;
+    if (!module_offsets || !aligned(module_offsets, 8) || !counts || !effect || !ci) return CQ_EINVAL;
+    if (n_boot > 0 && (!boot_idx || !boot || !aligned(boot_idx, 4))) return CQ_EINVAL;
+    if ((int64_t)(n_boot + 1) * n_modules > INT32_MAX) return CQ_EINVAL;
+    if (!workspace || workspace_bytes < cq_heldout_workspace_size(n_boot, n_modules) || !aligned(workspace, ALIGN))
+        return CQ_EWORKSPACE;
+    uint8_t* ws = (uint8_t*)workspace;
+    double* mm = (double*)ws;
+    double* reps = (double*)(ws + round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u));
+    return hip_status(cqk::launch_heldout(pa, pb, n_groups, module_offsets, n_modules, boot_idx, n_boot, alpha,
+                                          counts, effect, boot, ci, mm, reps, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -75,6 +75,12 @@ hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st);
 
+// Held-out comparison of two policies' per-group values: counts, effect, sorted bootstrap
+// replicates and the percentile interval; mm ((B + 1) * M) and reps (B) are workspace.
+hipError_t launch_heldout(const double* pa, const double* pb, int64_t n, const int64_t* off, int M,
+                          const int32_t* idx, int B, double alpha, int64_t* counts, double* effect,
+                          double* boot, double* ci, double* mm, double* reps, hipStream_t st);
+
 hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups, int P,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,
                         double* module_mean, double* macro, double* per_group, hipStream_t st);

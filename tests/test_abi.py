@@ -99,3 +99,24 @@ def test_multi_policy_proxy_rejects_bad_arguments():
     # without per_group the workspace must hold n_policies * n_groups values
     # (100 groups x 3 policies x 8 bytes = 2,400 > 2,048)
     assert f(FAKE, FAKE, 1, 4, 100, 3, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 2048, None) == -2
+
+
+def test_heldout_compare_rejects_bad_arguments():
+    lib = cq.load()
+    f = lib.cq_heldout_compare
+    ws = cq.cq_heldout_workspace_size(10, 2)
+    assert ws >= (11 * 2 + 10) * 8
+    ok = dict(pa=FAKE, pb=FAKE, n=100, off=FAKE, M=2, idx=FAKE, B=10, alpha=0.05, counts=FAKE, effect=FAKE,
+              boot=FAKE, ci=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["pa"], a["pb"], a["n"], a["off"], a["M"], a["idx"], a["B"], a["alpha"], a["counts"],
+                 a["effect"], a["boot"], a["ci"], a["ws"], a["wsb"], None)
+
+    assert call(alpha=0.0) == -1 and call(alpha=1.0) == -1
+    assert call(M=0) == -1 and call(B=-1) == -1 and call(n=-1) == -1
+    assert call(pa=None) == -1 and call(off=None) == -1 and call(ci=None) == -1
+    assert call(idx=None) == -1 and call(boot=None) == -1 and call(pa=FAKE + 4) == -1
+    assert call(ws=None) == -2 and call(wsb=ws - 8) == -2 and call(ws=FAKE + 64) == -2
