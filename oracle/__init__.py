@@ -317,3 +317,28 @@ def heldout_compare(pa, pb, module_offsets, boot_idx, alpha: float = 0.05):
         return float(reps[lo] + (reps[lo + 1] - reps[lo]) * t)
 
     return counts, effect, reps, (pct(alpha / 2.0), pct(1.0 - alpha / 2.0))
+
+
+# ---------------------------------------------------------------- environment diagonals
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (the top half of a binary32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def environment_diagonals(x_bits) -> np.ndarray:
+    """Separately normalized environment diagonals from calibration activations (CliffQuant
+    README, "What CliffQuant changes": activation-weighted sensitivity per calibration
+    environment, each environment normalized on its own).
+
+    Reading where the pages are silent: for environment e with tokens t = 1..T,
+    d_{e,i} = (1/T) sum_t x_{t,i}^2, then divided by its mean over the channels i, in binary64,
+    and rounded once to binary32.  x_bits: bfloat16 bit patterns [E, T, in].  Returns d
+    [in/128, E, 128] float32, the layout the solver takes with d_period = in/128.  An
+    environment whose activations are all zero gives NaN."""
+    x = bf16_to_f64(x_bits)
+    E, T, n = x.shape
+    m = (x * x).sum(axis=1) / float(T)                 # [E, in]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        d = m / m.mean(axis=1, keepdims=True)
+    return np.ascontiguousarray(d.astype(np.float32).reshape(E, n // GROUP, GROUP).transpose(1, 0, 2))

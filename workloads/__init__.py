@@ -32,7 +32,7 @@ import numpy as np
 GROUP = 128
 
 # stream ids inside one unit (matrix or chunk)
-_S_WEIGHT, _S_OUTLIER, _S_DBASE, _S_DPERT, _S_PERM, _S_STD, _S_DEVAL, _S_BOOT = range(8)
+_S_WEIGHT, _S_OUTLIER, _S_DBASE, _S_DPERT, _S_PERM, _S_STD, _S_DEVAL, _S_BOOT, _S_ACT = range(9)
 
 
 def _rng(k: int, unit: int, stream: int) -> np.random.Generator:
@@ -333,6 +333,31 @@ def bootstrap_indices(module_offsets, n_boot: int, seed: int = 0) -> np.ndarray:
         if hi > lo:
             idx[:, lo:hi] = rng.integers(lo, hi, size=(n_boot, hi - lo), dtype=np.int64)
     return idx
+
+
+# ---------------------------------------------------------------- calibration activations
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round binary32 values to bfloat16 bit patterns (nearest, ties to even)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def calibration_activations(k: int, m: int, T: int) -> np.ndarray:
+    """bfloat16 bit patterns [E, T, in] of calibration activations for matrix ``m`` of config
+    ``k`` (configs 0-2): token t of environment e has x_i ~ N(0, base_i pert_{e,i}) with the
+    per-channel base and per-environment perturbation of make_matrix's diagonals, so that the
+    diagonals estimated from them follow the same structure (model card, "Calibration and
+    evaluation data": four environments of 256-token windows; the model runs in 16 bits)."""
+    spec = config(k)
+    if k not in (0, 1, 2):
+        raise ValueError("calibration activations are drawn for configs 0-2")
+    inp = spec.matrices[m].inp
+    base = _rng(k, m, _S_DBASE).lognormal(0.0, 1.0, size=inp)
+    pert = _rng(k, m, _S_DPERT).lognormal(0.0, 0.5, size=(spec.E, inp))
+    std = np.sqrt(base[None, :] * pert).astype(np.float32)           # [E, in]
+    z = _rng(k, m, _S_ACT).standard_normal(size=(spec.E, T, inp), dtype=np.float32)
+    return f32_to_bf16_bits(z * std[:, None, :])
 
 
 # ---------------------------------------------------------------- the pages' example
