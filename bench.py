@@ -252,6 +252,18 @@ def measure_all_configs() -> dict:
     res["config0"] = matrix_pass(0)
     res["config1"] = matrix_pass(1)
     res["config4"] = matrix_pass(4)
+    # environment diagonals from calibration activations: config 1's gate/up (in 1,024) and down
+    # (in 3,584) inputs, E = 4, 8,192 bf16 tokens per environment; HBM-bound (2 bytes per element)
+    dg = {}
+    for m in (0, 2):
+        xb = torch.from_numpy(W.calibration_activations(1, m, 8192).view(np.int16)).to(dev)
+        E_, T_, n_ = xb.shape
+        _, ms = _timed(lambda: cq.environment_diagonals(xb), reps=5)
+        nbytes = E_ * T_ * n_ * 2 + n_ * E_ * 4
+        dg[f"in{n_}"] = {"E": E_, "tokens_per_env": T_, "ms": ms, "GB_per_s": nbytes / (ms / 1e3) / 1e9,
+                         "hbm_frac": nbytes / (ms / 1e3) / 8e12}
+        del xb
+    res["config1_diagonals"] = dg
     # config 2: candidate + pack + proxy on every matrix, exhaustive on the 10,000-group sample
     spec = W.config(2)
     cand_ms = pack_ms = proxy_ms = 0.0

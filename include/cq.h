@@ -186,6 +186,25 @@ int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64
                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Separately normalized environment diagonals from calibration activations
+ * (CliffQuant README, "What CliffQuant changes": activation-weighted sensitivity
+ * per calibration environment, each environment normalized on its own; model
+ * card, "Calibration and evaluation data": environments of 256-token windows,
+ * a 16-bit model runtime).
+ *   x   device uint16 [E][T][in]: bfloat16 bit patterns of the activations
+ *       entering one matrix, T tokens per environment, row-major.
+ *   d   out, float [in/128][E][128]: d_{e,i} = mean_t x_{t,i}^2 divided by its
+ *       mean over the channels i (binary64, rounded once), the layout
+ *       cq_quantize_groups takes with d_period = in/128.  An environment whose
+ *       activations are all zero gives NaN (the solver flags it).
+ * 1 <= E <= CQ_MAX_ENVS, T >= 1, in a multiple of 128 up to 2^24; x 16-byte
+ * aligned.  workspace: cq_diagonals_workspace_size(E, T, in) bytes.
+ */
+size_t cq_diagonals_workspace_size(int32_t E, int64_t T, int64_t in);
+int32_t cq_environment_diagonals(const uint16_t *x, int32_t E, int64_t T, int64_t in, float *d,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Held-out comparison of two scale policies on the proxy's per-group values
  * (CliffQuant README, "Held-out reconstruction proxy": the minimax policy's
  * wins, ties and losses against Pooled-WMSE by group, and the paired

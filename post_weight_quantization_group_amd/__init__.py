@@ -30,7 +30,8 @@ __all__ = [
     "cq_quantize_groups", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
-    "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "EXPORTED_SYMBOLS",
+    "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "cq_diagonals_workspace_size",
+    "cq_environment_diagonals", "environment_diagonals", "EXPORTED_SYMBOLS",
 ]
 
 GROUP = 128
@@ -41,7 +42,7 @@ _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
-                    "cq_heldout_compare")
+                    "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -85,6 +86,10 @@ def load():
         lib.cq_proxy_worst_env_wmse.argtypes = [P, P, I64, I32, I64, P, P, I32, P, P, P, P, SZ, P]
         lib.cq_proxy_worst_env_wmse_multi.restype = I32
         lib.cq_proxy_worst_env_wmse_multi.argtypes = [P, P, I64, I32, I64, I32, P, P, I32, P, P, P, P, SZ, P]
+        lib.cq_diagonals_workspace_size.restype = SZ
+        lib.cq_diagonals_workspace_size.argtypes = [I32, I64, I64]
+        lib.cq_environment_diagonals.restype = I32
+        lib.cq_environment_diagonals.argtypes = [P, I32, I64, I64, P, P, SZ, P]
         lib.cq_heldout_workspace_size.restype = SZ
         lib.cq_heldout_workspace_size.argtypes = [I32, I32]
         lib.cq_heldout_compare.restype = I32
@@ -174,6 +179,16 @@ def cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, n_policies, 
                                                 _p(module_offsets), n_modules, _p(module_mean), _p(macro),
                                                 _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
            "cq_proxy_worst_env_wmse_multi")
+
+
+def cq_diagonals_workspace_size(E: int, T: int, inp: int) -> int:
+    return load().cq_diagonals_workspace_size(E, T, inp)
+
+
+def cq_environment_diagonals(x, E, T, inp, d, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_environment_diagonals(_p(x), E, T, inp, _p(d), _p(workspace), ws_bytes, _stream(stream)),
+           "cq_environment_diagonals")
 
 
 def cq_heldout_workspace_size(n_boot: int, n_modules: int) -> int:
@@ -291,6 +306,19 @@ def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None,
     cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n, n_pol, scales, module_offsets, n_modules, mm, macro,
                                   pg, ws, stream)
     return pg, mm, macro
+
+
+def environment_diagonals(x, stream=None):
+    """Diagonals [in/128, E, 128] float32 from bfloat16 activations x [E, T, in] (a torch.bfloat16
+    or int16 device tensor holding the bit patterns)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [E, T, in]")
+    E, T, inp = x.shape
+    xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+    d = torch.empty((inp // GROUP, E, GROUP), dtype=torch.float32, device=x.device)
+    ws = _workspace(cq_diagonals_workspace_size(E, T, inp), x.device)
+    cq_environment_diagonals(xb, E, T, inp, d, ws, stream)
+    return d
 
 
 def heldout_compare(pa, pb, module_offsets, boot_idx, alpha=0.05, stream=None):

@@ -177,6 +177,24 @@ int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_p
                                          module_mean, macro, per_group, workspace, workspace_bytes, stream);
 }
 
+size_t cq_diagonals_workspace_size(int32_t E, int64_t T, int64_t in) {
+    if (E < 1 || E > CQ_MAX_ENVS || T < 1 || in < CQ_GROUP || in % CQ_GROUP != 0 || in > (int64_t)1 << 24) return 0;
+    return round_up((size_t)E * (size_t)cqk::diag_chunks(E, T, in) * (size_t)in * 8u) + round_up((size_t)E * (size_t)in * 8u);
+}
+
+int32_t cq_environment_diagonals(const uint16_t* x, int32_t E, int64_t T, int64_t in, float* d, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    if (E < 1 || E > CQ_MAX_ENVS || T < 1 || in < CQ_GROUP || in % CQ_GROUP != 0 || in > (int64_t)1 << 24)
+        return CQ_EINVAL;
+    if (!x || !d || !aligned(x, 16) || !aligned(d, 4)) return CQ_EINVAL;
+    const size_t need = cq_diagonals_workspace_size(E, T, in);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return CQ_EWORKSPACE;
+    uint8_t* ws = (uint8_t*)workspace;
+    double* part = (double*)ws;
+    double* msq = (double*)(ws + round_up((size_t)E * (size_t)cqk::diag_chunks(E, T, in) * (size_t)in * 8u));
+    return hip_status(cqk::launch_diagonals(x, E, T, in, d, part, msq, (hipStream_t)stream));
+}
+
 size_t cq_heldout_workspace_size(int32_t n_boot, int32_t n_modules) {
     if (n_boot < 0 || n_modules < 1) return 0;
     return round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u) + round_up((size_t)n_boot * 8u);

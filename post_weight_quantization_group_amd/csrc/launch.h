@@ -75,6 +75,12 @@ hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st);
 
+// Environment diagonals from bf16 activations [E][T][in] into d [in/128][E][128]; part
+// (E * diag_chunks * in) and msq (E * in) are workspace.
+int64_t diag_chunks(int E, int64_t T, int64_t in);
+hipError_t launch_diagonals(const uint16_t* x, int E, int64_t T, int64_t in, float* d, double* part, double* msq,
+                            hipStream_t st);
+
 // Held-out comparison of two policies' per-group values: counts, effect, sorted bootstrap
 // replicates and the percentile interval; mm ((B + 1) * M) and reps (B) are workspace.
 hipError_t launch_heldout(const double* pa, const double* pb, int64_t n, const int64_t* off, int M,

@@ -120,3 +120,18 @@ def test_heldout_compare_rejects_bad_arguments():
     assert call(pa=None) == -1 and call(off=None) == -1 and call(ci=None) == -1
     assert call(idx=None) == -1 and call(boot=None) == -1 and call(pa=FAKE + 4) == -1
     assert call(ws=None) == -2 and call(wsb=ws - 8) == -2 and call(ws=FAKE + 64) == -2
+
+
+def test_environment_diagonals_rejects_bad_arguments():
+    lib = cq.load()
+    f = lib.cq_environment_diagonals
+    ws = cq.cq_diagonals_workspace_size(4, 100, 256)
+    assert ws >= 4 * 256 * 8 and cq.cq_diagonals_workspace_size(4, 100, 200) == 0
+    assert f(FAKE, 0, 100, 256, FAKE, FAKE, ws, None) == -1       # E
+    assert f(FAKE, 33, 100, 256, FAKE, FAKE, ws, None) == -1
+    assert f(FAKE, 4, 0, 256, FAKE, FAKE, ws, None) == -1         # T
+    assert f(FAKE, 4, 100, 200, FAKE, FAKE, ws, None) == -1       # in % 128
+    assert f(FAKE + 8, 4, 100, 256, FAKE, FAKE, ws, None) == -1   # x alignment
+    assert f(FAKE, 4, 100, 256, None, FAKE, ws, None) == -1
+    assert f(FAKE, 4, 100, 256, FAKE, None, ws, None) == -2
+    assert f(FAKE, 4, 100, 256, FAKE, FAKE, ws - 8, None) == -2
