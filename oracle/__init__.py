@@ -342,3 +342,18 @@ def environment_diagonals(x_bits) -> np.ndarray:
     with np.errstate(invalid="ignore", divide="ignore"):
         d = m / m.mean(axis=1, keepdims=True)
     return np.ascontiguousarray(d.astype(np.float32).reshape(E, n // GROUP, GROUP).transpose(1, 0, 2))
+
+
+# ---------------------------------------------------------------- W4A16 consumer check
+def w4a16_matmul(x_bits, qweight, scales):
+    """y = x W^T with W dequantized from the GPTQ-v1 tensors (model card, "Quantization
+    configuration": GPTQ v1, 4 bits, group 128, symmetric; the W4A16 checkpoint keeps 16-bit
+    activations): W[o][k] = s[k/128][o] (u - 8) with u the nibble of qweight.  x_bits: bfloat16 bit
+    patterns [M, in]; qweight int32 [in/8, out]; scales binary16 bit patterns [in/128, out].
+    Returns y [M, out] in binary64 (the exact dequantized product up to binary64 rounding) and the
+    bound sum_k |x_k| |W[o][k]| per output, [M, out], for error bounds."""
+    codes, sbits = unpack_gptq_v1(qweight, scales)           # [out, in], [out, in/128]
+    svals = np.asarray(sbits, np.uint16).view(np.float16).astype(np.float64)
+    Wd = codes.astype(np.float64) * np.repeat(svals, GROUP, axis=1)
+    x = bf16_to_f64(x_bits)
+    return x @ Wd.T, np.abs(x) @ np.abs(Wd).T
