@@ -186,6 +186,21 @@ int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64
                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * W4A16 matmul over the GPTQ-v1 tensors, the consumer check of the packed
+ * output (Qwen3.5-0.8B-Base-CliffQuant-W4A16-G128 model card, "Quantization
+ * configuration": GPTQ v1, 4 bits, group 128, symmetric, 16-bit activations).
+ *   x        device uint16 [M][in]: bfloat16 bit patterns, 16-byte aligned.
+ *   qweight  device int32 [in/8][out], scales device uint16 [in/128][out]
+ *            (binary16 bit patterns): the cq_pack_gptq_v1 outputs.
+ *   y        out, float [M][out]: y[m][o] = sum_g s[g][o] sum_{k in g}
+ *            x[m][k] (u[k][o] - 8), each group's sum in fp32 on the matrix
+ *            cores (exact products), then one fp32 fma with its scale.
+ * in a multiple of 128; M up to 64 * 65535; M == 0 or out == 0 enqueues nothing.
+ */
+int32_t cq_w4a16_matmul(const uint16_t *x, const int32_t *qweight, const uint16_t *scales, int64_t M,
+                        int64_t out, int64_t in, float *y, void *stream);
+
+/*
  * Separately normalized environment diagonals from calibration activations
  * (CliffQuant README, "What CliffQuant changes": activation-weighted sensitivity
  * per calibration environment, each environment normalized on its own; model

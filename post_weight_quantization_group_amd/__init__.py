@@ -31,7 +31,7 @@ __all__ = [
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
     "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "cq_diagonals_workspace_size",
-    "cq_environment_diagonals", "environment_diagonals", "EXPORTED_SYMBOLS",
+    "cq_environment_diagonals", "environment_diagonals", "cq_w4a16_matmul", "w4a16_matmul", "EXPORTED_SYMBOLS",
 ]
 
 GROUP = 128
@@ -42,7 +42,8 @@ _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
-                    "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals")
+                    "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
+                    "cq_w4a16_matmul")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -86,6 +87,8 @@ def load():
         lib.cq_proxy_worst_env_wmse.argtypes = [P, P, I64, I32, I64, P, P, I32, P, P, P, P, SZ, P]
         lib.cq_proxy_worst_env_wmse_multi.restype = I32
         lib.cq_proxy_worst_env_wmse_multi.argtypes = [P, P, I64, I32, I64, I32, P, P, I32, P, P, P, P, SZ, P]
+        lib.cq_w4a16_matmul.restype = I32
+        lib.cq_w4a16_matmul.argtypes = [P, P, P, I64, I64, I64, P, P]
         lib.cq_diagonals_workspace_size.restype = SZ
         lib.cq_diagonals_workspace_size.argtypes = [I32, I64, I64]
         lib.cq_environment_diagonals.restype = I32
@@ -179,6 +182,22 @@ def cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, n_policies, 
                                                 _p(module_offsets), n_modules, _p(module_mean), _p(macro),
                                                 _p(per_group), _p(workspace), ws_bytes, _stream(stream)),
            "cq_proxy_worst_env_wmse_multi")
+
+
+def cq_w4a16_matmul(x, qweight, scales, M, out, inp, y, stream=None):
+    _check(load().cq_w4a16_matmul(_p(x), _p(qweight), _p(scales), M, out, inp, _p(y), _stream(stream)),
+           "cq_w4a16_matmul")
+
+
+def w4a16_matmul(x, qweight, scales, stream=None):
+    """y [M, out] float32 = x [M, in] (bfloat16, or int16 bit patterns) times the dequantized
+    GPTQ-v1 tensors (qweight int32 [in/8, out], scales int16 binary16 bits [in/128, out])."""
+    M, inp = x.shape
+    out = qweight.shape[1]
+    xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+    y = torch.empty((M, out), dtype=torch.float32, device=x.device)
+    cq_w4a16_matmul(xb, qweight, scales, M, out, inp, y, stream)
+    return y
 
 
 def cq_diagonals_workspace_size(E: int, T: int, inp: int) -> int:

@@ -177,6 +177,17 @@ int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_p
                                          module_mean, macro, per_group, workspace, workspace_bytes, stream);
 }
 
+int32_t cq_w4a16_matmul(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, int64_t M, int64_t out,
+                        int64_t in, float* y, void* stream) {
+    if (M < 0 || out < 0 || in < 0 || in % CQ_GROUP != 0) return CQ_EINVAL;
+    if (M == 0 || out == 0) return CQ_OK;
+    if (in == 0) return CQ_EINVAL;
+    if ((M + 63) / 64 > 65535 || (out + 63) / 64 > INT32_MAX) return CQ_EINVAL;
+    if (!x || !qweight || !scales || !y) return CQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(qweight, 4) || !aligned(scales, 2) || !aligned(y, 4)) return CQ_EINVAL;
+    return hip_status(cqk::launch_w4a16(x, qweight, scales, M, out, in, y, (hipStream_t)stream));
+}
+
 size_t cq_diagonals_workspace_size(int32_t E, int64_t T, int64_t in) {
     if (E < 1 || E > CQ_MAX_ENVS || T < 1 || in < CQ_GROUP || in % CQ_GROUP != 0 || in > (int64_t)1 << 24) return 0;
     return round_up((size_t)E * (size_t)cqk::diag_chunks(E, T, in) * (size_t)in * 8u) + round_up((size_t)E * (size_t)in * 8u);

@@ -75,6 +75,10 @@ hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st);
 
+// W4A16 matmul y [M][out] = x [M][in] (bf16) times the GPTQ-v1 tensors dequantized.
+hipError_t launch_w4a16(const uint16_t* x, const int32_t* qw, const uint16_t* scales, int64_t M, int64_t out,
+                        int64_t in, float* y, hipStream_t st);
+
 // Environment diagonals from bf16 activations [E][T][in] into d [in/128][E][128]; part
 // (E * diag_chunks * in) and msq (E * in) are workspace.
 int64_t diag_chunks(int E, int64_t T, int64_t in);

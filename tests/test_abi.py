@@ -135,3 +135,13 @@ def test_environment_diagonals_rejects_bad_arguments():
     assert f(FAKE, 4, 100, 256, None, FAKE, ws, None) == -1
     assert f(FAKE, 4, 100, 256, FAKE, None, ws, None) == -2
     assert f(FAKE, 4, 100, 256, FAKE, FAKE, ws - 8, None) == -2
+
+
+def test_w4a16_matmul_rejects_bad_arguments():
+    lib = cq.load()
+    f = lib.cq_w4a16_matmul
+    assert f(FAKE, FAKE, FAKE, 4, 64, 100, FAKE, None) == -1          # in % 128
+    assert f(FAKE + 8, FAKE, FAKE, 4, 64, 128, FAKE, None) == -1      # x alignment
+    assert f(FAKE, None, FAKE, 4, 64, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, 64 * 65536, 64, 128, FAKE, None) == -1  # M beyond the grid
+    assert f(None, None, None, 0, 64, 128, None, None) == 0           # empty
