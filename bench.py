@@ -7,7 +7,7 @@ scales, and the worst-environment weighted-MSE proxy for the three policies.  In
 resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = groups per second of whole steps; `roofline` describes the
-dominant kernel (the binary32 sweep) measured with HIP events on its own stream;
+headline kernel (the binary32 exhaustive sweep) measured with HIP events on its own stream;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same groups.
 """
 from __future__ import annotations
@@ -461,7 +461,7 @@ def main():
     ms_step = ms_total / args.steps
     value = n_total / (ms_step / 1e3)
 
-    # dominant kernel: the exhaustive sweep call, per launch (one launch per matrix).  Its work:
+    # headline kernel: the exhaustive sweep call, per launch (one launch per matrix).  Its work:
     # the active terms of the chunks no exact screen with its lower bound can skip, per group from
     # a seeded sample of 1,024 groups per matrix (against the optima the sweep returned), times
     # 2E + 4 flops; chunks of 128 patterns as in the kernel.
