@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "groups/s exact minimax FP16 scale search (G=128,E=4); % of FP32 VALU peak"
 SCALES = 31743
 PEAK_FP32_TFLOPS = 157.3  # 256 CU x 4 SIMD x 16 lanes x 2 (dual fp32) x 2 (fma) x 2.4 GHz
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 
 def flops_per_pattern(E: int) -> int:
@@ -264,6 +265,22 @@ def measure_all_configs() -> dict:
                          "hbm_frac": nbytes / (ms / 1e3) / 8e12}
         del xb
     res["config1_diagonals"] = dg
+    # the W4A16 consumer check: config 1's gate matrix (3584 x 1024) quantized by the exhaustive
+    # solver and packed, times M bf16 activation rows, on the matrix cores
+    A, dmat = W.make_matrix(1, 0)
+    w1, d1, p1 = W.matrix_groups(A, dmat)
+    out1, in1 = A.shape
+    r1 = cq.quantize_groups(torch.from_numpy(w1).to(dev), torch.from_numpy(d1).to(dev), p1)
+    qw1, sc1 = cq.pack_gptq_v1(r1["codes"].reshape(out1, in1), r1["scales"].reshape(out1, in1 // 128), out1, in1)
+    xs1 = torch.from_numpy(W.calibration_activations(1, 0, 8192)[0].view(np.int16)).to(dev)
+    wq = {}
+    for M in (16, 2048, 8192):
+        xm = xs1[:M].contiguous()
+        _, ms = _timed(lambda: cq.w4a16_matmul(xm, qw1, sc1), reps=10)
+        fl = 2.0 * M * out1 * in1
+        wq[f"M{M}"] = {"ms": ms, "TFLOP_per_s": fl / (ms / 1e3) / 1e12,
+                       "bf16_mfma_frac": fl / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)}
+    res["config1_w4a16"] = wq
     # config 2: candidate + pack + proxy on every matrix, exhaustive on the 10,000-group sample
     spec = W.config(2)
     cand_ms = pack_ms = proxy_ms = 0.0
