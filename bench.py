@@ -189,6 +189,66 @@ def _timed(fn, reps=1):
     return out, a.elapsed_time(b) / reps
 
 
+def measure_aux() -> dict:
+    """The rows beyond the solver: environment diagonals, the W4A16 consumer check and the held-out
+    comparison, each on config 1 or config 2 at the pages' sizes."""
+    import torch
+    import post_weight_quantization_group_amd as cq
+    import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    res = {}
+    # environment diagonals from calibration activations: config 1's gate/up (in 1,024) and down
+    # (in 3,584) inputs, E = 4, 8,192 bf16 tokens per environment; HBM-bound (2 bytes per element)
+    dg = {}
+    for m in (0, 2):
+        xb = torch.from_numpy(W.calibration_activations(1, m, 8192).view(np.int16)).to(dev)
+        E_, T_, n_ = xb.shape
+        _, ms = _timed(lambda: cq.environment_diagonals(xb), reps=5)
+        nbytes = E_ * T_ * n_ * 2 + n_ * E_ * 4
+        dg[f"in{n_}"] = {"E": E_, "tokens_per_env": T_, "ms": ms, "GB_per_s": nbytes / (ms / 1e3) / 1e9,
+                         "hbm_frac": nbytes / (ms / 1e3) / 8e12}
+        del xb
+    res["config1_diagonals"] = dg
+    # the W4A16 consumer check: config 1's gate matrix (3584 x 1024) quantized by the exhaustive
+    # solver and packed, times M bf16 activation rows, on the matrix cores
+    A, dmat = W.make_matrix(1, 0)
+    w1, d1, p1 = W.matrix_groups(A, dmat)
+    out1, in1 = A.shape
+    r1 = cq.quantize_groups(torch.from_numpy(w1).to(dev), torch.from_numpy(d1).to(dev), p1)
+    qw1, sc1 = cq.pack_gptq_v1(r1["codes"].reshape(out1, in1), r1["scales"].reshape(out1, in1 // 128), out1, in1)
+    xs1 = torch.from_numpy(W.calibration_activations(1, 0, 8192)[0].view(np.int16)).to(dev)
+    wq = {}
+    for M in (16, 2048, 8192):
+        xm = xs1[:M].contiguous()
+        _, ms = _timed(lambda: cq.w4a16_matmul(xm, qw1, sc1), reps=10)
+        fl = 2.0 * M * out1 * in1
+        wq[f"M{M}"] = {"ms": ms, "TFLOP_per_s": fl / (ms / 1e3) / 1e12,
+                       "bf16_mfma_frac": fl / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)}
+    res["config1_w4a16"] = wq
+    # held-out evaluation on config 2: 4,096 groups sampled across all 150 matrices, scales from
+    # the calibration diagonals, the three policies' proxy on held-out diagonals, and minimax
+    # against pooled with a 10,000-replicate module-stratified bootstrap
+    wh, dh, deh, offh = W.heldout_sample(2, 4096)
+    nh = wh.shape[0]
+    idxh = W.bootstrap_indices(offh, 10000, seed=0)
+    wt, dt, det = (torch.from_numpy(x).to(dev) for x in (wh, dh, deh))
+    ot, it = torch.from_numpy(offh).to(dev), torch.from_numpy(idxh).to(dev)
+    r = cq.quantize_groups(wt, dt, nh, method="exhaustive", pooled=True)
+    ab = cq.baseline_scales(wt, dt, nh, "absmax", objective=False)
+    sv = torch.stack((r["scales"], r["pooled_scales"], ab["scales"]))
+    (pgh, mmh, mach), ms_p = _timed(lambda: cq.proxy_worst_env_wmse_multi(wt, det, sv, ot, nh))
+    (cnt, eff, _, ci), ms_h = _timed(lambda: cq.heldout_compare(pgh[0].contiguous(), pgh[1].contiguous(), ot, it))
+    macro = mach.cpu().numpy()
+    res["config2_heldout"] = {"groups": nh, "modules": int(offh.size - 1), "E": 4, "replicates": 10000,
+                              "proxy_macro_minimax_pooled_absmax": [float(x) for x in macro],
+                              "minimax_wins_ties_losses_vs_pooled": [int(x) for x in cnt.cpu().numpy()],
+                              "effect_pooled_minus_minimax": float(eff.cpu().item()),
+                              "effect_ci95": [float(x) for x in ci.cpu().numpy()],
+                              "proxy_ms": ms_p, "compare_ms": ms_h}
+    return res
+
+
 def measure_all_configs() -> dict:
     """Throughput of every kernel on the five synthetic configs (reported beside the headline).
 
@@ -253,34 +313,7 @@ def measure_all_configs() -> dict:
     res["config0"] = matrix_pass(0)
     res["config1"] = matrix_pass(1)
     res["config4"] = matrix_pass(4)
-    # environment diagonals from calibration activations: config 1's gate/up (in 1,024) and down
-    # (in 3,584) inputs, E = 4, 8,192 bf16 tokens per environment; HBM-bound (2 bytes per element)
-    dg = {}
-    for m in (0, 2):
-        xb = torch.from_numpy(W.calibration_activations(1, m, 8192).view(np.int16)).to(dev)
-        E_, T_, n_ = xb.shape
-        _, ms = _timed(lambda: cq.environment_diagonals(xb), reps=5)
-        nbytes = E_ * T_ * n_ * 2 + n_ * E_ * 4
-        dg[f"in{n_}"] = {"E": E_, "tokens_per_env": T_, "ms": ms, "GB_per_s": nbytes / (ms / 1e3) / 1e9,
-                         "hbm_frac": nbytes / (ms / 1e3) / 8e12}
-        del xb
-    res["config1_diagonals"] = dg
-    # the W4A16 consumer check: config 1's gate matrix (3584 x 1024) quantized by the exhaustive
-    # solver and packed, times M bf16 activation rows, on the matrix cores
-    A, dmat = W.make_matrix(1, 0)
-    w1, d1, p1 = W.matrix_groups(A, dmat)
-    out1, in1 = A.shape
-    r1 = cq.quantize_groups(torch.from_numpy(w1).to(dev), torch.from_numpy(d1).to(dev), p1)
-    qw1, sc1 = cq.pack_gptq_v1(r1["codes"].reshape(out1, in1), r1["scales"].reshape(out1, in1 // 128), out1, in1)
-    xs1 = torch.from_numpy(W.calibration_activations(1, 0, 8192)[0].view(np.int16)).to(dev)
-    wq = {}
-    for M in (16, 2048, 8192):
-        xm = xs1[:M].contiguous()
-        _, ms = _timed(lambda: cq.w4a16_matmul(xm, qw1, sc1), reps=10)
-        fl = 2.0 * M * out1 * in1
-        wq[f"M{M}"] = {"ms": ms, "TFLOP_per_s": fl / (ms / 1e3) / 1e12,
-                       "bf16_mfma_frac": fl / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)}
-    res["config1_w4a16"] = wq
+    res.update(measure_aux())
     # config 2: candidate + pack + proxy on every matrix, exhaustive on the 10,000-group sample
     spec = W.config(2)
     cand_ms = pack_ms = proxy_ms = 0.0
@@ -319,26 +352,6 @@ def measure_all_configs() -> dict:
                           / (PEAK_FP32_TFLOPS * 1e12),
                       "sample_candidate_vs_exhaustive_scale_mismatches":
                           int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
-    # held-out evaluation on config 2: 4,096 groups sampled across all 150 matrices, scales from
-    # the calibration diagonals, the three policies' proxy on held-out diagonals, and minimax
-    # against pooled with a 10,000-replicate module-stratified bootstrap
-    wh, dh, deh, offh = W.heldout_sample(2, 4096)
-    nh = wh.shape[0]
-    idxh = W.bootstrap_indices(offh, 10000, seed=0)
-    wt, dt, det = (torch.from_numpy(x).to(dev) for x in (wh, dh, deh))
-    ot, it = torch.from_numpy(offh).to(dev), torch.from_numpy(idxh).to(dev)
-    r = cq.quantize_groups(wt, dt, nh, method="exhaustive", pooled=True)
-    ab = cq.baseline_scales(wt, dt, nh, "absmax", objective=False)
-    sv = torch.stack((r["scales"], r["pooled_scales"], ab["scales"]))
-    (pgh, mmh, mach), ms_p = _timed(lambda: cq.proxy_worst_env_wmse_multi(wt, det, sv, ot, nh))
-    (cnt, eff, _, ci), ms_h = _timed(lambda: cq.heldout_compare(pgh[0].contiguous(), pgh[1].contiguous(), ot, it))
-    macro = mach.cpu().numpy()
-    res["config2_heldout"] = {"groups": nh, "modules": int(offh.size - 1), "E": 4, "replicates": 10000,
-                              "proxy_macro_minimax_pooled_absmax": [float(x) for x in macro],
-                              "minimax_wins_ties_losses_vs_pooled": [int(x) for x in cnt.cpu().numpy()],
-                              "effect_pooled_minus_minimax": float(eff.cpu().item()),
-                              "effect_ci95": [float(x) for x in ci.cpu().numpy()],
-                              "proxy_ms": ms_p, "compare_ms": ms_h}
     # config 3: per-group diagonals
     w3, d3, cat3, _ = W.make_groups(3)
     n3 = w3.shape[0]
@@ -367,6 +380,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-candidate", action="store_true")
+    ap.add_argument("--aux-only", action="store_true",
+                    help="only measure the diagonals, W4A16 and held-out rows (one JSON line, no step)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also measure every kernel on the five synthetic configs (adds 'per_config')")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -377,6 +392,10 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): every group is independent, "
               "so several GPUs would each run this same benchmark on their own share.", file=sys.stderr)
         sys.exit(2)
+
+    if args.aux_only:
+        print(json.dumps({"aux": measure_aux()}), flush=True)
+        return
 
     import torch
 

@@ -59,11 +59,16 @@ __global__ __launch_bounds__(256) void heldout_module_means_kernel(const double*
     double v = __builtin_nan("");
     if (lo >= 0 && hi <= n && lo < hi) {
         const int32_t* draw = row == 0 ? nullptr : idx + (int64_t)(row - 1) * n;
+        // a draw outside the module marks the row bad and reads the module's first group instead,
+        // so the loop has no early exit and the loads of later steps issue ahead of the adds
         bool ok = true;
         double acc = 0.0;
+#pragma unroll 4
         for (int64_t j = lo; j < hi; ++j) {
-            const int64_t g = draw ? (int64_t)draw[j] : j;
-            if (g < lo || g >= hi) { ok = false; break; }
+            int64_t g = draw ? (int64_t)draw[j] : j;
+            const bool in = g >= lo && g < hi;
+            ok = ok && in;
+            g = in ? g : lo;
             const double dv = pb[g] - pa[g];
             acc = j == lo ? dv : acc + dv;
         }
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(256) void heldout_rank_kernel(const double* __restr
         __syncthreads();
         for (int k = threadIdx.x; k < tn; k += blockDim.x) tile[k] = order_key(reps[t0 + k]);
         __syncthreads();
-        for (int k = 0; k < tn; ++k) {
+#pragma unroll 8
+        for (int k = 0; k < tn; ++k) {  // unrolled: the LDS reads issue ahead of the compares
             const uint64_t kj = tile[k];
             rank += (kj < ki || (kj == ki && t0 + k < i)) ? 1 : 0;
         }
