@@ -202,8 +202,9 @@ int32_t cq_w4a16_matmul(const uint16_t *x, const int32_t *qweight, const uint16_
 
 /*
  * Separately normalized environment diagonals from calibration activations
- * (CliffQuant README, "What CliffQuant changes": activation-weighted sensitivity
- * per calibration environment, each environment normalized on its own; model
+ * (CliffQuant README, "What CliffQuant changes": each channel's sensitivity
+ * weighted by its activations, per calibration environment, each environment
+ * normalized on its own; model
  * card, "Calibration and evaluation data": environments of 256-token windows,
  * a 16-bit model runtime).
  *   x   device uint16 [E][T][in]: bfloat16 bit patterns of the activations
@@ -222,8 +223,9 @@ int32_t cq_environment_diagonals(const uint16_t *x, int32_t E, int64_t T, int64_
 /*
  * Held-out comparison of two scale policies on the proxy's per-group values
  * (CliffQuant README, "Held-out reconstruction proxy": the minimax policy's
- * wins, ties and losses against Pooled-WMSE by group, and the paired
- * module-stratified bootstrap effect with its 95% interval).
+ * wins, ties and losses against Pooled-WMSE by group, and a 95% interval for
+ * the effect from a bootstrap resampling within modules, paired across the
+ * policies).
  *   pa, pb          device double [n_groups]: per-group proxy values p_g of
  *                   policies A and B (e.g. two rows of the per_group output of
  *                   cq_proxy_worst_env_wmse_multi on held-out diagonals).

@@ -14,8 +14,8 @@ array reshuffles or means:
   "Held-out reconstruction proxy"; CliffQuant README, "Held-out
   reconstruction proxy");
 * the held-out comparison of two policies on that proxy: per-group wins, ties
-  and losses, the macro effect and its paired module-stratified bootstrap
-  interval (CliffQuant README, "Held-out reconstruction proxy").
+  and losses, the macro effect and the interval of a bootstrap that resamples
+  groups within modules, paired across the two policies (CliffQuant README, "Held-out reconstruction proxy").
 """
 from __future__ import annotations
 
@@ -267,7 +267,8 @@ def _seq_sum_rows(x: np.ndarray) -> np.ndarray:
 def heldout_compare(pa, pb, module_offsets, boot_idx, alpha: float = 0.05):
     """Policy A against policy B on per-group proxy values (CliffQuant README, "Held-out
     reconstruction proxy": CliffQuant's wins, ties and losses against Pooled-WMSE by group, and the
-    paired module-stratified bootstrap effect with its 95% interval).
+    bootstrap of the effect, resampling within modules and paired across policies, with its 95%
+    interval).
 
     Readings where the pages are silent:
     * a win of A is p_A < p_B, a tie p_A == p_B, a loss p_A > p_B (exact comparisons);
@@ -328,8 +329,8 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 def environment_diagonals(x_bits) -> np.ndarray:
     """Separately normalized environment diagonals from calibration activations (CliffQuant
-    README, "What CliffQuant changes": activation-weighted sensitivity per calibration
-    environment, each environment normalized on its own).
+    README, "What CliffQuant changes": each channel's sensitivity weighted by its activations, per
+    calibration environment, each environment normalized on its own).
 
     Reading where the pages are silent: for environment e with tokens t = 1..T,
     d_{e,i} = (1/T) sum_t x_{t,i}^2, then divided by its mean over the channels i, in binary64,

@@ -1,6 +1,6 @@
 // Separately normalized environment diagonals from calibration activations, for gfx950
-// (CliffQuant README, "What CliffQuant changes": activation-weighted sensitivity per calibration
-// environment, each environment normalized on its own; model card, "Calibration and evaluation
+// (CliffQuant README, "What CliffQuant changes": each channel's sensitivity weighted by its
+// activations, per calibration environment, each environment normalized on its own; model card, "Calibration and evaluation
 // data": four environments of calibration windows, a 16-bit model runtime).
 //
 // Reading where the pages are silent: d_{e,i} = (1/T) sum_t x_{t,i}^2 over environment e's T

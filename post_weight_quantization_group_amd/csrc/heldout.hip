@@ -1,7 +1,7 @@
 // Held-out comparison of two scale policies on the proxy's per-group values, for gfx950
 // (CliffQuant README, "Held-out reconstruction proxy": CliffQuant's wins, ties and losses
-// against Pooled-WMSE by group, and the paired module-stratified bootstrap effect with its 95%
-// interval).
+// against Pooled-WMSE by group, and a bootstrap of the effect that resamples groups within each
+// module, with the same draws for both policies, and its 95% interval).
 //
 // Readings where the pages are silent: A wins a group when p_A < p_B, ties when p_A == p_B;
 // the effect is the mean over modules of each module's mean of (p_B - p_A); replicate r
