@@ -208,7 +208,8 @@ int32_t cq_environment_diagonals(const uint16_t* x, int32_t E, int64_t T, int64_
 
 size_t cq_heldout_workspace_size(int32_t n_boot, int32_t n_modules) {
     if (n_boot < 0 || n_modules < 1) return 0;
-    return round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u) + round_up((size_t)n_boot * 8u);
+    return round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u) + round_up((size_t)n_boot * 8u) +
+           round_up((size_t)n_boot * 4u);
 }
 
 int32_t cq_heldout_compare(const double* pa, const double* pb, int64_t n_groups, const int64_t* module_offsets,
@@ -226,8 +227,9 @@ int32_t cq_heldout_compare(const double* pa, const double* pb, int64_t n_groups,
     uint8_t* ws = (uint8_t*)workspace;
     double* mm = (double*)ws;
     double* reps = (double*)(ws + round_up((size_t)(n_boot + 1) * (size_t)n_modules * 8u));
+    int32_t* rank = (int32_t*)((uint8_t*)reps + round_up((size_t)n_boot * 8u));
     return hip_status(cqk::launch_heldout(pa, pb, n_groups, module_offsets, n_modules, boot_idx, n_boot, alpha,
-                                          counts, effect, boot, ci, mm, reps, (hipStream_t)stream));
+                                          counts, effect, boot, ci, mm, reps, rank, (hipStream_t)stream));
 }
 
 }  // extern "C"

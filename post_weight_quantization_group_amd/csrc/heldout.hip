@@ -10,9 +10,11 @@
 // replicates.  Every sum runs left to right in binary64, so the results are the sequential
 // definition bit for bit.
 //
-// Launches: counts (one workgroup); module means, one thread per (row, module) with row 0 the
-// identity draw; macro means, one thread per row; a rank sort of the replicates under a total
-// order (NaN last, ties by index), tiled through LDS; the two percentiles.
+// Launches: counts (one workgroup); module means with row 0 the identity draw, either from LDS (the
+// differences and each row's draws staged there, one thread per module) or, for more than 4,096
+// groups, one thread per (row, module) from global memory; macro means, one thread per row; a rank
+// sort of the replicates under a total order (NaN last, ties by index): ranks counted over key
+// tiles on a 2-D grid and added with integer atomics, then a scatter; the two percentiles.
 #include "device.h"
 #include "launch.h"
 
@@ -77,17 +79,67 @@ __global__ __launch_bounds__(256) void heldout_module_means_kernel(const double*
     mm[t] = v;
 }
 
+// The same sums with the differences (once) and each row's draws staged in LDS: one workgroup per
+// MEANS_ROWS rows, one thread per module summing from LDS in the same order.  n <= MEANS_LDS_N.
+constexpr int MEANS_ROWS = 16;
+constexpr int MEANS_LDS_N = 4096;
+
+__global__ __launch_bounds__(256) void heldout_module_means_lds_kernel(const double* __restrict__ pa,
+                                                                       const double* __restrict__ pb, int n,
+                                                                       const int64_t* __restrict__ off, int M,
+                                                                       const int32_t* __restrict__ idx, int B,
+                                                                       double* __restrict__ mm) {
+    __shared__ double diff[MEANS_LDS_N];
+    __shared__ int32_t draw[MEANS_LDS_N];
+    for (int g = threadIdx.x; g < n; g += 256) diff[g] = pb[g] - pa[g];
+    const int r0 = blockIdx.x * MEANS_ROWS;
+    const int r1 = r0 + MEANS_ROWS < B + 1 ? r0 + MEANS_ROWS : B + 1;
+    for (int row = r0; row < r1; ++row) {
+        __syncthreads();
+        if (row == 0) {
+            for (int j = threadIdx.x; j < n; j += 256) draw[j] = j;
+        } else {
+            const int32_t* src = idx + (int64_t)(row - 1) * n;
+            for (int j = threadIdx.x; j < n; j += 256) draw[j] = src[j];
+        }
+        __syncthreads();
+        for (int m = threadIdx.x; m < M; m += 256) {
+            const int64_t lo = off[m], hi = off[m + 1];
+            double v = __builtin_nan("");
+            if (lo >= 0 && hi <= n && lo < hi) {
+                bool ok = true;
+                double acc = 0.0;
+#pragma unroll 4
+                for (int64_t j = lo; j < hi; ++j) {
+                    int64_t g = draw[j];
+                    const bool in = g >= lo && g < hi;
+                    ok = ok && in;
+                    g = in ? g : lo;
+                    const double dv = diff[g];
+                    acc = j == lo ? dv : acc + dv;
+                }
+                if (ok) v = acc / (double)(hi - lo);
+            }
+            mm[(int64_t)row * M + m] = v;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void heldout_macro_kernel(const double* __restrict__ mm, int M, int B,
                                                             double* __restrict__ effect,
-                                                            double* __restrict__ reps) {
+                                                            double* __restrict__ reps, int32_t* __restrict__ rank) {
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row > B) return;
     const double* r = mm + (int64_t)row * M;
     double acc = r[0];
     for (int m = 1; m < M; ++m) acc = acc + r[m];
     const double v = acc / (double)M;
-    if (row == 0) *effect = v;
-    else reps[row - 1] = v;
+    if (row == 0) {
+        *effect = v;
+    } else {
+        reps[row - 1] = v;
+        rank[row - 1] = 0;  // the rank counters the next launch adds into
+    }
 }
 
 // Total order on binary64 values with every NaN last: flip the sign bit of non-negative
@@ -100,25 +152,32 @@ __device__ __forceinline__ uint64_t order_key(double v) {
 
 constexpr int RANK_TILE = 1024;
 
+// grid (B / 256 rounded up, B / RANK_TILE rounded up): workgroup (x, y) counts, for its 256
+// replicates, the replicates of key tile y ordered before them, and adds the count to their rank
+// (integer sums: the same total in any order).
 __global__ __launch_bounds__(256) void heldout_rank_kernel(const double* __restrict__ reps, int B,
-                                                           double* __restrict__ sorted) {
+                                                           int32_t* __restrict__ rank) {
     __shared__ uint64_t tile[RANK_TILE];
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const double v = i < B ? reps[i] : 0.0;
-    const uint64_t ki = order_key(v);
-    int rank = 0;
-    for (int t0 = 0; t0 < B; t0 += RANK_TILE) {
-        const int tn = B - t0 < RANK_TILE ? B - t0 : RANK_TILE;
-        __syncthreads();
-        for (int k = threadIdx.x; k < tn; k += blockDim.x) tile[k] = order_key(reps[t0 + k]);
-        __syncthreads();
+    const uint64_t ki = order_key(i < B ? reps[i] : 0.0);
+    const int t0 = blockIdx.y * RANK_TILE;
+    const int tn = B - t0 < RANK_TILE ? B - t0 : RANK_TILE;
+    for (int k = threadIdx.x; k < tn; k += blockDim.x) tile[k] = order_key(reps[t0 + k]);
+    __syncthreads();
+    int cnt = 0;
 #pragma unroll 8
-        for (int k = 0; k < tn; ++k) {  // unrolled: the LDS reads issue ahead of the compares
-            const uint64_t kj = tile[k];
-            rank += (kj < ki || (kj == ki && t0 + k < i)) ? 1 : 0;
-        }
+    for (int k = 0; k < tn; ++k) {
+        const uint64_t kj = tile[k];
+        cnt += (kj < ki || (kj == ki && t0 + k < i)) ? 1 : 0;
     }
-    if (i < B) sorted[rank] = v;
+    if (i < B && cnt > 0) atomicAdd(&rank[i], cnt);
+}
+
+__global__ __launch_bounds__(256) void heldout_scatter_kernel(const double* __restrict__ reps,
+                                                              const int32_t* __restrict__ rank, int B,
+                                                              double* __restrict__ sorted) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < B) sorted[rank[i]] = reps[i];
 }
 
 __device__ __forceinline__ double percentile_sorted(const double* v, int B, double q) {
@@ -147,15 +206,23 @@ __global__ void heldout_nan_kernel(double* __restrict__ ci) {
 
 hipError_t launch_heldout(const double* pa, const double* pb, int64_t n, const int64_t* off, int M,
                           const int32_t* idx, int B, double alpha, int64_t* counts, double* effect,
-                          double* boot, double* ci, double* mm, double* reps, hipStream_t st) {
+                          double* boot, double* ci, double* mm, double* reps, int32_t* rank, hipStream_t st) {
     hipLaunchKernelGGL(heldout_counts_kernel, dim3(1), dim3(COUNT_THREADS), 0, st, pa, pb, n, counts);
-    const int64_t rows = (int64_t)(B + 1) * M;
-    hipLaunchKernelGGL(heldout_module_means_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, pa,
-                       pb, n, off, M, idx, B, mm);
+    if (n <= MEANS_LDS_N) {
+        hipLaunchKernelGGL(heldout_module_means_lds_kernel, dim3((unsigned)((B + 1 + MEANS_ROWS - 1) / MEANS_ROWS)),
+                           dim3(256), 0, st, pa, pb, (int)n, off, M, idx, B, mm);
+    } else {
+        const int64_t rows = (int64_t)(B + 1) * M;
+        hipLaunchKernelGGL(heldout_module_means_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, pa,
+                           pb, n, off, M, idx, B, mm);
+    }
     hipLaunchKernelGGL(heldout_macro_kernel, dim3((unsigned)((B + 1 + 255) / 256)), dim3(256), 0, st, mm, M, B,
-                       effect, reps);
+                       effect, reps, rank);
     if (B > 0) {
-        hipLaunchKernelGGL(heldout_rank_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, reps, B, boot);
+        hipLaunchKernelGGL(heldout_rank_kernel, dim3((unsigned)((B + 255) / 256), (unsigned)((B + RANK_TILE - 1) / RANK_TILE)),
+                           dim3(256), 0, st, reps, B, rank);
+        hipLaunchKernelGGL(heldout_scatter_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, reps, rank, B,
+                           boot);
         hipLaunchKernelGGL(heldout_ci_kernel, dim3(1), dim3(64), 0, st, boot, B, alpha, ci);
     } else {
         hipLaunchKernelGGL(heldout_nan_kernel, dim3(1), dim3(64), 0, st, ci);

@@ -86,10 +86,10 @@ hipError_t launch_diagonals(const uint16_t* x, int E, int64_t T, int64_t in, flo
                             hipStream_t st);
 
 // Held-out comparison of two policies' per-group values: counts, effect, sorted bootstrap
-// replicates and the percentile interval; mm ((B + 1) * M) and reps (B) are workspace.
+// replicates and the percentile interval; mm ((B + 1) * M), reps (B) and rank (B) are workspace.
 hipError_t launch_heldout(const double* pa, const double* pb, int64_t n, const int64_t* off, int M,
                           const int32_t* idx, int B, double alpha, int64_t* counts, double* effect,
-                          double* boot, double* ci, double* mm, double* reps, hipStream_t st);
+                          double* boot, double* ci, double* mm, double* reps, int32_t* rank, hipStream_t st);
 
 hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups, int P,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,

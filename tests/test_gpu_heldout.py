@@ -105,3 +105,23 @@ def _gpu_t(pa_t, pb_t, off, idx, alpha=0.05):
     c, e, b, ci = cq.heldout_compare(pa_t.contiguous(), pb_t.contiguous(), dev(off), dev(idx), alpha)
     torch.cuda.synchronize()
     return c.cpu().numpy(), e.cpu().item(), b.cpu().numpy(), ci.cpu().numpy()
+
+
+def test_more_groups_than_the_lds_path_holds():
+    """5,000 groups in 40 modules: the module means take the global-memory kernel."""
+    rng = np.random.default_rng(77)
+    sizes = rng.integers(1, 250, 40)
+    sizes[-1] += 5000 - sizes.sum() if sizes.sum() < 5000 else 0
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    assert n > 4096
+    pa = rng.lognormal(-8, 1, n)
+    pb = pa * (1 + rng.normal(0, 0.02, n))
+    idx = W.bootstrap_indices(off, 300, seed=77)
+    say(f"held-out comparison, global path: {n} groups, {sizes.size} modules")
+    gc, ge, gb, gci = _gpu(pa, pb, off, idx)
+    oc, oe, ob, oci = oracle.heldout_compare(pa, pb, off, idx)
+    assert list(gc) == list(oc)
+    _same([ge], [oe])
+    _same(gb, ob)
+    _same(gci, oci)
