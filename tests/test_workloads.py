@@ -90,3 +90,32 @@ def test_config4_diagonal_permutation_structure():
     # each env is a renormalised copy of one base row with 410 channels permuted
     same = np.isclose(dm[0] / dm[0].mean(), dm[1] / dm[1].mean(), rtol=1e-5)
     assert 4096 - 2 * 410 <= same.sum() <= 4096
+
+
+def test_heldout_inputs_are_seeded_and_laid_out_by_module():
+    a = W.heldout_sample(0, 50)
+    b = W.heldout_sample(0, 50)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    w, d, de, off = a
+    n = w.shape[0]
+    assert d.shape == de.shape == (n, 4, 128) and d.dtype == de.dtype == np.float32
+    assert off[0] == 0 and off[-1] == n and np.all(np.diff(off) > 0)
+    # held-out diagonals share the calibration base but not its perturbation
+    assert not np.array_equal(d, de)
+    r = np.log(de.astype(np.float64) / d.astype(np.float64))
+    assert abs(float(np.median(r))) < 0.3 and float(np.std(r)) > 0.3
+
+
+def test_bootstrap_indices_are_seeded():
+    off = np.array([0, 5, 9, 20])
+    assert np.array_equal(W.bootstrap_indices(off, 30, seed=1), W.bootstrap_indices(off, 30, seed=1))
+    assert not np.array_equal(W.bootstrap_indices(off, 30, seed=1), W.bootstrap_indices(off, 30, seed=2))
+
+
+def test_calibration_activations_are_seeded_bf16_with_the_diagonal_scale():
+    x = W.calibration_activations(0, 0, 64)
+    assert x.dtype == np.uint16 and x.shape == (4, 64, 256)
+    assert np.array_equal(x, W.calibration_activations(0, 0, 64))
+    v = (x.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isfinite(v)) and np.all((x & 0x7F80) != 0x7F80)
