@@ -9,7 +9,8 @@ module marshals numpy arrays into it and adds the two steps that are plain
 array reshuffles or means:
 
 * GPTQ-v1 packing (Qwen3.5-0.8B-Base-CliffQuant-W4A16-G128 model card,
-  "Quantization configuration": GPTQ v1, 4 bits, group 128, symmetric);
+  "Quantization configuration": GPTQ v1, 4 bits, group 128, symmetric; 2- and
+  8-bit codes and other group lengths packed the same way, field by field);
 * the module-macro worst-environment weighted-MSE proxy (same card,
   "Held-out reconstruction proxy"; CliffQuant README, "Held-out
   reconstruction proxy");
@@ -25,7 +26,9 @@ import subprocess
 
 import numpy as np
 
-GROUP = 128
+GROUP = 128                       # the group length the pages use
+QMIN, QMAX = -8, 7                # the code range the pages use (signed 4-bit)
+MAX_GROUP = 1024                  # longest group the oracle takes
 FIRST_BITS, LAST_BITS = 0x0001, 0x7BFF
 N_SCALES = LAST_BITS - FIRST_BITS + 1  # 31,743
 
@@ -57,18 +60,18 @@ def _load():
         I64, I32, U32 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
         lib.oracle_fp16_value.restype = ctypes.c_double
         lib.oracle_fp16_value.argtypes = [U32]
-        lib.oracle_solve.restype = None
-        lib.oracle_solve.argtypes = [P, P, I64, I32, I64, P, P, P, P, P, P, P, P, I32]
+        lib.oracle_solve.restype = I32
+        lib.oracle_solve.argtypes = [P, P, I64, I32, I64, I32, I32, I32, P, P, P, P, P, P, P, P, I32]
         lib.oracle_codes.restype = None
-        lib.oracle_codes.argtypes = [P, I64, U32, P]
-        lib.oracle_env_errors.restype = None
-        lib.oracle_env_errors.argtypes = [P, P, I64, I32, I64, P, P, I32]
-        lib.oracle_curve.restype = None
-        lib.oracle_curve.argtypes = [P, P, I32, P, P]
+        lib.oracle_codes.argtypes = [P, I64, U32, I32, I32, P]
+        lib.oracle_env_errors.restype = I32
+        lib.oracle_env_errors.argtypes = [P, P, I64, I32, I64, I32, I32, I32, P, P, I32]
+        lib.oracle_curve.restype = I32
+        lib.oracle_curve.argtypes = [P, P, I32, I32, I32, I32, P, P]
         lib.oracle_fp16_round.restype = U32
         lib.oracle_fp16_round.argtypes = [ctypes.c_float]
         lib.oracle_absmax.restype = None
-        lib.oracle_absmax.argtypes = [P, I64, P]
+        lib.oracle_absmax.argtypes = [P, I64, I32, I32, P]
         _lib = lib
     return _lib
 
@@ -77,13 +80,21 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _spec(qmin: int, qmax: int):
+    qmin, qmax = int(qmin), int(qmax)
+    if not (-128 <= qmin <= 0 <= qmax <= 127 and qmin < qmax):
+        raise ValueError("code range must satisfy -128 <= qmin <= 0 <= qmax <= 127, qmin < qmax")
+    return qmin, qmax
+
+
 def _groups(w, d, d_period):
     w = np.ascontiguousarray(w, dtype=np.float32)
     d = np.ascontiguousarray(d, dtype=np.float32)
-    if w.ndim != 2 or w.shape[1] != GROUP:
-        raise ValueError("w must be [n_groups, 128]")
-    if d.ndim != 3 or d.shape[2] != GROUP:
-        raise ValueError("d must be [n_d, E, 128]")
+    if w.ndim != 2 or not 1 <= w.shape[1] <= MAX_GROUP:
+        raise ValueError("w must be [n_groups, G] with 1 <= G <= 1024")
+    G = w.shape[1]
+    if d.ndim != 3 or d.shape[2] != G:
+        raise ValueError("d must be [n_d, E, G]")
     if d_period is None:
         d_period = d.shape[0]
     if not (1 <= d_period <= d.shape[0]):
@@ -91,7 +102,7 @@ def _groups(w, d, d_period):
     E = d.shape[1]
     if not (1 <= E <= 32):
         raise ValueError("E must be in 1..32")
-    return w, d, int(d_period), E
+    return w, d, int(d_period), E, G
 
 
 def fp16_value(bits: int) -> float:
@@ -104,25 +115,26 @@ def fp16_round(x: float) -> int:
     return int(_load().oracle_fp16_round(float(np.float32(x))))
 
 
-def codes_at(w, bits: int) -> np.ndarray:
-    """q_i = clip(round-half-even(fl32(w_i / s)), -8, 7) for every weight, at one scale."""
+def codes_at(w, bits: int, qmin: int = QMIN, qmax: int = QMAX) -> np.ndarray:
+    """q_i = clip(round-half-even(fl32(w_i / s)), qmin, qmax) for every weight, at one scale."""
+    qmin, qmax = _spec(qmin, qmax)
     w = np.ascontiguousarray(w, dtype=np.float32).ravel()
     out = np.empty(w.size, dtype=np.int8)
-    _load().oracle_codes(_ptr(w), w.size, int(bits), _ptr(out))
+    _load().oracle_codes(_ptr(w), w.size, int(bits), qmin, qmax, _ptr(out))
     return out
 
 
 class Solution:
     """Brute-force result per group (see ``solve``)."""
 
-    def __init__(self, n):
+    def __init__(self, n, G=GROUP):
         self.mm_bits = np.zeros(n, np.uint16)
         self.mm_F1 = np.zeros(n, np.float64)
         self.mm_F2 = np.zeros(n, np.float64)
         self.pl_bits = np.zeros(n, np.uint16)
         self.pl_P1 = np.zeros(n, np.float64)
         self.pl_P2 = np.zeros(n, np.float64)
-        self.codes = np.zeros((n, GROUP), np.int8)
+        self.codes = np.zeros((n, G), np.int8)
         self.ok = np.zeros(n, np.uint8)
 
     @staticmethod
@@ -142,106 +154,130 @@ class Solution:
         return self._gap(self.pl_P1, self.pl_P2)
 
 
-def solve(w, d, d_period=None, n_threads: int = 0) -> Solution:
+def solve(w, d, d_period=None, n_threads: int = 0, qmin: int = QMIN, qmax: int = QMAX) -> Solution:
     """Exhaustive minimax and pooled-WMSE scale selection over all 31,743 FP16 scales.
 
     CliffQuant README, "What CliffQuant changes": the objective, the code rule,
     the admissible set and the lower-bit-pattern tie rule; the pooled policy
     averages the environments first (README opening question; proxy table).
+    The quantizer is the README's "Use the solver" specification: codes in
+    [qmin, qmax], groups of G = w.shape[1] weights (the pages run [-8, 7], G = 128).
     """
-    w, d, d_period, E = _groups(w, d, d_period)
+    w, d, d_period, E, G = _groups(w, d, d_period)
+    qmin, qmax = _spec(qmin, qmax)
     n = w.shape[0]
-    r = Solution(n)
-    _load().oracle_solve(_ptr(w), _ptr(d), d_period, E, n,
-                         _ptr(r.mm_bits), _ptr(r.mm_F1), _ptr(r.mm_F2),
-                         _ptr(r.pl_bits), _ptr(r.pl_P1), _ptr(r.pl_P2),
-                         _ptr(r.codes), _ptr(r.ok), int(n_threads))
+    r = Solution(n, G)
+    rc = _load().oracle_solve(_ptr(w), _ptr(d), d_period, E, n, G, qmin, qmax,
+                              _ptr(r.mm_bits), _ptr(r.mm_F1), _ptr(r.mm_F2),
+                              _ptr(r.pl_bits), _ptr(r.pl_P1), _ptr(r.pl_P2),
+                              _ptr(r.codes), _ptr(r.ok), int(n_threads))
+    if rc != 0:
+        raise ValueError("the oracle rejected the quantizer specification")
     return r
 
 
-def env_errors(w, d, bits, d_period=None, n_threads: int = 0) -> np.ndarray:
+def env_errors(w, d, bits, d_period=None, n_threads: int = 0, qmin: int = QMIN, qmax: int = QMAX) -> np.ndarray:
     """[n_groups, E] per-environment weighted squared error at the given scales."""
-    w, d, d_period, E = _groups(w, d, d_period)
+    w, d, d_period, E, G = _groups(w, d, d_period)
+    qmin, qmax = _spec(qmin, qmax)
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     if bits.shape != (w.shape[0],):
         raise ValueError("one scale per group")
     out = np.empty((w.shape[0], E), np.float64)
-    _load().oracle_env_errors(_ptr(w), _ptr(d), d_period, E, w.shape[0], _ptr(bits), _ptr(out),
-                              int(n_threads))
+    rc = _load().oracle_env_errors(_ptr(w), _ptr(d), d_period, E, w.shape[0], G, qmin, qmax, _ptr(bits),
+                                   _ptr(out), int(n_threads))
+    if rc != 0:
+        raise ValueError("the oracle rejected the quantizer specification")
     return out
 
 
-def objective(w, d, bits, d_period=None, n_threads: int = 0) -> np.ndarray:
+def objective(w, d, bits, d_period=None, n_threads: int = 0, qmin: int = QMIN, qmax: int = QMAX) -> np.ndarray:
     """Worst-environment objective max_e F_e at the given scales."""
-    return env_errors(w, d, bits, d_period, n_threads).max(axis=1)
+    return env_errors(w, d, bits, d_period, n_threads, qmin, qmax).max(axis=1)
 
 
-def curve(w_group, d_group):
-    """(F[31743], P[31743]) over b = 1..0x7BFF for one group (w [128], d [E,128])."""
-    w = np.ascontiguousarray(w_group, dtype=np.float32).reshape(GROUP)
-    d = np.ascontiguousarray(d_group, dtype=np.float32)
+def curve(w_group, d_group, qmin: int = QMIN, qmax: int = QMAX):
+    """(F[31743], P[31743]) over b = 1..0x7BFF for one group (w [G], d [E, G])."""
+    qmin, qmax = _spec(qmin, qmax)
+    w = np.ascontiguousarray(w_group, dtype=np.float32).ravel()
+    G = w.size
+    d = np.ascontiguousarray(d_group, dtype=np.float32).reshape(-1, G)
     E = d.shape[0]
     F = np.empty(N_SCALES, np.float64)
     P = np.empty(N_SCALES, np.float64)
-    _load().oracle_curve(_ptr(w), _ptr(d), E, _ptr(F), _ptr(P))
+    if _load().oracle_curve(_ptr(w), _ptr(d), E, G, qmin, qmax, _ptr(F), _ptr(P)) != 0:
+        raise ValueError("the oracle rejected the quantizer specification")
     return F, P
 
 
-def absmax_bits(w) -> np.ndarray:
-    """AbsMax policy: fp16(fl32(max|w| / 7)), 0 -> 0x0001, overflow -> 0x7BFF."""
+def absmax_bits(w, qmax: int = QMAX) -> np.ndarray:
+    """AbsMax policy: fp16(fl32(max|w| / qmax)), 0 -> 0x0001, overflow -> 0x7BFF (qmax = 7 on the pages)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2 or not 1 <= int(qmax) <= 127:
+        raise ValueError("w must be [n_groups, G] and 1 <= qmax <= 127")
     out = np.empty(w.shape[0], np.uint16)
-    _load().oracle_absmax(_ptr(w), w.shape[0], _ptr(out))
+    _load().oracle_absmax(_ptr(w), w.shape[0], w.shape[1], int(qmax), _ptr(out))
     return out
 
 
-def codes_for(w, bits) -> np.ndarray:
-    """[n_groups, 128] codes of each group at its own scale."""
+def codes_for(w, bits, qmin: int = QMIN, qmax: int = QMAX) -> np.ndarray:
+    """[n_groups, G] codes of each group at its own scale."""
     w = np.ascontiguousarray(w, dtype=np.float32)
-    return np.stack([codes_at(w[g], int(bits[g])) for g in range(w.shape[0])]) if w.shape[0] else \
-        np.zeros((0, GROUP), np.int8)
+    if w.shape[0] == 0:
+        return np.zeros((0, w.shape[1] if w.ndim == 2 else GROUP), np.int8)
+    return np.stack([codes_at(w[g], int(bits[g]), qmin, qmax) for g in range(w.shape[0])])
 
 
 # ---------------------------------------------------------------- GPTQ-v1 packing
-def pack_gptq_v1(codes, grp_scale_bits, out: int, inp: int):
-    """GPTQ-v1 symmetric 4-bit packing of one matrix.
+def pack_gptq_v1(codes, grp_scale_bits, out: int, inp: int, bits: int = 4, group: int = GROUP):
+    """GPTQ-v1 symmetric packing of one matrix, `bits` in {2, 4, 8} (the pages use 4).
 
-    codes          -- [out, in] int8 in [-8, 7] (group g = row*(in/128) + in_chunk);
-    grp_scale_bits -- [out, in/128] binary16 bit patterns.
-    Returns (qweight [in/8, out] int32, scales [in/128, out] uint16): nibble j
-    (bits 4j..4j+3) of qweight[r, o] holds codes[o, 8r+j] + 8.
+    codes          -- [out, in] int8 in [-2^(bits-1), 2^(bits-1) - 1] (group g = row*(in/group) + in_chunk);
+    grp_scale_bits -- [out, in/group] binary16 bit patterns.
+    Returns (qweight [in*bits/32, out] int32, scales [in/group, out] uint16): field j
+    (bits j*bits .. j*bits + bits - 1, low field first) of qweight[r, o] holds
+    codes[o, (32/bits)*r + j] + 2^(bits-1).
     """
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    per = 32 // bits
     c = np.asarray(codes, dtype=np.int64).reshape(out, inp)
-    if inp % GROUP:
-        raise ValueError("in must be a multiple of 128")
-    u = (c + 8).reshape(out, inp // 8, 8)
-    word = np.zeros((out, inp // 8), dtype=np.uint64)
-    for j in range(8):
-        word |= (u[:, :, j].astype(np.uint64) << np.uint64(4 * j))
+    if inp % group or inp % per:
+        raise ValueError("in must be a multiple of the group length and of 32/bits")
+    u = (c + (1 << (bits - 1))).reshape(out, inp // per, per)
+    word = np.zeros((out, inp // per), dtype=np.uint64)
+    for j in range(per):
+        word |= (u[:, :, j].astype(np.uint64) << np.uint64(bits * j))
     qweight = word.T.astype(np.uint32).view(np.int32)
-    scales = np.asarray(grp_scale_bits, dtype=np.uint16).reshape(out, inp // GROUP).T
+    scales = np.asarray(grp_scale_bits, dtype=np.uint16).reshape(out, inp // group).T
     return np.ascontiguousarray(qweight), np.ascontiguousarray(scales)
 
 
-def unpack_gptq_v1(qweight, scales):
-    """Inverse of ``pack_gptq_v1``: (codes [out, in] int8, grp_scale_bits [out, in/128])."""
+def unpack_gptq_v1(qweight, scales, bits: int = 4):
+    """Inverse of ``pack_gptq_v1``: (codes [out, in] int8, grp_scale_bits [out, in/group])."""
+    per = 32 // bits
     q = np.asarray(qweight).view(np.uint32).astype(np.int64)
     rows, out = q.shape
-    nib = np.stack([(q >> (4 * j)) & 0xF for j in range(8)], axis=1)  # [in/8, 8, out]
-    codes = (nib.reshape(rows * 8, out).T - 8).astype(np.int8)
+    mask = (1 << bits) - 1
+    fld = np.stack([(q >> (bits * j)) & mask for j in range(per)], axis=1)  # [rows, per, out]
+    codes = (fld.reshape(rows * per, out).T - (1 << (bits - 1))).astype(np.int8)
     return codes, np.ascontiguousarray(np.asarray(scales, np.uint16).T)
 
 
 # ---------------------------------------------------------------- proxy
-def proxy(w, d_eval, bits, module_of_group, n_modules: int, d_period=None, n_threads: int = 0):
+def proxy(w, d_eval, bits, module_of_group, n_modules: int, d_period=None, n_threads: int = 0,
+          qmin: int = QMIN, qmax: int = QMAX):
     """Module-macro worst-environment weighted MSE.
 
-    Per group p_g = max_e (1/128) sum_i d_eval[e][i] (w_i - s_g q_i)^2; then the
+    Per group p_g = max_e (1/G) sum_i d_eval[e][i] (w_i - s_g q_i)^2; then the
     mean of p_g over each module's groups (in group order); then the mean over
-    modules (in module order).  Returns (per_group, module_mean, macro).
+    modules (in module order).  A module with no groups has no mean: NaN, and
+    the macro over modules is then NaN too (the reading the held-out comparison
+    takes for an empty module as well).  Returns (per_group, module_mean, macro).
     """
-    F = env_errors(w, d_eval, bits, d_period, n_threads)
-    per_group = (F / float(GROUP)).max(axis=1)
+    F = env_errors(w, d_eval, bits, d_period, n_threads, qmin, qmax)
+    G = np.asarray(w).shape[1]
+    per_group = (F / float(G)).max(axis=1)
     mod = np.asarray(module_of_group, dtype=np.int64)
     module_mean = np.zeros(n_modules, np.float64)
     for m in range(n_modules):
@@ -249,7 +285,7 @@ def proxy(w, d_eval, bits, module_of_group, n_modules: int, d_period=None, n_thr
         acc = 0.0
         for v in vals:
             acc = acc + float(v)
-        module_mean[m] = acc / len(vals) if len(vals) else 0.0
+        module_mean[m] = acc / len(vals) if len(vals) else float("nan")
     acc = 0.0
     for v in module_mean:
         acc = acc + float(v)

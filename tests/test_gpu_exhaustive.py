@@ -371,11 +371,12 @@ def test_proxy_multi_matches_single_calls_and_oracle(E, n_pol):
         np.testing.assert_array_equal(pg[k], p1.cpu().numpy())
         np.testing.assert_array_equal(mm[k], m1.cpu().numpy())
         assert np.isnan(mm[k, 1])
-        rp, rm, _ = oracle.proxy(w, d, bits[k], mods, 4, n)
+        rp, rm, rmac = oracle.proxy(w, d, bits[k], mods, 4, n)
         np.testing.assert_allclose(pg[k], rp, rtol=1e-6, atol=0)
-        keep = np.array([0, 2, 3])
-        np.testing.assert_allclose(mm[k, keep], rm[keep], rtol=1e-6, atol=0)
-        assert np.isnan(macro[k]) and np.isnan(mac1.cpu().item())
+        # every module, the empty one included: NaN on both sides (no mean of no groups)
+        assert np.isnan(rm[1])
+        np.testing.assert_allclose(mm[k], rm, rtol=1e-6, atol=0, equal_nan=True)
+        assert np.isnan(macro[k]) and np.isnan(mac1.cpu().item()) and np.isnan(rmac)
 
 
 def test_repeatable():

@@ -98,26 +98,38 @@ def _tiny_group(ws, ds):
     return w, d
 
 
-def _check_against_exact(ws, ds):
-    b, F1, F2, _ = X.solve(ws, ds)
-    w, d = _tiny_group(ws, ds)
-    r = oracle.solve(w, d)
-    exact_gap = float((F2 - F1) / F1) if F1 else (0.0 if F2 == 0 else np.inf)
-    if exact_gap > 1e-12:
-        assert int(r.mm_bits[0]) == b
-    else:
-        assert abs(r.mm_F1[0] - float(F1)) <= 1e-12 * float(F1)
-    assert r.mm_F1[0] == pytest.approx(float(F1), rel=1e-13, abs=0)
-    return b
+def _check_against_exact(ws, ds, qmin=-8, qmax=7, G=128, pos=None):
+    """The oracle on the group zero-padded to G (weights at positions `pos`, default the first
+    ones) against the exact brute force: minimax and pooled argmin bits where the exact runner-up
+    gap exceeds 1e-12, and both minima to binary64 rounding."""
+    ex = X.solve(ws, ds, qmin, qmax)
+    pos = list(range(len(ws))) if pos is None else list(pos)
+    w = np.zeros((1, G), np.float32)
+    d = np.zeros((1, len(ds), G), np.float32)
+    w[0, pos] = ws
+    d[0][:, pos] = np.asarray(ds, np.float32)
+    # diagonals of the zero weights are arbitrary: a zero weight adds 0 at every scale
+    d[0][:, [i for i in range(G) if i not in pos]] = 3.0
+    r = oracle.solve(w, d, qmin=qmin, qmax=qmax)
+    for name, bits, v1, v2, got_bits, got_v1 in (
+            ("minimax", ex.mm_bits, ex.F1, ex.F2, r.mm_bits[0], r.mm_F1[0]),
+            ("pooled", ex.pl_bits, ex.P1, ex.P2, r.pl_bits[0], r.pl_P1[0])):
+        exact_gap = float((v2 - v1) / v1) if v1 else (0.0 if v2 == 0 else np.inf)
+        if exact_gap > 1e-12:
+            assert int(got_bits) == bits, name
+        assert got_v1 == pytest.approx(float(v1), rel=1e-13, abs=0), name
+    return ex
 
 
 def test_pages_example_matches_exact_rational():
-    """The README's four-weight, two-environment example: oracle argmin == exact argmin."""
+    """The README's four-weight, two-environment example: oracle argmin == exact argmin, for the
+    minimax and the pooled policy (which differ here: 0x31E8 and 0x31E0)."""
     g = json.load(open(os.path.join(GOLDEN, "pages_example.json")))
     w, d = workloads.pages_example()
     assert np.array_equal(w[0, :4], np.float32(g["weights"]))
     assert np.array_equal(d[0, :, :4], np.float32(g["environment_diagonals"]))
-    _check_against_exact(g["weights"], g["environment_diagonals"])
+    ex = _check_against_exact(g["weights"], g["environment_diagonals"])
+    assert ex.mm_bits != ex.pl_bits
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
@@ -128,6 +140,66 @@ def test_random_tiny_groups_match_exact_rational(seed):
     ws = workloads.round_bf16(rng.normal(0, 0.05, n).astype(np.float32))
     ds = rng.lognormal(0, 1, (E, n)).astype(np.float32)
     _check_against_exact(list(ws), ds.tolist())
+
+
+def test_pooled_policy_matches_exact_rational_with_three_environments():
+    """Pooled objective pinned where it differs from every single environment's choice: three
+    environments that each weigh a different weight, so the average's argmin is none of the
+    per-environment argmins and a pooled sum that drops or misweighs an environment picks
+    another scale."""
+    ws = [0.8125, -0.296875, 0.1484375]
+    ds = [[4.0, 0.25, 0.5], [0.25, 4.0, 0.5], [0.5, 0.25, 4.0]]
+    ex = _check_against_exact(ws, ds)
+    singles = {X.solve(ws, [row]).mm_bits for row in ds}
+    assert ex.pl_bits not in singles
+
+
+# ---------------------------------------------------------------- other quantizer ranges and lengths
+@pytest.mark.parametrize("qmin,qmax,G,pos", [
+    (-4, 3, 64, (0, 21, 40, 63)),        # signed 3-bit, groups of 64
+    (-2, 1, 32, (3, 17, 31)),            # signed 2-bit, groups of 32
+    (-128, 127, 256, (5, 129, 200, 255)),  # signed 8-bit, groups of 256 (weights past index 128)
+    (0, 15, 128, (1, 64, 127)),          # unsigned 4-bit: negative weights take code 0
+])
+def test_quantizer_spec_matches_exact_rational(qmin, qmax, G, pos):
+    """The README's solver takes a quantizer specification (qmin, qmax) and a group of any length
+    (its example has four weights).  Tiny groups placed at scattered positions of longer groups,
+    two environments: oracle against the exact brute force with the same code range."""
+    rng = np.random.default_rng(qmax * 1000 + G)
+    ws = workloads.round_bf16(rng.normal(0, 0.05, len(pos)).astype(np.float32))
+    ws[0] = abs(ws[0]) * 3
+    ds = rng.lognormal(0, 1, (2, len(pos))).astype(np.float32)
+    _check_against_exact(list(ws), ds.tolist(), qmin, qmax, G, pos)
+
+
+def test_groups_of_other_lengths_are_laid_out_back_to_back():
+    """Three groups of 64 weights in one call, [n_groups][64] and diagonals [n_groups][E][64]: an
+    all-zero group (pattern 0x0001), then single weights whose winners are known in closed form
+    (the smallest binary16 scale at which the weight is an admissible code exactly)."""
+    G = 64
+    w = np.zeros((3, G), np.float32)
+    w[1, 10] = 0.75
+    w[2, 60] = -0.3125
+    d = np.ones((3, 2, G), np.float32)
+    r = oracle.solve(w, d, qmin=-4, qmax=3)
+    assert r.mm_bits[0] == 0x0001
+    # 0.75 = 3 * 0.25 (code 3, the largest); -0.3125 = -4 * 0.078125 (code -4, the smallest)
+    assert r.mm_bits[1] == int(np.float16(0.25).view(np.uint16))
+    assert r.mm_bits[2] == int(np.float16(0.078125).view(np.uint16))
+    assert r.mm_F1[1] == 0.0 and r.mm_F1[2] == 0.0
+    assert list(r.codes[1, 9:12]) == [0, 3, 0] and r.codes[2, 60] == -4
+
+
+def test_code_range_cases():
+    """Round half to even first, then clip to the range: at scale 1, [-2, 1] maps 1.5 -> 2 -> 1,
+    -2.5 -> -2, -3 -> -2; [0, 15] maps every negative weight to 0 and 15.5 -> 16 -> 15;
+    [-128, 127] maps 126.5 -> 126, 127.5 -> 128 -> 127, -128.5 -> -128."""
+    w = np.array([1.5, -2.5, -3.0, 0.5], np.float32)
+    assert list(oracle.codes_at(w, 0x3C00, -2, 1)) == [1, -2, -2, 0]
+    w = np.array([-0.75, -100.0, 15.5, 14.5, 2.5], np.float32)
+    assert list(oracle.codes_at(w, 0x3C00, 0, 15)) == [0, 0, 15, 14, 2]
+    w = np.array([126.5, 127.5, -128.5, -127.5], np.float32)
+    assert list(oracle.codes_at(w, 0x3C00, -128, 127)) == [126, 127, -128, -128]
 
 
 # ---------------------------------------------------------------- P3: E=1 closed form
@@ -171,6 +243,33 @@ def test_winner_is_local_min_of_frozen_code_envelope():
         assert float(f0) == pytest.approx(r.mm_F1[g], rel=1e-13)
         for nb in (b - 1, b + 1):
             assert frozen(nb) >= f0 * (1 - Fraction(1, 10 ** 12))
+
+
+def test_single_environment_pooled_equals_minimax_bit_for_bit():
+    """E = 1: P(s) = F_0(s) / 1 = F(s) exactly, so both policies pick the same pattern with the
+    same minimum and runner-up, bit for bit."""
+    w, d, p = workloads.matrix_groups(*workloads.make_matrix(0, 0))
+    r = oracle.solve(w[:12], d[:, 1:2], p, n_threads=8)
+    np.testing.assert_array_equal(r.pl_bits, r.mm_bits)
+    np.testing.assert_array_equal(r.pl_P1, r.mm_F1)
+    np.testing.assert_array_equal(r.pl_P2, r.mm_F2)
+
+
+def test_pooled_policy_is_minimax_on_the_mean_diagonal():
+    """sum_e F_e(s) / E is the single-environment objective with the mean diagonal (1/E) sum_e d_e,
+    exactly in real arithmetic.  The mean diagonal rounded to binary32 moves the objective by at
+    most 2^-24 relative, so wherever both gaps exceed 1e-6 the pooled pick equals the E = 1
+    minimax pick on the mean diagonal, and its objective matches to 1e-6."""
+    w, d, p = workloads.matrix_groups(*workloads.make_matrix(0, 0))
+    w = w[:24]
+    dbar = d.astype(np.float64).mean(axis=1, keepdims=True).astype(np.float32)
+    a = oracle.solve(w, d, p, n_threads=8)
+    b = oracle.solve(w, dbar, p, n_threads=8)
+    sure = (a.pl_gap > 1e-6) & (b.mm_gap > 1e-6)
+    assert sure.sum() >= 12
+    np.testing.assert_array_equal(a.pl_bits[sure], b.mm_bits[sure])
+    np.testing.assert_allclose(a.pl_P1, b.mm_F1, rtol=1e-6)
+    assert np.any(a.pl_bits != a.mm_bits)  # the pooled policy differs from the minimax one here
 
 
 # ---------------------------------------------------------------- P4: dominance
@@ -332,6 +431,12 @@ def test_absmax_policy_cases():
         m = np.float32(np.abs(w[g]).max())
         assert got[g] == int((m / np.float32(7)).astype(np.float16).view(np.uint16))
     assert got[2] == 0x0001 and got[3] == 0x7BFF and got[4] == 0x0001
+    # another code range: the largest magnitude maps to the largest positive code, max|w| / qmax
+    for qmax in (1, 3, 127):
+        got = oracle.absmax_bits(w[:2], qmax=qmax)
+        m = np.float32(np.abs(w[1]).max())
+        assert got[1] == int((m / np.float32(qmax)).astype(np.float16).view(np.uint16))
+        assert got[0] == int((np.float32(0.7) / np.float32(qmax)).astype(np.float16).view(np.uint16))
 
 
 # ---------------------------------------------------------------- GPTQ-v1 packing
@@ -358,6 +463,29 @@ def test_pack_round_trip():
     np.testing.assert_array_equal(s2, sb)
 
 
+@pytest.mark.parametrize("bits", [2, 8])
+def test_pack_other_widths_hand_values_and_round_trip(bits):
+    """bits = 2: sixteen 2-bit fields per int32, value code + 2; bits = 8: four bytes, code + 128;
+    low field first, transposed to [in * bits / 32, out]."""
+    per, zero = 32 // bits, 1 << (bits - 1)
+    out, inp = 2, 128
+    codes = np.zeros((out, inp), np.int8)
+    codes[0] = (np.arange(inp) % per) % (1 << bits) - zero
+    codes[1] = -zero
+    sb = np.array([[0x3C00], [0x3C01]], np.uint16)
+    qw, sc = oracle.pack_gptq_v1(codes, sb, out, inp, bits=bits)
+    assert qw.shape == (inp // per, out)
+    want0 = sum(((j % (1 << bits)) << (bits * j)) for j in range(per)) & 0xFFFFFFFF
+    assert np.all(qw[:, 0].view(np.uint32) == want0) and np.all(qw[:, 1] == 0)
+    assert list(sc[:, 1]) == [0x3C01]
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(-zero, zero, (8, 256)).astype(np.int8)
+    sb = rng.integers(1, 0x7C00, (8, 4)).astype(np.uint16)
+    c2, s2 = oracle.unpack_gptq_v1(*oracle.pack_gptq_v1(codes, sb, 8, 256, bits=bits, group=64), bits=bits)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, sb)
+
+
 # ---------------------------------------------------------------- proxy
 def test_proxy_hand_values():
     """w = 0.375 at s = 0.25: q = round-half-even(1.5) = 2, error -0.125, squared 1/64.
@@ -376,6 +504,22 @@ def test_proxy_hand_values():
     w[2, 7] = 0.0
     per, mod, macro = oracle.proxy(w, d, bits, [0, 1, 1], 2, d_period=1)
     assert list(mod) == [1 / 4096, 1 / 8192] and macro == (1 / 4096 + 1 / 8192) / 2
+
+
+def test_proxy_divides_by_the_group_length_and_empty_module_is_nan():
+    """Groups of 64: w = 0.375 at s = 0.25 gives error 1/64 per unit diagonal, so with diagonals 1
+    and 2 the worst environment's mean square is (2/64)/64 = 1/2048.  A module with no groups has
+    no mean (NaN), and neither has the macro over modules."""
+    w = np.zeros((2, 64), np.float32)
+    w[:, 0] = 0.375
+    d = np.zeros((1, 2, 64), np.float32)
+    d[0, 0, :] = 1.0
+    d[0, 1, :] = 2.0
+    bits = np.full(2, int(np.float16(0.25).view(np.uint16)), np.uint16)
+    per, mod, macro = oracle.proxy(w, d, bits, [0, 2], 3, d_period=1)
+    assert list(per) == [1 / 2048] * 2
+    assert mod[0] == 1 / 2048 and np.isnan(mod[1]) and mod[2] == 1 / 2048
+    assert np.isnan(macro)
 
 
 def test_minimax_proxy_not_worse_than_baselines_on_calibration_diagonals():
