@@ -54,8 +54,9 @@
 extern "C" {
 #endif
 
-#define CQ_ABI_VERSION 1
+#define CQ_ABI_VERSION 2
 #define CQ_GROUP 128
+#define CQ_MAX_GROUP 256 /* longest group cq_quantize_groups_spec takes */
 #define CQ_MAX_ENVS 32
 #define CQ_MAX_POLICIES 64
 #define CQ_MAX_BOOT (1 << 20)
@@ -67,13 +68,31 @@ extern "C" {
 #define CQ_EHIP (-3)         /* a HIP launch failed (hipGetLastError) */
 #define CQ_EUNSUPPORTED (-4) /* valid arguments this entry point does not serve */
 
-/* Solvers (cq_quantize_groups `method`). */
-#define CQ_EXHAUSTIVE 0 /* evaluate every one of the 31,743 scales */
-#define CQ_CANDIDATE 1  /* code-transition / vertex / intersection candidates */
+/* Solvers (cq_quantize_groups `method`); all three return the same result.
+ *  CQ_EXHAUSTIVE  the independent full-grid enumerator (README, "What CliffQuant changes": a
+ *                 separate reference evaluates every one of the 31,743 binary16 values): the
+ *                 binary32 objective of every weight at every scale, then binary64 rescoring of
+ *                 every scale its error bound cannot rule out.  No scale is skipped.
+ *  CQ_CANDIDATE   the production solver's idea (same section): candidates from code transitions,
+ *                 quadratic vertices and environment intersections; groups whose direct
+ *                 candidates tie exactly go to CQ_BOUNDED (README and model card, "Verification").
+ *  CQ_BOUNDED     branch and bound over the grid: stops at the first scale >= 2 max|w| (every
+ *                 larger one ties with it exactly and loses to it), takes chunk-constant codes in
+ *                 closed form and skips chunks of scales whose proven lower bound exceeds the
+ *                 best value screened; the outputs are those of the full grid. */
+#define CQ_EXHAUSTIVE 0
+#define CQ_CANDIDATE 1
+#define CQ_BOUNDED 2
 
-/* Baseline policies (cq_baseline_scales `which`). */
-#define CQ_ABSMAX 0      /* s = fp16(fl32(max_i |w_i| / 7)); 0 -> 0x0001, overflow -> 0x7BFF */
-#define CQ_POOLED_WMSE 1 /* minimise P(s) = (1/E) sum_e F_e(s) over the same grid and tie rule */
+/* Baseline policies (cq_baseline_scales `which`), the two the pages compare the minimax
+ * scales with (CliffQuant README, the opening question and the "Held-out reconstruction
+ * proxy" table; model card, "Held-out reconstruction proxy"):
+ *  CQ_ABSMAX       the matched AbsMax checkpoint's scale, s = fp16(fl32(max_i |w_i| / 7));
+ *                  0 -> 0x0001, overflow -> 0x7BFF.
+ *  CQ_POOLED_WMSE  the environments averaged before the scale is chosen: minimise
+ *                  P(s) = (1/E) sum_e F_e(s) over the same grid with the same tie rule. */
+#define CQ_ABSMAX 0
+#define CQ_POOLED_WMSE 1
 
 /* Per-group flag bits (cq_quantize_groups `flags`). */
 #define CQ_FLAG_BAD_INPUT 1u  /* non-finite w or d, or d < 0: scale 0, codes 0, objective NaN */
@@ -88,14 +107,15 @@ int32_t cq_abi_version(void);
 /* Static description of a status code. */
 const char *cq_status_string(int32_t status);
 
-/* Bytes of workspace cq_quantize_groups needs for `method`, E and n_groups
- * (also valid for cq_baseline_scales with CQ_POOLED_WMSE, method
- * CQ_EXHAUSTIVE).  Returns 0 for invalid arguments. */
+/* Bytes of workspace cq_quantize_groups (and cq_quantize_groups_spec) needs for
+ * `method`, E and n_groups (any group length); CQ_EXHAUSTIVE and CQ_BOUNDED
+ * return the same size, which is also what cq_baseline_scales with
+ * CQ_POOLED_WMSE needs.  Returns 0 for invalid arguments. */
 size_t cq_workspace_size(int32_t method, int32_t E, int64_t n_groups);
 
 /*
  * Minimax scale, codes and objective for n_groups groups.
- *   method       CQ_EXHAUSTIVE or CQ_CANDIDATE; both return the same result.
+ *   method       CQ_EXHAUSTIVE, CQ_CANDIDATE or CQ_BOUNDED; all return the same result.
  *   scales       out, required.
  *   codes        out, nullable.
  *   objective    out, nullable: F(s) at the chosen scale, binary64.
@@ -115,10 +135,29 @@ int32_t cq_quantize_groups(const float *w, const float *d, int64_t d_period, int
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * cq_quantize_groups for another quantizer (CliffQuant README, "Use the solver": the
+ * solver takes a quantizer specification with qmin and qmax and a group of any length,
+ * its example four weights): codes q_i = clip(round-half-even(w_i / s), qmin, qmax),
+ * groups of group_len weights.
+ *   w      float32 [n_groups][group_len], 4-byte aligned.
+ *   d      float32 [n_d][E][group_len], 4-byte aligned; group g uses slice g % d_period.
+ *   codes  out, nullable, int8 [n_groups][group_len].
+ * 1 <= group_len <= CQ_MAX_GROUP, -128 <= qmin <= 0 <= qmax <= 127, qmin < qmax (else
+ * CQ_EINVAL).  (128, -8, 7) is cq_quantize_groups itself, with its alignment rules; any
+ * other quantizer is served by CQ_EXHAUSTIVE only (CQ_EUNSUPPORTED for the other methods).
+ * Other outputs, workspace and errors as for cq_quantize_groups.
+ */
+int32_t cq_quantize_groups_spec(const float *w, const float *d, int32_t group_len, int32_t qmin, int32_t qmax,
+                                int64_t d_period, int32_t E, int64_t n_groups, int32_t method,
+                                uint16_t *scales, int8_t *codes, double *objective, uint8_t *flags,
+                                uint16_t *pooled_scales, double *pooled_objective,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Baseline scale policies.
  *   CQ_ABSMAX       d may be NULL when objective is NULL; no workspace needed.
- *   CQ_POOLED_WMSE  exhaustive sweep of P(s); workspace as for
- *                   cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups).
+ *   CQ_POOLED_WMSE  the argmin of P(s) over every scale (the CQ_BOUNDED search of P);
+ *                   workspace as for cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups).
  *   objective  nullable: for CQ_ABSMAX the worst-environment objective F at
  *              the AbsMax scale; for CQ_POOLED_WMSE the pooled objective P.
  */

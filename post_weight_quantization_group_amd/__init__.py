@@ -24,10 +24,10 @@ import os
 import torch
 
 __all__ = [
-    "CQError", "GROUP", "EXHAUSTIVE", "CANDIDATE", "ABSMAX", "POOLED_WMSE",
+    "CQError", "GROUP", "MAX_GROUP", "EXHAUSTIVE", "CANDIDATE", "BOUNDED", "ABSMAX", "POOLED_WMSE",
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
-    "cq_quantize_groups", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
+    "cq_quantize_groups", "cq_quantize_groups_spec", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
     "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "cq_diagonals_workspace_size",
@@ -35,11 +35,13 @@ __all__ = [
 ]
 
 GROUP = 128
-EXHAUSTIVE, CANDIDATE = 0, 1
+MAX_GROUP = 256
+EXHAUSTIVE, CANDIDATE, BOUNDED = 0, 1, 2
 ABSMAX, POOLED_WMSE = 0, 1
 FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 1, 2, 4, 8, 16
-_METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE}
+_METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE, "bounded": BOUNDED}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
+                    "cq_quantize_groups_spec",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
@@ -77,6 +79,8 @@ def load():
         lib.cq_workspace_size.argtypes = [I32, I32, I64]
         lib.cq_quantize_groups.restype = I32
         lib.cq_quantize_groups.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, P, P, P, SZ, P]
+        lib.cq_quantize_groups_spec.restype = I32
+        lib.cq_quantize_groups_spec.argtypes = [P, P, I32, I32, I32, I64, I32, I64, I32, P, P, P, P, P, P, P, SZ, P]
         lib.cq_baseline_scales.restype = I32
         lib.cq_baseline_scales.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, SZ, P]
         lib.cq_pack_gptq_v1.restype = I32
@@ -151,6 +155,16 @@ def cq_quantize_groups(w, d, d_period, E, n_groups, method, scales, codes=None, 
     _check(load().cq_quantize_groups(_p(w), _p(d), d_period, E, n_groups, method, _p(scales), _p(codes),
                                      _p(objective), _p(flags), _p(pooled_scales), _p(pooled_objective),
                                      _p(workspace), ws_bytes, _stream(stream)), "cq_quantize_groups")
+
+
+def cq_quantize_groups_spec(w, d, group_len, qmin, qmax, d_period, E, n_groups, method, scales, codes=None,
+                            objective=None, flags=None, pooled_scales=None, pooled_objective=None, workspace=None,
+                            stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_quantize_groups_spec(_p(w), _p(d), group_len, qmin, qmax, d_period, E, n_groups, method,
+                                          _p(scales), _p(codes), _p(objective), _p(flags), _p(pooled_scales),
+                                          _p(pooled_objective), _p(workspace), ws_bytes, _stream(stream)),
+           "cq_quantize_groups_spec")
 
 
 def cq_baseline_scales(w, d, d_period, E, n_groups, which, scales, codes=None, objective=None, workspace=None,
@@ -235,21 +249,33 @@ def _shape_check(w, d):
 
 
 def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled=False, workspace=None,
-                    stream=None):
+                    stream=None, qmin=-8, qmax=7):
     """Minimax scales (and codes, objective, flags; optionally the pooled policy) for every group.
 
+    w is float32 [n_groups, G] and d float32 [n_d, E, G]; G = 128 with codes in [qmin, qmax] =
+    [-8, 7] is the pages' quantizer, any other G <= 256 or range goes through
+    cq_quantize_groups_spec (method "exhaustive" only).  method: "exhaustive" (every scale),
+    "bounded" (branch and bound) or "candidate"; all give the same result.
     Returns a dict of device tensors: scales (uint16 bit patterns held in int16
     storage -> use ``.view(torch.uint16)`` or ``& 0xFFFF``), codes, objective,
     flags and, with ``pooled=True``, pooled_scales and pooled_objective.
     """
-    _shape_check(w, d)
+    G = w.shape[1] if w.dim() == 2 else -1
+    spec = (G, int(qmin), int(qmax)) != (GROUP, -8, 7)
+    if spec:
+        if w.dim() != 2 or not 1 <= G <= MAX_GROUP or w.dtype != torch.float32:
+            raise ValueError("w must be float32 [n_groups, G] with 1 <= G <= 256")
+        if d.dim() != 3 or d.shape[2] != G or d.dtype != torch.float32:
+            raise ValueError("d must be float32 [n_d, E, G]")
+    else:
+        _shape_check(w, d)
     n, E = w.shape[0], d.shape[1]
     d_period = d.shape[0] if d_period is None else int(d_period)
     m = _METHODS[method] if isinstance(method, str) else int(method)
     dev = w.device
     out = {
         "scales": torch.empty(n, dtype=torch.int16, device=dev),
-        "codes": torch.empty((n, GROUP), dtype=torch.int8, device=dev) if codes else None,
+        "codes": torch.empty((n, G), dtype=torch.int8, device=dev) if codes else None,
         "objective": torch.empty(n, dtype=torch.float64, device=dev),
         "flags": torch.empty(n, dtype=torch.uint8, device=dev),
     }
@@ -258,8 +284,12 @@ def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled
         out["pooled_objective"] = torch.empty(n, dtype=torch.float64, device=dev)
     if workspace is None:
         workspace = _workspace(cq_workspace_size(m, E, n), dev)
-    cq_quantize_groups(w, d, d_period, E, n, m, out["scales"], out["codes"], out["objective"], out["flags"],
-                       out.get("pooled_scales"), out.get("pooled_objective"), workspace, stream)
+    if spec:
+        cq_quantize_groups_spec(w, d, G, qmin, qmax, d_period, E, n, m, out["scales"], out["codes"], out["objective"],
+                                out["flags"], out.get("pooled_scales"), out.get("pooled_objective"), workspace, stream)
+    else:
+        cq_quantize_groups(w, d, d_period, E, n, m, out["scales"], out["codes"], out["objective"], out["flags"],
+                           out.get("pooled_scales"), out.get("pooled_objective"), workspace, stream)
     return out
 
 
@@ -358,25 +388,29 @@ def heldout_compare(pa, pb, module_offsets, boot_idx, alpha=0.05, stream=None):
     return counts, effect, boot[:n_boot], ci
 
 
-def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax: int = 7, method="candidate",
+def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax: int = 7, method=None,
                            device="cuda"):
-    """One group, in the shape of the pages' solver call (CliffQuant README, "Use the solver").
+    """One group, in the shape of the pages' solver call (CliffQuant README, "Use the solver": the
+    weights, the environment diagonals and a quantizer specification with qmin and qmax).
 
-    ``weights`` has at most 128 entries, ``environment_diagonals`` is [E][len(weights)].
-    The group is zero-padded to 128 (a zero weight adds nothing at any scale).  Returns
-    (scale as float, objective, codes list).  Only qmin=-8, qmax=7 is served.
+    ``weights`` has at most 256 entries, ``environment_diagonals`` is [E][len(weights)].  For
+    the pages' range [-8, 7] a group shorter than 128 is zero-padded to 128 (a zero weight adds
+    nothing at any scale) and any method serves it (default "candidate"); other ranges run the
+    group at its own length through the exhaustive method.  Returns (scale as float, objective,
+    codes list).
     """
-    if (qmin, qmax) != (-8, 7):
-        raise NotImplementedError("only the signed 4-bit range [-8, 7] is implemented")
     n = len(weights)
-    if not 1 <= n <= GROUP:
-        raise ValueError("1..128 weights")
+    if not 1 <= n <= MAX_GROUP:
+        raise ValueError("1..256 weights")
     E = len(environment_diagonals)
-    w = torch.zeros((1, GROUP), dtype=torch.float32)
+    L = GROUP if (qmin, qmax) == (-8, 7) and n <= GROUP else n
+    if method is None:
+        method = "candidate" if L == GROUP and (qmin, qmax) == (-8, 7) else "exhaustive"
+    w = torch.zeros((1, L), dtype=torch.float32)
     w[0, :n] = torch.tensor(weights, dtype=torch.float32)
-    d = torch.zeros((1, E, GROUP), dtype=torch.float32)
+    d = torch.zeros((1, E, L), dtype=torch.float32)
     d[0, :, :n] = torch.tensor(environment_diagonals, dtype=torch.float32)
-    r = quantize_groups(w.to(device), d.to(device), method=method)
+    r = quantize_groups(w.to(device), d.to(device), method=method, qmin=qmin, qmax=qmax)
     torch.cuda.current_stream().synchronize()
     bits = int(r["scales"].cpu().view(torch.uint16)[0]) if hasattr(torch, "uint16") else \
         int(r["scales"].cpu()[0]) & 0xFFFF

@@ -14,18 +14,38 @@ inline size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? CQ_OK : CQ_EHIP; }
 
-// Exhaustive-sweep workspace: [counter | pad][int32 queue of n_groups][slice parts]
-size_t sweep_ws(int64_t n) {
-    return ALIGN + round_up((size_t)n * 4u) + round_up(sizeof(cqk::SlicePart) * cqk::SLICE_PARTS);
-}
+// Full-grid workspace: [counter | pad][int32 queue of n_groups]
+size_t full_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u); }
+// Bounded-sweep workspace: [counter | pad][int32 queue of n_groups][slice parts]
+size_t sweep_ws(int64_t n) { return full_ws(n) + round_up(sizeof(cqk::SlicePart) * cqk::SLICE_PARTS); }
 // Candidate workspace: [tie counter | pad][int32 tie list][sweep workspace]
 size_t cand_ws(int64_t n) { return ALIGN + round_up((size_t)n * 4u) + sweep_ws(n); }
 
-bool groups_ok(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups) {
+bool groups_ok(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups, size_t align = 16) {
     if (n_groups < 0 || E < 1 || E > CQ_MAX_ENVS) return false;
     if (n_groups == 0) return true;
     if (!w || !d || d_period < 1) return false;
-    return aligned(w, 16) && aligned(d, 16);
+    return aligned(w, align) && aligned(d, align);
+}
+
+bool spec_ok(int32_t G, int32_t qmin, int32_t qmax) {
+    return G >= 1 && G <= CQ_MAX_GROUP && qmin >= -128 && qmin <= 0 && qmax >= 0 && qmax <= 127 && qmin < qmax;
+}
+
+int32_t run_fullgrid(const float* w, const float* d, int32_t G, int32_t qmin, int32_t qmax, int64_t d_period, int32_t E,
+                     int64_t n_groups, uint16_t* scales, int8_t* codes, double* objective, uint8_t* flags,
+                     uint16_t* pooled_scales, double* pooled_objective, int want_minimax, uint8_t* ws,
+                     hipStream_t st) {
+    cqk::FullArgs a{};
+    a.w = w; a.d = d; a.d_period = d_period; a.G = G; a.qmin = qmin; a.qmax = qmax;
+    a.ratio = cqk::fullgrid_ratio(G, qmin, qmax, E);
+    a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
+    a.pscales = pooled_scales; a.pobjective = pooled_objective;
+    a.want_minimax = want_minimax;
+    a.want_pooled = (pooled_scales || pooled_objective) ? 1 : 0;
+    a.fb_count = (int32_t*)ws;
+    a.fb_list = (int32_t*)(ws + ALIGN);
+    return hip_status(cqk::launch_fullgrid(a, E, n_groups, st));
 }
 
 }  // namespace
@@ -47,7 +67,9 @@ const char* cq_status_string(int32_t s) {
 
 size_t cq_workspace_size(int32_t method, int32_t E, int64_t n_groups) {
     if (E < 1 || E > CQ_MAX_ENVS || n_groups < 0) return 0;
-    if (method == CQ_EXHAUSTIVE) return sweep_ws(n_groups);
+    // the full grid needs less than the bounded sweep; one size serves both, and the pooled
+    // baseline (a bounded sweep) accepts the CQ_EXHAUSTIVE size too
+    if (method == CQ_EXHAUSTIVE || method == CQ_BOUNDED) return sweep_ws(n_groups);
     if (method == CQ_CANDIDATE) return cand_ws(n_groups);
     return 0;
 }
@@ -57,7 +79,7 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
                            uint16_t* pooled_scales, double* pooled_objective, void* workspace,
                            size_t workspace_bytes, void* stream) {
     if (!groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
-    if (method != CQ_EXHAUSTIVE && method != CQ_CANDIDATE) return CQ_EINVAL;
+    if (method != CQ_EXHAUSTIVE && method != CQ_CANDIDATE && method != CQ_BOUNDED) return CQ_EINVAL;
     if (n_groups > 0 && !scales) return CQ_EINVAL;
     if (n_groups > INT32_MAX) return CQ_EINVAL;
     if (method == CQ_CANDIDATE && (pooled_scales || pooled_objective)) return CQ_EUNSUPPORTED;
@@ -66,7 +88,10 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return CQ_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
-    if (method == CQ_EXHAUSTIVE) {
+    if (method == CQ_EXHAUSTIVE)
+        return run_fullgrid(w, d, CQ_GROUP, -8, 7, d_period, E, n_groups, scales, codes, objective, flags,
+                            pooled_scales, pooled_objective, 1, ws, st);
+    if (method == CQ_BOUNDED) {
         cqk::SweepArgs a{};
         a.w = w; a.d = d; a.d_period = d_period;
         a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
@@ -103,6 +128,26 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     return hip_status(cqk::launch_sweep(a, E, n_groups, st));
 }
 
+int32_t cq_quantize_groups_spec(const float* w, const float* d, int32_t group_len, int32_t qmin, int32_t qmax,
+                                int64_t d_period, int32_t E, int64_t n_groups, int32_t method, uint16_t* scales,
+                                int8_t* codes, double* objective, uint8_t* flags, uint16_t* pooled_scales,
+                                double* pooled_objective, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!spec_ok(group_len, qmin, qmax)) return CQ_EINVAL;
+    if (method != CQ_EXHAUSTIVE && method != CQ_CANDIDATE && method != CQ_BOUNDED) return CQ_EINVAL;
+    if (group_len == CQ_GROUP && qmin == -8 && qmax == 7)
+        return cq_quantize_groups(w, d, d_period, E, n_groups, method, scales, codes, objective, flags, pooled_scales,
+                                  pooled_objective, workspace, workspace_bytes, stream);
+    if (method != CQ_EXHAUSTIVE) return CQ_EUNSUPPORTED;
+    if (!groups_ok(w, d, d_period, E, n_groups, 4)) return CQ_EINVAL;
+    if (n_groups > 0 && !scales) return CQ_EINVAL;
+    if (n_groups > INT32_MAX) return CQ_EINVAL;
+    if (n_groups == 0) return CQ_OK;
+    if (!workspace || workspace_bytes < cq_workspace_size(method, E, n_groups) || !aligned(workspace, ALIGN))
+        return CQ_EWORKSPACE;
+    return run_fullgrid(w, d, group_len, qmin, qmax, d_period, E, n_groups, scales, codes, objective, flags,
+                        pooled_scales, pooled_objective, 1, (uint8_t*)workspace, (hipStream_t)stream);
+}
+
 int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups,
                            int32_t which, uint16_t* scales, int8_t* codes, double* objective, void* workspace,
                            size_t workspace_bytes, void* stream) {
@@ -118,7 +163,7 @@ int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int
     if (!groups_ok(w, d, d_period, E, n_groups)) return CQ_EINVAL;
     if (n_groups == 0) return CQ_OK;
     if (!scales) return CQ_EINVAL;
-    const size_t need = cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups);
+    const size_t need = cq_workspace_size(CQ_BOUNDED, E, n_groups);
     if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return CQ_EWORKSPACE;
     uint8_t* ws = (uint8_t*)workspace;
     cqk::SweepArgs a{};

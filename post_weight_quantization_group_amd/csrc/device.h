@@ -87,6 +87,34 @@ __device__ __forceinline__ double env_error_codes_f64(const float* w, const floa
     return F;
 }
 
+// The code rule for the code range [qlo, qhi] (a quantizer specification): one correctly rounded
+// binary32 division, round half to even, clip.
+__device__ __forceinline__ float exact_code_range(float w, float s, float qlo, float qhi) {
+    const float x = w / s;
+    const float r = __builtin_rintf(x);
+    return __builtin_amdgcn_fmed3f(r, qlo, qhi);
+}
+
+// env_error_f64 for a group of n weights and the code range [qlo, qhi]: the same operations in
+// the same order (i = 0..n-1), the code decided by the binary64 product as argued there (the
+// argument does not depend on the size of the quotient).
+__device__ __forceinline__ double env_error_f64_n(const float* w, const float* d, int dstride, int n,
+                                                  double s, double inv, double qlo, double qhi) {
+    double F = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+        const double wi = (double)w[i];
+        double r = __builtin_rint(wi * inv);
+        r = r < qlo ? qlo : (r > qhi ? qhi : r);
+        const double sq = s * r;
+        const double t = wi - sq;
+        const double t2 = t * t;
+        const double term = (double)d[i * dstride] * t2;
+        F = F + term;
+    }
+    return F;
+}
+
 // binary32 x >= 0 to the nearest binary16 pattern, ties to even; 0x7C00 on overflow.
 __device__ __forceinline__ uint32_t f32_to_half_bits_rne(float x) {
     if (!(x < 65520.0f)) return 0x7C00u;

@@ -1,0 +1,548 @@
+// Full-grid exhaustive FP16 scale search for gfx950: every one of the 31,743
+// positive finite binary16 scales, every weight, every environment.
+//
+// This is the independent enumerator the pages describe next to the production
+// solver (CliffQuant repository README, "What CliffQuant changes": a separate
+// reference evaluates every one of the 31,743 binary16 values; README and model
+// card, "Verification": solver cases matched exhaustive FP16 enumeration).  No
+// scale is skipped, no range of the grid is cut off and no term is taken in
+// closed form: for each group the kernel forms the binary32 objective at all
+// 31,743 patterns from all G weights, then rescores in binary64 every pattern
+// the binary32 error bound cannot rule out.
+//
+// The quantizer is a parameter (README, "Use the solver": a quantizer
+// specification with qmin and qmax, and groups of any length): codes are
+// clip(round-half-even(w/s), qmin, qmax), groups hold G <= 256 weights.
+//
+// Work split.  One 256-thread workgroup per group.  Weights and diagonals are
+// staged in LDS (diagonals transposed to [i][e], one 16-byte broadcast read per
+// weight at E = 4).  Each wave takes chunks of 64*NS consecutive patterns, NS
+// per lane, and runs all G weights against its NS scales with the E
+// per-environment sums in registers:
+//     x = w' * RN(1/s'),  q = rint(x) (clipped when the chunk can clip),
+//     e = fma(-s', q, w'),  e^2,  then E fmas into the sums.
+// A chunk cannot clip when every |w'| is at most (range end + 1/4) times its
+// smallest scale; the clip is then left out (it cannot change any code).
+// Patterns are rotated over the lanes from chunk to chunk so that scales a power
+// of two apart (which tie exactly when one outlier alone carries a code) land in
+// different lanes.  Each lane keeps its best three (value, pattern) keys per
+// policy; minimax F = max_e F_e and pooled P = sum_e F_e come from the same sums.
+//
+// Exactness (u = 2^-24).  The binary32 value is a screen with a proven bound:
+//   * weights are pre-scaled by 2^k (max |w'| in [1, 2)) and scales by the same
+//     2^k, which changes no quotient and no code; a range check guarantees that
+//     every nonzero term d e^2 is a normal binary32 number (else the group goes
+//     to the binary64 sweep below);
+//   * RN(1/s') is correctly rounded, so x~ = x (1 + t) with |t| <= 2.0001 u.  The
+//     code from x~ differs from the exact one only when x lies within 2.0001 u |x|
+//     of a half-integer, |x| <= X = max(-qmin, qmax) + 1/2; both codes then leave
+//     |x - q| within 1/2 -+ 2.0001 u X, so the term grows by a factor of at most
+//     1 + 16.001 u X and never shrinks (the exact code is the nearer one);
+//   * e is exact unless clipped (then one rounding); e^2 and the G fmas of the
+//     sum give every term at most G + 3 roundings on its way into F_e.
+//   So (1 - (G+3)u) F <= F~ <= (1 + (G+3)u)(1 + 16.001 u X) F, and the pooled sum
+//   meets E - 1 more roundings.  Every pattern whose value is at most the
+//   smallest one times the host-computed ratio (these bounds, with margin) is
+//   rescored in binary64 in the definition's order, which decides the winner
+//   and the lower-bit-pattern tie; the rescored value equals the oracle's bit
+//   for bit.  A zero binary32 value is exact (every term is normal or zero), so
+//   when the smallest value is 0 the lowest such pattern wins directly.  When a
+//   lane's third key lies inside the bound (it may have dropped a fourth), or
+//   more than CAP patterns survive, the group goes to the binary64 sweep.
+#include "device.h"
+#include "launch.h"
+
+namespace cqk {
+namespace full {
+
+// Scales per lane per chunk: eight up to E = 4, then fewer so that the NS * E sums stay at 32
+// registers.  A wave's chunk is 64 * NS consecutive patterns.
+constexpr int ns_for(int E) { return E <= 4 ? 8 : 32 / E; }
+constexpr int chunk_for(int E) { return 64 * ns_for(E); }
+constexpr int nchunk_for(int E) { return ((int)N_SCALES + chunk_for(E) - 1) / chunk_for(E); }
+constexpr int CAP = 256;                                // shortlist capacity per group
+constexpr int GMAX = 256;                               // longest group
+constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
+
+constexpr int min_blocks_for(int E) { return E <= 4 ? 5 : (E == 8 ? 4 : (E == 16 ? 2 : 1)); }
+
+template <int E>
+struct Smem {
+    float w[GMAX];                  // the weights as given (rescoring, codes)
+    __align__(16) float wp[GMAX];   // pre-scaled by 2^k (screen)
+    __align__(16) float dt[GMAX * E];  // [i][e]
+    float redf[4 * 8];
+    uint64_t redk[4 * 4];
+    uint32_t cand_b[CAP];
+    uint8_t cand_tag[CAP];
+    double cand_F[CAP];
+    double cand_P[CAP];
+    double pairF[BLOCK];
+    int n_cand;
+    int overflow;
+    uint32_t win_b[2];
+    double win_F[2];
+    uint8_t win_flags[2];
+};
+
+__device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
+    if (v < k[2]) {
+        if (v < k[1]) {
+            k[2] = k[1];
+            if (v < k[0]) { k[1] = k[0]; k[0] = v; }
+            else k[1] = v;
+        } else {
+            k[2] = v;
+        }
+    }
+}
+
+// A value held in a vector register: keeps the clip bounds out of scalar registers, which the
+// hot loop's v_med3 would otherwise read through the scalar operand port.
+__device__ __forceinline__ float in_vgpr(float x) {
+    float r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+    return r;
+}
+
+// One chunk: every lane runs the n weights against its NS scales, the per-environment sums in
+// registers.  The weight and its E diagonals are LDS broadcasts shared by the NS scales.
+template <int E, int NS, bool CLIP>
+__device__ __forceinline__ void chunk_terms(const float* __restrict__ wp, const float* __restrict__ dt, int n,
+                                            const float (&nsv)[NS], const float (&inv)[NS], float qlo, float qhi,
+                                            float (&acc)[NS][E]) {
+#pragma unroll 2
+    for (int i = 0; i < n; ++i) {
+        const float wi = wp[i];
+        float di[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) di[e] = dt[i * E + e];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const float x = wi * inv[t];
+            float r = __builtin_rintf(x);
+            if (CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
+            const float ev = __builtin_fmaf(nsv[t], r, wi);
+            const float e2 = ev * ev;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(di[e], e2, acc[t][e]);
+        }
+    }
+}
+
+// binary64 rescoring of shortlist entries [0, n): cand_F = max_e F_e, cand_P = (sum_e F_e)/E,
+// each F_e summed i = 0..G-1 in the definition's order (the oracle's value bit for bit).
+template <int E>
+__device__ void rescore(Smem<E>& sm, int n, int G, int E_real, double qlo, double qhi) {
+    constexpr int PER = BLOCK / E;
+    const int t = threadIdx.x;
+    for (int base = 0; base < n; base += PER) {
+        const int nb = min(PER, n - base);
+        if (t < nb * E) {
+            const int j = base + t / E, e = t % E;
+            const double s = (double)half_bits_value(sm.cand_b[j]);
+            sm.pairF[t] = env_error_f64_n(sm.w, sm.dt + e, E, G, s, 1.0 / s, qlo, qhi);
+        }
+        __syncthreads();
+        if (t < nb) {
+            double F = sm.pairF[t * E], P = sm.pairF[t * E];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                const double v = sm.pairF[t * E + e];
+                F = v > F ? v : F;
+                P = P + v;
+            }
+            sm.cand_F[base + t] = F;
+            sm.cand_P[base + t] = P / (double)E_real;
+        }
+        __syncthreads();
+    }
+}
+
+// One wave: the lexicographic (value, bits) winner among the entries tagged `tag`, and its
+// flags (more than one entry: near tie; another pattern with the same value: exact tie).
+template <int E>
+__device__ void pick_winner(Smem<E>& sm, int n, uint8_t tag, int slot) {
+    const int lane = threadIdx.x & 63;
+    uint64_t bv = ~0ull;
+    uint32_t bb = 0xFFFFFFFFu;
+    int count = 0;
+    for (int j = lane; j < n; j += 64) {
+        if (!(sm.cand_tag[j] & tag)) continue;
+        const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
+        const uint64_t vb = __builtin_bit_cast(uint64_t, v);  // values are >= 0: bits order as values
+        const uint32_t b = sm.cand_b[j];
+        ++count;
+        if (vb < bv || (vb == bv && b < bb)) { bv = vb; bb = b; }
+    }
+    const uint64_t best_v = wave_min_u64(bv);
+    const uint32_t best_b = (uint32_t)wave_min_u64(bv == best_v ? (uint64_t)bb : ~0ull);
+    int tie = 0;
+    for (int j = lane; j < n; j += 64) {
+        if (!(sm.cand_tag[j] & tag)) continue;
+        const double v = tag == TAG_MINIMAX ? sm.cand_F[j] : sm.cand_P[j];
+        if (__builtin_bit_cast(uint64_t, v) == best_v && sm.cand_b[j] != best_b) tie = 1;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        count += (int)lane_xor((uint32_t)count, o);
+        tie |= (int)lane_xor((uint32_t)tie, o);
+    }
+    if (lane == 0) {
+        sm.win_b[slot] = best_b;
+        sm.win_F[slot] = __builtin_bit_cast(double, best_v);
+        sm.win_flags[slot] = (uint8_t)((count > 1 ? FLAG_NEAR_TIE : 0) | (tie ? FLAG_EXACT_TIE : 0));
+    }
+}
+
+__device__ __forceinline__ void append_cand(uint32_t* cb, uint8_t* ct, int* n, uint32_t b, uint8_t tag) {
+    const int j = atomicAdd(n, 1);
+    if (j < CAP) { cb[j] = b; ct[j] = tag; }
+}
+
+__device__ __forceinline__ void queue_f64(const FullArgs& a, int64_t g) {
+    const int j = atomicAdd(a.fb_count, 1);
+    a.fb_list[j] = (int32_t)g;
+}
+
+template <int E>
+__device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
+    const int tid = threadIdx.x;
+    const int G = a.G;
+    const float* wg = a.w + g * G;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
+
+    // ---- staging (environments a.E..E-1 are zero padding)
+    for (int i = tid; i < G; i += BLOCK) sm.w[i] = wg[i];
+    for (int j = tid; j < E * G; j += BLOCK) {
+        const int e = j / G, i = j - e * G;
+        sm.dt[i * E + e] = e < a.E ? dg[j] : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- input checks and ranges: bad, max|w|, max w+, max w-, min nonzero |w|, max d, min nonzero d
+    float v[7] = {0.0f, 0.0f, 0.0f, 0.0f, -__builtin_inff(), 0.0f, -__builtin_inff()};
+    for (int i = tid; i < G; i += BLOCK) {
+        const float x = sm.w[i];
+        if (!__builtin_isfinite(x)) v[0] = 1.0f;
+        const float ax = fabsf(x);
+        v[1] = fmaxf(v[1], ax);
+        v[2] = fmaxf(v[2], x);
+        v[3] = fmaxf(v[3], -x);
+        if (ax > 0.0f) v[4] = fmaxf(v[4], -ax);
+    }
+    for (int j = tid; j < E * G; j += BLOCK) {
+        const float x = sm.dt[j];
+        if (!(x >= 0.0f) || !__builtin_isfinite(x)) v[0] = 1.0f;
+        else {
+            v[5] = fmaxf(v[5], x);
+            if (x > 0.0f) v[6] = fmaxf(v[6], -x);
+        }
+    }
+    block_max_fn<7>(v, sm.redf);
+    const bool bad = v[0] != 0.0f;
+    if (bad) {
+        for (int i = tid; i < G; i += BLOCK)
+            if (a.codes) a.codes[g * G + i] = 0;
+        if (tid == 0) {
+            if (a.scales) a.scales[g] = 0;
+            if (a.objective) a.objective[g] = __builtin_nan("");
+            if (a.pscales) a.pscales[g] = 0;
+            if (a.pobjective) a.pobjective[g] = __builtin_nan("");
+            if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
+        }
+        return;
+    }
+    const float wmax = v[1], wpos = v[2], wneg = v[3], wmin_nz = -v[4], dmax = v[5], dmin_nz = -v[6];
+
+    // ---- power-of-two pre-scaling and the no-underflow / no-overflow guarantee: every nonzero
+    // residual is at least the smaller of ulp(w') >= 2^-24 min|w'| and the binary16 grid spacing
+    // 2^-24 * 2^k, so e^2 >= elb^2 must stay normal, also times the smallest nonzero diagonal
+    int k = 0;
+    if (wmax > 0.0f) {
+        int ex;
+        frexpf(wmax, &ex);
+        k = min(100, max(-100, 1 - ex));
+    }
+    bool safe = dmax <= 0x1p100f;
+    if (wmin_nz < __builtin_inff()) {
+        const double elb = fmin(ldexp(1.0, k - 24), (double)wmin_nz * ldexp(1.0, k - 24));
+        const double e2 = elb * elb;
+        safe = safe && e2 >= 0x1p-120 && (dmin_nz == __builtin_inff() || (double)dmin_nz * e2 >= 0x1p-120);
+    }
+    if (!safe) {
+        if (tid == 0) queue_f64(a, g);
+        return;
+    }
+    const float pk = ldexpf(1.0f, k);
+    for (int i = tid; i < G; i += BLOCK) sm.wp[i] = sm.w[i] * pk;
+    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    __syncthreads();
+
+    // ---- binary32 screen over all 31,743 scales
+    const int lane = tid & 63, wave = tid >> 6;
+    const float qlo = in_vgpr((float)a.qmin), qhi = in_vgpr((float)a.qmax);
+    // no weight clips in a chunk whose smallest scale s0 has w+ <= (qmax + 1/4) s0 and
+    // w- <= (-qmin + 1/4) s0: |x~| stays below the range end plus 1/2
+    const float cpos = wpos * pk / ((float)a.qmax + 0.25f), cneg = wneg * pk / (0.25f - (float)a.qmin);
+    const float cmax = fmaxf(cpos, cneg) * (1.0f + 0x1p-20f);
+    constexpr int NS = ns_for(E), CHUNK = chunk_for(E), NCHUNK = nchunk_for(E);
+    uint64_t mk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
+    uint64_t qk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
+    for (int c = wave; c < NCHUNK; c += BLOCK / 64) {
+        float nsv[NS], inv[NS];
+        float acc[NS][E];
+        const int rot = (lane + 5 * c) & 63;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
+            const float s = half_bits_value(b) * pk;
+            nsv[t] = -s;
+            inv[t] = 1.0f / s;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+        }
+        const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        if (cmax <= s0)
+            chunk_terms<E, NS, false>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, acc);
+        else
+            chunk_terms<E, NS, true>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, acc);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
+            if (b > BITS_LAST) continue;
+            float Fm = acc[t][0], Ps = acc[t][0];
+#pragma unroll
+            for (int e = 1; e < E; ++e) {
+                const float x = acc[t][e];
+                Fm = fmaxf(Fm, x);
+                Ps = Ps + x;
+            }
+            if (a.want_minimax) top3_insert(mk, key_of(Fm, b));
+            if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
+        }
+    }
+
+    // ---- each policy's smallest key, its runner-up, and the shortlist
+    uint64_t kv[2] = {mk[0], qk[0]};
+    block_min_u64n<2>(kv, sm.redk);
+    uint64_t kv2[2] = {mk[0] == kv[0] ? mk[1] : mk[0], qk[0] == kv[1] ? qk[1] : qk[0]};
+    block_min_u64n<2>(kv2, sm.redk + 8);
+    for (int pol = 0; pol < 2; ++pol) {
+        const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
+        if (!want) continue;
+        const uint64_t* kk = pol == 0 ? mk : qk;
+        const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
+        const uint64_t M1 = kv[pol], S2 = kv2[pol];
+        const float m = key_value(M1);
+        if (m == 0.0f) {
+            // a zero binary32 value is exact: the lowest such pattern wins, value 0
+            if (tid == 0) {
+                sm.win_b[pol] = key_bits(M1);
+                sm.win_F[pol] = 0.0;
+                sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
+            }
+        } else {
+            const float T = m * a.ratio;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
+                    if (r == 2) sm.overflow = 1;
+                    else append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(kk[r]), tag);
+                }
+            }
+            if (tid == 0) sm.win_b[pol] = 0xFFFFFFFFu;  // decided by rescoring
+        }
+    }
+    __syncthreads();
+    const int n = sm.n_cand;
+    if (sm.overflow || n > CAP) {
+        if (tid == 0) queue_f64(a, g);
+        return;
+    }
+
+    // ---- binary64 rescoring and the lower-bit-pattern rule
+    rescore<E>(sm, n, G, a.E, (double)a.qmin, (double)a.qmax);
+    if (wave < 2) {
+        const bool want = wave == 0 ? a.want_minimax : a.want_pooled;
+        if (want && sm.win_b[wave] == 0xFFFFFFFFu)
+            pick_winner<E>(sm, n, wave == 0 ? TAG_MINIMAX : TAG_POOLED, wave);
+    }
+    __syncthreads();
+
+    // ---- outputs
+    const float fqlo = (float)a.qmin, fqhi = (float)a.qmax;
+    const int cp = a.want_minimax ? 0 : 1;  // the policy whose codes are written
+    const float sc = half_bits_value(sm.win_b[cp]);
+    if (a.codes)
+        for (int i = tid; i < G; i += BLOCK) a.codes[g * G + i] = (int8_t)exact_code_range(sm.w[i], sc, fqlo, fqhi);
+    if (tid == 0) {
+        if (a.want_minimax) {
+            a.scales[g] = (uint16_t)sm.win_b[0];
+            if (a.objective) a.objective[g] = sm.win_F[0];
+            if (a.flags) a.flags[g] = sm.win_flags[0];
+        }
+        if (a.want_pooled) {
+            if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
+            if (a.pobjective) a.pobjective[g] = sm.win_F[1];
+            if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+        }
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void full_screen_kernel(FullArgs a) {
+    __shared__ Smem<E> sm;
+    screen_group<E>(a, (int64_t)blockIdx.x + a.group_offset, sm);
+}
+
+// ------------------------------------------------------------------ binary64 sweep
+// Every scale in binary64, each environment summed in the definition's order; the lexicographic
+// (value, bits) minimum and the runner-up value give the answer with no screen at all.  For the
+// groups whose binary32 screen could not be guaranteed or was inconclusive.
+template <int E>
+struct F64Smem {
+    float w[GMAX];
+    float dt[GMAX * E];
+    double rv[BLOCK], rv2[BLOCK];
+    uint32_t rb[BLOCK];
+    double pv[BLOCK], pv2[BLOCK];
+    uint32_t pb[BLOCK];
+};
+
+__device__ __forceinline__ bool lex_less(double v, uint32_t b, double v2, uint32_t b2) {
+    return v < v2 || (v == v2 && b < b2);
+}
+
+// Fold (v, b) into a (best, best bits, second value) triple.
+__device__ __forceinline__ void fold(double v, uint32_t b, double& bv, uint32_t& bb, double& sv) {
+    if (lex_less(v, b, bv, bb)) { sv = bv; bv = v; bb = b; }
+    else if (v < sv) sv = v;
+}
+
+template <int E>
+__device__ void f64_group(const FullArgs& a, int64_t g, F64Smem<E>& sm) {
+    const int tid = threadIdx.x, G = a.G;
+    const float* wg = a.w + g * G;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
+    for (int i = tid; i < G; i += BLOCK) sm.w[i] = wg[i];
+    for (int j = tid; j < E * G; j += BLOCK) {
+        const int e = j / G, i = j - e * G;
+        sm.dt[i * E + e] = e < a.E ? dg[j] : 0.0f;
+    }
+    __syncthreads();
+    const double qlo = (double)a.qmin, qhi = (double)a.qmax;
+    double bF = __builtin_inf(), sF = __builtin_inf(), bP = __builtin_inf(), sP = __builtin_inf();
+    uint32_t bFb = 0xFFFFFFFFu, bPb = 0xFFFFFFFFu;
+    for (uint32_t b = BITS_FIRST + tid; b <= BITS_LAST; b += BLOCK) {
+        const double s = (double)half_bits_value(b), inv = 1.0 / s;
+        double F = 0.0, P = 0.0;
+        for (int e = 0; e < E; ++e) {
+            const double fe = env_error_f64_n(sm.w, sm.dt + e, E, G, s, inv, qlo, qhi);
+            F = e == 0 ? fe : (fe > F ? fe : F);
+            P = e == 0 ? fe : P + fe;
+        }
+        P = P / (double)a.E;
+        fold(F, b, bF, bFb, sF);
+        fold(P, b, bP, bPb, sP);
+    }
+    sm.rv[tid] = bF; sm.rb[tid] = bFb; sm.rv2[tid] = sF;
+    sm.pv[tid] = bP; sm.pb[tid] = bPb; sm.pv2[tid] = sP;
+    __syncthreads();
+    for (int st = BLOCK / 2; st > 0; st >>= 1) {
+        if (tid < st) {
+            double bv = sm.rv[tid], sv = sm.rv2[tid];
+            uint32_t bb = sm.rb[tid];
+            fold(sm.rv[tid + st], sm.rb[tid + st], bv, bb, sv);
+            sv = sm.rv2[tid + st] < sv ? sm.rv2[tid + st] : sv;
+            sm.rv[tid] = bv; sm.rb[tid] = bb; sm.rv2[tid] = sv;
+            double pv = sm.pv[tid], psv = sm.pv2[tid];
+            uint32_t pb = sm.pb[tid];
+            fold(sm.pv[tid + st], sm.pb[tid + st], pv, pb, psv);
+            psv = sm.pv2[tid + st] < psv ? sm.pv2[tid + st] : psv;
+            sm.pv[tid] = pv; sm.pb[tid] = pb; sm.pv2[tid] = psv;
+        }
+        __syncthreads();
+    }
+    const uint32_t win = a.want_minimax ? sm.rb[0] : sm.pb[0];
+    if (a.codes) {
+        const float s = half_bits_value(win);
+        for (int i = tid; i < G; i += BLOCK)
+            a.codes[g * G + i] = (int8_t)exact_code_range(sm.w[i], s, (float)a.qmin, (float)a.qmax);
+    }
+    if (tid == 0) {
+        const uint8_t fF = FLAG_FP64_SWEEP | (sm.rv2[0] == sm.rv[0] ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0);
+        const uint8_t fP = FLAG_FP64_SWEEP | (sm.pv2[0] == sm.pv[0] ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0);
+        if (a.want_minimax) {
+            a.scales[g] = (uint16_t)sm.rb[0];
+            if (a.objective) a.objective[g] = sm.rv[0];
+            if (a.flags) a.flags[g] = fF;
+        }
+        if (a.want_pooled) {
+            if (a.pscales) a.pscales[g] = (uint16_t)sm.pb[0];
+            if (a.pobjective) a.pobjective[g] = sm.pv[0];
+            if (!a.want_minimax && a.flags) a.flags[g] = fP;
+        }
+    }
+    __syncthreads();
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK) void full_f64_kernel(FullArgs a) {
+    __shared__ F64Smem<E> sm;
+    const int cnt = *a.fb_count;
+    for (int k = blockIdx.x; k < cnt; k += gridDim.x) f64_group<E>(a, (int64_t)a.fb_list[k], sm);
+}
+
+__global__ void full_zero_kernel(int32_t* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
+}
+
+template <int E>
+hipError_t launch_e(const FullArgs& a_in, int64_t n_groups, hipStream_t st) {
+    FullArgs a = a_in;
+    hipLaunchKernelGGL(full_zero_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
+    const int64_t step = 1ll << 30;  // grid.x is limited to 2^31 - 1 blocks
+    for (int64_t off = 0; off < n_groups; off += step) {
+        FullArgs b = a;
+        b.group_offset = off;
+        const int64_t n = n_groups - off < step ? n_groups - off : step;
+        hipLaunchKernelGGL(full_screen_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+    }
+    const int fb_blocks = (int)(n_groups < 1024 ? n_groups : 1024);
+    hipLaunchKernelGGL(full_f64_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace full
+
+// The shortlist ratio for G weights, codes in [qmin, qmax] and E environments: (1 + hi)/(1 - lo)
+// with the bounds of the header, widened by 8 u for the roundings of the threshold itself and
+// rounded up to binary32.
+float fullgrid_ratio(int G, int qmin, int qmax, int E) {
+    const double u = 0x1p-24;
+    const double X = (double)(-qmin > qmax ? -qmin : qmax) + 0.5;
+    const double hi = (1.0 + 1.0001 * (G + 3 + E) * u) * (1.0 + 16.001 * X * u) - 1.0;
+    const double lo = 1.0001 * (G + 3 + E) * u;
+    const double r = (1.0 + hi) / (1.0 - lo) * (1.0 + 8.0 * u);
+    float f = (float)r;
+    if ((double)f < r) f = nextafterf(f, 2.0f);
+    return f;
+}
+
+hipError_t launch_fullgrid(const FullArgs& a_in, int E, int64_t n_groups, hipStream_t st) {
+    FullArgs a = a_in;
+    a.E = E;
+    if (n_groups == 0) return hipSuccess;
+    switch (pad_envs(E)) {
+        case 1: return full::launch_e<1>(a, n_groups, st);
+        case 2: return full::launch_e<2>(a, n_groups, st);
+        case 4: return full::launch_e<4>(a, n_groups, st);
+        case 8: return full::launch_e<8>(a, n_groups, st);
+        case 16: return full::launch_e<16>(a, n_groups, st);
+        case 32: return full::launch_e<32>(a, n_groups, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace cqk

@@ -53,6 +53,31 @@ struct SweepArgs {
 // a.list when a.list is set (then n_groups bounds the list length).
 hipError_t launch_sweep(const SweepArgs& a, int E, int64_t n_groups, hipStream_t st);
 
+// Full-grid exhaustive search (every scale, every weight; binary32 screen, binary64 rescoring,
+// binary64 sweep of unsettled groups) for groups of G weights and codes in [qmin, qmax].
+struct FullArgs {
+    const float* w;            // [n_groups][G]
+    const float* d;            // [n_d][E][G]
+    int64_t d_period;
+    int E;                     // environments in d (kernels run the next power of two, zero-padded)
+    int G;                     // 1..256
+    int qmin, qmax;            // -128 <= qmin <= 0 <= qmax <= 127, qmin < qmax
+    float ratio;               // shortlist ratio (fullgrid_ratio)
+    int64_t group_offset;      // first group of this launch (set by the launcher)
+    uint16_t* scales;
+    int8_t* codes;             // [n_groups][G]
+    double* objective;
+    uint8_t* flags;
+    uint16_t* pscales;
+    double* pobjective;
+    int want_minimax;
+    int want_pooled;
+    int32_t* fb_count;         // groups queued for the binary64 sweep (cleared by the launcher)
+    int32_t* fb_list;          // n_groups entries
+};
+float fullgrid_ratio(int G, int qmin, int qmax, int E);
+hipError_t launch_fullgrid(const FullArgs& a, int E, int64_t n_groups, hipStream_t st);
+
 struct CandArgs {
     const float* w;
     const float* d;

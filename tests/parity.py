@@ -47,28 +47,39 @@ def check_policy(name, w, d, d_period, gpu_bits, gpu_obj, best_bits, F1, gap, ob
     return int(np.count_nonzero(gpu_bits == best_bits)), int(close.sum())
 
 
-def check_minimax(w, d, d_period, r, sol, codes=True):
+def check_minimax(w, d, d_period, r, sol, codes=True, qmin=-8, qmax=7):
     """GPU result dict `r` against an oracle Solution `sol` for the same groups."""
     bits = bits_np(r["scales"])
     obj = r["objective"].cpu().numpy()
     same, near = check_policy("minimax", w, d, d_period, bits, obj, sol.mm_bits, sol.mm_F1, sol.mm_gap,
-                              lambda b: oracle.objective(w, d, b, d_period, threads()))
+                              lambda b: oracle.objective(w, d, b, d_period, threads(), qmin, qmax))
     if codes and r.get("codes") is not None:
-        want = oracle.codes_for(w, bits)
+        want = oracle.codes_for(w, bits, qmin, qmax)
         got = r["codes"].cpu().numpy()
         diff = np.nonzero(np.any(got != want, axis=1))[0]
         assert diff.size == 0, f"codes differ on groups {diff[:5]}"
     return same, near
 
 
-def check_pooled(w, d, d_period, pbits_t, pobj_t, sol):
+def check_pooled(w, d, d_period, pbits_t, pobj_t, sol, qmin=-8, qmax=7):
     bits = bits_np(pbits_t)
     obj = pobj_t.cpu().numpy()
 
     def pooled_at(b):
-        Fe = oracle.env_errors(w, d, b, d_period, threads())
+        Fe = oracle.env_errors(w, d, b, d_period, threads(), qmin, qmax)
         P = Fe[:, 0].copy()
         for e in range(1, Fe.shape[1]):
             P = P + Fe[:, e]
         return P / Fe.shape[1]
     return check_policy("pooled", w, d, d_period, bits, obj, sol.pl_bits, sol.pl_P1, sol.pl_gap, pooled_at)
+
+
+def check_same_result(a, b, label, keys=("scales", "codes", "objective", "pooled_scales", "pooled_objective")):
+    """Two GPU result dicts of the same groups (two methods, or two launch shapes) agree bit for bit
+    on every output they both carry."""
+    for k in keys:
+        if a.get(k) is None or b.get(k) is None:
+            continue
+        x, y = a[k].cpu().numpy(), b[k].cpu().numpy()
+        bad = np.nonzero(np.any((x != y).reshape(x.shape[0], -1), axis=1))[0]
+        assert bad.size == 0, f"{label}: {k} differs on {bad.size} groups, e.g. {bad[:5]}"

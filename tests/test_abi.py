@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert cq.cq_abi_version() == 1
+    assert cq.cq_abi_version() == 2
     assert cq.cq_status_string(0) == "ok"
     assert "workspace" in cq.cq_status_string(-2)
     assert cq.cq_status_string(123) == "unknown status"
@@ -42,6 +42,7 @@ def test_workspace_sizes():
     assert cq.cq_workspace_size(cq.EXHAUSTIVE, 0, 10) == 0
     assert cq.cq_workspace_size(cq.EXHAUSTIVE, 33, 10) == 0
     assert cq.cq_workspace_size(7, 4, 10) == 0
+    assert cq.cq_workspace_size(cq.BOUNDED, 4, 1000) == cq.cq_workspace_size(cq.EXHAUSTIVE, 4, 1000)
     assert cq.cq_proxy_workspace_size(10) >= 80
 
 
@@ -66,6 +67,28 @@ def _quant(**kw):
 ])
 def test_quantize_rejects_before_launch(kw, status):
     assert _quant(**kw) == status
+
+
+def _spec(**kw):
+    lib = cq.load()
+    a = dict(w=FAKE, d=FAKE, G=64, qmin=-4, qmax=3, d_period=1, E=4, n=10, method=0, scales=FAKE, ws=FAKE,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.cq_quantize_groups_spec(a["w"], a["d"], a["G"], a["qmin"], a["qmax"], a["d_period"], a["E"], a["n"],
+                                       a["method"], a["scales"], None, None, None, None, None, a["ws"], a["wsb"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), -1), (dict(G=257), -1), (dict(qmin=1), -1), (dict(qmax=-1), -1), (dict(qmin=0, qmax=0), -1),
+    (dict(qmin=-129), -1), (dict(qmax=128), -1), (dict(method=3), -1), (dict(method=1), -4), (dict(method=2), -4),
+    (dict(w=FAKE + 2), -1), (dict(E=33), -1), (dict(scales=None), -1), (dict(ws=None), -2),
+    (dict(ws=FAKE, wsb=16), -2), (dict(n=0, w=None, d=None, scales=None), 0),
+    # the pages' quantizer through the spec entry takes cq_quantize_groups' checks (16-byte alignment)
+    (dict(G=128, qmin=-8, qmax=7, w=FAKE + 4), -1), (dict(G=128, qmin=-8, qmax=7, method=5), -1),
+])
+def test_quantize_spec_rejects_before_launch(kw, status):
+    assert _spec(**kw) == status
 
 
 def test_zero_groups_is_a_no_op():

@@ -1,0 +1,112 @@
+"""GPU parity of the full-grid exhaustive kernel (every scale, every weight): against the oracle,
+against the bounded sweep bit for bit, and for other quantizers (the README's "Use the solver"
+takes a code range and a group of any length) against the oracle run with the same quantizer.
+
+Every call goes through the C ABI (libcq.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import post_weight_quantization_group_amd as cq
+import workloads as W
+from parity import bits_np, check_minimax, check_pooled, check_same_result, dev, say, threads
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, d, d_period, method="exhaustive", pooled=True, qmin=-8, qmax=7):
+    r = cq.quantize_groups(dev(w), dev(d), d_period, method=method, pooled=pooled, qmin=qmin, qmax=qmax)
+    torch.cuda.synchronize()
+    return r
+
+
+def test_full_grid_config0_all_groups():
+    say("full grid, config 0: 128 groups, E=4, minimax + pooled")
+    w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
+    r = _run(w, d, p)
+    sol = oracle.solve(w, d, p, n_threads=threads())
+    same, near = check_minimax(w, d, p, r, sol)
+    check_pooled(w, d, p, r["pooled_scales"], r["pooled_objective"], sol)
+    say(f"  bits equal {same}/128, near ties {near}")
+
+
+def test_full_grid_equals_bounded_sweep_on_a_config1_matrix():
+    """Config 1's gate matrix, all 28,672 groups: the full grid and the branch-and-bound sweep
+    return the same scales, codes and binary64 objectives for both policies."""
+    w, d, p = W.matrix_groups(*W.make_matrix(1, 0))
+    say(f"full grid vs bounded: {w.shape[0]} groups")
+    a = _run(w, d, p, "exhaustive")
+    b = _run(w, d, p, "bounded")
+    check_same_result(a, b, "config 1 gate")
+
+
+# (qmin, qmax, group length, environments): signed 3-, 2- and 8-bit codes, unsigned 4-bit codes,
+# the pages' range on longer, shorter and ragged groups
+SPECS = [(-4, 3, 64, 4), (-2, 1, 32, 3), (-128, 127, 128, 4), (0, 15, 128, 2), (-8, 7, 256, 4),
+         (-8, 7, 4, 2), (-8, 7, 100, 5), (-4, 3, 200, 1)]
+
+
+def _spec_groups(qmin, qmax, G, E, n, seed):
+    """Seeded groups of G weights (bf16-valued normal weights with 2% outliers x8, a few tiny and
+    all-zero groups, constructed exact ties) and per-group lognormal diagonals."""
+    rng = np.random.default_rng(seed)
+    w = W.round_bf16((rng.normal(0, 0.02, (n, G)) * np.where(rng.random((n, G)) < 0.02, 8.0, 1.0))
+                     .astype(np.float32))
+    w[1] = 0.0
+    w[2] = (rng.uniform(-1, 1, G) * 1e-5).astype(np.float32)
+    # symmetric +-c n pairs: zero error at s = c and c/2 (and, for wide ranges, smaller powers)
+    c = 2.0 ** -7
+    m = rng.integers(1, min(qmax, 3) + 1, G // 2) if qmax >= 1 else np.ones(G // 2)
+    pair = np.zeros(G, np.float32)
+    pair[: 2 * (G // 2)] = np.concatenate([m * c, -m * c]).astype(np.float32)
+    w[3] = pair
+    d = rng.lognormal(0, 1, (n, E, G)).astype(np.float32)
+    if E > 1:
+        d[3, 1] = d[3, 0]
+    return w, d
+
+
+@pytest.mark.parametrize("qmin,qmax,G,E", SPECS, ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in SPECS])
+def test_quantizer_spec_against_oracle(qmin, qmax, G, E):
+    n = 48
+    w, d = _spec_groups(qmin, qmax, G, E, n, seed=1000 + G + qmax)
+    say(f"quantizer [{qmin}, {qmax}], G={G}, E={E}: {n} groups")
+    r = _run(w, d, n, qmin=qmin, qmax=qmax)
+    sol = oracle.solve(w, d, n, n_threads=threads(), qmin=qmin, qmax=qmax)
+    same, near = check_minimax(w, d, n, r, sol, qmin=qmin, qmax=qmax)
+    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol, qmin=qmin, qmax=qmax)
+    bits = bits_np(r["scales"])
+    assert bits[1] == 0x0001 and r["objective"].cpu().numpy()[1] == 0.0
+    flags = r["flags"].cpu().numpy()
+    assert flags[1] & cq.FLAG_EXACT_TIE
+    say(f"  bits equal {same}/{n}, near ties {near}, flags {np.bincount(flags, minlength=32)[[0, 2, 6, 16, 18, 22]]}")
+
+
+def test_pages_example_at_its_own_length_and_other_ranges():
+    """The README's four-weight call with other code ranges: the group runs at length 4."""
+    ws = [0.9, -0.4, 0.2, -1.1]
+    ds = [[1.0, 0.8, 0.5, 1.2], [0.6, 1.4, 0.9, 0.7]]
+    w = np.array([ws], np.float32)
+    d = np.array([ds], np.float32)
+    for qmin, qmax in ((-8, 7), (-4, 3), (-2, 1), (-128, 127), (0, 15)):
+        sol = oracle.solve(w, d, qmin=qmin, qmax=qmax)
+        scale, obj, codes = cq.solve_breakpoint_exact(ws, ds, qmin=qmin, qmax=qmax, method="exhaustive")
+        assert scale == oracle.fp16_value(sol.mm_bits[0]) and obj == sol.mm_F1[0], (qmin, qmax)
+        assert codes == list(sol.codes[0]), (qmin, qmax)
+
+
+def test_spec_entry_with_the_pages_quantizer_is_the_plain_entry():
+    """Group length 128 and [-8, 7] through the spec entry: the same results as cq_quantize_groups,
+    for every method."""
+    w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
+    wt, dt = dev(w), dev(d)
+    n, E = w.shape[0], d.shape[1]
+    for m in (cq.EXHAUSTIVE, cq.BOUNDED, cq.CANDIDATE):
+        ws = torch.empty(cq.cq_workspace_size(m, E, n), dtype=torch.uint8, device="cuda")
+        s1 = torch.empty(n, dtype=torch.int16, device="cuda")
+        s2 = torch.empty(n, dtype=torch.int16, device="cuda")
+        cq.cq_quantize_groups(wt, dt, p, E, n, m, s1, workspace=ws)
+        cq.cq_quantize_groups_spec(wt, dt, 128, -8, 7, p, E, n, m, s2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2), m
