@@ -1,14 +1,18 @@
 """Benchmark: exact minimax FP16 group-scale selection (W4, groups of 128) on one MI355X.
 
-One step = the whole hot path over one batch: for every matrix of the workload, the
-exhaustive minimax sweep (the pooled-WMSE policy decided in the same sweep, codes emitted),
-the candidate-set solver, the AbsMax baseline, GPTQ-v1 packing of the minimax codes and
-scales, and the worst-environment weighted-MSE proxy for the three policies.  Inputs are
-resident in HBM before timing starts.
+One step = the whole hot path over config 1 (the MLP block: gate and up 3584x1024, down
+1024x3584; 86,016 groups, E = 4): for every matrix, the full-grid exhaustive search (all
+31,743 scales for every weight; minimax and the pooled-WMSE policy from the same sums, codes
+emitted), the candidate-set solver (which must agree with it), the AbsMax baseline, GPTQ-v1
+packing of the minimax codes and scales, and the worst-environment weighted-MSE proxy of the
+three policies.  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` = groups per second of whole steps; `roofline` describes the
-headline kernel (the binary32 exhaustive sweep) measured with HIP events on its own stream;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same groups.
+dominant kernel, the full-grid search, on the algorithmic count of every scale of every weight
+(31,743 x 128 x (2E + 4) flop per group), with HIP events on its launch stream.  `bounded_path`
+times the same step with the branch-and-bound search in place of the full grid (the same
+outputs); `config2_pass` runs the candidate solver and one-launch packing over all 3,883,008
+groups of config 2; `cpu_baseline` times the CPU oracle on a bounded sample of config 1.
 """
 from __future__ import annotations
 
@@ -35,133 +39,71 @@ def flops_per_pattern(E: int) -> int:
     return 128 * (2 * E + 4)
 
 
-def screened_patterns(w: np.ndarray) -> np.ndarray:
-    """Scale patterns the exhaustive sweep evaluates per group: 1 up to the first binary16 scale
-    >= 2 max|w| (every one when 2 max|w| > 65504).  From there on every code is 0 and the
-    objective is the same value at every pattern, so the lowest of them stands for all."""
-    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
-    t = 2.0 * np.abs(w.astype(np.float64)).max(axis=1)
-    return np.minimum(np.searchsorted(grid, t, side="left") + 1, SCALES)
-
-
-def active_terms(w: np.ndarray) -> float:
-    """Terms (scale, weight) over the screened patterns whose code is neither 0 nor held at the
-    clip end.  Weight i has code 0 at scale s when s >= 2|w_i|, and its code is held at 7 (w > 0)
-    or -8 (w < 0) for every scale below w/6.5 (w > 0) or up to |w|/7.5 (w < 0).  Both kinds of
-    term have a closed form at every scale (d w^2, and a quadratic in s with fixed coefficients),
-    so the sweep sums them once per chunk of scales; the active ones each take a quotient, a
-    rounding, a residual, a square and E weighted sums."""
-    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
-    a = np.abs(w.astype(np.float64))
-    top = screened_patterns(w)[:, None]
-    nonzero = np.minimum(np.searchsorted(grid, 2.0 * a, side="left"), top)
-    held = np.where(w > 0, np.searchsorted(grid, a / 6.5, side="left"),
-                    np.searchsorted(grid, a / 7.5, side="right"))
-    held = np.minimum(np.where(w == 0, 0, held), top)
-    return float((nonzero - held).sum())
-
-
-def necessary_terms(w: np.ndarray, d: np.ndarray, opt_m: np.ndarray, opt_p: np.ndarray, chunk: int = 128):
-    """Active terms (see active_terms) of the chunks of `chunk` consecutive patterns that the
-    binary32 screen cannot skip, per group, and the number of those chunks.  The screen skips a
-    chunk when a lower bound on the objective over it exceeds 1.001 times the best value screened
-    so far, for minimax and for pooled; the bound is the code-0 prefix sum (weights with clip key
-    <= s_lo/15) plus, for weights clipped throughout (clip key > s_hi), d (|w| - |q| s_hi)^2 when
-    positive.  The best value screened is never below the optimum, so every chunk whose bound is
-    at most 1.0009 times the optimum (binary64 here, a margin for the screen's binary32) is
-    screened: the count is a lower bound on the work done.  w [n, 128], d [n, E, 128], opt_m the
-    minimax optimum and opt_p the pooled optimum times E (a sum over environments)."""
-    grid = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
-    top = screened_patterns(w)
-    w64, d64 = w.astype(np.float64), d.astype(np.float64)
-    a = np.abs(w64)
-    nonzero = np.minimum(np.searchsorted(grid, 2.0 * a, side="left"), top[:, None])
-    held = np.where(w64 > 0, np.searchsorted(grid, a / 6.5, side="left"), np.searchsorted(grid, a / 7.5, side="right"))
-    held = np.minimum(np.where(w64 == 0, 0, held), top[:, None])
-    key = np.where(w64 > 0, w64 / 6.5, a / 7.5)
-    qa = np.where(w64 > 0, 7.0, 8.0)
-    terms = np.zeros(w.shape[0])
-    chunks = np.zeros(w.shape[0])
-    for j in range(w.shape[0]):
-        nch = (int(top[j]) - 1) // chunk + 1
-        c0 = np.arange(nch) * chunk                        # first pattern index (0-based) of each chunk
-        c1 = np.minimum(c0 + chunk, int(top[j]))           # one past the last
-        lo, hi = grid[c0], grid[c1 - 1]
-        zmask = key[j][None, :] <= lo[:, None] / 15.0      # [nch, 128]
-        cmask = key[j][None, :] > hi[:, None]
-        t = np.maximum(0.0, a[j][None, :] - qa[j][None, :] * hi[:, None]) * cmask
-        zt = np.where(zmask, a[j][None, :] ** 2, 0.0)
-        lb = np.einsum("ce,ke->kc", d64[j], t * t + zt)   # [nch, E]
-        need = lb.max(axis=1) <= 1.0009 * opt_m[j]
-        if opt_p is not None:
-            need |= lb.sum(axis=1) <= 1.0009 * opt_p[j]
-        ov = np.minimum(nonzero[j][None, :], c1[:, None]) - np.maximum(held[j][None, :], c0[:, None])
-        terms[j] = np.clip(ov, 0, None)[need].sum()
-        chunks[j] = need.sum()
-    return terms, chunks
-
-
-def sampled_sweep_flops(w: np.ndarray, d: np.ndarray, d_period: int, r: dict, E: int, pooled: bool,
-                        n_sample: int = 512, seed: int = 2024) -> float:
-    """The sweep's work over all groups of w (2E + 4 flops per unskippable active term, see
-    necessary_terms), from a seeded sample of its groups and the optima in r (quantize_groups)."""
-    rng = np.random.default_rng(seed)
-    n = w.shape[0]
-    idx = np.sort(rng.choice(n, size=min(n_sample, n), replace=False))
-    om = r["objective"].cpu().numpy()[idx]
-    op = r["pooled_objective"].cpu().numpy()[idx] * E if pooled else None
-    terms, _ = necessary_terms(w[idx], d[idx % d_period], om, op, chunk=128)
-    return float(terms.mean()) * n * (2 * E + 4)
-
-
-def sweep_flops(w: np.ndarray, E: int) -> float:
-    """Algorithmic flops of the exhaustive sweep over the groups w [n, 128]: 2E + 4 per active
-    term (a quotient multiply, a residual fma, a square and E weighted fmas)."""
-    return active_terms(w) * (2 * E + 4)
-
-
 def full_grid_flops(n_groups: int, E: int) -> float:
-    """The same count for a plain sweep of every weight at every one of the 31,743 scales."""
+    """Algorithmic flops of the full-grid search of n_groups groups: every scale of every weight."""
     return float(n_groups) * SCALES * flops_per_pattern(E)
 
 
-def sweep_traffic(config: int):
-    """HBM bytes per sweep launch from the committed counter summary (FETCH_SIZE and WRITE_SIZE
-    passes, each scaled by a 256 MiB device copy), or None when that summary is missing, covers
-    another workload, or was taken on sweep sources other than the current ones."""
-    import hashlib
-    import re
-    path = os.path.join(ROOT, "profiles", "sweep_f32_config1_hbm_counters.md")
-    if config != 1 or not os.path.exists(path):
-        return None
-    text = open(path).read()
-    t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
-    h = re.search(r"^sweep_sources_sha256: ([0-9a-f]{64})$", text, re.M)
-    if not t or not h:
-        return None
-    return int(t.group(1)) if sweep_sources_hash() == h.group(1) else None
-
-
-def sweep_sources_hash() -> str:
-    """sha256 of the sweep's sources (sweep.hip, device.h, launch.h) with comments and blank
-    space removed: a change of comments alone leaves the kernel, and its counters, as they were."""
+def sources_hash(files) -> str:
+    """sha256 of the named kernel sources (in csrc/) with comments and blank space removed: a change
+    of comments alone leaves the kernel, and the counters taken on it, as they were."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "post_weight_quantization_group_amd", "csrc")
-    text = "".join(open(os.path.join(csrc, f)).read() for f in ("sweep.hip", "device.h", "launch.h"))
+    text = "".join(open(os.path.join(csrc, f)).read() for f in files)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = re.sub(r"\s+", "", text)
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+FULLGRID_SOURCES = ("fullgrid.hip", "device.h", "launch.h")
+BOUNDED_SOURCES = ("sweep.hip", "device.h", "launch.h")
+CANDIDATE_SOURCES = ("candidate.hip", "sweep.hip", "device.h", "launch.h")
+
+
+def profile_values(name: str, files) -> dict:
+    """The `key: value` lines of a committed counter summary under profiles/, or {} when it is
+    missing or was taken on kernel sources other than the current ones (its `sources_sha256`)."""
+    import re
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return {}
+    vals = dict(re.findall(r"^([a-z0-9_]+): (\S+)$", open(path).read(), re.M))
+    if vals.get("sources_sha256") != sources_hash(files):
+        return {}
+    out = {}
+    for k, v in vals.items():
+        if k == "sources_sha256":
+            continue
+        try:
+            out[k] = float(v) if "." in v or "e" in v else int(v)
+        except ValueError:
+            out[k] = v
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(k: int, budget_s: float) -> dict:
+    """The oracle as it stands (brute force over all 31,743 scales, minimax and pooled from one
+    sweep) on the host's cores: a seeded sample of config k sized to about budget_s seconds with
+    every core, then 128 groups on one thread."""
     import oracle
     import workloads as W
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     threads = max(1, min(cores, 256))
     gids = W.sample_groups(k, W.config(k).n_groups, salt=99)
-    w, d, _ = W.gather_matrix_groups(k, gids)
+    w, d, _ = W.gather_matrix_groups(k, gids[:max(4096, threads * 64)])
     # calibrate on one group per thread, then size the sample to the time budget
     t0 = time.perf_counter()
     oracle.solve(w[:threads], d[:threads], threads, n_threads=threads)
@@ -170,9 +112,14 @@ def cpu_baseline(k: int, budget_s: float) -> dict:
     t0 = time.perf_counter()
     oracle.solve(w[:n], d[:n], n, n_threads=threads)
     dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.solve(w[:128], d[:128], 128, n_threads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": n / dt, "unit": "groups/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} seeded groups of the same workload, brute force over all 31,743 scales "
-                      f"(minimax and pooled), {dt:.1f} s wall"}
+                      f"(minimax and pooled), {dt:.1f} s wall on {threads} threads",
+            "cpu_model": _cpu_model(), "single_thread_groups_per_s": 128 / dt1,
+            "single_thread_sample": f"128 groups on one thread, {dt1:.1f} s"}
 
 
 def _timed(fn, reps=1):
@@ -249,12 +196,73 @@ def measure_aux() -> dict:
     return res
 
 
+def config2_pass(dev) -> dict:
+    """Config 2 at full size: the candidate solver on every one of the 3,883,008 groups (one call
+    per matrix, each with its own diagonals) into codes and scales laid out matrix after matrix,
+    then GPTQ-v1 packing of all 150 matrices in one launch.  Returns the timings (HIP events on the
+    launch stream) and the fallback count."""
+    import torch
+
+    import post_weight_quantization_group_amd as cq
+    import workloads as W
+    spec = W.config(2)
+    mats = []
+    for m, mat in enumerate(spec.matrices):
+        w, d, p = W.matrix_groups(*W.make_matrix(2, m))
+        mats.append((torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev), p, mat))
+    n_all = sum(t[0].shape[0] for t in mats)
+    codes = torch.empty((n_all, 128), dtype=torch.int8, device=dev)
+    scales = torch.empty(n_all, dtype=torch.int16, device=dev)
+    obj = torch.empty(n_all, dtype=torch.float64, device=dev)
+    flags = torch.empty(n_all, dtype=torch.uint8, device=dev)
+    nmax = max(t[0].shape[0] for t in mats)
+    ws = torch.empty(cq.cq_workspace_size(cq.CANDIDATE, 4, nmax), dtype=torch.uint8, device=dev)
+    shapes = [(t[3].out, t[3].inp) for t in mats]
+    qweight = torch.empty(n_all * 16, dtype=torch.int32, device=dev)
+    qscales = torch.empty(n_all, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def solve():
+        g0 = 0
+        for w, d, p, _ in mats:
+            n = w.shape[0]
+            cq.cq_quantize_groups(w, d, p, 4, n, cq.CANDIDATE, scales[g0:g0 + n], codes[g0:g0 + n],
+                                  obj[g0:g0 + n], flags[g0:g0 + n], None, None, ws)
+            g0 += n
+
+    def pack():
+        cq.cq_pack_gptq_v1_multi(codes, scales, len(shapes), [o for o, _ in shapes], [i for _, i in shapes],
+                                 qweight, qscales)
+    solve()
+    pack()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    reps = 3
+    t_solve = t_pack = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        solve()
+        ev[1].record(stream)
+        pack()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_solve += ev[0].elapsed_time(ev[1]) / reps
+        t_pack += ev[1].elapsed_time(ev[2]) / reps
+    fb = int(torch.count_nonzero(flags & cq.FLAG_FALLBACK).item())
+    pack_bytes = n_all * (128 + 2 + 64 + 2)
+    return {"groups": n_all, "E": 4, "candidate_ms": t_solve, "candidate_groups_per_s": n_all / t_solve * 1e3,
+            "candidate_fallback_groups": fb, "pack_ms": t_pack, "pack_launches": 1,
+            "pack_GB_per_s": pack_bytes / (t_pack / 1e3) / 1e9, "pack_hbm_frac": pack_bytes / (t_pack / 1e3) / 8e12,
+            "pack_bytes": pack_bytes}
+
+
 def measure_all_configs() -> dict:
     """Throughput of every kernel on the five synthetic configs (reported beside the headline).
 
-    config 0/1/4: exhaustive (minimax + pooled in one sweep), candidate, AbsMax, pack, proxies;
-    config 2: candidate, pack and proxy on all 150 matrices, exhaustive on the seeded
-    10,000-group sample; config 3: exhaustive and candidate on all 262,144 groups.
+    config 0/1/4: full grid (minimax + pooled from the same sums), bounded search, candidate,
+    AbsMax, pack, proxies; config 2: the full-size candidate and packing pass plus the seeded
+    10,000-group sample through the full grid and the bounded search; config 3: every search on all
+    262,144 groups.  Fractions of the FP32 peak count every scale of every weight (full grid).
     """
     import torch
 
@@ -262,24 +270,46 @@ def measure_all_configs() -> dict:
     import workloads as W
     dev = torch.device("cuda:0")
     res = {}
+    peak = PEAK_FP32_TFLOPS * 1e12
 
-    def matrix_pass(k, mats_idx=None):
+    def searches(wt, dt, p, n, E, pooled, tot):
+        r, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="exhaustive", pooled=pooled))
+        tot["full_ms"] += ms
+        b, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="bounded", pooled=pooled))
+        tot["bounded_ms"] += ms
+        c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
+        tot["candidate_ms"] += ms
+        tot["fallback"] += int(torch.count_nonzero(c["flags"] & cq.FLAG_FALLBACK).item())
+        tot["fp64_sweep"] += int(torch.count_nonzero(r["flags"] & cq.FLAG_FP64_SWEEP).item())
+        tot["mismatch"] += int(torch.count_nonzero(r["scales"] != c["scales"]).item())
+        tot["mismatch"] += int(torch.count_nonzero(r["scales"] != b["scales"]).item())
+        tot["groups"] += n
+        tot["flops"] += full_grid_flops(n, E)
+        return r
+
+    def summary(tot, E):
+        return {"groups": tot["groups"], "E": E,
+                "full_grid_groups_per_s": tot["groups"] / tot["full_ms"] * 1e3,
+                "full_grid_frac_fp32_peak": tot["flops"] / (tot["full_ms"] / 1e3) / peak,
+                "bounded_groups_per_s": tot["groups"] / tot["bounded_ms"] * 1e3,
+                "candidate_groups_per_s": tot["groups"] / tot["candidate_ms"] * 1e3,
+                "candidate_fallback_groups": tot["fallback"], "full_grid_fp64_sweep_groups": tot["fp64_sweep"],
+                "scale_mismatches_between_methods": tot["mismatch"]}
+
+    def new_tot():
+        return {"full_ms": 0.0, "bounded_ms": 0.0, "candidate_ms": 0.0, "absmax_ms": 0.0, "pack_ms": 0.0,
+                "proxy_ms": 0.0, "groups": 0, "fallback": 0, "fp64_sweep": 0, "mismatch": 0, "flops": 0.0}
+
+    def matrix_pass(k):
         spec = W.config(k)
         E = spec.E
-        idx = range(len(spec.matrices)) if mats_idx is None else mats_idx
-        tot = {"exhaustive_ms": 0.0, "candidate_ms": 0.0, "absmax_ms": 0.0, "pack_ms": 0.0, "proxy_ms": 0.0,
-               "groups": 0, "fallback": 0, "fp64_sweep": 0, "mismatch": 0, "flops": 0.0}
+        tot = new_tot()
         module_means = {"minimax": [], "pooled": [], "absmax": []}
-        for m in idx:
-            mat = spec.matrices[m]
+        for m, mat in enumerate(spec.matrices):
             w, d, p = W.matrix_groups(*W.make_matrix(k, m))
             n = w.shape[0]
             wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
-            r, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="exhaustive", pooled=True))
-            tot["exhaustive_ms"] += ms
-            tot["flops"] += sampled_sweep_flops(w, d, p, r, E, True)
-            c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
-            tot["candidate_ms"] += ms
+            r = searches(wt, dt, p, n, E, True, tot)
             ab, ms = _timed(lambda: cq.baseline_scales(wt, dt, p, "absmax", objective=False))
             tot["absmax_ms"] += ms
             codes = r["codes"].reshape(mat.out, mat.inp)
@@ -292,82 +322,26 @@ def measure_all_configs() -> dict:
             tot["proxy_ms"] += ms
             for j, name in enumerate(("minimax", "pooled", "absmax")):
                 module_means[name].append(float(mm.cpu()[j, 0]))
-            f = c["flags"].cpu().numpy()
-            tot["fallback"] += int(np.count_nonzero(f & cq.FLAG_FALLBACK))
-            tot["fp64_sweep"] += int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP))
-            tot["mismatch"] += int(torch.count_nonzero(r["scales"] != c["scales"]).item())
-            tot["groups"] += n
-        out = {"groups": tot["groups"], "E": E,
-               "exhaustive_groups_per_s": tot["groups"] / tot["exhaustive_ms"] * 1e3,
-               "exhaustive_frac_fp32_peak": tot["flops"] / (tot["exhaustive_ms"] / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
-               "candidate_groups_per_s": tot["groups"] / tot["candidate_ms"] * 1e3,
-               "candidate_hbm_frac": tot["groups"] * 642 / (tot["candidate_ms"] / 1e3) / 8e12,
-               "absmax_groups_per_s": tot["groups"] / tot["absmax_ms"] * 1e3,
-               "pack_ms": tot["pack_ms"], "pack_hbm_frac": tot["groups"] * 196 / (tot["pack_ms"] / 1e3) / 8e12,
-               "proxy_ms": tot["proxy_ms"],
-               "candidate_fallback_groups": tot["fallback"], "exhaustive_fp64_sweep_groups": tot["fp64_sweep"],
-               "candidate_vs_exhaustive_scale_mismatches": tot["mismatch"],
-               "proxy_module_macro": {k2: float(np.mean(v)) for k2, v in module_means.items()}}
+        out = summary(tot, E)
+        out.update({"absmax_groups_per_s": tot["groups"] / tot["absmax_ms"] * 1e3, "pack_ms": tot["pack_ms"],
+                    "proxy_ms": tot["proxy_ms"],
+                    "proxy_module_macro": {k2: float(np.mean(v)) for k2, v in module_means.items()}})
         return out
 
     res["config0"] = matrix_pass(0)
     res["config1"] = matrix_pass(1)
     res["config4"] = matrix_pass(4)
     res.update(measure_aux())
-    # config 2: candidate + pack + proxy on every matrix, exhaustive on the 10,000-group sample
-    spec = W.config(2)
-    cand_ms = pack_ms = proxy_ms = 0.0
-    fb = n_all = 0
-    means = []
-    for m, mat in enumerate(spec.matrices):
-        w, d, p = W.matrix_groups(*W.make_matrix(2, m))
-        n = w.shape[0]
-        wt, dt = torch.from_numpy(w).to(dev), torch.from_numpy(d).to(dev)
-        c, ms = _timed(lambda: cq.quantize_groups(wt, dt, p, method="candidate"))
-        cand_ms += ms
-        codes = c["codes"].reshape(mat.out, mat.inp)
-        sc = c["scales"].reshape(mat.out, mat.inp // 128)
-        _, ms = _timed(lambda: cq.pack_gptq_v1(codes, sc, mat.out, mat.inp))
-        pack_ms += ms
-        off = torch.tensor([0, n], dtype=torch.int64, device=dev)
-        (_, mm, _), ms = _timed(lambda: cq.proxy_worst_env_wmse(wt, dt, c["scales"], off, p, per_group=False))
-        proxy_ms += ms
-        means.append(float(mm.cpu()[0]))
-        fb += int(np.count_nonzero(c["flags"].cpu().numpy() & cq.FLAG_FALLBACK))
-        n_all += n
+    res["config2"] = config2_pass(dev)
     gids = W.sample_groups(2, 10000)
     ws_, ds_, _ = W.gather_matrix_groups(2, gids)
-    wt, dt = torch.from_numpy(ws_).to(dev), torch.from_numpy(ds_).to(dev)
-    r, ms_x = _timed(lambda: cq.quantize_groups(wt, dt, ws_.shape[0], method="exhaustive"))
-    c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, ws_.shape[0], method="candidate"))
-    res["config2"] = {"groups": n_all, "E": 4, "candidate_groups_per_s": n_all / cand_ms * 1e3,
-                      "candidate_hbm_frac": n_all * 642 / (cand_ms / 1e3) / 8e12,
-                      "candidate_ms": cand_ms, "candidate_fallback_groups": fb,
-                      "pack_ms": pack_ms, "pack_hbm_frac": n_all * 196 / (pack_ms / 1e3) / 8e12,
-                      "proxy_ms": proxy_ms, "proxy_module_macro_minimax": float(np.mean(means)),
-                      "sample_groups": int(ws_.shape[0]),
-                      "sample_exhaustive_groups_per_s": ws_.shape[0] / ms_x * 1e3,
-                      "sample_exhaustive_frac_fp32_peak":
-                          sampled_sweep_flops(ws_, ds_, ws_.shape[0], r, 4, False) / (ms_x / 1e3)
-                          / (PEAK_FP32_TFLOPS * 1e12),
-                      "sample_candidate_vs_exhaustive_scale_mismatches":
-                          int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
-    # config 3: per-group diagonals
-    w3, d3, cat3, _ = W.make_groups(3)
-    n3 = w3.shape[0]
-    wt, dt = torch.from_numpy(w3).to(dev), torch.from_numpy(d3).to(dev)
-    r, ms_x = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="exhaustive", pooled=False))
-    flops3 = sampled_sweep_flops(w3, d3, n3, r, 8, False)
-    del d3
-    c, ms_c = _timed(lambda: cq.quantize_groups(wt, dt, n3, method="candidate"))
-    fl = c["flags"].cpu().numpy()
-    res["config3"] = {"groups": n3, "E": 8, "exhaustive_groups_per_s": n3 / ms_x * 1e3,
-                      "exhaustive_frac_fp32_peak": flops3 / (ms_x / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
-                      "candidate_groups_per_s": n3 / ms_c * 1e3,
-                      "candidate_fallback_groups": int(np.count_nonzero(fl & cq.FLAG_FALLBACK)),
-                      "exhaustive_fp64_sweep_groups": int(np.count_nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)),
-                      "candidate_vs_exhaustive_scale_mismatches":
-                          int(torch.count_nonzero(r["scales"] != c["scales"]).item())}
+    tot = new_tot()
+    searches(torch.from_numpy(ws_).to(dev), torch.from_numpy(ds_).to(dev), ws_.shape[0], ws_.shape[0], 4, True, tot)
+    res["config2"]["sample"] = summary(tot, 4)
+    w3, d3, _, _ = W.make_groups(3)
+    tot = new_tot()
+    searches(torch.from_numpy(w3).to(dev), torch.from_numpy(d3).to(dev), w3.shape[0], w3.shape[0], 8, True, tot)
+    res["config3"] = summary(tot, 8)
     return res
 
 
@@ -376,10 +350,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-candidate", action="store_true")
+    ap.add_argument("--no-config2", action="store_true", help="skip the full-size config 2 candidate and packing pass")
+    ap.add_argument("--no-bounded", action="store_true", help="skip the step with the bounded search")
     ap.add_argument("--aux-only", action="store_true",
                     help="only measure the diagonals, W4A16 and held-out rows (one JSON line, no step)")
     ap.add_argument("--all-configs", action="store_true",
@@ -402,9 +376,8 @@ def main():
     import post_weight_quantization_group_amd as cq
     import workloads as W
 
-    spec = W.config(args.config)
-    if spec.per_group:
-        raise SystemExit("the benchmark workload is a matrix config")
+    k = 1
+    spec = W.config(k)
     E = spec.E
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -412,12 +385,11 @@ def main():
 
     mats = []
     for m, mat in enumerate(spec.matrices):
-        A, dm = W.make_matrix(args.config, m)
+        A, dm = W.make_matrix(k, m)
         w, d, p = W.matrix_groups(A, dm)
         n = w.shape[0]
         t = {
             "name": mat.name, "out": mat.out, "inp": mat.inp, "n": n, "p": p,
-            "w_np": w, "d_np": d, "patterns": float(screened_patterns(w).mean()),
             "w": torch.from_numpy(w).to(dev), "d": torch.from_numpy(d).to(dev),
             "sc3": torch.empty((3, n), dtype=torch.int16, device=dev),
             "codes": torch.empty((n, 128), dtype=torch.int8, device=dev),
@@ -449,31 +421,24 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    use_candidate = not args.no_candidate
-    if use_candidate:
-        try:
-            t = mats[0]
-            cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.CANDIDATE, t["cscales"], t["ccodes"],
-                                  t["cobj"], t["cflags"], None, None, t["cws"])
-        except cq.CQError:
-            use_candidate = False
     torch.cuda.synchronize()
 
-    sweep_ev = []
-
-    def step(record):
+    def step(method, ev):
+        """The whole path over config 1 with `method` deciding minimax and pooled; launches of the
+        search and of the candidate solver bracketed by HIP events on the launch stream."""
         for t in mats:
-            if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3)) if ev is not None else (None,) * 3
+            if a is not None:
                 a.record(stream)
-            cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.EXHAUSTIVE, t["scales"], t["codes"],
+            cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], method, t["scales"], t["codes"],
                                   t["obj"], t["flags"], t["pscales"], t["pobj"], t["ws"])
-            if record:
+            if b is not None:
                 b.record(stream)
-                sweep_ev.append((a, b, t))
-            if use_candidate:
-                cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.CANDIDATE, t["cscales"],
-                                      t["ccodes"], t["cobj"], t["cflags"], None, None, t["cws"])
+            cq.cq_quantize_groups(t["w"], t["d"], t["p"], E, t["n"], cq.CANDIDATE, t["cscales"],
+                                  t["ccodes"], t["cobj"], t["cflags"], None, None, t["cws"])
+            if c is not None:
+                c.record(stream)
+                ev.append((a, b, c, t))
             cq.cq_baseline_scales(t["w"], t["d"], t["p"], E, t["n"], cq.ABSMAX, t["ascales"], t["acodes"],
                                   t["aobj"])
             cq.cq_pack_gptq_v1(t["codes"], t["scales"], t["out"], t["inp"], t["qweight"], t["qscales"])
@@ -481,44 +446,33 @@ def main():
             cq.cq_proxy_worst_env_wmse_multi(t["w"], t["d"], t["p"], E, t["n"], 3, t["sc3"], t["off"], 1, t["mm"],
                                              t["macro"], t["pg"])
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step(True)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    def timed_steps(method, steps, warmup):
+        for _ in range(warmup):
+            step(method, None)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = []
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for _ in range(steps):
+            step(method, ev)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = t0.elapsed_time(t1) / steps
+        search_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
+        cand_ms = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev]))
+        return ms_step, search_ms, cand_ms, wall
+
+    ms_step, full_ms, cand_ms, wall = timed_steps(cq.EXHAUSTIVE, args.steps, args.warmup)
     value = n_total / (ms_step / 1e3)
-
-    # headline kernel: the exhaustive sweep call, per launch (one launch per matrix).  Its work:
-    # the active terms of the chunks no exact screen with its lower bound can skip, per group from
-    # a seeded sample of 1,024 groups per matrix (against the optima the sweep returned), times
-    # 2E + 4 flops; chunks of 128 patterns as in the kernel.
-    rng = np.random.default_rng(2024)
-    nec_chunks, all_terms = [], []
-    for t in mats:
-        idx = np.sort(rng.choice(t["n"], size=min(1024, t["n"]), replace=False))
-        om = t["obj"].cpu().numpy()[idx]
-        op = t["pobj"].cpu().numpy()[idx] * E
-        terms, chunks = necessary_terms(t["w_np"][idx], t["d_np"][idx % t["p"]], om, op, chunk=128)
-        t["flops"] = float(terms.mean()) * t["n"] * (2 * E + 4)
-        nec_chunks.append(float(chunks.mean()))
-        all_terms.append(active_terms(t["w_np"][idx]) / idx.size)
-    durs = [a.elapsed_time(b) for a, b, _ in sweep_ev]
-    avg_ms = float(np.mean(durs))
-    avg_groups = float(np.mean([t["n"] for _, _, t in sweep_ev]))
-    avg_flops = float(np.mean([t["flops"] for _, _, t in sweep_ev]))
-    achieved = avg_flops / (avg_ms / 1e3) / 1e12
-    patterns = float(np.mean([t["patterns"] for t in mats]))
-    flags = torch.cat([t["flags"] for t in mats]).cpu().numpy()
-
+    flags = torch.cat([t["flags"] for t in mats])
+    cflags = torch.cat([t["cflags"] for t in mats])
+    mism = sum(int(torch.count_nonzero(t["scales"] != t["cscales"]).item()) for t in mats)
+    groups_per_launch = float(np.mean([t["n"] for t in mats]))
+    flops_per_launch = full_grid_flops(groups_per_launch, E)
+    achieved = flops_per_launch / (full_ms / 1e3) / 1e12
+    fg = profile_values("fullgrid_config1_counters.md", FULLGRID_SOURCES)
     line = {
         "metric": METRIC,
         "value": value,
@@ -532,29 +486,44 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"config {args.config}: " + spec.description, "groups": n_total, "E": E,
+        "config": {"workload": "config 1: " + spec.description, "groups": n_total, "E": E,
                    "matrices": [f"{t['name']} {t['out']}x{t['inp']}" for t in mats],
-                   "candidate_solver_in_step": use_candidate},
+                   "step": "per matrix: full-grid exhaustive search (minimax and pooled, codes), candidate-set "
+                           "solver, AbsMax, GPTQ-v1 packing, proxy of the three policies"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": sweep_traffic(args.config),
-                     "kernel": "binary32 exhaustive sweep (cq_quantize_groups, CQ_EXHAUSTIVE)",
-                     "launch_ms": avg_ms, "groups_per_launch": avg_groups,
-                     "flops_per_launch": avg_flops, "flops_per_active_term": 2 * E + 4,
-                     "patterns_per_group": patterns,
-                     "chunks_per_group": float(np.mean([(t["patterns"] - 1) // 128 + 1 for t in mats])),
-                     "unskippable_chunks_per_group": float(np.mean(nec_chunks)),
-                     "active_terms_per_group_unskippable": avg_flops / avg_groups / (2 * E + 4),
-                     "active_terms_per_group_all_chunks": float(np.mean(all_terms))},
-        "sweep_groups_per_s": avg_groups / (avg_ms / 1e3),
-        "sweep_full_grid_equivalent_tflops": full_grid_flops(avg_groups, E) / (avg_ms / 1e3) / 1e12,
-        "flag_counts": {"near_tie": int(np.count_nonzero(flags & 2)), "exact_tie": int(np.count_nonzero(flags & 4)),
-                        "fp64_sweep": int(np.count_nonzero(flags & 16))},
+                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": fg.get("traffic_bytes_per_launch"),
+                     "kernel": "full-grid exhaustive search (cq_quantize_groups, CQ_EXHAUSTIVE: "
+                               "full_screen_kernel<4> plus two short launches)",
+                     "launch_ms": full_ms, "groups_per_launch": groups_per_launch,
+                     "flops_per_launch": flops_per_launch,
+                     "flops_per_group": SCALES * flops_per_pattern(E),
+                     "counting": "31,743 scales x 128 weights x (2E + 4) flop per group: a quotient multiply, "
+                                 "a residual fma (2), a square and E weighted fmas (2E)"},
+        "full_grid_groups_per_s": groups_per_launch / (full_ms / 1e3),
+        "candidate_launch_ms": cand_ms,
+        "candidate_vs_full_grid_scale_mismatches": mism,
+        "flag_counts": {"near_tie": int(torch.count_nonzero(flags & 2).item()),
+                        "exact_tie": int(torch.count_nonzero(flags & 4).item()),
+                        "fp64_sweep": int(torch.count_nonzero(flags & 16).item()),
+                        "candidate_fallback": int(torch.count_nonzero(cflags & 8).item())},
         "wall_s": wall,
     }
+    if fg:
+        line["roofline"]["counters"] = {k2: v for k2, v in fg.items() if k2 != "traffic_bytes_per_launch"}
+    if not args.no_bounded:
+        ms_b, bnd_ms, cand_b, wall_b = timed_steps(cq.BOUNDED, args.steps, args.warmup)
+        line["bounded_path"] = {
+            "what": "the same step with the branch-and-bound search (CQ_BOUNDED) in place of the full grid: "
+                    "the same outputs",
+            "groups_per_s": n_total / (ms_b / 1e3), "ms_per_step": ms_b,
+            "bounded_launch_ms": bnd_ms, "candidate_launch_ms": cand_b,
+            "counters": profile_values("bounded_candidate_config1_counters.md", CANDIDATE_SOURCES) or None}
+    if not args.no_config2:
+        line["config2_pass"] = config2_pass(dev)
     if args.all_configs:
         line["per_config"] = measure_all_configs()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(k, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

@@ -183,6 +183,26 @@ int32_t cq_pack_gptq_v1(const int8_t *codes, const uint16_t *grp_scales, int64_t
                         int32_t *qweight, uint16_t *scales, void *stream);
 
 /*
+ * GPTQ-v1 packing of n_mats matrices in one launch (model card, "Verification": the packed
+ * checkpoint holds 150 module-buffer sets, each unpacked again; "Quantization configuration":
+ * GPTQ v1, 4-bit, group size 128, symmetric).  Matrix k has shape outs[k] x ins[k]; every array
+ * holds the matrices back to back in order, each block exactly what cq_pack_gptq_v1 takes or
+ * writes for that matrix alone:
+ *   codes       int8 [sum_k outs[k] * ins[k]], matrix k from offset sum_{j<k} outs[j] * ins[j].
+ *   grp_scales  uint16, matrix k from offset sum_{j<k} outs[j] * ins[j] / 128.
+ *   qweight     out, int32, matrix k's [ins[k]/8][outs[k]] from offset sum_{j<k} outs[j] * ins[j] / 8.
+ *   scales      out, uint16, matrix k's [ins[k]/128][outs[k]] from offset sum_{j<k} outs[j] * ins[j] / 128.
+ *   outs, ins   HOST int64 arrays [n_mats], read before the call returns.
+ * 0 <= n_mats <= CQ_MAX_PACK_MATRICES; every ins[k] a multiple of 128 (ins[k] / 128 <= 65535);
+ * shapes below 2^31 each and 2^46 elements in all; else CQ_EINVAL.  Alignment as for
+ * cq_pack_gptq_v1.
+ */
+#define CQ_MAX_PACK_MATRICES 256
+int32_t cq_pack_gptq_v1_multi(const int8_t *codes, const uint16_t *grp_scales, int32_t n_mats,
+                              const int64_t *outs, const int64_t *ins, int32_t *qweight, uint16_t *scales,
+                              void *stream);
+
+/*
  * Module-macro worst-environment weighted MSE (Qwen3.5-0.8B-Base-CliffQuant-
  * W4A16-G128 model card, "Held-out reconstruction proxy"; CliffQuant README,
  * "Held-out reconstruction proxy").

@@ -27,7 +27,8 @@ __all__ = [
     "CQError", "GROUP", "MAX_GROUP", "EXHAUSTIVE", "CANDIDATE", "BOUNDED", "ABSMAX", "POOLED_WMSE",
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
-    "cq_quantize_groups", "cq_quantize_groups_spec", "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
+    "cq_quantize_groups", "cq_quantize_groups_spec", "cq_baseline_scales", "cq_pack_gptq_v1",
+    "cq_pack_gptq_v1_multi", "pack_gptq_v1_multi", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
     "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "cq_diagonals_workspace_size",
@@ -42,7 +43,7 @@ FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE, "bounded": BOUNDED}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_quantize_groups_spec",
-                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_proxy_workspace_size",
+                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_pack_gptq_v1_multi", "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
                     "cq_w4a16_matmul")
@@ -85,6 +86,8 @@ def load():
         lib.cq_baseline_scales.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, SZ, P]
         lib.cq_pack_gptq_v1.restype = I32
         lib.cq_pack_gptq_v1.argtypes = [P, P, I64, I64, P, P, P]
+        lib.cq_pack_gptq_v1_multi.restype = I32
+        lib.cq_pack_gptq_v1_multi.argtypes = [P, P, I32, P, P, P, P, P]
         lib.cq_proxy_workspace_size.restype = SZ
         lib.cq_proxy_workspace_size.argtypes = [I64]
         lib.cq_proxy_worst_env_wmse.restype = I32
@@ -178,6 +181,15 @@ def cq_baseline_scales(w, d, d_period, E, n_groups, which, scales, codes=None, o
 def cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream=None):
     _check(load().cq_pack_gptq_v1(_p(codes), _p(grp_scales), out, inp, _p(qweight), _p(scales),
                                   _stream(stream)), "cq_pack_gptq_v1")
+
+
+def cq_pack_gptq_v1_multi(codes, grp_scales, n_mats, outs, ins, qweight, scales, stream=None):
+    """outs, ins: host sequences of n_mats shapes (marshalled to int64 host arrays)."""
+    o = (ctypes.c_int64 * max(1, n_mats))(*[int(x) for x in outs])
+    i = (ctypes.c_int64 * max(1, n_mats))(*[int(x) for x in ins])
+    _check(load().cq_pack_gptq_v1_multi(_p(codes), _p(grp_scales), n_mats, ctypes.cast(o, ctypes.c_void_p),
+                                        ctypes.cast(i, ctypes.c_void_p), _p(qweight), _p(scales), _stream(stream)),
+           "cq_pack_gptq_v1_multi")
 
 
 def cq_proxy_worst_env_wmse(w, d_eval, d_period, E, n_groups, scales, module_offsets, n_modules, module_mean,
@@ -318,6 +330,19 @@ def pack_gptq_v1(codes, grp_scales, out: int, inp: int, stream=None):
     qweight = torch.empty((inp // 8, out), dtype=torch.int32, device=codes.device)
     scales = torch.empty((inp // GROUP, out), dtype=torch.int16, device=codes.device)
     cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream)
+    return qweight, scales
+
+
+def pack_gptq_v1_multi(codes, grp_scales, shapes, stream=None):
+    """GPTQ-v1 packing of several matrices in one launch.  codes int8 and grp_scales int16 (binary16
+    bits) hold the matrices back to back (flat, or any contiguous tensor); shapes is a list of
+    (out, in).  Returns (qweight, scales) as flat int32 and int16 tensors holding each matrix's
+    [in/8, out] and [in/128, out] blocks back to back."""
+    n_el = sum(int(o) * int(i) for o, i in shapes)
+    qweight = torch.empty(n_el // 8, dtype=torch.int32, device=codes.device)
+    scales = torch.empty(n_el // GROUP, dtype=torch.int16, device=codes.device)
+    cq_pack_gptq_v1_multi(codes, grp_scales, len(shapes), [o for o, _ in shapes], [i for _, i in shapes], qweight,
+                          scales, stream)
     return qweight, scales
 
 

@@ -188,6 +188,31 @@ int32_t cq_pack_gptq_v1(const int8_t* codes, const uint16_t* grp_scales, int64_t
     return hip_status(cqk::launch_pack(codes, grp_scales, out, in, qweight, scales, (hipStream_t)stream));
 }
 
+int32_t cq_pack_gptq_v1_multi(const int8_t* codes, const uint16_t* grp_scales, int32_t n_mats, const int64_t* outs,
+                              const int64_t* ins, int32_t* qweight, uint16_t* scales, void* stream) {
+    if (n_mats < 0 || n_mats > CQ_MAX_PACK_MATRICES) return CQ_EINVAL;
+    if (n_mats == 0) return CQ_OK;
+    if (!outs || !ins) return CQ_EINVAL;
+    cqk::PackShapes m{};
+    m.n = n_mats;
+    int64_t elems = 0, tiles = 0;
+    for (int32_t k = 0; k < n_mats; ++k) {
+        const int64_t o = outs[k], i = ins[k];
+        if (o < 0 || i < 0 || i % CQ_GROUP != 0 || o > INT32_MAX || i > INT32_MAX) return CQ_EINVAL;
+        if (i / CQ_GROUP > 65535) return CQ_EINVAL;
+        m.out[k] = (int32_t)o;
+        m.in[k] = (int32_t)i;
+        elems += o * i;
+        tiles += (o + 63) / 64 * (i / CQ_GROUP);
+        if (elems > ((int64_t)1 << 46)) return CQ_EINVAL;
+    }
+    if (tiles == 0) return CQ_OK;
+    if (!codes || !grp_scales || !qweight || !scales) return CQ_EINVAL;
+    if (!aligned(codes, 16) || !aligned(grp_scales, 2) || !aligned(qweight, 4) || !aligned(scales, 2))
+        return CQ_EINVAL;
+    return hip_status(cqk::launch_pack_multi(codes, grp_scales, m, qweight, scales, (hipStream_t)stream));
+}
+
 size_t cq_proxy_workspace_size(int64_t n_groups) {
     return n_groups < 0 ? 0 : round_up((size_t)n_groups * 8u);
 }

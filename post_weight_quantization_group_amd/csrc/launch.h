@@ -100,6 +100,17 @@ hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st);
 
+// Shapes of the matrices one multi-matrix packing launch takes (passed by value as the kernel
+// argument; 2 KB).
+constexpr int PACK_MAX_MATS = 256;
+struct PackShapes {
+    int32_t n;
+    int32_t out[PACK_MAX_MATS];
+    int32_t in[PACK_MAX_MATS];
+};
+hipError_t launch_pack_multi(const int8_t* codes, const uint16_t* grp_scales, const PackShapes& m,
+                             int32_t* qweight, uint16_t* scales, hipStream_t st);
+
 // W4A16 matmul y [M][out] = x [M][in] (bf16) times the GPTQ-v1 tensors dequantized.
 hipError_t launch_w4a16(const uint16_t* x, const int32_t* qw, const uint16_t* scales, int64_t M, int64_t out,
                         int64_t in, float* y, hipStream_t st);

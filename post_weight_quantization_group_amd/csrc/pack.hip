@@ -63,6 +63,96 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ co
     }
 }
 
+// Several matrices in one launch: matrix k's codes, group scales and outputs follow those of
+// matrices 0..k-1 back to back (offsets from the prefix sums of out * in).  Each workgroup forms
+// the tile and element prefix sums of the (at most 256) shapes once, then loops over tiles,
+// finding each tile's matrix by a binary search of the prefix; a tile is the same 64 x 128
+// transpose as in pack_kernel.
+__global__ __launch_bounds__(256) void pack_multi_kernel(const int8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ grp_scales, PackShapes m,
+                                                         int64_t total_tiles, int32_t* __restrict__ qweight,
+                                                         uint16_t* __restrict__ scales) {
+    __shared__ __align__(16) uint8_t tile[PT_ROWS * PT_STRIDE];
+    __shared__ int64_t tpre[PACK_MAX_MATS + 1], epre[PACK_MAX_MATS + 1];
+    const int tid = threadIdx.x;
+    // inclusive scans (Hillis-Steele) of the tiles and the elements of each matrix
+    int64_t tv = 0, ev = 0;
+    if (tid < m.n) {
+        tv = (int64_t)((m.out[tid] + PT_ROWS - 1) / PT_ROWS) * (m.in[tid] / G);
+        ev = (int64_t)m.out[tid] * m.in[tid];
+    }
+    tpre[tid + 1] = tv;
+    epre[tid + 1] = ev;
+    if (tid == 0) { tpre[0] = 0; epre[0] = 0; }
+    __syncthreads();
+    for (int o = 1; o < PACK_MAX_MATS; o <<= 1) {
+        const int64_t a = tid + 1 > o ? tpre[tid + 1 - o] : 0, b = tid + 1 > o ? epre[tid + 1 - o] : 0;
+        __syncthreads();
+        tpre[tid + 1] += a;
+        epre[tid + 1] += b;
+        __syncthreads();
+    }
+    for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+        int lo = 0, hi = m.n - 1;  // the last k with tpre[k] <= t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tpre[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int k = lo;
+        const int64_t out = m.out[k], in = m.in[k], ngc = in / G;
+        const int64_t local = t - tpre[k];
+        const int64_t rt = (out + PT_ROWS - 1) / PT_ROWS;
+        const int64_t c = local / rt, o0 = (local - c * rt) * PT_ROWS;
+        const int8_t* cm = codes + epre[k];
+        const uint16_t* gm = grp_scales + epre[k] / G;
+        int32_t* qm = qweight + epre[k] / 8;
+        uint16_t* sm = scales + epre[k] / G;
+        {
+            const int row = tid >> 2, q = tid & 3;
+            const int64_t o = o0 + row;
+            if (o < out) {
+                const int4* src = (const int4*)(cm + o * in + c * G + q * 32);
+                const int4 v0 = src[0], v1 = src[1];
+                uint32_t* dst = (uint32_t*)(tile + row * PT_STRIDE + q * 32);
+                dst[0] = (uint32_t)v0.x; dst[1] = (uint32_t)v0.y; dst[2] = (uint32_t)v0.z; dst[3] = (uint32_t)v0.w;
+                dst[4] = (uint32_t)v1.x; dst[5] = (uint32_t)v1.y; dst[6] = (uint32_t)v1.z; dst[7] = (uint32_t)v1.w;
+            }
+        }
+        __syncthreads();
+        const int col = tid & 63;
+        const int64_t o = o0 + col;
+        if (o < out) {
+            const uint8_t* trow = tile + col * PT_STRIDE;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int rl = (tid >> 6) + 4 * kk;
+                const uint32_t lo32 = *(const uint32_t*)(trow + rl * 8);
+                const uint32_t hi32 = *(const uint32_t*)(trow + rl * 8 + 4);
+                uint32_t word = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    word |= ((((lo32 >> (8 * j)) & 0xFFu) + 8u) & 0xFu) << (4 * j);
+                    word |= ((((hi32 >> (8 * j)) & 0xFFu) + 8u) & 0xFu) << (4 * (j + 4));
+                }
+                qm[(c * 16 + rl) * out + o] = (int32_t)word;
+            }
+            if (tid < 64) sm[c * out + o] = gm[o * ngc + c];
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_pack_multi(const int8_t* codes, const uint16_t* grp_scales, const PackShapes& m,
+                             int32_t* qweight, uint16_t* scales, hipStream_t st) {
+    int64_t total = 0;
+    for (int k = 0; k < m.n; ++k) total += (int64_t)((m.out[k] + PT_ROWS - 1) / PT_ROWS) * (m.in[k] / G);
+    if (total == 0) return hipSuccess;
+    const int64_t grid = total < 8192 ? total : 8192;
+    hipLaunchKernelGGL(pack_multi_kernel, dim3((unsigned)grid), dim3(256), 0, st, codes, grp_scales, m, total,
+                       qweight, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st) {
     if (out == 0 || in == 0) return hipSuccess;

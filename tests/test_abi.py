@@ -111,6 +111,24 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.cq_baseline_scales(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE + 8, None, None, 0, None) == -1  # codes
 
 
+def test_pack_multi_rejects_bad_arguments():
+    lib = cq.load()
+    f = lib.cq_pack_gptq_v1_multi
+    import ctypes as C
+
+    def arr(*v):
+        return C.cast((C.c_int64 * len(v))(*v), C.c_void_p)
+    assert f(FAKE, FAKE, -1, arr(4), arr(128), FAKE, FAKE, None) == -1
+    assert f(FAKE, FAKE, 257, arr(4), arr(128), FAKE, FAKE, None) == -1          # too many matrices
+    assert f(FAKE, FAKE, 2, arr(4, 4), arr(128, 100), FAKE, FAKE, None) == -1    # in % 128
+    assert f(FAKE, FAKE, 1, arr(-1), arr(128), FAKE, FAKE, None) == -1
+    assert f(FAKE, FAKE, 1, None, arr(128), FAKE, FAKE, None) == -1
+    assert f(FAKE + 1, FAKE, 1, arr(4), arr(128), FAKE, FAKE, None) == -1        # codes alignment
+    assert f(None, FAKE, 1, arr(4), arr(128), FAKE, FAKE, None) == -1
+    assert f(None, None, 0, None, None, None, None, None) == 0                   # nothing to pack
+    assert f(None, None, 2, arr(0, 0), arr(128, 256), None, None, None) == 0     # empty matrices
+
+
 def test_multi_policy_proxy_rejects_bad_arguments():
     lib = cq.load()
     f = lib.cq_proxy_worst_env_wmse_multi

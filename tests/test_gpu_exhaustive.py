@@ -1,4 +1,5 @@
-"""GPU parity: the exhaustive sweep, the baselines, the packer and the proxy against the oracle.
+"""GPU parity: the exhaustive searches (the full grid and the bounded sweep), the baselines, the
+packer and the proxy against the oracle.
 
 Every call goes through the C ABI (libcq.so).  Inputs are the seeded synthetic configs; the
 oracle runs on the host on the same arrays (all groups where it takes seconds, seeded
@@ -11,9 +12,10 @@ import torch
 import oracle
 import post_weight_quantization_group_amd as cq
 import workloads as W
-from parity import bits_np, check_minimax, check_pooled, dev, say, threads
+from parity import bits_np, check_minimax, check_pooled, check_same_result, dev, say, threads
 
 pytestmark = pytest.mark.gpu
+BOTH = pytest.mark.parametrize("method", ["exhaustive", "bounded"])
 
 
 def _run(w, d, d_period, method="exhaustive", pooled=True):
@@ -22,10 +24,11 @@ def _run(w, d, d_period, method="exhaustive", pooled=True):
     return r
 
 
-def test_config0_all_groups():
-    say("config 0: 128 groups, E=4, exhaustive + pooled")
+@BOTH
+def test_config0_all_groups(method):
+    say(f"config 0: 128 groups, E=4, {method} + pooled")
     w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
-    r = _run(w, d, p)
+    r = _run(w, d, p, method)
     sol = oracle.solve(w, d, p, n_threads=threads())
     same, near = check_minimax(w, d, p, r, sol)
     check_pooled(w, d, p, r["pooled_scales"], r["pooled_objective"], sol)
@@ -34,20 +37,22 @@ def test_config0_all_groups():
     say(f"  bits equal {same}/128, near ties {near}, flags {np.bincount(flags)}")
 
 
-def test_pages_example_and_tiny_groups():
+@BOTH
+def test_pages_example_and_tiny_groups(method):
     w, d = W.pages_example()
-    r = _run(w, d, 1)
+    r = _run(w, d, 1, method)
     sol = oracle.solve(w, d)
     check_minimax(w, d, 1, r, sol)
     check_pooled(w, d, 1, r["pooled_scales"], r["pooled_objective"], sol)
     scale, obj, codes = cq.solve_breakpoint_exact([0.9, -0.4, 0.2, -1.1],
                                                   [[1.0, 0.8, 0.5, 1.2], [0.6, 1.4, 0.9, 0.7]],
-                                                  method="exhaustive")
+                                                  method=method)
     assert scale == oracle.fp16_value(sol.mm_bits[0]) and obj == sol.mm_F1[0]
     assert codes == list(sol.codes[0, :4])
 
 
-def test_constructed_ties_and_edge_groups():
+@BOTH
+def test_constructed_ties_and_edge_groups(method):
     """All-zero (0x0001), symmetric pairs (c/2), single weights, a subnormal-scale group."""
     rng = np.random.default_rng(7)
     ws, ds = [], []
@@ -68,7 +73,7 @@ def test_constructed_ties_and_edge_groups():
     d[:, 1] = d[:, 0]
     d[-1, 2] = 0.0
     d[-1, 2, 5] = 128.0
-    r = _run(w, d, n)
+    r = _run(w, d, n, method)
     sol = oracle.solve(w, d, n)
     check_minimax(w, d, n, r, sol)
     check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
@@ -81,10 +86,10 @@ def test_constructed_ties_and_edge_groups():
 
 
 def test_top_pattern_ranges_sliced_and_unsliced():
-    """Where the sweep stops (the first scale >= 2 max|w|): past the grid (2 max|w| > 65504,
-    every pattern screened), in the last binade, in the subnormal range, and after a lone
+    """Where the bounded sweep stops (the first scale >= 2 max|w|): past the grid (2 max|w| >
+    65504, every pattern screened), in the last binade, in the subnormal range, and after a lone
     weight.  Twelve groups go through the sliced path; the same groups tiled to 1,200 go one
-    workgroup each and must give identical results."""
+    workgroup each and must give identical results.  The full grid gives the same on the twelve."""
     rng = np.random.default_rng(23)
     ws = []
     big = rng.normal(0, 3000, 128)
@@ -103,13 +108,14 @@ def test_top_pattern_ranges_sliced_and_unsliced():
     w = W.round_bf16(np.stack(ws).astype(np.float32))
     n = w.shape[0]
     d = rng.lognormal(0, 1, (n, 4, 128)).astype(np.float32)
-    r = _run(w, d, n)
+    r = _run(w, d, n, "bounded")
     sol = oracle.solve(w, d, n, n_threads=threads())
     check_minimax(w, d, n, r, sol)
     check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
+    check_same_result(r, _run(w, d, n, "exhaustive"), "full grid against the bounded sweep")
     reps = 100
     wt, dt = np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1))
-    rt = _run(wt, dt, n * reps)
+    rt = _run(wt, dt, n * reps, "bounded")
     for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
         a = r[key].cpu().numpy()
         b = rt[key].cpu().numpy().reshape((reps,) + a.shape)
@@ -148,7 +154,8 @@ def test_optimum_far_from_the_absmax_scale():
     d = np.stack(ds).astype(np.float32)
     n = w.shape[0]
     say(f"optimum far from max|w|/7: {n} groups, sliced and tiled")
-    r = _run(w, d, n)
+    r = _run(w, d, n, "bounded")
+    check_same_result(r, _run(w, d, n, "exhaustive"), "full grid against the bounded sweep")
     sol = oracle.solve(w, d, n, n_threads=threads())
     check_minimax(w, d, n, r, sol)
     check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
@@ -159,51 +166,53 @@ def test_optimum_far_from_the_absmax_scale():
     torch.cuda.synchronize()
     check_minimax(w, d, n, c, sol)
     reps = 100
-    rt = _run(np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1)), n * reps)
+    rt = _run(np.tile(w, (reps, 1)), np.tile(d, (reps, 1, 1)), n * reps, "bounded")
     for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
         a = r[key].cpu().numpy()
         b = rt[key].cpu().numpy().reshape((reps,) + a.shape)
         assert np.all(b == a[None]), key
 
 
-def test_thirty_two_environments_both_methods():
-    """E = 32, the largest environment count: exhaustive (minimax and pooled) and candidate
-    against the oracle on 16 groups with per-group diagonals."""
+def test_thirty_two_environments_every_method():
+    """E = 32, the largest environment count: the full grid and the bounded sweep (minimax and
+    pooled) and the candidate solver against the oracle on 16 groups with per-group diagonals."""
     rng = np.random.default_rng(31)
     n = 16
     w = W.round_bf16(rng.normal(0, 0.03, (n, 128)).astype(np.float32))
     w[::5, 7] *= 8.0
     d = rng.lognormal(0, 1.2, (n, 32, 128)).astype(np.float32)
     sol = oracle.solve(w, d, n, n_threads=threads())
-    r = _run(w, d, n)
-    check_minimax(w, d, n, r, sol)
-    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
+    for method in ("exhaustive", "bounded"):
+        r = _run(w, d, n, method)
+        check_minimax(w, d, n, r, sol)
+        check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol)
     c = _run(w, d, n, method="candidate", pooled=False)
     check_minimax(w, d, n, c, sol)
 
 
 def test_batch_sizes_around_the_slicing_switch():
-    """1,023 groups run sliced, 1,024 and 1,025 one workgroup each: every batch gives bit for bit
-    what the same groups give inside one full-matrix run."""
+    """Bounded sweep: 1,023 groups run sliced, 1,024 and 1,025 one workgroup each: every batch
+    gives bit for bit what the same groups give inside one full-matrix run."""
     w, d, p = W.matrix_groups(*W.make_matrix(1, 0))
-    full = _run(w, d, p)
+    full = _run(w, d, p, "bounded")
     for n in (1023, 1024, 1025):
         # keep whole d periods so that every group sees its own diagonal slice
-        r = _run(w[:n], d, p)
+        r = _run(w[:n], d, p, "bounded")
         for key in ("scales", "objective", "flags", "pooled_scales", "pooled_objective", "codes"):
             a = r[key].cpu().numpy()
             b = full[key].cpu().numpy()[:n]
             assert np.array_equal(a, b), (n, key)
 
 
-def test_bad_inputs_are_flagged():
+@BOTH
+def test_bad_inputs_are_flagged(method):
     rng = np.random.default_rng(3)
     w = rng.normal(0, 0.02, (4, 128)).astype(np.float32)
     d = rng.lognormal(0, 1, (4, 2, 128)).astype(np.float32)
     w[1, 3] = np.nan
     d[2, 1, 7] = -1.0
     w[3, 0] = np.inf
-    r = _run(w, d, 4)
+    r = _run(w, d, 4, method)
     flags = r["flags"].cpu().numpy()
     assert list(flags & cq.FLAG_BAD_INPUT) == [0, 1, 1, 1]
     assert list(bits_np(r["scales"])[1:]) == [0, 0, 0]
@@ -212,7 +221,8 @@ def test_bad_inputs_are_flagged():
     assert bits_np(r["scales"])[0] == sol.mm_bits[0]
 
 
-def test_fp64_sweep_path_matches_oracle():
+@BOTH
+def test_fp64_sweep_path_matches_oracle(method):
     """Groups outside the binary32 screen's guaranteed range (a diagonal entry of 1e-38, a
     weight 2^-60 next to ordinary ones) are decided by the full binary64 sweep."""
     rng = np.random.default_rng(11)
@@ -220,7 +230,7 @@ def test_fp64_sweep_path_matches_oracle():
     d = rng.lognormal(0, 1, (3, 4, 128)).astype(np.float32)
     d[0, 1, 3] = 1e-38
     w[1, 9] = 2.0 ** -60
-    r = _run(w, d, 3)
+    r = _run(w, d, 3, method)
     sol = oracle.solve(w, d, 3)
     check_minimax(w, d, 3, r, sol)
     check_pooled(w, d, 3, r["pooled_scales"], r["pooled_objective"], sol)
@@ -229,15 +239,17 @@ def test_fp64_sweep_path_matches_oracle():
     assert not flags[2] & cq.FLAG_FP64_SWEEP
 
 
-def test_empty_batch():
+@pytest.mark.parametrize("method", ["exhaustive", "bounded", "candidate"])
+def test_empty_batch(method):
     w = torch.zeros((0, 128), dtype=torch.float32, device="cuda")
     d = torch.ones((1, 4, 128), dtype=torch.float32, device="cuda")
-    r = cq.quantize_groups(w, d, 1)
+    r = cq.quantize_groups(w, d, 1, method=method)
     torch.cuda.synchronize()
     assert r["scales"].numel() == 0
 
 
-def test_config1_full_size_sampled():
+@BOTH
+def test_config1_full_size_sampled(method):
     """Config 1 at full size (the benchmark's launch configuration, one call per matrix); the
     oracle checks a seeded sample of 192 groups; properties checked on every group."""
     spec = W.config(1)
@@ -248,7 +260,7 @@ def test_config1_full_size_sampled():
         w, d, p = W.matrix_groups(A, dm)
         say(f"config 1 {mat.name}: {w.shape[0]} groups")
         wt, dt = dev(w), dev(d)
-        r = cq.quantize_groups(wt, dt, p, pooled=True)
+        r = cq.quantize_groups(wt, dt, p, method=method, pooled=True)
         ab = cq.baseline_scales(wt, dt, p, "absmax")
         torch.cuda.synchronize()
         # properties on every group
@@ -308,10 +320,11 @@ def test_absmax_objective_every_env_count(E):
     np.testing.assert_array_equal(ab0["codes"].cpu().numpy(), ab["codes"].cpu().numpy())
 
 
-def test_pooled_baseline_entry_matches_fused():
+@BOTH
+def test_pooled_baseline_entry_matches_fused(method):
     w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
     wt, dt = dev(w), dev(d)
-    r = cq.quantize_groups(wt, dt, p, pooled=True)
+    r = cq.quantize_groups(wt, dt, p, method=method, pooled=True)
     b = cq.baseline_scales(wt, dt, p, "pooled")
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits_np(b["scales"]), bits_np(r["pooled_scales"]))
@@ -331,6 +344,50 @@ def test_pack_matches_oracle():
         rq, rs = oracle.pack_gptq_v1(codes, sb, out, inp)
         np.testing.assert_array_equal(qw.cpu().numpy(), rq)
         np.testing.assert_array_equal(bits_np(sc), rs)
+
+
+def test_pack_multi_matches_oracle_per_matrix():
+    """Several matrices in one launch, back to back: ragged row counts (a partial 64-row tile, one
+    row), an empty matrix, and config 2's shapes; every block equals the oracle's packing of that
+    matrix alone."""
+    rng = np.random.default_rng(41)
+    shapes = [(809, 4096), (0, 256), (64, 256), (803, 4096), (65, 128), (1, 384), (809, 4096)]
+    codes = [rng.integers(-8, 8, (o, i)).astype(np.int8) for o, i in shapes]
+    sbits = [rng.integers(1, 0x7C00, (o, i // 128)).astype(np.uint16) for o, i in shapes]
+    flat_c = np.concatenate([c.ravel() for c in codes])
+    flat_s = np.concatenate([b.ravel() for b in sbits])
+    qw, sc = cq.pack_gptq_v1_multi(dev(flat_c), dev(flat_s.view(np.int16)), shapes)
+    torch.cuda.synchronize()
+    qw, sc = qw.cpu().numpy(), bits_np(sc)
+    eq = es = 0
+    for (o, i), c, b in zip(shapes, codes, sbits):
+        rq, rs = oracle.pack_gptq_v1(c, b, o, i)
+        np.testing.assert_array_equal(qw[eq:eq + o * i // 8].reshape(i // 8, o), rq)
+        np.testing.assert_array_equal(sc[es:es + o * i // 128].reshape(i // 128, o), rs)
+        eq += o * i // 8
+        es += o * i // 128
+    assert eq == qw.size and es == sc.size
+
+
+def test_pack_multi_all_of_config2_equals_per_matrix_calls():
+    """All 150 matrices of config 2 (3,883,008 groups) in one launch against 150 single-matrix calls."""
+    spec = W.config(2)
+    shapes = [(m.out, m.inp) for m in spec.matrices]
+    n_el = sum(o * i for o, i in shapes)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    codes = torch.randint(-8, 8, (n_el,), dtype=torch.int8, device="cuda", generator=g)
+    sc16 = torch.randint(1, 0x7C00, (n_el // 128,), dtype=torch.int16, device="cuda", generator=g)
+    qw, sc = cq.pack_gptq_v1_multi(codes, sc16, shapes)
+    eq = es = ec = 0
+    for o, i in shapes:
+        q1, s1 = cq.pack_gptq_v1(codes[ec:ec + o * i].reshape(o, i), sc16[ec // 128:(ec + o * i) // 128].reshape(o, i // 128),
+                                 o, i)
+        assert torch.equal(qw[eq:eq + o * i // 8], q1.reshape(-1))
+        assert torch.equal(sc[es:es + o * i // 128], s1.reshape(-1))
+        eq += o * i // 8
+        es += o * i // 128
+        ec += o * i
+    torch.cuda.synchronize()
 
 
 def test_proxy_matches_oracle():
@@ -379,9 +436,10 @@ def test_proxy_multi_matches_single_calls_and_oracle(E, n_pol):
         assert np.isnan(macro[k]) and np.isnan(mac1.cpu().item()) and np.isnan(rmac)
 
 
-def test_repeatable():
+@BOTH
+def test_repeatable(method):
     w, d, p = W.matrix_groups(*W.make_matrix(0, 0))
-    a = _run(w, d, p)
-    b = _run(w, d, p)
+    a = _run(w, d, p, method)
+    b = _run(w, d, p, method)
     for k in ("scales", "codes", "objective", "flags", "pooled_scales", "pooled_objective"):
         assert torch.equal(a[k], b[k]), k
