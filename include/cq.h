@@ -67,6 +67,7 @@ extern "C" {
 #define CQ_EWORKSPACE (-2)   /* workspace missing, misaligned or too small */
 #define CQ_EHIP (-3)         /* a HIP launch failed (hipGetLastError) */
 #define CQ_EUNSUPPORTED (-4) /* valid arguments this entry point does not serve */
+#define CQ_ELIMIT (-5)       /* more groups than cq_quantize_groups_noalloc's fixed scratch holds */
 
 /* Solvers (cq_quantize_groups `method`); all three return the same result.
  *  CQ_EXHAUSTIVE  the independent full-grid enumerator (README, "What CliffQuant changes": a
@@ -152,6 +153,22 @@ int32_t cq_quantize_groups_spec(const float *w, const float *d, int32_t group_le
                                 uint16_t *scales, int8_t *codes, double *objective, uint8_t *flags,
                                 uint16_t *pooled_scales, double *pooled_objective,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cq_quantize_groups for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments without
+ * the workspace, and the same results.  The scratch space lives in a fixed array of the library
+ * on each GPU (about 12.6 MB, held until the process ends), found at the first call on that
+ * device; the call itself allocates nothing.
+ *   n_groups  0..CQ_NOALLOC_MAX_GROUPS, else CQ_ELIMIT before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array; the kernels clear what must start at zero,
+ * but calls that overlap on one GPU (other streams, other host threads) race.
+ */
+#define CQ_NOALLOC_MAX_GROUPS (1 << 20)
+int32_t cq_quantize_groups_noalloc(const float *w, const float *d, int64_t d_period, int32_t E,
+                                   int64_t n_groups, int32_t method,
+                                   uint16_t *scales, int8_t *codes, double *objective, uint8_t *flags,
+                                   uint16_t *pooled_scales, double *pooled_objective, void *stream);
 
 /*
  * Baseline scale policies.

@@ -27,7 +27,8 @@ __all__ = [
     "CQError", "GROUP", "MAX_GROUP", "EXHAUSTIVE", "CANDIDATE", "BOUNDED", "ABSMAX", "POOLED_WMSE",
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
-    "cq_quantize_groups", "cq_quantize_groups_spec", "cq_baseline_scales", "cq_pack_gptq_v1",
+    "cq_quantize_groups", "cq_quantize_groups_spec", "cq_quantize_groups_noalloc", "cq_baseline_scales",
+    "cq_pack_gptq_v1",
     "cq_pack_gptq_v1_multi", "pack_gptq_v1_multi", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
@@ -42,7 +43,7 @@ ABSMAX, POOLED_WMSE = 0, 1
 FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 1, 2, 4, 8, 16
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE, "bounded": BOUNDED}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
-                    "cq_quantize_groups_spec",
+                    "cq_quantize_groups_spec", "cq_quantize_groups_noalloc",
                     "cq_baseline_scales", "cq_pack_gptq_v1", "cq_pack_gptq_v1_multi", "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
@@ -80,6 +81,8 @@ def load():
         lib.cq_workspace_size.argtypes = [I32, I32, I64]
         lib.cq_quantize_groups.restype = I32
         lib.cq_quantize_groups.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, P, P, P, SZ, P]
+        lib.cq_quantize_groups_noalloc.restype = I32
+        lib.cq_quantize_groups_noalloc.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, P, P, P]
         lib.cq_quantize_groups_spec.restype = I32
         lib.cq_quantize_groups_spec.argtypes = [P, P, I32, I32, I32, I64, I32, I64, I32, P, P, P, P, P, P, P, SZ, P]
         lib.cq_baseline_scales.restype = I32
@@ -158,6 +161,13 @@ def cq_quantize_groups(w, d, d_period, E, n_groups, method, scales, codes=None, 
     _check(load().cq_quantize_groups(_p(w), _p(d), d_period, E, n_groups, method, _p(scales), _p(codes),
                                      _p(objective), _p(flags), _p(pooled_scales), _p(pooled_objective),
                                      _p(workspace), ws_bytes, _stream(stream)), "cq_quantize_groups")
+
+
+def cq_quantize_groups_noalloc(w, d, d_period, E, n_groups, method, scales, codes=None, objective=None, flags=None,
+                               pooled_scales=None, pooled_objective=None, stream=None):
+    _check(load().cq_quantize_groups_noalloc(_p(w), _p(d), d_period, E, n_groups, method, _p(scales), _p(codes),
+                                             _p(objective), _p(flags), _p(pooled_scales), _p(pooled_objective),
+                                             _stream(stream)), "cq_quantize_groups_noalloc")
 
 
 def cq_quantize_groups_spec(w, d, group_len, qmin, qmax, d_period, E, n_groups, method, scales, codes=None,

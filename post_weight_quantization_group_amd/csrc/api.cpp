@@ -61,6 +61,7 @@ const char* cq_status_string(int32_t s) {
         case CQ_EWORKSPACE: return "workspace missing, misaligned or too small";
         case CQ_EHIP: return "HIP launch failed";
         case CQ_EUNSUPPORTED: return "not supported by this entry point";
+        case CQ_ELIMIT: return "more groups than the fixed scratch of the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
