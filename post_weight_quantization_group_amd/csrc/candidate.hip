@@ -774,10 +774,11 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
 }
 
-// Workgroups per CU.  Up to E = 4, six fit the LDS (25.7 KB each at E = 4, with the unions in
-// CandSmem) and run 2% faster than five (five beat four by 11%) on gfx950; at E = 16 three (with
-// some spills) beat two by 13%.
-constexpr int cand_min_blocks(int E) { return E <= 4 ? 6 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
+// Workgroups per CU.  Up to E = 4 five (94 registers, no spills; five beat four by 11% on
+// gfx950).  Six fit the LDS too (25.7 KB each at E = 4, with the unions in CandSmem) and ran 2%
+// faster, but only by spilling 24 registers to scratch, about 370 MB of write traffic per
+// 28,672-group launch.  At E = 16 three (with some spills) beat two by 13%.
+constexpr int cand_min_blocks(int E) { return E <= 4 ? 5 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
 
 template <int E>
 __global__ __launch_bounds__(BLOCK, cand_min_blocks(E)) void candidate_kernel(CandArgs a, int64_t group_offset) {
