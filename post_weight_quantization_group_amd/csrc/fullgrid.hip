@@ -61,6 +61,13 @@ constexpr int ns_for(int E) { return E <= 4 ? 8 : 32 / E; }
 constexpr int chunk_for(int E) { return 64 * ns_for(E); }
 constexpr int nchunk_for(int E) { return ((int)N_SCALES + chunk_for(E) - 1) / chunk_for(E); }
 constexpr int CAP = 256;                                // shortlist capacity per group
+// The screen's LDS row of a weight: the pre-scaled weight, then from float doff_for(E) its E
+// diagonals; one address serves a weight and its diagonals.  The vector path reads the diagonals
+// as 16-byte broadcasts (offset 4, rows of a multiple of four floats); the matrix-core path
+// (E >= 16) reads one float per lane, so its rows are packed (offset 1), which keeps six
+// workgroups per CU within the LDS at E = 16.
+constexpr int doff_for(int E) { return E >= 16 ? 1 : 4; }
+constexpr int row_for(int E) { return E < 4 ? 8 : E + doff_for(E); }
 constexpr int GMAX = 256;                               // longest group
 constexpr uint8_t TAG_MINIMAX = 1, TAG_POOLED = 2;
 
@@ -78,8 +85,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 template <int E>
 struct Smem {
     float w[GMAX];                  // the weights as given (rescoring, codes)
-    __align__(16) float wp[GMAX];   // pre-scaled by 2^k (screen)
-    __align__(16) float dt[GMAX * E];  // [i][e]
+    // row i: w'_i = w_i 2^k (the screen's weight), zeros up to doff_for(E), then d[0..E-1][i] (the
+    // environments past the call's E and the padding of E < 4 are zeros)
+    __align__(16) float rows[GMAX * row_for(E)];
     float redf[4 * 8];
     uint64_t redk[4 * 4];
     uint32_t cand_b[CAP];
@@ -117,15 +125,17 @@ __device__ __forceinline__ float in_vgpr(float x) {
 // One chunk: every lane runs the n weights against its NS scales, the per-environment sums in
 // registers.  The weight and its E diagonals are LDS broadcasts shared by the NS scales.
 template <int E, int NS, bool CLIP>
-__device__ __forceinline__ void chunk_terms(const float* __restrict__ wp, const float* __restrict__ dt, int n,
+__device__ __forceinline__ void chunk_terms(const float* __restrict__ rows, int n,
                                             const float (&nsv)[NS], const float (&inv)[NS], float qlo, float qhi,
                                             float (&acc)[NS][E]) {
-#pragma unroll 2
+    constexpr int RS = row_for(E);
+#pragma unroll 4
     for (int i = 0; i < n; ++i) {
-        const float wi = wp[i];
+        const float* row = rows + i * RS;
+        const float wi = row[0];
         float di[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) di[e] = dt[i * E + e];
+        for (int e = 0; e < E; ++e) di[e] = row[doff_for(E) + e];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const float x = wi * inv[t];
@@ -146,15 +156,17 @@ __device__ __forceinline__ void chunk_terms(const float* __restrict__ wp, const 
 // vector path, one fused multiply-add per term, and the vector unit is left the quotient, the
 // rounding, the clip, the residual and the square.
 template <int E, int NS, bool CLIP>
-__device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ wp, const float* __restrict__ dt, int n,
+__device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, int n,
                                                const float (&nsv)[NS], const float (&inv)[NS], float qlo,
                                                float qhi, int lane4, v4f (&acc)[NS][E / 4]) {
+    constexpr int RS = row_for(E);
 #pragma unroll 2
     for (int i = 0; i < n; ++i) {
-        const float wi = wp[i];
+        const float* row = rows + i * RS;
+        const float wi = row[0];
         float dl[E / 4];
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k) dl[k] = dt[i * E + 4 * k + lane4];
+        for (int k = 0; k < E / 4; ++k) dl[k] = row[doff_for(E) + 4 * k + lane4];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const float x = wi * inv[t];
@@ -179,7 +191,7 @@ __device__ void rescore(Smem<E>& sm, int n, int G, int E_real, double qlo, doubl
         if (t < nb * E) {
             const int j = base + t / E, e = t % E;
             const double s = (double)half_bits_value(sm.cand_b[j]);
-            sm.pairF[t] = env_error_f64_n(sm.w, sm.dt + e, E, G, s, 1.0 / s, qlo, qhi);
+            sm.pairF[t] = env_error_f64_n(sm.w, sm.rows + doff_for(E) + e, row_for(E), G, s, 1.0 / s, qlo, qhi);
         }
         __syncthreads();
         if (t < nb) {
@@ -251,10 +263,11 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
 
     // ---- staging (environments a.E..E-1 are zero padding)
+    constexpr int RS = row_for(E);
     for (int i = tid; i < G; i += BLOCK) sm.w[i] = wg[i];
-    for (int j = tid; j < E * G; j += BLOCK) {
-        const int e = j / G, i = j - e * G;
-        sm.dt[i * E + e] = e < a.E ? dg[j] : 0.0f;
+    for (int j = tid; j < G * RS; j += BLOCK) {
+        const int i = j / RS, f = j - i * RS, e = f - doff_for(E);
+        sm.rows[j] = (e >= 0 && e < a.E) ? dg[(int64_t)e * G + i] : 0.0f;
     }
     __syncthreads();
 
@@ -269,8 +282,8 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
         v[3] = fmaxf(v[3], -x);
         if (ax > 0.0f) v[4] = fmaxf(v[4], -ax);
     }
-    for (int j = tid; j < E * G; j += BLOCK) {
-        const float x = sm.dt[j];
+    for (int j = tid; j < G * RS; j += BLOCK) {
+        const float x = sm.rows[j];  // the weight slots are still zero here
         if (!(x >= 0.0f) || !__builtin_isfinite(x)) v[0] = 1.0f;
         else {
             v[5] = fmaxf(v[5], x);
@@ -313,7 +326,7 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
         return;
     }
     const float pk = ldexpf(1.0f, k);
-    for (int i = tid; i < G; i += BLOCK) sm.wp[i] = sm.w[i] * pk;
+    for (int i = tid; i < G; i += BLOCK) sm.rows[i * RS] = sm.w[i] * pk;
     if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
     __syncthreads();
 
@@ -336,7 +349,10 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
             const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
             const float s = half_bits_value(b) * pk;
             nsv[t] = -s;
-            inv[t] = 1.0f / s;
+            // hardware reciprocal and one Newton step: within one binary32 rounding of 1/s, the
+            // accuracy the error bound assumes
+            const float r0 = __builtin_amdgcn_rcpf(s);
+            inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
         }
         const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
         if constexpr (use_mfma(E)) {
@@ -346,9 +362,9 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
 #pragma unroll
                 for (int k = 0; k < E / 4; ++k) am[t][k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
             if (cmax <= s0)
-                chunk_terms_mf<E, NS, false>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, lane & 3, am);
+                chunk_terms_mf<E, NS, false>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
             else
-                chunk_terms_mf<E, NS, true>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, lane & 3, am);
+                chunk_terms_mf<E, NS, true>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
 #pragma unroll
             for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -359,9 +375,9 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
             if (cmax <= s0)
-                chunk_terms<E, NS, false>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, acc);
+                chunk_terms<E, NS, false>(sm.rows, G, nsv, inv, qlo, qhi, acc);
             else
-                chunk_terms<E, NS, true>(sm.wp, sm.dt, G, nsv, inv, qlo, qhi, acc);
+                chunk_terms<E, NS, true>(sm.rows, G, nsv, inv, qlo, qhi, acc);
         }
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
