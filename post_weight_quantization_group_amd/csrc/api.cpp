@@ -45,6 +45,7 @@ int32_t run_fullgrid(const float* w, const float* d, int32_t G, int32_t qmin, in
     a.want_pooled = (pooled_scales || pooled_objective) ? 1 : 0;
     a.fb_count = (int32_t*)ws;
     a.fb_list = (int32_t*)(ws + ALIGN);
+    a.parts = (cqk::SlicePart*)(ws + full_ws(n_groups));  // the workspace is sweep_ws(n_groups) bytes
     return hip_status(cqk::launch_fullgrid(a, E, n_groups, st));
 }
 

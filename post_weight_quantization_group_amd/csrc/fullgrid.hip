@@ -97,6 +97,9 @@ struct Smem {
     double pairF[BLOCK];
     int n_cand;
     int overflow;
+    int n_key[2];                   // slices: keys stored per policy
+    uint32_t ov_bits[2];            // slices: the smallest value not kept (binary32 bits)
+    float thr[2];                   // each policy's shortlist threshold (-1: decided by the zero rule)
     uint32_t win_b[2];
     double win_F[2];
     uint8_t win_flags[2];
@@ -255,8 +258,11 @@ __device__ __forceinline__ void queue_f64(const FullArgs& a, int64_t g) {
     a.fb_list[j] = (int32_t)g;
 }
 
+// Staging and input checks for group g: w and the screen rows into LDS, the pre-scale 2^k and the
+// chunk clip threshold.  Returns 0 (screen it), 1 (a non-finite or negative input) or 2 (outside
+// the binary32 screen's guaranteed range).  Every workgroup of a group computes the same.
 template <int E>
-__device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
+__device__ int stage_group(const FullArgs& a, int64_t g, Smem<E>& sm, float& pk_out, float& cmax_out) {
     const int tid = threadIdx.x;
     const int G = a.G;
     const float* wg = a.w + g * G;
@@ -291,19 +297,7 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
         }
     }
     block_max_fn<7>(v, sm.redf);
-    const bool bad = v[0] != 0.0f;
-    if (bad) {
-        for (int i = tid; i < G; i += BLOCK)
-            if (a.codes) a.codes[g * G + i] = 0;
-        if (tid == 0) {
-            if (a.scales) a.scales[g] = 0;
-            if (a.objective) a.objective[g] = __builtin_nan("");
-            if (a.pscales) a.pscales[g] = 0;
-            if (a.pobjective) a.pobjective[g] = __builtin_nan("");
-            if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
-        }
-        return;
-    }
+    if (v[0] != 0.0f) return 1;
     const float wmax = v[1], wpos = v[2], wneg = v[3], wmin_nz = -v[4], dmax = v[5], dmin_nz = -v[6];
 
     // ---- power-of-two pre-scaling and the no-underflow / no-overflow guarantee: every nonzero
@@ -321,26 +315,49 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
         const double e2 = elb * elb;
         safe = safe && e2 >= 0x1p-120 && (dmin_nz == __builtin_inff() || (double)dmin_nz * e2 >= 0x1p-120);
     }
-    if (!safe) {
-        if (tid == 0) queue_f64(a, g);
-        return;
-    }
+    if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
     for (int i = tid; i < G; i += BLOCK) sm.rows[i * RS] = sm.w[i] * pk;
-    if (tid == 0) { sm.n_cand = 0; sm.overflow = 0; }
+    if (tid == 0) {
+        sm.n_cand = 0;
+        sm.overflow = 0;
+        sm.n_key[0] = sm.n_key[1] = 0;
+        sm.ov_bits[0] = sm.ov_bits[1] = 0xFFFFFFFFu;
+    }
     __syncthreads();
-
-    // ---- binary32 screen over all 31,743 scales
-    const int lane = tid & 63, wave = tid >> 6;
-    const float qlo = in_vgpr((float)a.qmin), qhi = in_vgpr((float)a.qmax);
     // no weight clips in a chunk whose smallest scale s0 has w+ <= (qmax + 1/4) s0 and
     // w- <= (-qmin + 1/4) s0: |x~| stays below the range end plus 1/2
     const float cpos = wpos * pk / ((float)a.qmax + 0.25f), cneg = wneg * pk / (0.25f - (float)a.qmin);
-    const float cmax = fmaxf(cpos, cneg) * (1.0f + 0x1p-20f);
+    cmax_out = fmaxf(cpos, cneg) * (1.0f + 0x1p-20f);
+    pk_out = pk;
+    return 0;
+}
+
+// The outputs of a group with a non-finite or negative input.
+__device__ void write_bad(const FullArgs& a, int64_t g) {
+    const int tid = threadIdx.x;
+    if (a.codes)
+        for (int i = tid; i < a.G; i += BLOCK) a.codes[g * a.G + i] = 0;
+    if (tid == 0) {
+        if (a.scales) a.scales[g] = 0;
+        if (a.objective) a.objective[g] = __builtin_nan("");
+        if (a.pscales) a.pscales[g] = 0;
+        if (a.pobjective) a.pobjective[g] = __builtin_nan("");
+        if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
+    }
+}
+
+// The binary32 screen of the chunks c with (c / 4) % S == slice (all of them when S = 1): every
+// lane's best three (value, pattern) keys per policy.
+template <int E>
+__device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax, int slice, int S,
+                            uint64_t (&mk)[3], uint64_t (&qk)[3]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, G = a.G;
+    const float qlo = in_vgpr((float)a.qmin), qhi = in_vgpr((float)a.qmax);
     constexpr int NS = ns_for(E), CHUNK = chunk_for(E), NCHUNK = nchunk_for(E);
-    uint64_t mk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
-    uint64_t qk[3] = {KEY_NONE, KEY_NONE, KEY_NONE};
-    for (int c = wave; c < NCHUNK; c += BLOCK / 64) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
+    for (int c = wave + 4 * slice; c < NCHUNK; c += 4 * S) {
         float nsv[NS], inv[NS];
         float acc[NS][E];
         const int rot = (lane + 5 * c) & 63;
@@ -394,46 +411,18 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
             if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
         }
     }
+}
 
-    // ---- each policy's smallest key, its runner-up, and the shortlist
-    uint64_t kv[2] = {mk[0], qk[0]};
-    block_min_u64n<2>(kv, sm.redk);
-    uint64_t kv2[2] = {mk[0] == kv[0] ? mk[1] : mk[0], qk[0] == kv[1] ? qk[1] : qk[0]};
-    block_min_u64n<2>(kv2, sm.redk + 8);
-    for (int pol = 0; pol < 2; ++pol) {
-        const bool want = pol == 0 ? a.want_minimax : a.want_pooled;
-        if (!want) continue;
-        const uint64_t* kk = pol == 0 ? mk : qk;
-        const uint8_t tag = pol == 0 ? TAG_MINIMAX : TAG_POOLED;
-        const uint64_t M1 = kv[pol], S2 = kv2[pol];
-        const float m = key_value(M1);
-        if (m == 0.0f) {
-            // a zero binary32 value is exact: the lowest such pattern wins, value 0
-            if (tid == 0) {
-                sm.win_b[pol] = key_bits(M1);
-                sm.win_F[pol] = 0.0;
-                sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
-            }
-        } else {
-            const float T = m * a.ratio;
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
-                    if (r == 2) sm.overflow = 1;
-                    else append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(kk[r]), tag);
-                }
-            }
-            if (tid == 0) sm.win_b[pol] = 0xFFFFFFFFu;  // decided by rescoring
-        }
-    }
-    __syncthreads();
+// After the shortlist (sm.cand_*, sm.n_cand, sm.overflow, and win_b of the zero rule): the binary64
+// sweep when the screen was inconclusive, else rescoring, the lower-bit-pattern rule and outputs.
+template <int E>
+__device__ void decide_and_write(const FullArgs& a, int64_t g, Smem<E>& sm) {
+    const int tid = threadIdx.x, wave = tid >> 6, G = a.G;
     const int n = sm.n_cand;
     if (sm.overflow || n > CAP) {
         if (tid == 0) queue_f64(a, g);
         return;
     }
-
-    // ---- binary64 rescoring and the lower-bit-pattern rule
     rescore<E>(sm, n, G, a.E, (double)a.qmin, (double)a.qmax);
     if (wave < 2) {
         const bool want = wave == 0 ? a.want_minimax : a.want_pooled;
@@ -441,8 +430,6 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
             pick_winner<E>(sm, n, wave == 0 ? TAG_MINIMAX : TAG_POOLED, wave);
     }
     __syncthreads();
-
-    // ---- outputs
     const float fqlo = (float)a.qmin, fqhi = (float)a.qmax;
     const int cp = a.want_minimax ? 0 : 1;  // the policy whose codes are written
     const float sc = half_bits_value(sm.win_b[cp]);
@@ -462,10 +449,164 @@ __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
     }
 }
 
+// The zero rule or the shortlist threshold of one policy from its smallest key M1 and runner-up
+// S2: a zero binary32 value is exact (every term is normal or zero), so the lowest such pattern
+// wins with value 0; otherwise every key within the ratio of M1 is rescored.  Thread 0 only.
+template <int E>
+__device__ float policy_threshold(const FullArgs& a, Smem<E>& sm, int pol, uint64_t M1, uint64_t S2) {
+    const float m = key_value(M1);
+    if (m == 0.0f) {
+        sm.win_b[pol] = key_bits(M1);
+        sm.win_F[pol] = 0.0;
+        sm.win_flags[pol] = (S2 != KEY_NONE && key_value(S2) == 0.0f) ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0;
+        return -1.0f;  // nothing to rescore
+    }
+    sm.win_b[pol] = 0xFFFFFFFFu;  // decided by rescoring
+    return m * a.ratio;
+}
+
+// One workgroup per group: the whole grid, the shortlist from every lane's keys, the decision.
+template <int E>
+__device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
+    const int tid = threadIdx.x;
+    float pk, cmax;
+    const int st = stage_group<E>(a, g, sm, pk, cmax);
+    if (st == 1) { write_bad(a, g); return; }
+    if (st == 2) { if (tid == 0) queue_f64(a, g); return; }
+    uint64_t mk[3], qk[3];
+    screen_keys<E>(a, sm, pk, cmax, 0, 1, mk, qk);
+
+    // ---- each policy's smallest key, its runner-up, and the shortlist
+    uint64_t kv[2] = {mk[0], qk[0]};
+    block_min_u64n<2>(kv, sm.redk);
+    uint64_t kv2[2] = {mk[0] == kv[0] ? mk[1] : mk[0], qk[0] == kv[1] ? qk[1] : qk[0]};
+    block_min_u64n<2>(kv2, sm.redk + 8);
+    if (tid == 0) {
+        for (int pol = 0; pol < 2; ++pol)
+            if (pol == 0 ? a.want_minimax : a.want_pooled) sm.thr[pol] = policy_threshold<E>(a, sm, pol, kv[pol], kv2[pol]);
+    }
+    __syncthreads();
+    for (int pol = 0; pol < 2; ++pol) {
+        if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
+        const uint64_t* kk = pol == 0 ? mk : qk;
+        const float T = sm.thr[pol];
+        if (T < 0.0f) continue;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
+                if (r == 2) sm.overflow = 1;
+                else append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(kk[r]), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
+            }
+        }
+    }
+    __syncthreads();
+    decide_and_write<E>(a, g, sm);
+}
+
 template <int E>
 __global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void full_screen_kernel(FullArgs a) {
     __shared__ Smem<E> sm;
     screen_group<E>(a, (int64_t)blockIdx.x + a.group_offset, sm);
+}
+
+// ------------------------------------------------------------------ few groups: slices
+// Below about a thousand groups one workgroup per group leaves most CUs idle, so a group's chunks
+// are split over S workgroups (slices).  Slice s screens the chunks c with (c / 4) % S == s and
+// leaves in its SlicePart, per policy: its smallest and second keys; every key within the ratio
+// of its own smallest (up to SLICE_KEYS); and the smallest value it could not keep (a lane's third
+// key within that ratio, which may hide a fourth; or its smallest value when the keys overflowed).
+// The merge takes the group's smallest key over the slices: the global threshold is no larger than
+// any slice's, so every key within it is stored unless a slice's unkept value lies within it too,
+// which sends the group to the binary64 sweep.
+template <int E>
+__global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void full_slice_kernel(FullArgs a) {
+    __shared__ Smem<E> sm;
+    const int S = a.slices, tid = threadIdx.x;
+    const int64_t g = (int64_t)blockIdx.x / S;
+    const int slice = (int)(blockIdx.x % S);
+    SlicePart& P = a.parts[blockIdx.x];
+    float pk, cmax;
+    if (stage_group<E>(a, g, sm, pk, cmax) != 0) return;  // the merge stages the group again
+    uint64_t mk[3], qk[3];
+    screen_keys<E>(a, sm, pk, cmax, slice, S, mk, qk);
+    uint64_t kv[2] = {mk[0], qk[0]};
+    block_min_u64n<2>(kv, sm.redk);
+    uint64_t kv2[2] = {mk[0] == kv[0] ? mk[1] : mk[0], qk[0] == kv[1] ? qk[1] : qk[0]};
+    block_min_u64n<2>(kv2, sm.redk + 8);
+#pragma unroll
+    for (int pol = 0; pol < 2; ++pol) {
+        const uint64_t* kk = pol == 0 ? mk : qk;
+        const float T = key_value(kv[pol]) * a.ratio;  // 0 when the slice's smallest value is 0
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            if (kk[r] != KEY_NONE && key_value(kk[r]) <= T) {
+                if (r == 2) {
+                    atomicMin(&sm.ov_bits[pol], __float_as_uint(key_value(kk[r])));
+                } else {
+                    const int j = atomicAdd(&sm.n_key[pol], 1);
+                    if (j < SLICE_KEYS) P.keys[pol][j] = kk[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        P.status = 0;
+#pragma unroll
+        for (int pol = 0; pol < 2; ++pol) {
+            const int n = sm.n_key[pol];
+            P.n[pol] = (uint32_t)(n < SLICE_KEYS ? n : SLICE_KEYS);
+            // keys lost to the list's capacity: no stored value above the slice's smallest is sure
+            P.ov[pol] = n > SLICE_KEYS ? __float_as_uint(key_value(kv[pol])) : sm.ov_bits[pol];
+            P.m1[pol] = kv[pol];
+            P.s2[pol] = kv2[pol];
+        }
+    }
+}
+
+template <int E>
+__global__ __launch_bounds__(BLOCK) void full_merge_kernel(FullArgs a) {
+    __shared__ Smem<E> sm;
+    const int S = a.slices, tid = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    float pk, cmax;
+    const int st = stage_group<E>(a, g, sm, pk, cmax);
+    if (st == 1) { write_bad(a, g); return; }
+    if (st == 2) { if (tid == 0) queue_f64(a, g); return; }
+    const SlicePart* parts = a.parts + g * S;
+    if (tid == 0) {
+        for (int pol = 0; pol < 2; ++pol) {
+            if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
+            // the group's smallest key and runner-up over the slices
+            uint64_t M1 = KEY_NONE, S2 = KEY_NONE;
+            for (int s = 0; s < S; ++s) {
+                const uint64_t m = parts[s].m1[pol], m2 = parts[s].s2[pol];
+                if (m < M1) { S2 = M1 < m2 ? M1 : m2; M1 = m; }
+                else if (m < S2) S2 = m;
+            }
+            const float T = policy_threshold<E>(a, sm, pol, M1, S2);
+            sm.thr[pol] = T;
+            if (T >= 0.0f)
+                for (int s = 0; s < S; ++s)
+                    if (parts[s].ov[pol] != 0xFFFFFFFFu && __uint_as_float(parts[s].ov[pol]) <= T) sm.overflow = 1;
+        }
+    }
+    __syncthreads();
+    for (int pol = 0; pol < 2; ++pol) {
+        if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
+        const float T = sm.thr[pol];
+        if (T < 0.0f) continue;
+        for (int j = tid; j < S * SLICE_KEYS; j += BLOCK) {
+            const int s = j / SLICE_KEYS, k = j - s * SLICE_KEYS;
+            if (k < (int)parts[s].n[pol]) {
+                const uint64_t key = parts[s].keys[pol][k];
+                if (key_value(key) <= T)
+                    append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(key), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
+            }
+        }
+    }
+    __syncthreads();
+    decide_and_write<E>(a, g, sm);
 }
 
 // ------------------------------------------------------------------ binary64 sweep
@@ -574,12 +715,26 @@ template <int E>
 hipError_t launch_e(const FullArgs& a_in, int64_t n_groups, hipStream_t st) {
     FullArgs a = a_in;
     hipLaunchKernelGGL(full_zero_kernel, dim3(1), dim3(64), 0, st, a.fb_count);
-    const int64_t step = 1ll << 30;  // grid.x is limited to 2^31 - 1 blocks
-    for (int64_t off = 0; off < n_groups; off += step) {
-        FullArgs b = a;
-        b.group_offset = off;
-        const int64_t n = n_groups - off < step ? n_groups - off : step;
-        hipLaunchKernelGGL(full_screen_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+    // few groups: S slices per group, about 2,048 workgroups in all, at most one chunk per wave
+    constexpr int S_MAX = nchunk_for(E) / 4 < 32 ? nchunk_for(E) / 4 : 32;
+    int S = 1;
+    if (n_groups < 1024 && a.parts) {
+        S = (int)((2048 + n_groups - 1) / n_groups);
+        S = S > S_MAX ? S_MAX : S;
+        while (S > 1 && n_groups * S > SLICE_PARTS) --S;
+    }
+    a.slices = S;
+    if (S > 1) {
+        hipLaunchKernelGGL(full_slice_kernel<E>, dim3((unsigned)(n_groups * S)), dim3(BLOCK), 0, st, a);
+        hipLaunchKernelGGL(full_merge_kernel<E>, dim3((unsigned)n_groups), dim3(BLOCK), 0, st, a);
+    } else {
+        const int64_t step = 1ll << 30;  // grid.x is limited to 2^31 - 1 blocks
+        for (int64_t off = 0; off < n_groups; off += step) {
+            FullArgs b = a;
+            b.group_offset = off;
+            const int64_t n = n_groups - off < step ? n_groups - off : step;
+            hipLaunchKernelGGL(full_screen_kernel<E>, dim3((unsigned)n), dim3(BLOCK), 0, st, b);
+        }
     }
     const int fb_blocks = (int)(n_groups < 1024 ? n_groups : 1024);
     hipLaunchKernelGGL(full_f64_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);

@@ -74,6 +74,8 @@ struct FullArgs {
     int want_pooled;
     int32_t* fb_count;         // groups queued for the binary64 sweep (cleared by the launcher)
     int32_t* fb_list;          // n_groups entries
+    SlicePart* parts;          // SLICE_PARTS entries (few groups split over slices); nullable
+    int slices;                // workgroups per group (set by the launcher)
 };
 float fullgrid_ratio(int G, int qmin, int qmax, int E);
 hipError_t launch_fullgrid(const FullArgs& a, int E, int64_t n_groups, hipStream_t st);

@@ -76,10 +76,11 @@ def check_pooled(w, d, d_period, pbits_t, pobj_t, sol, qmin=-8, qmax=7):
 
 def check_same_result(a, b, label, keys=("scales", "codes", "objective", "pooled_scales", "pooled_objective")):
     """Two GPU result dicts of the same groups (two methods, or two launch shapes) agree bit for bit
-    on every output they both carry."""
+    on every output they both carry (floating outputs compared as bit patterns, so NaN equals NaN)."""
     for k in keys:
         if a.get(k) is None or b.get(k) is None:
             continue
         x, y = a[k].cpu().numpy(), b[k].cpu().numpy()
+        x, y = x.reshape(x.shape[0], -1).view(np.uint8), y.reshape(y.shape[0], -1).view(np.uint8)
         bad = np.nonzero(np.any((x != y).reshape(x.shape[0], -1), axis=1))[0]
         assert bad.size == 0, f"{label}: {k} differs on {bad.size} groups, e.g. {bad[:5]}"

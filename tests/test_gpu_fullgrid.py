@@ -110,3 +110,31 @@ def test_spec_entry_with_the_pages_quantizer_is_the_plain_entry():
         cq.cq_quantize_groups_spec(wt, dt, 128, -8, 7, p, E, n, m, s2, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(s1, s2), m
+
+
+SLICE_CASES = [(-8, 7, 128, 1), (-8, 7, 128, 2), (-8, 7, 128, 4), (-8, 7, 128, 8), (-8, 7, 128, 16),
+               (-8, 7, 128, 32), (-4, 3, 64, 3)]
+
+
+@pytest.mark.parametrize("qmin,qmax,G,E", SLICE_CASES, ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in SLICE_CASES])
+def test_sliced_small_batches_equal_one_workgroup_per_group(qmin, qmax, G, E):
+    """Below 1,024 groups a group's scales are split over several workgroups whose key lists are
+    merged; from 1,024 groups on each group has one workgroup.  The same groups give the same
+    scales, codes and binary64 objectives both ways, for both policies, and the same input and
+    exact-tie flags (which groups the binary64 sweep settles may differ), including an
+    all-zero group (zero rule), constructed ties, a non-finite input and a group outside the
+    binary32 screen's range (binary64 sweep)."""
+    n = 1040
+    w, d = _spec_groups(qmin, qmax, G, E, n, seed=2000 + E + G)
+    w[4, 3] = np.nan
+    d[5, 0, 0] = 2.0 ** 101
+    say(f"slices vs one workgroup per group: [{qmin}, {qmax}], G={G}, E={E}, {n} groups")
+    full = _run(w, d, n, qmin=qmin, qmax=qmax)
+    keys = ("scales", "codes", "objective", "pooled_scales", "pooled_objective")
+    mask = cq.FLAG_BAD_INPUT | cq.FLAG_EXACT_TIE
+    for m in (1, 6, 300, 1023):
+        sub = _run(np.ascontiguousarray(w[:m]), np.ascontiguousarray(d[:m]), m, qmin=qmin, qmax=qmax)
+        check_same_result({k: full[k][:m] for k in keys}, sub, f"{m} groups", keys)
+        fa, fb = full["flags"][:m].cpu().numpy() & mask, sub["flags"].cpu().numpy() & mask
+        assert np.array_equal(fa, fb), f"{m} groups: flags differ on {np.nonzero(fa != fb)[0][:5]}"
+    assert bits_np(full["scales"])[4] == 0 and full["flags"].cpu().numpy()[4] & cq.FLAG_BAD_INPUT

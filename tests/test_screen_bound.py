@@ -85,26 +85,6 @@ def test_chunk_bounds_hold_at_every_scale(j):
         assert skippable > 0.5
 
 
-def test_unskippable_count_is_a_subset_of_the_grid():
-    """bench.necessary_terms counts at least the chunk that holds the minimax optimum and never
-    more active terms than the whole grid has."""
-    import bench
-    rng = np.random.default_rng(9)
-    w1, d1, p1 = W.matrix_groups(*W.make_matrix(1, 0))
-    idx = np.sort(rng.choice(w1.shape[0], 8, replace=False))
-    w, d = w1[idx], d1[idx % p1]
-    opt_m, opt_p = [], []
-    for j in range(len(idx)):
-        top = int(bench.screened_patterns(w[j:j + 1])[0])
-        F = _objectives(w[j].astype(np.float64), d[j].astype(np.float64), top)
-        opt_m.append(F.max(axis=0).min())
-        opt_p.append(F.sum(axis=0).min())
-    terms, chunks = bench.necessary_terms(w, d, np.array(opt_m), np.array(opt_p), chunk=CHUNK)
-    assert np.all(chunks >= 1)
-    assert np.all(terms > 0)
-    assert terms.sum() <= bench.active_terms(w)
-
-
 @pytest.mark.parametrize("j", range(10))
 def test_candidate_window_drops_only_scales_above_the_probe(j):
     """The candidate solver ignores every scale s <= lo, lo = max_i (|w_i| - sqrt(1.0001 U /
