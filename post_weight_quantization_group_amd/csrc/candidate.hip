@@ -55,6 +55,9 @@ constexpr double SEL_SLACK = 1e-12;
 template <int E>
 struct CandSmem {
     static constexpr int RCAP = rcap_for(E);
+    // Up to four environments the rescoring terms of PER_T scales are formed in LDS
+    static constexpr bool TERMS = E <= 4;
+    static constexpr int PER_T = TERMS ? 8 / E : 1;
     __align__(16) float w[G];
     __align__(16) float d[E * G];  // [e][i]
     union {
@@ -63,22 +66,28 @@ struct CandSmem {
             double q_lo[QCAP];
             uint32_t q_b[QCAP];
         };
-        double pairF[BLOCK];   // rescoring sums: written first after the shortlist is taken
+        struct {               // the codes of the kept runs' first patterns (read last before
+                               // the candidates are listed), then of the shortlisted scales with
+                               // their rescoring sums (written first after the shortlist is taken)
+            uint8_t qbuf[RCAP][G];
+            double pairF[BLOCK];
+        };
+        // rescoring terms d_ei (w_i - s q_i)^2 (rows padded by one: the summing lanes read
+        // distinct banks)
+        double term[PER_T][TERMS ? E : 1][G + 1];
     };
     uint8_t magp[BLOCK];
-    double part[3][4 * E];
+    double part[2][E];
     double A[E], B0[E], C0[E];
     double wtot[BLOCK / 64][8];
     double redd[BLOCK / 64];
-    float redf[BLOCK / 64];
+    float redf[2 * (BLOCK / 64)];
     int redi[BLOCK / 64];
     uint32_t run_lo[RCAP], run_hi[RCAP];
-    uint8_t qbuf[RCAP][G];
     double run_B[RCAP][E], run_C[RCAP][E];
     uint32_t cand_b[CCAP];
     double cand_F[CCAP];
     int n_runs, n_q, n_cand, n_ev;
-    uint32_t win_lo, win_hi;          // the window of patterns that can hold the optimum
     uint32_t win_b;
     double win_F;
     int win_state, win_count;
@@ -186,7 +195,8 @@ __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
 // true at the last.  The boundary a/(c+1/2) rounded to binary16 lands within a pattern of it;
 // a short walk confirms the first true pattern and bisection covers anything else.
 __device__ __forceinline__ uint32_t first_at_most(float a, int c) {
-    const float tau = a / ((float)(2 * c + 1) * 0.5f);
+    // a guess only (the walk and the bisection below decide): a reciprocal and a product
+    const float tau = a * __builtin_amdgcn_rcpf((float)(2 * c + 1) * 0.5f);
     uint32_t b = f32_to_half_bits_rne(tau);
     b = b < BITS_FIRST + 1 ? BITS_FIRST + 1 : (b > BITS_LAST ? BITS_LAST : b);
     for (int k = 0; k < 4; ++k) {
@@ -294,7 +304,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     // ---- staging and input checks (environments a.E..E-1 are zero padding)
     if (tid < G) sm.w[tid] = wg[tid];
     for (int j = tid; j < E * G; j += BLOCK) sm.d[j] = j / G < a.E ? dg[j] : 0.0f;
-    if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; sm.win_lo = BITS_FIRST; sm.win_hi = BITS_LAST; }
+    if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; sm.n_ev = 0; }
     __syncthreads();
     float bad = 0.0f;
     if (tid < G && !__builtin_isfinite(sm.w[tid])) bad = 1.0f;
@@ -302,7 +312,10 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         const float v = sm.d[j];
         if (!(v >= 0.0f) || !__builtin_isfinite(v)) bad = 1.0f;
     }
-    if (block_max_f(bad, sm.redf) != 0.0f) {
+    // whether an input is bad, and max|w|, in one reduction
+    float red2[2] = {bad, tid < G ? fabsf(sm.w[tid]) : 0.0f};
+    block_max_fn<2>(red2, sm.redf);
+    if (red2[0] != 0.0f) {
         if (tid < G && a.codes) a.codes[g * G + tid] = 0;
         if (tid == 0) {
             a.scales[g] = 0;
@@ -311,7 +324,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
         return;
     }
-    const float wmax = block_max_f(tid < G ? fabsf(sm.w[tid]) : 0.0f, sm.redf);
+    const float wmax = red2[1];
 
     // ---- 0. where the optimum can lie.  U = F at s_a = binary16(max|w|/9) (binary64) bounds
     //         the optimum from above; the minimax optimum usually lies near there, below the
@@ -323,6 +336,8 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     //         pattern that can hold the optimum; only transitions above it matter.  Thread i < G
     //         takes weight i: its residual at s_a (waves 0 and 1 sum each environment by a DPP
     //         scan) and then its bound.
+    uint32_t win_lo = BITS_FIRST;  // the window of patterns that can hold the optimum
+    const uint32_t win_hi = BITS_LAST;
     uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 9.0f));
     b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > BITS_LAST ? BITS_LAST : b_a);
     {
@@ -349,26 +364,19 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             lo = (aw - __builtin_sqrt(1.0001 * U / dmax)) / qa * (1.0 - 0x1p-40);
         }
         lo = -block_min_d(-lo, sm.redd);  // the largest bound over the weights
-        if (tid == 0) {
-            // the first pattern above lo (never above b_a: F(s_a) <= U)
-            uint32_t b = BITS_FIRST;
-            if (lo >= (double)half_bits_value(BITS_FIRST)) {
-                b = f32_to_half_bits_rne((float)lo);
-                b = b < BITS_FIRST ? BITS_FIRST : (b > b_a ? b_a : b);
-                while (b > BITS_FIRST && (double)half_bits_value(b - 1) > lo) --b;
-                while (b < b_a && (double)half_bits_value(b) <= lo) ++b;
-            }
-            sm.win_lo = b;
-            sm.win_hi = BITS_LAST;
+        // the first pattern above lo (never above b_a: F(s_a) <= U), the same in every thread
+        uint32_t b = BITS_FIRST;
+        if (lo >= (double)half_bits_value(BITS_FIRST)) {
+            b = f32_to_half_bits_rne((float)lo);
+            b = b < BITS_FIRST ? BITS_FIRST : (b > b_a ? b_a : b);
+            while (b > BITS_FIRST && (double)half_bits_value(b - 1) > lo) --b;
+            while (b < b_a && (double)half_bits_value(b) <= lo) ++b;
         }
-        __syncthreads();
+        win_lo = b;
     }
-    const uint32_t win_lo = sm.win_lo, win_hi = sm.win_hi;
 
     // ---- 1. code transitions inside the window: thread t handles weight t/2, thresholds
     //         c = 4(t&1) .. 4(t&1)+3; the events are appended in any order (the sort orders them)
-    if (tid == 0) sm.n_ev = 0;
-    __syncthreads();
     {
         const int i = tid >> 1, c0 = 4 * (tid & 1);
         const float wi = sm.w[i];
@@ -378,13 +386,22 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = c0 + k;
+            bool hit = false;
+            uint32_t key = 0;
             if (wi != 0.0f && c <= cmax && !mag_at_most(aw, c, win_lo)) {
                 ++m0;  // the magnitude at the window's first pattern exceeds c
                 if (mag_at_most(aw, c, win_hi)) {
-                    const int j = atomicAdd(&sm.n_ev, 1);
-                    sm.ev[j] = (first_at_most(aw, c) << 11) | ((uint32_t)i << 4) | (uint32_t)c;
+                    hit = true;
+                    key = (first_at_most(aw, c) << 11) | ((uint32_t)i << 4) | (uint32_t)c;
                 }
             }
+            // one LDS atomic per wave: the wave's hits take consecutive slots in lane order
+            const uint64_t m = __ballot(hit);
+            int base = 0;
+            if (lane == 0 && m) base = atomicAdd(&sm.n_ev, (int)__popcll(m));
+            base = __builtin_amdgcn_readfirstlane(base);
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (hit) sm.ev[base + rank] = key;
         }
         sm.magp[tid] = (uint8_t)m0;
     }
@@ -455,11 +472,13 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     __syncthreads();
 
     // ---- 2b. coefficients at the window's first pattern: A = sum d w^2, B0 = sum d |w| |q|,
-    //          C0 = sum d q^2
-    if (tid < 4 * E) {
-        const int e = tid >> 2, q4 = tid & 3;
+    //          C0 = sum d q^2 (wave w takes environments w, w + 4, ...; lane l weights l and
+    //          l + 64; a butterfly sums the wave)
+    for (int e = wave; e < E; e += BLOCK / 64) {
         double A = 0.0, B = 0.0, C = 0.0;
-        for (int i = 32 * q4; i < 32 * q4 + 32; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = lane + 64 * h;
             const double dv = (double)sm.d[e * G + i];
             const double wv = (double)sm.w[i];
             const double m = (double)(sm.magp[2 * i] + sm.magp[2 * i + 1]);
@@ -467,16 +486,13 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             B += dv * (fabs(wv) * m);
             C += dv * (m * m);
         }
-        sm.part[0][tid] = A; sm.part[1][tid] = B; sm.part[2][tid] = C;
-    }
-    __syncthreads();
-    if (tid < E) {
-        const double* p0 = sm.part[0] + 4 * tid;
-        const double* p1 = sm.part[1] + 4 * tid;
-        const double* p2 = sm.part[2] + 4 * tid;
-        sm.A[tid] = ((p0[0] + p0[1]) + p0[2]) + p0[3];
-        sm.B0[tid] = ((p1[0] + p1[1]) + p1[2]) + p1[3];
-        sm.C0[tid] = ((p2[0] + p2[1]) + p2[2]) + p2[3];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            A += lane_xor(A, o);
+            B += lane_xor(B, o);
+            C += lane_xor(C, o);
+        }
+        if (lane == 0) { sm.A[e] = A; sm.B0[e] = B; sm.C0[e] = C; }
     }
     __syncthreads();
 
@@ -489,26 +505,40 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     const int e0 = 4 * tid;
     // Fixed run slots of this thread: slot 0 is the run before the first event (thread 0 only),
     // slot 1+k the run that starts at event e0+k (empty when the next event has the same pattern).
-    uint32_t r_lo[5], r_hi[5];
+    uint32_t r_pat[5];  // first pattern | last pattern << 16
+    auto r_lo = [&](int j) { return r_pat[j] & 0xFFFFu; };
+    auto r_hi = [&](int j) { return r_pat[j] >> 16; };
     bool r_ok[5];
-    double r_flo[5], r_fhi[5], r_lb[5], r_mlo[5], r_mhi[5];
+    double r_flo[5], r_fhi[5], r_lb[5];
     r_ok[0] = tid == 0;
-    r_lo[0] = win_lo;
-    r_hi[0] = (n_ev > 0 ? (sm.ev[0] >> 11) : (win_hi + 1)) - 1;
+    r_pat[0] = win_lo | (((n_ev > 0 ? (sm.ev[0] >> 11) : (win_hi + 1)) - 1) << 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int ev_k = e0 + k;
         const uint32_t t = ev_k < n_ev ? (sm.ev[ev_k] >> 11) : 0u;
         const uint32_t tn = ev_k + 1 < n_ev ? (sm.ev[ev_k + 1] >> 11) : (win_hi + 1);
         r_ok[k + 1] = ev_k < n_ev && tn > t;
-        r_lo[k + 1] = t;
-        r_hi[k + 1] = tn - 1;
+        r_pat[k + 1] = t | (((tn - 1) & 0xFFFFu) << 16);
     }
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
         r_flo[j] = -__builtin_inf(); r_fhi[j] = -__builtin_inf(); r_lb[j] = -__builtin_inf();
-        r_mlo[j] = 0.0; r_mhi[j] = 0.0;
     }
+    // Magnitude bound of a run end, max_e (A_e + 2 B0_e s + C0_e s^2), taken from the maxima of
+    // A, B0 and C0 over the environments: never smaller, so the allowances only grow.
+    // Up to four environments there is one batch: each run's end values are final after its
+    // fold and go straight into U (the upper bound from the run ends); beyond, the per-run
+    // maxima are held over the batches and the magnitude maxima are read after them.
+    constexpr bool ONE_BATCH = E <= 4;
+    double am = 0.0, b2m = 0.0, cm = 0.0;
+    auto read_mag = [&]() {
+        double bm = 0.0;
+        for (int e = 0; e < E; ++e) { am = fmax(am, sm.A[e]); bm = fmax(bm, sm.B0[e]); cm = fmax(cm, sm.C0[e]); }
+        b2m = 2.0 * bm;
+    };
+    auto mag = [&](double s) { return __builtin_fma(s, __builtin_fma(cm, s, b2m), am); };
+    if constexpr (ONE_BATCH) read_mag();
+    double U = __builtin_inf();
 #pragma unroll 1
     for (int eb = 0; eb < E; eb += 4) {
         constexpr int NB = E < 4 ? E : 4;  // environments in this batch
@@ -549,7 +579,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         }
         // fold this batch into run slot j with the current coefficients
         auto fold = [&](int j) {
-            const double slo = (double)half_bits_value(r_lo[j]), shi = (double)half_bits_value(r_hi[j]);
+            const double slo = (double)half_bits_value(r_lo(j)), shi = (double)half_bits_value(r_hi(j));
 #pragma unroll
             for (int v = 0; v < NB; ++v) {
                 const double A = sm.A[eb + v], B = cB[v], C = cC[v], B2 = -2.0 * B;
@@ -572,6 +602,11 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
                 r_fhi[j] = fmax(r_fhi[j], fh);
                 r_lb[j] = fmax(r_lb[j], fv);
             }
+            if constexpr (ONE_BATCH) {
+                U = fmin(U, fmin(r_flo[j] + ERR_REL * mag(slo), r_fhi[j] + ERR_REL * mag(shi)));
+                r_flo[j] = -__builtin_inf();  // dead from here on
+                r_fhi[j] = -__builtin_inf();
+            }
         };
         if (r_ok[0]) fold(0);
 #pragma unroll
@@ -590,33 +625,24 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
             if (r_ok[k + 1]) fold(k + 1);
         }
     }
-    // Magnitude bound of each run end, max_e (A_e + 2 B0_e s + C0_e s^2), taken from the maxima
-    // of A, B0 and C0 over the environments: never smaller, so the allowances only grow.
-    {
-        double am = 0.0, bm = 0.0, cm = 0.0;
-        for (int e = 0; e < E; ++e) { am = fmax(am, sm.A[e]); bm = fmax(bm, sm.B0[e]); cm = fmax(cm, sm.C0[e]); }
-        const double b2 = 2.0 * bm;
+    // upper bound U from the run ends, and each run's lower bound minus its error allowance
+    if constexpr (!ONE_BATCH) {
+        read_mag();
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
-            const double slo = (double)half_bits_value(r_lo[j]), shi = (double)half_bits_value(r_hi[j]);
-            r_mlo[j] = __builtin_fma(slo, __builtin_fma(cm, slo, b2), am);
-            r_mhi[j] = __builtin_fma(shi, __builtin_fma(cm, shi, b2), am);
+            const double slo = (double)half_bits_value(r_lo(j)), shi = (double)half_bits_value(r_hi(j));
+            if (r_ok[j]) U = fmin(U, fmin(r_flo[j] + ERR_REL * mag(slo), r_fhi[j] + ERR_REL * mag(shi)));
         }
     }
-    // upper bound U from the run ends, and each run's lower bound minus its error allowance
-    double U = __builtin_inf();
-#pragma unroll
-    for (int j = 0; j < 5; ++j)
-        if (r_ok[j]) U = fmin(U, fmin(r_flo[j] + ERR_REL * r_mlo[j], r_fhi[j] + ERR_REL * r_mhi[j]));
     U = block_min_d(U, sm.redd);
 
     // ---- 3b. keep the runs whose lower bound can reach U, and recompute their coefficients
     //          directly from the codes at the run's first pattern
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-        if (r_ok[j] && r_lb[j] - 2.0 * ERR_REL * r_mhi[j] <= U) {  // the magnitude bound grows with s
+        if (r_ok[j] && r_lb[j] - 2.0 * ERR_REL * mag((double)half_bits_value(r_hi(j))) <= U) {  // grows with s
             const int r = atomicAdd(&sm.n_runs, 1);
-            if (r < RCAP) { sm.run_lo[r] = r_lo[j]; sm.run_hi[r] = r_hi[j]; }
+            if (r < RCAP) { sm.run_lo[r] = r_lo(j); sm.run_hi[r] = r_hi(j); }
         }
     }
     __syncthreads();
@@ -694,27 +720,63 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     // ---- 4. direct binary64 rescoring (definition order) and the reduction
     // The codes of a batch of shortlisted scales come first, from all threads, into qbuf (free by
     // now); each (scale, environment) sum then runs in the definition's order.
-    constexpr int PER = BLOCK / E < CandSmem<E>::RCAP ? BLOCK / E : CandSmem<E>::RCAP;
-    for (int base = 0; base < n; base += PER) {
-        const int nb = min(PER, n - base);
-        for (int j = tid; j < nb * G; j += BLOCK) {
-            const int c = j / G, i = j % G;
-            sm.qbuf[c][i] = (uint8_t)(int8_t)exact_code(sm.w[i], half_bits_value(sm.cand_b[base + c]));
-        }
-        __syncthreads();
-        if (tid < nb * E) {
-            const int c = tid / E, e = tid % E;
-            const double s = (double)half_bits_value(sm.cand_b[base + c]);
-            sm.pairF[tid] = env_error_codes_f64(sm.w, sm.d + e * G, 1, reinterpret_cast<const int8_t*>(sm.qbuf[c]), s);
-        }
-        __syncthreads();
-        if (tid < nb) {
-            double F = sm.pairF[tid * E];
+    if constexpr (CandSmem<E>::TERMS) {
+        // All threads form the terms of a batch of scales (the code, residual, square and
+        // weighting as in the definition); one lane per (scale, environment) then adds them in
+        // the definition's order, and lane butterflies take the maximum over the environments.
+        constexpr int PT = CandSmem<E>::PER_T;
+        for (int base = 0; base < n; base += PT) {
+            const int nb = min(PT, n - base);
+            for (int j = tid; j < nb * G; j += BLOCK) {
+                const int c = j / G, i = j % G;
+                const float sf = half_bits_value(sm.cand_b[base + c]);
+                const double sq = (double)sf * (double)exact_code(sm.w[i], sf);
+                const double t = (double)sm.w[i] - sq;
+                const double t2 = t * t;
 #pragma unroll
-            for (int e = 1; e < E; ++e) F = sm.pairF[tid * E + e] > F ? sm.pairF[tid * E + e] : F;
-            sm.cand_F[base + tid] = F;
+                for (int e = 0; e < E; ++e) sm.term[c][e][i] = (double)sm.d[e * G + i] * t2;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const int c = lane / E, e = lane % E;
+                double F = 0.0;
+                if (lane < nb * E) {
+                    const double* tr = sm.term[c][e];
+#pragma unroll 16
+                    for (int i = 0; i < G; ++i) F = F + tr[i];
+                }
+#pragma unroll
+                for (int o = 1; o < E; o <<= 1) {
+                    const double u = lane_xor(F, o);
+                    F = u > F ? u : F;
+                }
+                if (lane < nb * E && e == 0) sm.cand_F[base + c] = F;
+            }
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        constexpr int PER = BLOCK / E < CandSmem<E>::RCAP ? BLOCK / E : CandSmem<E>::RCAP;
+        for (int base = 0; base < n; base += PER) {
+            const int nb = min(PER, n - base);
+            for (int j = tid; j < nb * G; j += BLOCK) {
+                const int c = j / G, i = j % G;
+                sm.qbuf[c][i] = (uint8_t)(int8_t)exact_code(sm.w[i], half_bits_value(sm.cand_b[base + c]));
+            }
+            __syncthreads();
+            if (tid < nb * E) {
+                const int c = tid / E, e = tid % E;
+                const double s = (double)half_bits_value(sm.cand_b[base + c]);
+                sm.pairF[tid] = env_error_codes_f64(sm.w, sm.d + e * G, 1, reinterpret_cast<const int8_t*>(sm.qbuf[c]), s);
+            }
+            __syncthreads();
+            if (tid < nb) {
+                double F = sm.pairF[tid * E];
+    #pragma unroll
+                for (int e = 1; e < E; ++e) F = sm.pairF[tid * E + e] > F ? sm.pairF[tid * E + e] : F;
+                sm.cand_F[base + tid] = F;
+            }
+            __syncthreads();
+        }
     }
     if (tid < 64) {
         // wave 0: the lexicographic (value, bits) minimum, each lane over every 64th entry and
@@ -778,7 +840,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
 // gfx950).  Six fit the LDS too (25.7 KB each at E = 4, with the unions in CandSmem) and ran 2%
 // faster, but only by spilling 24 registers to scratch, about 370 MB of write traffic per
 // 28,672-group launch.  At E = 16 three (with some spills) beat two by 13%.
-constexpr int cand_min_blocks(int E) { return E <= 4 ? 5 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
+constexpr int cand_min_blocks(int E) { return E <= 4 ? 6 : (E == 8 ? 3 : (E == 16 ? 3 : 1)); }
 
 template <int E>
 __global__ __launch_bounds__(BLOCK, cand_min_blocks(E)) void candidate_kernel(CandArgs a, int64_t group_offset) {
