@@ -55,9 +55,8 @@ constexpr double SEL_SLACK = 1e-12;
 template <int E>
 struct CandSmem {
     static constexpr int RCAP = rcap_for(E);
-    // Up to four environments the rescoring terms of PER_T scales are formed in LDS
-    static constexpr bool TERMS = E <= 4;
-    static constexpr int PER_T = TERMS ? 8 / E : 1;
+    // the rescoring terms of PER_T scales at a time are formed in LDS
+    static constexpr int PER_T = E <= 8 ? 8 / E : 1;
     __align__(16) float w[G];
     __align__(16) float d[E * G];  // [e][i]
     union {
@@ -66,19 +65,16 @@ struct CandSmem {
             double q_lo[QCAP];
             uint32_t q_b[QCAP];
         };
-        struct {               // the codes of the kept runs' first patterns (read last before
-                               // the candidates are listed), then of the shortlisted scales with
-                               // their rescoring sums (written first after the shortlist is taken)
-            uint8_t qbuf[RCAP][G];
-            double pairF[BLOCK];
-        };
-        // rescoring terms d_ei (w_i - s q_i)^2 (rows padded by one: the summing lanes read
-        // distinct banks)
-        double term[PER_T][TERMS ? E : 1][G + 1];
+        uint8_t qbuf[RCAP][G];  // the codes of the kept runs' first patterns (read last before
+                                // the candidates are listed)
+        // rescoring terms d_ei (w_i - s q_i)^2, written first after the shortlist is taken (rows
+        // padded by one: the summing lanes read distinct banks)
+        double term[PER_T][E][G + 1];
     };
     uint8_t magp[BLOCK];
     double part[2][E];
     double A[E], B0[E], C0[E];
+    double mag_c[3];  // max_e A_e, 2 max_e B0_e, max_e C0_e: the magnitude bound's coefficients
     double wtot[BLOCK / 64][8];
     double redd[BLOCK / 64];
     float redf[2 * (BLOCK / 64)];
@@ -186,8 +182,14 @@ __device__ __forceinline__ void wave_sort(uint32_t* ev, int log_n, int lane) {
     for (int r = 0; r < KPT; ++r) ev[KPT * lane + r] = key[r];
 }
 
+// The value of a finite binary16 pattern by one hardware conversion (exact: every binary16 value
+// is a binary32 value).
+__device__ __forceinline__ float half_value_hw(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
-    const float hs = (float)(2 * c + 1) * 0.5f * half_bits_value(b);
+    const float hs = (float)(2 * c + 1) * 0.5f * half_value_hw(b);
     return a < hs || (a == hs && (c & 1) == 0);
 }
 
@@ -195,9 +197,10 @@ __device__ __forceinline__ bool mag_at_most(float a, int c, uint32_t b) {
 // true at the last.  The boundary a/(c+1/2) rounded to binary16 lands within a pattern of it;
 // a short walk confirms the first true pattern and bisection covers anything else.
 __device__ __forceinline__ uint32_t first_at_most(float a, int c) {
-    // a guess only (the walk and the bisection below decide): a reciprocal and a product
+    // a guess only (the walk and the bisection below decide): a reciprocal, a product and a
+    // hardware conversion to binary16 (infinity above the range, clamped below)
     const float tau = a * __builtin_amdgcn_rcpf((float)(2 * c + 1) * 0.5f);
-    uint32_t b = f32_to_half_bits_rne(tau);
+    uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)tau);
     b = b < BITS_FIRST + 1 ? BITS_FIRST + 1 : (b > BITS_LAST ? BITS_LAST : b);
     for (int k = 0; k < 4; ++k) {
         const bool here = mag_at_most(a, c, b), before = mag_at_most(a, c, b - 1);
@@ -216,14 +219,14 @@ __device__ __forceinline__ uint32_t first_at_most(float a, int c) {
 
 template <int E>
 __device__ __forceinline__ double quad_run(const CandSmem<E>& sm, int r, double s, double& err) {
-    double F = sm.A[0] + s * (sm.run_C[r][0] * s - 2.0 * sm.run_B[r][0]), mag = 0.0;
-    for (int e = 0; e < E; ++e) {
+    double F = sm.A[0] + s * (sm.run_C[r][0] * s - 2.0 * sm.run_B[r][0]);
+    for (int e = 1; e < E; ++e) {
         const double f = sm.A[e] + s * (sm.run_C[r][e] * s - 2.0 * sm.run_B[r][e]);
         F = f > F ? f : F;
-        const double m = sm.A[e] + s * (sm.C0[e] * s + 2.0 * sm.B0[e]);
-        mag = m > mag ? m : mag;
     }
-    err = ERR_REL * mag;
+    // the magnitude bound from the maxima of A, B0 and C0 over the environments (never smaller
+    // than max_e (A_e + 2 B0_e s + C0_e s^2))
+    err = ERR_REL * __builtin_fma(s, __builtin_fma(sm.mag_c[2], s, sm.mag_c[1]), sm.mag_c[0]);
     return F;
 }
 
@@ -538,6 +541,11 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     };
     auto mag = [&](double s) { return __builtin_fma(s, __builtin_fma(cm, s, b2m), am); };
     if constexpr (ONE_BATCH) read_mag();
+    if (tid == 0) {  // for the candidates' allowances (read after several barriers)
+        double a0 = 0.0, b0 = 0.0, c0 = 0.0;
+        for (int e = 0; e < E; ++e) { a0 = fmax(a0, sm.A[e]); b0 = fmax(b0, sm.B0[e]); c0 = fmax(c0, sm.C0[e]); }
+        sm.mag_c[0] = a0; sm.mag_c[1] = 2.0 * b0; sm.mag_c[2] = c0;
+    }
     double U = __builtin_inf();
 #pragma unroll 1
     for (int eb = 0; eb < E; eb += 4) {
@@ -718,65 +726,38 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
 
     // ---- 4. direct binary64 rescoring (definition order) and the reduction
-    // The codes of a batch of shortlisted scales come first, from all threads, into qbuf (free by
-    // now); each (scale, environment) sum then runs in the definition's order.
-    if constexpr (CandSmem<E>::TERMS) {
-        // All threads form the terms of a batch of scales (the code, residual, square and
-        // weighting as in the definition); one lane per (scale, environment) then adds them in
-        // the definition's order, and lane butterflies take the maximum over the environments.
-        constexpr int PT = CandSmem<E>::PER_T;
-        for (int base = 0; base < n; base += PT) {
-            const int nb = min(PT, n - base);
-            for (int j = tid; j < nb * G; j += BLOCK) {
-                const int c = j / G, i = j % G;
-                const float sf = half_bits_value(sm.cand_b[base + c]);
-                const double sq = (double)sf * (double)exact_code(sm.w[i], sf);
-                const double t = (double)sm.w[i] - sq;
-                const double t2 = t * t;
+    // All threads form the terms of a batch of scales in LDS (free by now; the code, residual,
+    // square and weighting as in the definition); one lane per (scale, environment) then adds
+    // them in the definition's order, and lane butterflies take the maximum over the environments.
+    constexpr int PT = CandSmem<E>::PER_T;
+    for (int base = 0; base < n; base += PT) {
+        const int nb = min(PT, n - base);
+        for (int j = tid; j < nb * G; j += BLOCK) {
+            const int c = j / G, i = j % G;
+            const float sf = half_bits_value(sm.cand_b[base + c]);
+            const double sq = (double)sf * (double)exact_code(sm.w[i], sf);
+            const double t = (double)sm.w[i] - sq;
+            const double t2 = t * t;
 #pragma unroll
-                for (int e = 0; e < E; ++e) sm.term[c][e][i] = (double)sm.d[e * G + i] * t2;
-            }
-            __syncthreads();
-            if (wave == 0) {
-                const int c = lane / E, e = lane % E;
-                double F = 0.0;
-                if (lane < nb * E) {
-                    const double* tr = sm.term[c][e];
+            for (int e = 0; e < E; ++e) sm.term[c][e][i] = (double)sm.d[e * G + i] * t2;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int c = lane / E, e = lane % E;
+            double F = 0.0;
+            if (lane < nb * E) {
+                const double* tr = sm.term[c][e];
 #pragma unroll 16
-                    for (int i = 0; i < G; ++i) F = F + tr[i];
-                }
+                for (int i = 0; i < G; ++i) F = F + tr[i];
+            }
 #pragma unroll
-                for (int o = 1; o < E; o <<= 1) {
-                    const double u = lane_xor(F, o);
-                    F = u > F ? u : F;
-                }
-                if (lane < nb * E && e == 0) sm.cand_F[base + c] = F;
+            for (int o = 1; o < E; o <<= 1) {
+                const double u = lane_xor(F, o);
+                F = u > F ? u : F;
             }
-            __syncthreads();
+            if (lane < nb * E && e == 0) sm.cand_F[base + c] = F;
         }
-    } else {
-        constexpr int PER = BLOCK / E < CandSmem<E>::RCAP ? BLOCK / E : CandSmem<E>::RCAP;
-        for (int base = 0; base < n; base += PER) {
-            const int nb = min(PER, n - base);
-            for (int j = tid; j < nb * G; j += BLOCK) {
-                const int c = j / G, i = j % G;
-                sm.qbuf[c][i] = (uint8_t)(int8_t)exact_code(sm.w[i], half_bits_value(sm.cand_b[base + c]));
-            }
-            __syncthreads();
-            if (tid < nb * E) {
-                const int c = tid / E, e = tid % E;
-                const double s = (double)half_bits_value(sm.cand_b[base + c]);
-                sm.pairF[tid] = env_error_codes_f64(sm.w, sm.d + e * G, 1, reinterpret_cast<const int8_t*>(sm.qbuf[c]), s);
-            }
-            __syncthreads();
-            if (tid < nb) {
-                double F = sm.pairF[tid * E];
-    #pragma unroll
-                for (int e = 1; e < E; ++e) F = sm.pairF[tid * E + e] > F ? sm.pairF[tid * E + e] : F;
-                sm.cand_F[base + tid] = F;
-            }
-            __syncthreads();
-        }
+        __syncthreads();
     }
     if (tid < 64) {
         // wave 0: the lexicographic (value, bits) minimum, each lane over every 64th entry and

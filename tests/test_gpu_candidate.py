@@ -143,3 +143,19 @@ def test_many_fallbacks_take_both_list_paths():
     sol = oracle.solve(w[sel], d[sel], sel.size, n_threads=threads())
     sub = {k: (v[torch.from_numpy(sel).cuda()] if v is not None else None) for k, v in c.items()}
     check_minimax(w[sel], d[sel], sel.size, sub, sol)
+
+
+def test_candidate_subnormal_scales():
+    """Groups whose optimum lies among the subnormal binary16 scales (max|w| from 1e-7 to 1e-4,
+    so that max|w|/7 < 2^-14) or straddles the smallest normal one, against the oracle and the
+    full grid: the transition search converts patterns to values and back in that range."""
+    rng = np.random.default_rng(33)
+    n = 64
+    mag = 10.0 ** rng.uniform(-7, -4, n)
+    w = (rng.normal(0, 1, (n, 128)) * mag[:, None] * np.where(rng.random((n, 128)) < 0.03, 6.0, 1.0)).astype(np.float32)
+    d = rng.lognormal(0, 1, (n, 4, 128)).astype(np.float32)
+    c, x = _both(w, d, n)
+    _agree(c, x, "subnormal scales")
+    sol = oracle.solve(w, d, n, n_threads=threads())
+    check_minimax(w, d, n, c, sol)
+    assert np.count_nonzero(bits_np(c["scales"]) < 0x0400) > n // 4
