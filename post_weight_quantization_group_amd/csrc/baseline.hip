@@ -6,14 +6,13 @@
 // as s = binary16(round-to-nearest-even(fl32(max_i |w_i| / 7))), a result of
 // 0 becoming the smallest positive scale and an overflow the largest finite.
 // Without the objective, one 128-thread workgroup per group: a max-reduce,
-// one division, the conversion and the codes.  With it, a 256-thread
-// workgroup takes GB = max(1, 16 / E) consecutive groups: their weights and
-// diagonal slices go to LDS in coalesced 16-byte loads, one wave per group
-// forms max|w| and the scale, all threads form the terms d_e (w - s q)^2 of
-// every (group, environment, weight) in LDS with every operation rounded on
-// its own, and one lane per (group, environment) adds its 128 terms in index
-// order, so each environment's sum is the sequential binary64 definition bit
-// for bit; the maximum over environments follows in LDS.
+// one division, the conversion and the codes.  With it, one thread per
+// (group, environment): the thread reads its group's weights, forms the same
+// scale, and adds its environment's terms d_e (w - s q)^2 for i = 0..127 in
+// index order with every operation rounded on its own, so each environment's
+// sum is the sequential binary64 definition bit for bit; environment 0's
+// thread writes the codes and the scale, and the maximum over environments
+// goes through LDS.
 #include "device.h"
 #include "launch.h"
 
@@ -41,6 +40,9 @@ __global__ __launch_bounds__(128) void absmax_kernel(const float* __restrict__ w
     if (tid == 0) scales[g] = (uint16_t)b;
 }
 
+__device__ __forceinline__ float abs_max4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
 __device__ __forceinline__ double absmax_term(float wf, float df, double s, double inv) {
     // the operations of env_error_f64 for one weight
     const double wi = (double)wf;
@@ -55,97 +57,69 @@ __device__ __forceinline__ uint32_t code_byte(float wv, float s) {
     return (uint32_t)(uint8_t)(int8_t)exact_code(wv, s);
 }
 
-// Groups per workgroup of the objective kernel: GB * E <= 16 sums (E <= 16), else one group.
-__host__ __device__ constexpr int absmax_gb(int E) { return E >= 16 ? 1 : 16 / E; }
-// Dynamic LDS of the objective kernel: weights [GB][G], diagonals [GB][E][G] (binary32), terms
-// [GB * E][G + 1] (binary64; rows padded by one so that the summing lanes read distinct banks),
-// then the scales' patterns, reciprocals and per-environment sums.
-__host__ __device__ constexpr size_t absmax_lds(int E) {
-    return (size_t)absmax_gb(E) * G * 4 + (size_t)absmax_gb(E) * E * G * 4 +
-           (size_t)absmax_gb(E) * E * (G + 1) * 8 + (size_t)absmax_gb(E) * 16 + (size_t)absmax_gb(E) * E * 8;
-}
-
+// blockDim.x = 256; the workgroup holds gpb = 256 / E groups, thread c = (c / E, c % E).
 __global__ __launch_bounds__(256) void absmax_objective_kernel(const float* __restrict__ w,
                                                                const float* __restrict__ d, int64_t d_period,
-                                                               int E, int64_t group_offset, int64_t n_groups,
-                                                               uint16_t* scales, int8_t* codes, double* objective) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    const int GB = absmax_gb(E);
-    float* sw = (float*)lds;                                    // [GB][G]
-    float* sd = sw + GB * G;                                    // [GB][E][G]
-    double* st = (double*)(sd + GB * E * G);                    // [GB * E][G + 1]
-    double* sinv = st + GB * E * (G + 1);                       // [GB]
-    double* sfe = sinv + GB;                                    // [GB * E]
-    uint32_t* sb = (uint32_t*)(sfe + GB * E);                   // [GB]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t g0 = group_offset + (int64_t)blockIdx.x * GB;
-    const int ng = (int)(n_groups - g0 < GB ? n_groups - g0 : GB);
-
-    // ---- staging: the groups' weights (contiguous) and each group's diagonal slice
-    for (int j = tid; j < ng * (G / 4); j += BLOCK)
-        ((float4*)sw)[j] = ((const float4*)(w + g0 * G))[j];
-    for (int j = tid; j < ng * E * (G / 4); j += BLOCK) {
-        const int gl = j / (E * (G / 4)), r = j - gl * (E * (G / 4));
-        ((float4*)sd)[j] = ((const float4*)(d + ((g0 + gl) % d_period) * (int64_t)(E * G)))[r];
-    }
-    __syncthreads();
-
-    // ---- max|w| and the scale, one wave per group
-    for (int gl = wave; gl < ng; gl += BLOCK / 64) {
-        const float m = wave_max_f(fmaxf(fabsf(sw[gl * G + lane]), fabsf(sw[gl * G + lane + 64])));
-        if (lane == 0) {
-            const uint32_t b = absmax_bits(m);
-            sb[gl] = b;
-            sinv[gl] = 1.0 / (double)half_bits_value(b);
-        }
-    }
-    __syncthreads();
-
-    // ---- every term, and the codes (four weights per thread, one 32-bit store)
-    for (int j = tid; j < ng * E * G; j += BLOCK) {
-        const int row = j / G, i = j - row * G, gl = row / E;
-        const double s64 = (double)half_bits_value(sb[gl]);
-        st[row * (G + 1) + i] = absmax_term(sw[gl * G + i], sd[row * G + i], s64, sinv[gl]);
-    }
-    if (codes) {
-        for (int j = tid; j < ng * (G / 4); j += BLOCK) {
-            const int gl = j / (G / 4);
-            const float s = half_bits_value(sb[gl]);
-            const float4 v = ((const float4*)sw)[j];
-            ((uint32_t*)(codes + g0 * G))[j] = code_byte(v.x, s) | (code_byte(v.y, s) << 8) |
-                                               (code_byte(v.z, s) << 16) | (code_byte(v.w, s) << 24);
-        }
-    }
-    __syncthreads();
-
-    // ---- each environment's sum in index order, then the maximum over environments
-    if (tid < ng * E) {
-        const double* tr = st + tid * (G + 1);
+                                                               int E, int gpb, int64_t n_groups,
+                                                               uint16_t* scales, int8_t* codes,
+                                                               double* objective) {
+    __shared__ double fe[256];
+    const int c = threadIdx.x;
+    const int gl = c / E, e = c - gl * E;
+    const int64_t g = (int64_t)blockIdx.x * gpb + gl;
+    const bool live = gl < gpb && g < n_groups;
+    if (live) {
+        const float4* wr = (const float4*)(w + g * G);
+        float m = 0.0f;
+#pragma unroll 8
+        for (int k = 0; k < G / 4; ++k) m = fmaxf(m, abs_max4(wr[k]));
+        const uint32_t b = absmax_bits(m);
+        const float s = half_bits_value(b);
+        const double s64 = (double)s, inv = 1.0 / s64;
+        const float4* dr = (const float4*)(d + (g % d_period) * (int64_t)(E * G) + (int64_t)e * G);
         double F = 0.0;
-#pragma unroll 16
-        for (int i = 0; i < G; ++i) F = F + tr[i];
-        sfe[tid] = F;
+#pragma unroll 4
+        for (int k = 0; k < G / 4; ++k) {
+            const float4 v = wr[k], dv = dr[k];
+            F = F + absmax_term(v.x, dv.x, s64, inv);
+            F = F + absmax_term(v.y, dv.y, s64, inv);
+            F = F + absmax_term(v.z, dv.z, s64, inv);
+            F = F + absmax_term(v.w, dv.w, s64, inv);
+        }
+        fe[c] = F;
+        if (e == 0) {
+            scales[g] = (uint16_t)b;
+            if (codes) {
+                uint4* cr = (uint4*)(codes + g * G);
+#pragma unroll 2
+                for (int k = 0; k < G / 16; ++k) {
+                    uint32_t q[4];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const float4 v = wr[4 * k + h];
+                        q[h] = code_byte(v.x, s) | (code_byte(v.y, s) << 8) | (code_byte(v.z, s) << 16) |
+                               (code_byte(v.w, s) << 24);
+                    }
+                    cr[k] = make_uint4(q[0], q[1], q[2], q[3]);
+                }
+            }
+        }
     }
     __syncthreads();
-    if (tid < ng) {
-        double F = sfe[tid * E];
-        for (int k = 1; k < E; ++k) F = sfe[tid * E + k] > F ? sfe[tid * E + k] : F;
-        objective[g0 + tid] = F;
-        scales[g0 + tid] = (uint16_t)sb[tid];
+    if (live && e == 0) {
+        double F = fe[c];
+        for (int k = 1; k < E; ++k) F = fe[c + k] > F ? fe[c + k] : F;
+        objective[g] = F;
     }
 }
 
 hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                          uint16_t* scales, int8_t* codes, double* objective, hipStream_t st) {
     if (objective) {
-        const int gb = absmax_gb(E);
-        const int64_t blocks = (n_groups + gb - 1) / gb;
-        const int64_t step = 1ll << 30;  // grid.x is limited to 2^31 - 1 blocks
-        for (int64_t off = 0; off < blocks; off += step) {
-            const int64_t nb = blocks - off < step ? blocks - off : step;
-            hipLaunchKernelGGL(absmax_objective_kernel, dim3((unsigned)nb), dim3(BLOCK), absmax_lds(E), st, w, d,
-                               d_period, E, off * gb, n_groups, scales, codes, objective);
-        }
+        const int gpb = BLOCK / E;
+        const int64_t blocks = (n_groups + gpb - 1) / gpb;
+        hipLaunchKernelGGL(absmax_objective_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, st, w, d, d_period, E,
+                           gpb, n_groups, scales, codes, objective);
         return hipGetLastError();
     }
     const int64_t step = 1ll << 30;

@@ -296,13 +296,13 @@ def test_absmax_matches_oracle():
 
 @pytest.mark.parametrize("E", [1, 3, 4, 8, 17, 32])
 def test_absmax_objective_every_env_count(E):
-    """The objective kernel (max(1, 16 // E) groups per workgroup, one summing lane per (group,
-    environment)) at environment counts that fill a workgroup unevenly, a group count that leaves
-    the last workgroup ragged, and d shared with a period: scales, codes and the binary64
-    objective equal the oracle's bit for bit, and the scales and codes equal those of the call
-    without the objective."""
+    """The per-(group, environment) objective kernel at environment counts that fill a 256-thread
+    workgroup unevenly, a group count that leaves the last workgroup ragged, and d shared with a
+    period: scales, codes and the binary64 objective equal the oracle's bit for bit, and the
+    scales and codes equal those of the call without the objective."""
     rng = np.random.default_rng(100 + E)
-    n = 197
+    gpb = 256 // E
+    n = 3 * gpb + 5
     w = (rng.standard_normal((n, 128)) * np.exp(rng.uniform(-6, 2, (n, 1)))).astype(np.float32)
     w[0] = 0.0
     w[1, 7] = 3.0e4
