@@ -163,7 +163,6 @@ __device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, i
                                                const float (&nsv)[NS], const float (&inv)[NS], float qlo,
                                                float qhi, int lane4, v4f (&acc)[NS][E / 4]) {
     constexpr int RS = row_for(E);
-#pragma unroll 2
     for (int i = 0; i < n; ++i) {
         const float* row = rows + i * RS;
         const float wi = row[0];
@@ -237,9 +236,9 @@ __device__ void pick_winner(Smem<E>& sm, int n, uint8_t tag, int slot) {
         if (__builtin_bit_cast(uint64_t, v) == best_v && sm.cand_b[j] != best_b) tie = 1;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        count += (int)lane_xor((uint32_t)count, o);
-        tie |= (int)lane_xor((uint32_t)tie, o);
+    for (int k = 0; k < 6; ++k) {  // lane distances 32, 16, .., 1 (a counted loop, fully unrolled)
+        count += (int)lane_xor((uint32_t)count, 32 >> k);
+        tie |= (int)lane_xor((uint32_t)tie, 32 >> k);
     }
     if (lane == 0) {
         sm.win_b[slot] = best_b;
