@@ -105,6 +105,11 @@ struct Smem {
     uint8_t win_flags[2];
 };
 
+// The value of a finite binary16 pattern by one hardware conversion (exact).
+__device__ __forceinline__ float half_value_hw(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
 __device__ __forceinline__ void top3_insert(uint64_t (&k)[3], uint64_t v) {
     if (v < k[2]) {
         if (v < k[1]) {
@@ -363,14 +368,14 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = min(BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t), BITS_LAST);
-            const float s = half_bits_value(b) * pk;
+            const float s = half_value_hw(b) * pk;
             nsv[t] = -s;
             // hardware reciprocal and one Newton step: within one binary32 rounding of 1/s, the
             // accuracy the error bound assumes
             const float r0 = __builtin_amdgcn_rcpf(s);
             inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
         }
-        const float s0 = half_bits_value(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        const float s0 = half_value_hw(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
         if constexpr (use_mfma(E)) {
             v4f am[NS][E / 4];
 #pragma unroll
@@ -399,13 +404,16 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
         for (int t = 0; t < NS; ++t) {
             const uint32_t b = BITS_FIRST + (uint32_t)(c * CHUNK + rot + 64 * t);
             if (b > BITS_LAST) continue;
-            float Fm = acc[t][0], Ps = acc[t][0];
+            // the sums are +0 or positive: their maximum is that of their bit patterns
+            uint32_t Fb = __float_as_uint(acc[t][0]);
+            float Ps = acc[t][0];
 #pragma unroll
             for (int e = 1; e < E; ++e) {
                 const float x = acc[t][e];
-                Fm = fmaxf(Fm, x);
+                Fb = max(Fb, __float_as_uint(x));
                 Ps = Ps + x;
             }
+            const float Fm = __uint_as_float(Fb);
             if (a.want_minimax) top3_insert(mk, key_of(Fm, b));
             if (a.want_pooled) top3_insert(qk, key_of(Ps, b));
         }
