@@ -61,17 +61,20 @@ def check_minimax(w, d, d_period, r, sol, codes=True, qmin=-8, qmax=7):
     return same, near
 
 
+def pooled_at(w, d, d_period, b, qmin=-8, qmax=7):
+    """The oracle's pooled objective (environment sums added in order, then / E) at given bits."""
+    Fe = oracle.env_errors(w, d, b, d_period, threads(), qmin, qmax)
+    P = Fe[:, 0].copy()
+    for e in range(1, Fe.shape[1]):
+        P = P + Fe[:, e]
+    return P / Fe.shape[1]
+
+
 def check_pooled(w, d, d_period, pbits_t, pobj_t, sol, qmin=-8, qmax=7):
     bits = bits_np(pbits_t)
     obj = pobj_t.cpu().numpy()
-
-    def pooled_at(b):
-        Fe = oracle.env_errors(w, d, b, d_period, threads(), qmin, qmax)
-        P = Fe[:, 0].copy()
-        for e in range(1, Fe.shape[1]):
-            P = P + Fe[:, e]
-        return P / Fe.shape[1]
-    return check_policy("pooled", w, d, d_period, bits, obj, sol.pl_bits, sol.pl_P1, sol.pl_gap, pooled_at)
+    return check_policy("pooled", w, d, d_period, bits, obj, sol.pl_bits, sol.pl_P1, sol.pl_gap,
+                        lambda b: pooled_at(w, d, d_period, b, qmin, qmax))
 
 
 def check_same_result(a, b, label, keys=("scales", "codes", "objective", "pooled_scales", "pooled_objective")):
