@@ -14,13 +14,14 @@
 // specification with qmin and qmax, and groups of any length): codes are
 // clip(round-half-even(w/s), qmin, qmax), groups hold G <= 256 weights.
 //
-// Work split.  One 256-thread workgroup per group.  Weights and diagonals are
-// staged in LDS (diagonals transposed to [i][e], one 16-byte broadcast read per
-// weight at E = 4).  Each wave takes chunks of 64*NS consecutive patterns, NS
-// per lane, and runs all G weights against its NS scales with the E
-// per-environment sums in registers:
-//     x = w' * RN(1/s'),  q = rint(x) (clipped when the chunk can clip),
-//     e = fma(-s', q, w'),  e^2,  then E fmas into the sums.
+// Work split.  One 256-thread workgroup per group (below 1,024 groups, several
+// workgroups per group, each on a share of the chunks, and a merge).  Weights
+// and diagonals are staged in LDS as one row per weight: the pre-scaled weight
+// and its E diagonals behind one address.  Each wave takes chunks of 64*NS
+// consecutive patterns, NS per lane, and runs all G weights against its NS
+// scales with the E per-environment sums in registers:
+//     x = w' * r (r the reciprocal of s', below),  q = rint(x) (clipped when the
+//     chunk can clip),  e = fma(-s', q, w'),  e^2,  then E fmas into the sums.
 // A chunk cannot clip when every |w'| is at most (range end + 1/4) times its
 // smallest scale; the clip is then left out (it cannot change any code).
 // Patterns are rotated over the lanes from chunk to chunk so that scales a power
@@ -33,8 +34,12 @@
 //     2^k, which changes no quotient and no code; a range check guarantees that
 //     every nonzero term d e^2 is a normal binary32 number (else the group goes
 //     to the binary64 sweep below);
-//   * RN(1/s') is correctly rounded, so x~ = x (1 + t) with |t| <= 2.0001 u.  The
-//     code from x~ differs from the exact one only when x lies within 2.0001 u |x|
+//   * r is the hardware estimate r0 = (1/s')(1 + t0), |t0| <= 2^-23, refined by
+//     one Newton step with fmas: fma(-s', r0, 1) is exactly -t0 (a multiple of
+//     2^-47 below 2^-23 in magnitude) and r = fma(r0, -t0, r0) = RN((1/s')(1 - t0^2)),
+//     within (u + 2^-46) of 1/s' relatively; so x~ = RN(w' r) = x (1 + t) with
+//     |t| <= 2 u + 2^-46 + u^2 < 2.0001 u, as for a correctly rounded reciprocal.
+//     The code from x~ differs from the exact one only when x lies within 2.0001 u |x|
 //     of a half-integer, |x| <= X = max(-qmin, qmax) + 1/2; both codes then leave
 //     |x - q| within 1/2 -+ 2.0001 u X, so the term grows by a factor of at most
 //     1 + 16.001 u X and never shrinks (the exact code is the nearer one);
