@@ -10,10 +10,11 @@
 // exact);
 // the group's scale then enters with one fp32 fma per output.
 //
-// A 256-thread workgroup computes a 64 x 128 tile of y (four waves, each two 32 x 32 MFMA tiles
-// side by side).  Per group it stages the x tile [64][128] and the dequantized codes, transposed
-// to [128][128] so that each lane reads its eight consecutive k at once, in LDS; 8 MFMA steps
-// per tile cover the group, while the next group's tiles are already being loaded.
+// A 256-thread workgroup computes a 128 x 128 tile of y (four waves, each a 64 x 64 block of
+// 2 x 2 MFMA tiles of 32 x 32).  Per group it stages the x tile [128][128] and the dequantized
+// codes, transposed to [128][128] so that each lane reads its eight consecutive k at once, in
+// LDS; 8 MFMA steps per tile cover the group, while the next group's tiles are already being
+// loaded.
 // Lane layout of the instruction (checked on gfx950): lane l holds A[l % 32][8 (l / 32) + j] and
 // B[8 (l / 32) + j][l % 32], j = 0..7; result register r of lane l is D[8 (r / 4) + 4 (l / 32) +
 // r % 4][l % 32].  Each lane's 16 results share one output column, hence one scale per group.
@@ -26,7 +27,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int TM = 64, TN = 128, KG = 128;
+constexpr int TN = 128, KG = 128;
 constexpr int XS = KG + 8;  // LDS row stride (bf16) of both tiles: rows 16 bytes apart in banks
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -45,23 +46,25 @@ __device__ __forceinline__ uint4 codes_bf16(uint32_t word) {
     return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
-// A 64 x 128 tile of y per workgroup; wave w computes rows 32 (w / 2) .. +31 and columns
-// 64 (w % 2) .. +63 as two 32 x 32 MFMA tiles.  The next group's x tile and code words are
-// loaded into registers while the current group's MFMAs run.
-__global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ qw,
+// A TM x 128 tile of y per workgroup (TM = 128 rows, four waves as 2 x 2 blocks of 64 x 64, each
+// a 2 x 2 arrangement of 32 x 32 MFMA tiles).  The dequantized codes of a group are staged once
+// per workgroup and serve all TM rows; the next group's x tile and code words are loaded into
+// registers while the current group's MFMAs run.
+constexpr int TMB = 128;
+__global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ qw,
                                                     const uint16_t* __restrict__ scales, int64_t M, int64_t out,
                                                     int64_t in, float* __restrict__ y) {
-    __shared__ __align__(16) uint16_t xs[TM * XS];  // [m][k]
-    __shared__ __align__(16) uint16_t bs[TN * XS];  // [n][k], the codes u - 8 as bf16
+    __shared__ __align__(16) uint16_t xs[TMB * XS];  // [m][k]
+    __shared__ __align__(16) uint16_t bs[TN * XS];   // [n][k], the codes u - 8 as bf16
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+    const int64_t m0 = (int64_t)blockIdx.y * TMB, n0 = (int64_t)blockIdx.x * TN;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
     const int64_t n_groups = in / KG;
-    uint4 xv[4];
+    uint4 xv[8];
     uint32_t qv[8];
     auto fetch = [&](int64_t g) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {  // 64 rows x 128 bf16: 1,024 16-byte pieces
+        for (int p = 0; p < 8; ++p) {  // 128 rows x 128 bf16: 2,048 16-byte pieces
             const int piece = tid + 256 * p, row = piece >> 4, col = (piece & 15) * 8;
             xv[p] = make_uint4(0, 0, 0, 0);
             if (m0 + row < M) xv[p] = *reinterpret_cast<const uint4*>(x + (m0 + row) * in + g * KG + col);
@@ -73,16 +76,18 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
             if (n0 + n < out) qv[p] = (uint32_t)qw[(g * (KG / 8) + r) * out + n0 + n];
         }
     };
-    f32x16 acc[2];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
     fetch(0);
     for (int64_t g = 0; g < n_groups; ++g) {
         __syncthreads();  // the previous group's MFMAs have read the tiles
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < 8; ++p) {
             const int piece = tid + 256 * p, row = piece >> 4, col = (piece & 15) * 8;
             *reinterpret_cast<uint4*>(xs + row * XS + col) = xv[p];
         }
@@ -93,27 +98,34 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
         }
         __syncthreads();
         if (g + 1 < n_groups) fetch(g + 1);
-        f32x16 part[2];
+        f32x16 part[2][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) part[t][r] = 0.0f;
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[i][t][r] = 0.0f;
         const uint16_t* arow = xs + (wm + (lane & 31)) * XS + 8 * (lane >> 5);
         const uint16_t* brow = bs + (wn + (lane & 31)) * XS + 8 * (lane >> 5);
 #pragma unroll
         for (int ks = 0; ks < KG / 16; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(arow + 32 * XS + 16 * ks);
             const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(brow + 16 * ks);
             const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(brow + 32 * XS + 16 * ks);
-            part[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, part[0], 0, 0, 0);
-            part[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, part[1], 0, 0, 0);
+            part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, part[0][0], 0, 0, 0);
+            part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, part[0][1], 0, 0, 0);
+            part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, part[1][0], 0, 0, 0);
+            part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, part[1][1], 0, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int64_t col = n0 + wn + 32 * t + (lane & 31);
             const float sc = col < out ? half_bits_to_float(scales[g * out + col]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][r] = __builtin_fmaf(sc, part[t][r], acc[t][r]);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][t][r] = __builtin_fmaf(sc, part[i][t][r], acc[i][t][r]);
         }
     }
 #pragma unroll
@@ -121,10 +133,12 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
         const int64_t col = n0 + wn + 32 * t + (lane & 31);
         if (col < out) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < M) y[row * out + col] = acc[t][r];
-            }
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (row < M) y[row * out + col] = acc[i][t][r];
+                }
         }
     }
 }
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
 
 hipError_t launch_w4a16(const uint16_t* x, const int32_t* qw, const uint16_t* scales, int64_t M, int64_t out,
                         int64_t in, float* y, hipStream_t st) {
-    const dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
+    const dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + TMB - 1) / TMB));
     hipLaunchKernelGGL(w4a16_kernel, grid, dim3(256), 0, st, x, qw, scales, M, out, in, y);
     return hipGetLastError();
 }
