@@ -46,9 +46,9 @@ __device__ __forceinline__ uint4 codes_bf16(uint32_t word) {
     return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
-// A TM x 128 tile of y per workgroup (TM = 128 rows, four waves as 2 x 2 blocks of 64 x 64, each
+// A TMB x 128 tile of y per workgroup (TMB = 128 rows, four waves as 2 x 2 blocks of 64 x 64, each
 // a 2 x 2 arrangement of 32 x 32 MFMA tiles).  The dequantized codes of a group are staged once
-// per workgroup and serve all TM rows; the next group's x tile and code words are loaded into
+// per workgroup and serve all TMB rows; the next group's x tile and code words are loaded into
 // registers while the current group's MFMAs run.
 constexpr int TMB = 128;
 __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ qw,
