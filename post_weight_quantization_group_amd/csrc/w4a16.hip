@@ -46,25 +46,27 @@ __device__ __forceinline__ uint4 codes_bf16(uint32_t word) {
     return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
-// A TMB x 128 tile of y per workgroup (TMB = 128 rows, four waves as 2 x 2 blocks of 64 x 64, each
-// a 2 x 2 arrangement of 32 x 32 MFMA tiles).  The dequantized codes of a group are staged once
-// per workgroup and serve all TMB rows; the next group's x tile and code words are loaded into
+// A (64 MT) x 128 tile of y per workgroup: four waves as 2 x 2 blocks of (32 MT) x 64, each an
+// MT x 2 arrangement of 32 x 32 MFMA tiles (MT = 2 for throughput; MT = 1 for a few rows, where
+// the larger tile would mostly multiply padding).  The dequantized codes of a group are staged once
+// per workgroup and serve all its rows; the next group's x tile and code words are loaded into
 // registers while the current group's MFMAs run.
-constexpr int TMB = 128;
+template <int MT>
 __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ qw,
                                                     const uint16_t* __restrict__ scales, int64_t M, int64_t out,
                                                     int64_t in, float* __restrict__ y) {
+    constexpr int TMB = 64 * MT;
     __shared__ __align__(16) uint16_t xs[TMB * XS];  // [m][k]
     __shared__ __align__(16) uint16_t bs[TN * XS];   // [n][k], the codes u - 8 as bf16
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m0 = (int64_t)blockIdx.y * TMB, n0 = (int64_t)blockIdx.x * TN;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = (wave >> 1) * 32 * MT, wn = (wave & 1) * 64;
     const int64_t n_groups = in / KG;
-    uint4 xv[8];
+    uint4 xv[4 * MT];
     uint32_t qv[8];
     auto fetch = [&](int64_t g) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {  // 128 rows x 128 bf16: 2,048 16-byte pieces
+        for (int p = 0; p < 4 * MT; ++p) {  // TMB rows x 128 bf16: 16 TMB 16-byte pieces
             const int piece = tid + 256 * p, row = piece >> 4, col = (piece & 15) * 8;
             xv[p] = make_uint4(0, 0, 0, 0);
             if (m0 + row < M) xv[p] = *reinterpret_cast<const uint4*>(x + (m0 + row) * in + g * KG + col);
@@ -76,9 +78,9 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
             if (n0 + n < out) qv[p] = (uint32_t)qw[(g * (KG / 8) + r) * out + n0 + n];
         }
     };
-    f32x16 acc[2][2];
+    f32x16 acc[MT][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
     for (int64_t g = 0; g < n_groups; ++g) {
         __syncthreads();  // the previous group's MFMAs have read the tiles
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < 4 * MT; ++p) {
             const int piece = tid + 256 * p, row = piece >> 4, col = (piece & 15) * 8;
             *reinterpret_cast<uint4*>(xs + row * XS + col) = xv[p];
         }
@@ -98,9 +100,9 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
         }
         __syncthreads();
         if (g + 1 < n_groups) fetch(g + 1);
-        f32x16 part[2][2];
+        f32x16 part[MT][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -109,21 +111,21 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
         const uint16_t* brow = bs + (wn + (lane & 31)) * XS + 8 * (lane >> 5);
 #pragma unroll
         for (int ks = 0; ks < KG / 16; ++ks) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(arow + 32 * XS + 16 * ks);
             const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(brow + 16 * ks);
             const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(brow + 32 * XS + 16 * ks);
-            part[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, part[0][0], 0, 0, 0);
-            part[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, part[0][1], 0, 0, 0);
-            part[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, part[1][0], 0, 0, 0);
-            part[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, part[1][1], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * i * XS + 16 * ks);
+                part[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, part[i][0], 0, 0, 0);
+                part[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, part[i][1], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int64_t col = n0 + wn + 32 * t + (lane & 31);
             const float sc = col < out ? half_bits_to_float(scales[g * out + col]) : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][t][r] = __builtin_fmaf(sc, part[i][t][r], acc[i][t][r]);
         }
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
         const int64_t col = n0 + wn + 32 * t + (lane & 31);
         if (col < out) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -147,8 +149,13 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
 
 hipError_t launch_w4a16(const uint16_t* x, const int32_t* qw, const uint16_t* scales, int64_t M, int64_t out,
                         int64_t in, float* y, hipStream_t st) {
-    const dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + TMB - 1) / TMB));
-    hipLaunchKernelGGL(w4a16_kernel, grid, dim3(256), 0, st, x, qw, scales, M, out, in, y);
+    if (M <= 64) {
+        const dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + 63) / 64));
+        hipLaunchKernelGGL(w4a16_kernel<1>, grid, dim3(256), 0, st, x, qw, scales, M, out, in, y);
+    } else {
+        const dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + 127) / 128));
+        hipLaunchKernelGGL(w4a16_kernel<2>, grid, dim3(256), 0, st, x, qw, scales, M, out, in, y);
+    }
     return hipGetLastError();
 }
 
