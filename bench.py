@@ -138,7 +138,8 @@ def _timed(fn, reps=1):
 
 def measure_aux() -> dict:
     """The rows beyond the solver: environment diagonals, the W4A16 consumer check and the held-out
-    comparison, each on config 1 or config 2 at the pages' sizes."""
+    comparison, each on config 1 or config 2 at the pages' sizes; and the full grid on other
+    quantizers (code ranges and group lengths)."""
     import torch
     import post_weight_quantization_group_amd as cq
     import workloads as W
@@ -193,6 +194,25 @@ def measure_aux() -> dict:
                               "effect_pooled_minus_minimax": float(eff.cpu().item()),
                               "effect_ci95": [float(x) for x in ci.cpu().numpy()],
                               "proxy_ms": ms_p, "compare_ms": ms_h}
+    # other quantizers (README, "Use the solver": a code range and a group of any length): the
+    # full grid on 28,672 seeded groups each, E = 4, every scale of every weight; flops count
+    # 31,743 x G x (2E + 4) per group as for the pages' quantizer
+    rng = np.random.default_rng(2024)
+    sq = {}
+    for qmin, qmax, G in ((-4, 3, 64), (-2, 1, 32), (0, 15, 128), (-128, 127, 256)):
+        n, E = 28672, 4
+        ws = W.round_bf16((rng.normal(0, 0.02, (n, G)) * np.where(rng.random((n, G)) < 0.01, 8.0, 1.0))
+                          .astype(np.float32))
+        ds = rng.lognormal(0, 1, (n // 8, E, G)).astype(np.float32)
+        wt, dt = torch.from_numpy(ws).to(dev), torch.from_numpy(ds).to(dev)
+        r, ms = _timed(lambda: cq.quantize_groups(wt, dt, n // 8, method="exhaustive", qmin=qmin, qmax=qmax), reps=3)
+        fl = float(n) * SCALES * G * (2 * E + 4)
+        sq[f"q{qmin}..{qmax}_G{G}"] = {"groups": n, "E": E, "ms": ms, "groups_per_s": n / (ms / 1e3),
+                                       "TFLOP_per_s": fl / (ms / 1e3) / 1e12,
+                                       "frac_fp32_peak": fl / (ms / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
+                                       "fp64_sweep_groups": int(torch.count_nonzero(r["flags"] & cq.FLAG_FP64_SWEEP).item()),
+                                       "near_tie_groups": int(torch.count_nonzero(r["flags"] & cq.FLAG_NEAR_TIE).item())}
+    res["spec_quantizers_full_grid"] = sq
     return res
 
 
