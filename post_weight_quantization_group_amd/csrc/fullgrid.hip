@@ -463,7 +463,8 @@ __device__ void decide_and_write(const FullArgs& a, int64_t g, Smem<E>& sm) {
 
 // The zero rule or the shortlist threshold of one policy from its smallest key M1 and runner-up
 // S2: a zero binary32 value is exact (every term is normal or zero), so the lowest such pattern
-// wins with value 0; otherwise every key within the ratio of M1 is rescored.  Thread 0 only.
+// wins with value 0; otherwise every key within the ratio of M1 is rescored.  One thread per
+// policy.
 template <int E>
 __device__ float policy_threshold(const FullArgs& a, Smem<E>& sm, int pol, uint64_t M1, uint64_t S2) {
     const float m = key_value(M1);
@@ -482,7 +483,12 @@ template <int E>
 __device__ void screen_group(const FullArgs& a, int64_t g, Smem<E>& sm) {
     const int tid = threadIdx.x;
     float pk, cmax;
+    // A workgroup starts beside others that keep the SIMDs busy with the screen, and the oldest
+    // waves issue first: its staging runs at a raised wave priority, so that it joins the screen
+    // soon instead of waiting for issue slots.
+    __builtin_amdgcn_s_setprio(3);
     const int st = stage_group<E>(a, g, sm, pk, cmax);
+    __builtin_amdgcn_s_setprio(0);
     if (st == 1) { write_bad(a, g); return; }
     if (st == 2) { if (tid == 0) queue_f64(a, g); return; }
     uint64_t mk[3], qk[3];
@@ -586,35 +592,45 @@ __global__ __launch_bounds__(BLOCK) void full_merge_kernel(FullArgs a) {
     if (st == 1) { write_bad(a, g); return; }
     if (st == 2) { if (tid == 0) queue_f64(a, g); return; }
     const SlicePart* parts = a.parts + g * S;
-    if (tid == 0) {
-        for (int pol = 0; pol < 2; ++pol) {
-            if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
-            // the group's smallest key and runner-up over the slices
-            uint64_t M1 = KEY_NONE, S2 = KEY_NONE;
-            for (int s = 0; s < S; ++s) {
-                const uint64_t m = parts[s].m1[pol], m2 = parts[s].s2[pol];
-                if (m < M1) { S2 = M1 < m2 ? M1 : m2; M1 = m; }
-                else if (m < S2) S2 = m;
-            }
-            const float T = policy_threshold<E>(a, sm, pol, M1, S2);
-            sm.thr[pol] = T;
-            if (T >= 0.0f)
-                for (int s = 0; s < S; ++s)
-                    if (parts[s].ov[pol] != 0xFFFFFFFFu && __uint_as_float(parts[s].ov[pol]) <= T) sm.overflow = 1;
-        }
+    const int lane = tid & 63, wave = tid >> 6;
+    float* pre = reinterpret_cast<float*>(sm.pairF);  // [2][64]: inclusive prefix sums of the key counts
+    if (wave < 2 && (wave == 0 ? a.want_minimax : a.want_pooled)) {
+        // wave 0 minimax, wave 1 pooled: lane sl < S holds slice sl's smallest and second keys,
+        // its unkept value and its count of stored keys (S <= 32)
+        const int pol = wave;
+        const bool in = lane < S;
+        const uint64_t m = in ? parts[lane].m1[pol] : KEY_NONE;
+        const uint64_t m2 = in ? parts[lane].s2[pol] : KEY_NONE;
+        const uint32_t ov = in ? parts[lane].ov[pol] : 0xFFFFFFFFu;
+        const float cnt = in ? (float)parts[lane].n[pol] : 0.0f;  // at most 128: exact
+        // the group's smallest key and its runner-up (the slices screen disjoint patterns, so
+        // the keys are distinct)
+        const uint64_t M1 = wave_min_u64(m);
+        const uint64_t S2 = wave_min_u64(m == M1 ? m2 : m);
+        float T = 0.0f;
+        if (lane == 0) T = policy_threshold<E>(a, sm, pol, M1, S2);
+        T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(T)));
+        if (lane == 0) sm.thr[pol] = T;
+        // a slice's unkept value within the threshold sends the group to the binary64 sweep
+        if (T >= 0.0f && in && ov != 0xFFFFFFFFu && __uint_as_float(ov) <= T) sm.overflow = 1;
+        pre[pol * 64 + lane] = wave_inclusive_sum_f32(cnt);
     }
     __syncthreads();
+    // every stored key within the threshold joins the shortlist: entry j of the slices' stored
+    // keys, in slice order, is key j - (keys before slice sl) of the slice sl it falls in
     for (int pol = 0; pol < 2; ++pol) {
         if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
         const float T = sm.thr[pol];
         if (T < 0.0f) continue;
-        for (int j = tid; j < S * SLICE_KEYS; j += BLOCK) {
-            const int s = j / SLICE_KEYS, k = j - s * SLICE_KEYS;
-            if (k < (int)parts[s].n[pol]) {
-                const uint64_t key = parts[s].keys[pol][k];
-                if (key_value(key) <= T)
-                    append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(key), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
-            }
+        const float* pp = pre + pol * 64;
+        const int total = (int)pp[S - 1];
+        for (int j = tid; j < total; j += BLOCK) {
+            int sl = 0;
+            while ((int)pp[sl] <= j) ++sl;  // ends: j < total = pp[S - 1]
+            const int k = j - (sl == 0 ? 0 : (int)pp[sl - 1]);
+            const uint64_t key = parts[sl].keys[pol][k];
+            if (key_value(key) <= T)
+                append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(key), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
         }
     }
     __syncthreads();
