@@ -640,15 +640,19 @@ __global__ __launch_bounds__(BLOCK) void full_merge_kernel(FullArgs a) {
 // ------------------------------------------------------------------ binary64 sweep
 // Every scale in binary64, each environment summed in the definition's order; the lexicographic
 // (value, bits) minimum and the runner-up value give the answer with no screen at all.  For the
-// groups whose binary32 screen could not be guaranteed or was inconclusive.
+// groups whose binary32 screen could not be guaranteed or was inconclusive (flat objectives with
+// thousands of exactly tied patterns among them).  One 1,024-thread workgroup per group, one scale
+// per thread at a time: each weight's code, residual and square once, then its term added to the
+// E environments' running sums, so that every sum still runs i = 0..G-1 with every operation
+// rounded on its own.
+constexpr int F64_BLOCK = 1024, F64_WAVES = F64_BLOCK / 64;
+
 template <int E>
 struct F64Smem {
     float w[GMAX];
-    float dt[GMAX * E];
-    double rv[BLOCK], rv2[BLOCK];
-    uint32_t rb[BLOCK];
-    double pv[BLOCK], pv2[BLOCK];
-    uint32_t pb[BLOCK];
+    float dt[GMAX * E];  // [i][e]
+    double rv[F64_WAVES], rv2[F64_WAVES], pv[F64_WAVES], pv2[F64_WAVES];
+    uint32_t rb[F64_WAVES], pb[F64_WAVES];
 };
 
 __device__ __forceinline__ bool lex_less(double v, uint32_t b, double v2, uint32_t b2) {
@@ -660,14 +664,29 @@ __device__ __forceinline__ void fold(double v, uint32_t b, double& bv, uint32_t&
     if (lex_less(v, b, bv, bb)) { sv = bv; bv = v; bb = b; }
     else if (v < sv) sv = v;
 }
+// Merge another triple: the lexicographic best of the two bests, and the smallest value of the rest.
+__device__ __forceinline__ void merge3(double v, uint32_t b, double s, double& bv, uint32_t& bb, double& sv) {
+    fold(v, b, bv, bb, sv);
+    sv = s < sv ? s : sv;
+}
+// The triple over the 64 lanes of a wave (every lane ends with it).
+__device__ __forceinline__ void wave_merge3(double& bv, uint32_t& bb, double& sv) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {  // lane distances 32, 16, .., 1
+        const int o = 32 >> k;
+        const double v = lane_xor(bv, o), s = lane_xor(sv, o);
+        const uint32_t b = lane_xor(bb, o);
+        merge3(v, b, s, bv, bb, sv);
+    }
+}
 
 template <int E>
 __device__ void f64_group(const FullArgs& a, int64_t g, F64Smem<E>& sm) {
-    const int tid = threadIdx.x, G = a.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, G = a.G;
     const float* wg = a.w + g * G;
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
-    for (int i = tid; i < G; i += BLOCK) sm.w[i] = wg[i];
-    for (int j = tid; j < E * G; j += BLOCK) {
+    for (int i = tid; i < G; i += F64_BLOCK) sm.w[i] = wg[i];
+    for (int j = tid; j < E * G; j += F64_BLOCK) {
         const int e = j / G, i = j - e * G;
         sm.dt[i * E + e] = e < a.E ? dg[j] : 0.0f;
     }
@@ -675,41 +694,54 @@ __device__ void f64_group(const FullArgs& a, int64_t g, F64Smem<E>& sm) {
     const double qlo = (double)a.qmin, qhi = (double)a.qmax;
     double bF = __builtin_inf(), sF = __builtin_inf(), bP = __builtin_inf(), sP = __builtin_inf();
     uint32_t bFb = 0xFFFFFFFFu, bPb = 0xFFFFFFFFu;
-    for (uint32_t b = BITS_FIRST + tid; b <= BITS_LAST; b += BLOCK) {
+    for (uint32_t b = BITS_FIRST + tid; b <= BITS_LAST; b += F64_BLOCK) {
         const double s = (double)half_bits_value(b), inv = 1.0 / s;
-        double F = 0.0, P = 0.0;
-        for (int e = 0; e < E; ++e) {
-            const double fe = env_error_f64_n(sm.w, sm.dt + e, E, G, s, inv, qlo, qhi);
-            F = e == 0 ? fe : (fe > F ? fe : F);
-            P = e == 0 ? fe : P + fe;
+        double f[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = 0.0;
+        for (int i = 0; i < G; ++i) {
+            // the operations of env_error_f64_n for weight i, shared by the environments
+            const double wi = (double)sm.w[i];
+            double r = __builtin_rint(wi * inv);
+            r = r < qlo ? qlo : (r > qhi ? qhi : r);
+            const double sq = s * r;
+            const double t = wi - sq;
+            const double t2 = t * t;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const double term = (double)sm.dt[i * E + e] * t2;
+                f[e] = f[e] + term;
+            }
+        }
+        double F = f[0], P = f[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) {
+            F = f[e] > F ? f[e] : F;
+            P = P + f[e];
         }
         P = P / (double)a.E;
         fold(F, b, bF, bFb, sF);
         fold(P, b, bP, bPb, sP);
     }
-    sm.rv[tid] = bF; sm.rb[tid] = bFb; sm.rv2[tid] = sF;
-    sm.pv[tid] = bP; sm.pb[tid] = bPb; sm.pv2[tid] = sP;
-    __syncthreads();
-    for (int st = BLOCK / 2; st > 0; st >>= 1) {
-        if (tid < st) {
-            double bv = sm.rv[tid], sv = sm.rv2[tid];
-            uint32_t bb = sm.rb[tid];
-            fold(sm.rv[tid + st], sm.rb[tid + st], bv, bb, sv);
-            sv = sm.rv2[tid + st] < sv ? sm.rv2[tid + st] : sv;
-            sm.rv[tid] = bv; sm.rb[tid] = bb; sm.rv2[tid] = sv;
-            double pv = sm.pv[tid], psv = sm.pv2[tid];
-            uint32_t pb = sm.pb[tid];
-            fold(sm.pv[tid + st], sm.pb[tid + st], pv, pb, psv);
-            psv = sm.pv2[tid + st] < psv ? sm.pv2[tid + st] : psv;
-            sm.pv[tid] = pv; sm.pb[tid] = pb; sm.pv2[tid] = psv;
-        }
-        __syncthreads();
+    wave_merge3(bF, bFb, sF);
+    wave_merge3(bP, bPb, sP);
+    if (lane == 0) {
+        sm.rv[wave] = bF; sm.rb[wave] = bFb; sm.rv2[wave] = sF;
+        sm.pv[wave] = bP; sm.pb[wave] = bPb; sm.pv2[wave] = sP;
     }
+    __syncthreads();
+    if (tid == 0) {
+        for (int k = 1; k < F64_WAVES; ++k) {
+            merge3(sm.rv[k], sm.rb[k], sm.rv2[k], sm.rv[0], sm.rb[0], sm.rv2[0]);
+            merge3(sm.pv[k], sm.pb[k], sm.pv2[k], sm.pv[0], sm.pb[0], sm.pv2[0]);
+        }
+    }
+    __syncthreads();
     const uint32_t win = a.want_minimax ? sm.rb[0] : sm.pb[0];
     if (a.codes) {
-        const float s = half_bits_value(win);
-        for (int i = tid; i < G; i += BLOCK)
-            a.codes[g * G + i] = (int8_t)exact_code_range(sm.w[i], s, (float)a.qmin, (float)a.qmax);
+        const float sc = half_bits_value(win);
+        for (int i = tid; i < G; i += F64_BLOCK)
+            a.codes[g * G + i] = (int8_t)exact_code_range(sm.w[i], sc, (float)a.qmin, (float)a.qmax);
     }
     if (tid == 0) {
         const uint8_t fF = FLAG_FP64_SWEEP | (sm.rv2[0] == sm.rv[0] ? (FLAG_NEAR_TIE | FLAG_EXACT_TIE) : 0);
@@ -729,7 +761,7 @@ __device__ void f64_group(const FullArgs& a, int64_t g, F64Smem<E>& sm) {
 }
 
 template <int E>
-__global__ __launch_bounds__(BLOCK) void full_f64_kernel(FullArgs a) {
+__global__ __launch_bounds__(F64_BLOCK) void full_f64_kernel(FullArgs a) {
     __shared__ F64Smem<E> sm;
     const int cnt = *a.fb_count;
     for (int k = blockIdx.x; k < cnt; k += gridDim.x) f64_group<E>(a, (int64_t)a.fb_list[k], sm);
@@ -765,7 +797,7 @@ hipError_t launch_e(const FullArgs& a_in, int64_t n_groups, hipStream_t st) {
         }
     }
     const int fb_blocks = (int)(n_groups < 1024 ? n_groups : 1024);
-    hipLaunchKernelGGL(full_f64_kernel<E>, dim3(fb_blocks), dim3(BLOCK), 0, st, a);
+    hipLaunchKernelGGL(full_f64_kernel<E>, dim3(fb_blocks), dim3(F64_BLOCK), 0, st, a);
     return hipGetLastError();
 }
 

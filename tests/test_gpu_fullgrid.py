@@ -138,3 +138,24 @@ def test_sliced_small_batches_equal_one_workgroup_per_group(qmin, qmax, G, E):
         fa, fb = full["flags"][:m].cpu().numpy() & mask, sub["flags"].cpu().numpy() & mask
         assert np.array_equal(fa, fb), f"{m} groups: flags differ on {np.nonzero(fa != fb)[0][:5]}"
     assert bits_np(full["scales"])[4] == 0 and full["flags"].cpu().numpy()[4] & cq.FLAG_BAD_INPUT
+
+
+def test_flat_objectives_take_the_binary64_sweep():
+    """Config 3's one-channel groups (one environment weighs a single channel): that environment's
+    error is the same at every scale that rounds its weight to 0, and where the other environments
+    stay below it the minimax objective is flat, with hundreds of patterns tied exactly.  The
+    screen's shortlist overflows and the binary64 sweep decides; the result against the oracle."""
+    w, d, cat, _ = W.make_groups(3, np.arange(8192))
+    sel = np.nonzero(cat == W.CAT_ONE_CHANNEL)[0]
+    r = _run(w[sel], d[sel], sel.size)
+    swept = sel[np.nonzero(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)[0]]
+    say(f"one-channel groups {sel.size}, decided by the binary64 sweep {swept.size}")
+    assert swept.size > 0
+    ws, ds = w[swept], d[swept]
+    r = _run(ws, ds, swept.size)
+    assert np.all(r["flags"].cpu().numpy() & cq.FLAG_FP64_SWEEP)
+    sol = oracle.solve(ws, ds, swept.size, n_threads=threads())
+    same, near = check_minimax(ws, ds, swept.size, r, sol)
+    check_pooled(ws, ds, swept.size, r["pooled_scales"], r["pooled_objective"], sol)
+    flags = r["flags"].cpu().numpy()
+    say(f"  bits equal {same}/{swept.size}, exact ties flagged {int(np.count_nonzero(flags & cq.FLAG_EXACT_TIE))}")
