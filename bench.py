@@ -94,24 +94,35 @@ def _cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def host_threads() -> int:
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(cores, 256))
+
+
+def oracle_rate(w, d, budget_s: float, threads: int):
+    """(groups, wall seconds) of the oracle as it stands on a prefix of the groups (w, d), one
+    diagonal slice per group, sized to about budget_s seconds on `threads` threads after a
+    calibration on one group per thread."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.solve(w[:threads], d[:threads], min(threads, w.shape[0]), n_threads=threads)
+    t1 = time.perf_counter() - t0
+    n = int(min(w.shape[0], max(threads, budget_s / max(t1, 1e-3) * threads)))
+    t0 = time.perf_counter()
+    oracle.solve(w[:n], d[:n], n, n_threads=threads)
+    return n, time.perf_counter() - t0
+
+
 def cpu_baseline(k: int, budget_s: float) -> dict:
     """The oracle as it stands (brute force over all 31,743 scales, minimax and pooled from one
     sweep) on the host's cores: a seeded sample of config k sized to about budget_s seconds with
     every core, then 128 groups on one thread."""
     import oracle
     import workloads as W
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    threads = max(1, min(cores, 256))
+    threads = host_threads()
     gids = W.sample_groups(k, W.config(k).n_groups, salt=99)
     w, d, _ = W.gather_matrix_groups(k, gids[:max(4096, threads * 64)])
-    # calibrate on one group per thread, then size the sample to the time budget
-    t0 = time.perf_counter()
-    oracle.solve(w[:threads], d[:threads], threads, n_threads=threads)
-    t1 = time.perf_counter() - t0
-    n = int(min(w.shape[0], max(threads, budget_s / max(t1, 1e-3) * threads)))
-    t0 = time.perf_counter()
-    oracle.solve(w[:n], d[:n], n, n_threads=threads)
-    dt = time.perf_counter() - t0
+    n, dt = oracle_rate(w, d, budget_s, threads)
     t0 = time.perf_counter()
     oracle.solve(w[:128], d[:128], 128, n_threads=1)
     dt1 = time.perf_counter() - t0
@@ -276,13 +287,16 @@ def config2_pass(dev) -> dict:
             "pack_bytes": pack_bytes}
 
 
-def measure_all_configs() -> dict:
+def measure_all_configs(oracle_budget_s=None) -> dict:
     """Throughput of every kernel on the five synthetic configs (reported beside the headline).
 
     config 0/1/4: full grid (minimax + pooled from the same sums), bounded search, candidate,
     AbsMax, pack, proxies; config 2: the full-size candidate and packing pass plus the seeded
     10,000-group sample through the full grid and the bounded search; config 3: every search on all
     262,144 groups.  Fractions of the FP32 peak count every scale of every weight (full grid).
+    With oracle_budget_s, the oracle is timed beside each config on the host's cores, on a prefix
+    of that config's seeded oracle sample (all of config 0; config 2's 10,000-group sample; seeded
+    samples of the others) sized to about that many seconds.
     """
     import torch
 
@@ -348,9 +362,20 @@ def measure_all_configs() -> dict:
                     "proxy_module_macro": {k2: float(np.mean(v)) for k2, v in module_means.items()}})
         return out
 
-    res["config0"] = matrix_pass(0)
-    res["config1"] = matrix_pass(1)
-    res["config4"] = matrix_pass(4)
+    threads = host_threads()
+
+    def oracle_beside(w, d, what):
+        n, dt = oracle_rate(w, d, oracle_budget_s, threads)
+        return {"groups": n, "wall_s": dt, "groups_per_s": n / dt, "threads": threads,
+                "sample": f"the first {n} of {what}, brute force over all 31,743 scales (minimax and pooled)"}
+
+    for k in (0, 1, 4):
+        res[f"config{k}"] = matrix_pass(k)
+        if oracle_budget_s:
+            count = {0: 128, 1: 8192, 4: 16384}[k]
+            gids = W.sample_groups(k, count, salt=99)
+            wo, do, _ = W.gather_matrix_groups(k, gids)
+            res[f"config{k}"]["oracle"] = oracle_beside(wo, do, f"{gids.size} seeded groups")
     res.update(measure_aux())
     res["config2"] = config2_pass(dev)
     gids = W.sample_groups(2, 10000)
@@ -358,10 +383,15 @@ def measure_all_configs() -> dict:
     tot = new_tot()
     searches(torch.from_numpy(ws_).to(dev), torch.from_numpy(ds_).to(dev), ws_.shape[0], ws_.shape[0], 4, True, tot)
     res["config2"]["sample"] = summary(tot, 4)
+    if oracle_budget_s:
+        res["config2"]["sample"]["oracle"] = oracle_beside(ws_, ds_, "the seeded 10,000-group sample")
     w3, d3, _, _ = W.make_groups(3)
     tot = new_tot()
     searches(torch.from_numpy(w3).to(dev), torch.from_numpy(d3).to(dev), w3.shape[0], w3.shape[0], 8, True, tot)
     res["config3"] = summary(tot, 8)
+    if oracle_budget_s:
+        gids = W.sample_groups(3, 65536, salt=99)
+        res["config3"]["oracle"] = oracle_beside(w3[gids], d3[gids], "65,536 seeded groups")
     return res
 
 
@@ -541,7 +571,7 @@ def main():
     if not args.no_config2:
         line["config2_pass"] = config2_pass(dev)
     if args.all_configs:
-        line["per_config"] = measure_all_configs()
+        line["per_config"] = measure_all_configs(None if args.no_cpu_baseline else args.cpu_budget / 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(k, args.cpu_budget)
     print(json.dumps(line), flush=True)
