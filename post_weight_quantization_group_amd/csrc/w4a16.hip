@@ -34,14 +34,17 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// 8 codes of one output (one qweight word) as bf16 pairs: code k of the word is nibble k, minus 8
+// 8 codes of one output (one qweight word) as bf16 pairs: code k of the word is nibble k, minus 8.
+// u XOR 8 read as a signed 4-bit field is u - 8; its binary32 value is a small integer, whose upper
+// half is its bf16 pattern, and one byte permute packs two of them.
 __device__ __forceinline__ uint4 codes_bf16(uint32_t word) {
+    const uint32_t v = word ^ 0x88888888u;
     uint32_t h[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float lo = (float)((int)((word >> (8 * j)) & 0xFu) - 8);
-        const float hi = (float)((int)((word >> (8 * j + 4)) & 0xFu) - 8);
-        h[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        const float lo = (float)((int32_t)(v << (28 - 8 * j)) >> 28);
+        const float hi = (float)((int32_t)(v << (24 - 8 * j)) >> 28);
+        h[j] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
     }
     return make_uint4(h[0], h[1], h[2], h[3]);
 }
@@ -59,7 +62,16 @@ __global__ __launch_bounds__(256, 2) void w4a16_kernel(const uint16_t* __restric
     __shared__ __align__(16) uint16_t xs[TMB * XS];  // [m][k]
     __shared__ __align__(16) uint16_t bs[TN * XS];   // [n][k], the codes u - 8 as bf16
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * TMB, n0 = (int64_t)blockIdx.x * TN;
+    // workgroups are dealt to the eight XCDs in turn: all column tiles of a row block go to one XCD,
+    // so that its L2 serves the row block's activations to all of them
+    const int64_t nx = gridDim.x, ny = gridDim.y, L = (int64_t)blockIdx.y * nx + blockIdx.x;
+    int64_t bx = L % nx, by = L / nx;
+    if (ny % 8 == 0) {
+        const int64_t j = L >> 3;
+        by = 8 * (j / nx) + (L & 7);
+        bx = j % nx;
+    }
+    const int64_t m0 = by * TMB, n0 = bx * TN;
     const int wm = (wave >> 1) * 32 * MT, wn = (wave & 1) * 64;
     const int64_t n_groups = in / KG;
     uint4 xv[4 * MT];
