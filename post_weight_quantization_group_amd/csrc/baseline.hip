@@ -7,12 +7,13 @@
 // 0 becoming the smallest positive scale and an overflow the largest finite.
 // Without the objective, one 128-thread workgroup per group: a max-reduce,
 // one division, the conversion and the codes.  With it, one thread per
-// (group, environment): the thread reads its group's weights, forms the same
-// scale, and adds its environment's terms d_e (w - s q)^2 for i = 0..127 in
-// index order with every operation rounded on its own, so each environment's
-// sum is the sequential binary64 definition bit for bit; environment 0's
-// thread writes the codes and the scale, and the maximum over environments
-// goes through LDS.
+// (group, environment): the thread loads its group's weights into registers
+// (all loads in flight at once), forms the same scale, and adds its
+// environment's terms d_e (w - s q)^2 for i = 0..127 in index order with every
+// operation rounded on its own, so each environment's sum is the sequential
+// binary64 definition bit for bit; the group's E threads share the codes (each
+// a contiguous share), environment 0's thread writes the scale, and the
+// maximum over environments goes through LDS.
 #include "device.h"
 #include "launch.h"
 
@@ -46,8 +47,8 @@ __device__ __forceinline__ float abs_max4(float4 v) {
 __device__ __forceinline__ double absmax_term(float wf, float df, double s, double inv) {
     // the operations of env_error_f64 for one weight
     const double wi = (double)wf;
-    double r = __builtin_rint(wi * inv);
-    r = r < -8.0 ? -8.0 : (r > 7.0 ? 7.0 : r);
+    // the product is finite (no NaN), so max/min clip exactly as the comparisons do
+    const double r = __builtin_fmin(__builtin_fmax(__builtin_rint(wi * inv), -8.0), 7.0);
     const double sq = s * r;
     const double t = wi - sq;
     const double t2 = t * t;
@@ -57,7 +58,9 @@ __device__ __forceinline__ uint32_t code_byte(float wv, float s) {
     return (uint32_t)(uint8_t)(int8_t)exact_code(wv, s);
 }
 
-// blockDim.x = 256; the workgroup holds gpb = 256 / E groups, thread c = (c / E, c % E).
+// blockDim.x = 256; the workgroup holds gpb = 256 / E groups, thread c = (c / E, c % E).  A thread
+// holds its group's 128 weights in registers (every load in flight at once), forms the scale, then
+// loads its environment's diagonals in two halves and adds the terms in index order.
 __global__ __launch_bounds__(256) void absmax_objective_kernel(const float* __restrict__ w,
                                                                const float* __restrict__ d, int64_t d_period,
                                                                int E, int gpb, int64_t n_groups,
@@ -70,38 +73,51 @@ __global__ __launch_bounds__(256) void absmax_objective_kernel(const float* __re
     const bool live = gl < gpb && g < n_groups;
     if (live) {
         const float4* wr = (const float4*)(w + g * G);
+        float4 wv[G / 4];
+#pragma unroll
+        for (int k = 0; k < G / 4; ++k) wv[k] = wr[k];
         float m = 0.0f;
-#pragma unroll 8
-        for (int k = 0; k < G / 4; ++k) m = fmaxf(m, abs_max4(wr[k]));
+#pragma unroll
+        for (int k = 0; k < G / 4; ++k) m = fmaxf(m, abs_max4(wv[k]));
         const uint32_t b = absmax_bits(m);
         const float s = half_bits_value(b);
         const double s64 = (double)s, inv = 1.0 / s64;
         const float4* dr = (const float4*)(d + (g % d_period) * (int64_t)(E * G) + (int64_t)e * G);
         double F = 0.0;
-#pragma unroll 4
-        for (int k = 0; k < G / 4; ++k) {
-            const float4 v = wr[k], dv = dr[k];
-            F = F + absmax_term(v.x, dv.x, s64, inv);
-            F = F + absmax_term(v.y, dv.y, s64, inv);
-            F = F + absmax_term(v.z, dv.z, s64, inv);
-            F = F + absmax_term(v.w, dv.w, s64, inv);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float4 dv[G / 8];
+#pragma unroll
+            for (int k = 0; k < G / 8; ++k) dv[k] = dr[h * (G / 8) + k];
+#pragma unroll
+            for (int k = 0; k < G / 8; ++k) {
+                const float4 v = wv[h * (G / 8) + k];
+                F = F + absmax_term(v.x, dv[k].x, s64, inv);
+                F = F + absmax_term(v.y, dv[k].y, s64, inv);
+                F = F + absmax_term(v.z, dv[k].z, s64, inv);
+                F = F + absmax_term(v.w, dv[k].w, s64, inv);
+            }
         }
         fe[c] = F;
-        if (e == 0) {
-            scales[g] = (uint16_t)b;
-            if (codes) {
-                uint4* cr = (uint4*)(codes + g * G);
-#pragma unroll 2
-                for (int k = 0; k < G / 16; ++k) {
-                    uint32_t q[4];
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const float4 v = wr[4 * k + h];
-                        q[h] = code_byte(v.x, s) | (code_byte(v.y, s) << 8) | (code_byte(v.z, s) << 16) |
-                               (code_byte(v.w, s) << 24);
-                    }
-                    cr[k] = make_uint4(q[0], q[1], q[2], q[3]);
+        if (e == 0) scales[g] = (uint16_t)b;
+        if (codes) {
+            // the group's E threads share its codes: thread e takes weights [e per, (e + 1) per)
+            const int per = (G + E - 1) / E, i0 = e * per, i1 = i0 + per < G ? i0 + per : G;
+            if (per % 4 == 0 && G % E == 0) {
+                // four codes per 16-byte load and 4-byte store
+                const float4* wg = (const float4*)(w + g * G);
+                uint32_t* cg = (uint32_t*)(codes + g * G);
+#pragma unroll 8
+                for (int j = i0 / 4; j < i1 / 4; ++j) {
+                    const float4 v = wg[j];
+                    cg[j] = code_byte(v.x, s) | (code_byte(v.y, s) << 8) | (code_byte(v.z, s) << 16) |
+                            (code_byte(v.w, s) << 24);
                 }
+            } else {
+                const float* wg = w + g * G;
+                int8_t* cg = codes + g * G;
+#pragma unroll 8
+                for (int i = i0; i < i1; ++i) cg[i] = (int8_t)exact_code(wg[i], s);
             }
         }
     }
