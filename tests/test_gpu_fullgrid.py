@@ -159,3 +159,32 @@ def test_flat_objectives_take_the_binary64_sweep():
     check_pooled(ws, ds, swept.size, r["pooled_scales"], r["pooled_objective"], sol)
     flags = r["flags"].cpu().numpy()
     say(f"  bits equal {same}/{swept.size}, exact ties flagged {int(np.count_nonzero(flags & cq.FLAG_EXACT_TIE))}")
+
+
+def _random_specs(count, seed):
+    """Seeded quantizers: code ranges with qmin <= 0 <= qmax (one-sided ones included), group
+    lengths from 1 to 256 and 1 to 9 environments."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        qmin, qmax = -int(rng.integers(0, 21)), int(rng.integers(0, 21))
+        if qmin < qmax:
+            out.append((qmin, qmax, int(rng.integers(1, 257)), int(rng.integers(1, 10))))
+    return out
+
+
+RANDOM_SPECS = _random_specs(10, 2026) + [(0, 7, 50, 3), (-8, 0, 90, 2)]  # and two one-sided ranges
+
+
+@pytest.mark.parametrize("qmin,qmax,G,E", RANDOM_SPECS, ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in RANDOM_SPECS])
+def test_seeded_random_quantizers_against_oracle(qmin, qmax, G, E):
+    """Ten seeded quantizers (code range, group length, environment count) beyond the listed ones,
+    and two one-sided code ranges, 24 groups each of the same structure: minimax and pooled against
+    the oracle run with the same quantizer."""
+    n = 24
+    w, d = _spec_groups(qmin, qmax, G, E, n, seed=7000 + 31 * G + qmax - qmin)
+    r = _run(w, d, n, qmin=qmin, qmax=qmax)
+    sol = oracle.solve(w, d, n, n_threads=threads(), qmin=qmin, qmax=qmax)
+    same, near = check_minimax(w, d, n, r, sol, qmin=qmin, qmax=qmax)
+    check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol, qmin=qmin, qmax=qmax)
+    say(f"quantizer [{qmin}, {qmax}], G={G}, E={E}: bits equal {same}/{n}, near ties {near}")
