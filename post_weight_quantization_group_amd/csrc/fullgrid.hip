@@ -544,7 +544,10 @@ __global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void full_slice_kernel(Fu
     const int slice = (int)(blockIdx.x % S);
     SlicePart& P = a.parts[blockIdx.x];
     float pk, cmax;
-    if (stage_group<E>(a, g, sm, pk, cmax) != 0) return;  // the merge stages the group again
+    __builtin_amdgcn_s_setprio(3);  // as in the one-workgroup path: staging beside busy waves
+    const int st = stage_group<E>(a, g, sm, pk, cmax);
+    __builtin_amdgcn_s_setprio(0);
+    if (st != 0) return;  // the merge stages the group again
     uint64_t mk[3], qk[3];
     screen_keys<E>(a, sm, pk, cmax, slice, S, mk, qk);
     uint64_t kv[2] = {mk[0], qk[0]};
@@ -616,22 +619,29 @@ __global__ __launch_bounds__(BLOCK) void full_merge_kernel(FullArgs a) {
         pre[pol * 64 + lane] = wave_inclusive_sum_f32(cnt);
     }
     __syncthreads();
-    // every stored key within the threshold joins the shortlist: entry j of the slices' stored
-    // keys, in slice order, is key j - (keys before slice sl) of the slice sl it falls in
+    // every stored key within the threshold joins the shortlist.  The stored keys of both policies
+    // form one index range, minimax first (one round of loads): entry j of a policy's keys, in
+    // slice order, is key j - (keys before slice sl) of the slice sl it falls in, found by a binary
+    // search of the prefix sums
+    int tot[2];
+#pragma unroll
     for (int pol = 0; pol < 2; ++pol) {
-        if (!(pol == 0 ? a.want_minimax : a.want_pooled)) continue;
-        const float T = sm.thr[pol];
-        if (T < 0.0f) continue;
+        const bool live = (pol == 0 ? a.want_minimax : a.want_pooled) && sm.thr[pol] >= 0.0f;
+        tot[pol] = live ? (int)pre[pol * 64 + S - 1] : 0;
+    }
+    for (int j = tid; j < tot[0] + tot[1]; j += BLOCK) {
+        const int pol = j < tot[0] ? 0 : 1, jj = pol == 0 ? j : j - tot[0];
         const float* pp = pre + pol * 64;
-        const int total = (int)pp[S - 1];
-        for (int j = tid; j < total; j += BLOCK) {
-            int sl = 0;
-            while ((int)pp[sl] <= j) ++sl;  // ends: j < total = pp[S - 1]
-            const int k = j - (sl == 0 ? 0 : (int)pp[sl - 1]);
-            const uint64_t key = parts[sl].keys[pol][k];
-            if (key_value(key) <= T)
-                append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(key), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
+        int lo = 0, hi = S - 1;  // pp[S - 1] = tot[pol] > jj
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)pp[mid] > jj) hi = mid;
+            else lo = mid + 1;
         }
+        const int k = jj - (lo == 0 ? 0 : (int)pp[lo - 1]);
+        const uint64_t key = parts[lo].keys[pol][k];
+        if (key_value(key) <= sm.thr[pol])
+            append_cand(sm.cand_b, sm.cand_tag, &sm.n_cand, key_bits(key), pol == 0 ? TAG_MINIMAX : TAG_POOLED);
     }
     __syncthreads();
     decide_and_write<E>(a, g, sm);
