@@ -200,6 +200,24 @@ int32_t cq_pack_gptq_v1(const int8_t *codes, const uint16_t *grp_scales, int64_t
                         int32_t *qweight, uint16_t *scales, void *stream);
 
 /*
+ * GPTQ-v1 packing of one [out][in] matrix for another quantizer (CliffQuant README, "Use the
+ * solver": the solver takes a quantizer specification; the model card's format, "Quantization
+ * configuration", with the field width and the group length as parameters).
+ *   codes       int8 [out][in], values in [-2^(bits-1), 2^(bits-1) - 1].
+ *   grp_scales  uint16 [out][in/group_len] (binary16 bit patterns).
+ *   qweight     out, int32 [in*bits/32][out]: field j (bits j*bits .. j*bits + bits - 1, low
+ *               field first) of qweight[r][o] is codes[o][(32/bits) r + j] + 2^(bits-1).
+ *   scales      out, uint16 [in/group_len][out]: scales[c][o] = grp_scales[o][c].
+ * bits in {2, 4, 8}; 1 <= group_len <= CQ_MAX_GROUP; out >= 0, in >= 0, in a multiple of
+ * group_len and of 32/bits; else CQ_EINVAL (bits = 4 with group_len = 128 gives what
+ * cq_pack_gptq_v1 gives).  Codes outside the range are packed modulo 2^bits (the caller
+ * guarantees the range).  codes and qweight 4-byte aligned, grp_scales and scales 2-byte.
+ * Two launches on `stream`.
+ */
+int32_t cq_pack_gptq_v1_spec(const int8_t *codes, const uint16_t *grp_scales, int64_t out, int64_t in,
+                             int32_t bits, int32_t group_len, int32_t *qweight, uint16_t *scales, void *stream);
+
+/*
  * GPTQ-v1 packing of n_mats matrices in one launch (model card, "Verification": the packed
  * checkpoint holds 150 module-buffer sets, each unpacked again; "Quantization configuration":
  * GPTQ v1, 4-bit, group size 128, symmetric).  Matrix k has shape outs[k] x ins[k]; every array

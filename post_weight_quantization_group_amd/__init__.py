@@ -28,7 +28,7 @@ __all__ = [
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
     "cq_quantize_groups", "cq_quantize_groups_spec", "cq_quantize_groups_noalloc", "cq_baseline_scales",
-    "cq_pack_gptq_v1",
+    "cq_pack_gptq_v1", "cq_pack_gptq_v1_spec",
     "cq_pack_gptq_v1_multi", "pack_gptq_v1_multi", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
@@ -44,7 +44,8 @@ FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE, "bounded": BOUNDED}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_quantize_groups_spec", "cq_quantize_groups_noalloc",
-                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_pack_gptq_v1_multi", "cq_proxy_workspace_size",
+                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_pack_gptq_v1_spec", "cq_pack_gptq_v1_multi",
+                    "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
                     "cq_w4a16_matmul")
@@ -89,6 +90,8 @@ def load():
         lib.cq_baseline_scales.argtypes = [P, P, I64, I32, I64, I32, P, P, P, P, SZ, P]
         lib.cq_pack_gptq_v1.restype = I32
         lib.cq_pack_gptq_v1.argtypes = [P, P, I64, I64, P, P, P]
+        lib.cq_pack_gptq_v1_spec.restype = I32
+        lib.cq_pack_gptq_v1_spec.argtypes = [P, P, I64, I64, I32, I32, P, P, P]
         lib.cq_pack_gptq_v1_multi.restype = I32
         lib.cq_pack_gptq_v1_multi.argtypes = [P, P, I32, P, P, P, P, P]
         lib.cq_proxy_workspace_size.restype = SZ
@@ -191,6 +194,11 @@ def cq_baseline_scales(w, d, d_period, E, n_groups, which, scales, codes=None, o
 def cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream=None):
     _check(load().cq_pack_gptq_v1(_p(codes), _p(grp_scales), out, inp, _p(qweight), _p(scales),
                                   _stream(stream)), "cq_pack_gptq_v1")
+
+
+def cq_pack_gptq_v1_spec(codes, grp_scales, out, inp, bits, group_len, qweight, scales, stream=None):
+    _check(load().cq_pack_gptq_v1_spec(_p(codes), _p(grp_scales), out, inp, bits, group_len, _p(qweight),
+                                       _p(scales), _stream(stream)), "cq_pack_gptq_v1_spec")
 
 
 def cq_pack_gptq_v1_multi(codes, grp_scales, n_mats, outs, ins, qweight, scales, stream=None):
@@ -335,11 +343,15 @@ def baseline_scales(w, d, d_period=None, which="absmax", codes=True, objective=T
     return out
 
 
-def pack_gptq_v1(codes, grp_scales, out: int, inp: int, stream=None):
-    """GPTQ-v1 (qweight int32 [in/8, out], scales int16-stored fp16 bits [in/128, out])."""
-    qweight = torch.empty((inp // 8, out), dtype=torch.int32, device=codes.device)
-    scales = torch.empty((inp // GROUP, out), dtype=torch.int16, device=codes.device)
-    cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream)
+def pack_gptq_v1(codes, grp_scales, out: int, inp: int, stream=None, bits: int = 4, group: int = GROUP):
+    """GPTQ-v1 (qweight int32 [in*bits/32, out], scales int16-stored fp16 bits [in/group, out]);
+    4-bit fields and groups of 128 by default, else bits in {2, 4, 8} and any group length."""
+    qweight = torch.empty((inp * bits // 32, out), dtype=torch.int32, device=codes.device)
+    scales = torch.empty((inp // group, out), dtype=torch.int16, device=codes.device)
+    if bits == 4 and group == GROUP:
+        cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream)
+    else:
+        cq_pack_gptq_v1_spec(codes, grp_scales, out, inp, bits, group, qweight, scales, stream)
     return qweight, scales
 
 

@@ -190,6 +190,22 @@ int32_t cq_pack_gptq_v1(const int8_t* codes, const uint16_t* grp_scales, int64_t
     return hip_status(cqk::launch_pack(codes, grp_scales, out, in, qweight, scales, (hipStream_t)stream));
 }
 
+int32_t cq_pack_gptq_v1_spec(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in, int32_t bits,
+                             int32_t group_len, int32_t* qweight, uint16_t* scales, void* stream) {
+    if (bits != 2 && bits != 4 && bits != 8) return CQ_EINVAL;
+    if (group_len < 1 || group_len > CQ_MAX_GROUP) return CQ_EINVAL;
+    if (out < 0 || in < 0 || in % group_len != 0 || in % (32 / bits) != 0) return CQ_EINVAL;
+    if (out == 0 || in == 0) return CQ_OK;
+    if (!codes || !grp_scales || !qweight || !scales) return CQ_EINVAL;
+    if (!aligned(codes, 4) || !aligned(grp_scales, 2) || !aligned(qweight, 4) || !aligned(scales, 2))
+        return CQ_EINVAL;
+    if ((in + 127) / 128 > 65535 || (out + 63) / 64 > INT32_MAX || (in / group_len) > INT64_MAX / (out + 1) ||
+        ((in / group_len) * out + 255) / 256 > INT32_MAX)
+        return CQ_EINVAL;
+    return hip_status(cqk::launch_pack_spec(codes, grp_scales, out, in, bits, group_len, qweight, scales,
+                                            (hipStream_t)stream));
+}
+
 int32_t cq_pack_gptq_v1_multi(const int8_t* codes, const uint16_t* grp_scales, int32_t n_mats, const int64_t* outs,
                               const int64_t* ins, int32_t* qweight, uint16_t* scales, void* stream) {
     if (n_mats < 0 || n_mats > CQ_MAX_PACK_MATRICES) return CQ_EINVAL;

@@ -99,6 +99,8 @@ hipError_t launch_candidate(const CandArgs& a, int E, hipStream_t st);
 hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                          uint16_t* scales, int8_t* codes, double* objective, hipStream_t st);
 
+hipError_t launch_pack_spec(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in, int bits,
+                            int group_len, int32_t* qweight, uint16_t* scales, hipStream_t st);
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st);
 

@@ -153,6 +153,59 @@ hipError_t launch_pack_multi(const int8_t* codes, const uint16_t* grp_scales, co
     return hipGetLastError();
 }
 
+// Other field widths and group lengths (bits in {2, 4, 8}, any group length): the same transpose of
+// 64 output rows through LDS over 128-channel tiles (the last one may be shorter; `in` is a multiple
+// of 32 / bits, hence of 4), then one qweight word per (field row, output): field j of the word for
+// channels (32/bits) r .. (32/bits) r + 32/bits - 1 is code + 2^(bits-1) modulo 2^bits.
+__global__ __launch_bounds__(256) void pack_spec_kernel(const int8_t* __restrict__ codes, int64_t out, int64_t in,
+                                                        int bits, int32_t* __restrict__ qweight) {
+    __shared__ uint32_t tile[PT_ROWS][33];  // 64 rows x 128 code bytes, one padding word per row
+    const int tid = threadIdx.x;
+    const int64_t o0 = (int64_t)blockIdx.x * PT_ROWS, c0 = (int64_t)blockIdx.y * 128;
+    const int nch = (int)(in - c0 < 128 ? in - c0 : 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // 64 rows x 32 four-byte words
+        const int idx = tid + 256 * k, row = idx >> 5, wc = idx & 31;
+        uint32_t v = 0;
+        if (o0 + row < out && 4 * wc < nch) v = *(const uint32_t*)(codes + (o0 + row) * in + c0 + 4 * wc);
+        tile[row][wc] = v;
+    }
+    __syncthreads();
+    const int per = 32 / bits, col = tid & 63, nr = nch / per;
+    const uint32_t mask = (1u << bits) - 1u, bias = 1u << (bits - 1);
+    const int64_t o = o0 + col;
+    if (o < out)
+        for (int rl = tid >> 6; rl < nr; rl += 4) {
+            uint32_t word = 0;
+            for (int j = 0; j < per; ++j) {
+                const int ch = rl * per + j;
+                const uint32_t byte = (tile[col][ch >> 2] >> (8 * (ch & 3))) & 0xFFu;
+                word |= ((byte + bias) & mask) << (bits * j);
+            }
+            qweight[(c0 / per + rl) * out + o] = (int32_t)word;
+        }
+}
+
+// scales[c][o] = grp_scales[o][c], one thread per output element (output-fastest).
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __restrict__ grp_scales, int64_t out,
+                                                          int64_t ngc, uint16_t* __restrict__ scales) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= ngc * out) return;
+    const int64_t c = t / out, o = t - c * out;
+    scales[t] = grp_scales[o * ngc + c];
+}
+
+hipError_t launch_pack_spec(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in, int bits,
+                            int group_len, int32_t* qweight, uint16_t* scales, hipStream_t st) {
+    if (out == 0 || in == 0) return hipSuccess;
+    const dim3 grid((unsigned)((out + PT_ROWS - 1) / PT_ROWS), (unsigned)((in + 127) / 128));
+    hipLaunchKernelGGL(pack_spec_kernel, grid, dim3(256), 0, st, codes, out, in, bits, qweight);
+    const int64_t ngc = in / group_len, n = ngc * out;
+    hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, grp_scales, out, ngc,
+                       scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                        int32_t* qweight, uint16_t* scales, hipStream_t st) {
     if (out == 0 || in == 0) return hipSuccess;

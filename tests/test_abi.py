@@ -186,3 +186,17 @@ def test_w4a16_matmul_rejects_bad_arguments():
     assert f(FAKE, None, FAKE, 4, 64, 128, FAKE, None) == -1
     assert f(FAKE, FAKE, FAKE, 64 * 65536, 64, 128, FAKE, None) == -1  # M beyond the grid
     assert f(None, None, None, 0, 64, 128, None, None) == 0           # empty
+
+
+def test_pack_spec_rejects_bad_arguments():
+    f = cq.load().cq_pack_gptq_v1_spec
+    assert f(FAKE, FAKE, 4, 128, 3, 128, FAKE, FAKE, None) == -1         # field width
+    assert f(FAKE, FAKE, 4, 128, 4, 0, FAKE, FAKE, None) == -1           # group length
+    assert f(FAKE, FAKE, 4, 128, 4, 257, FAKE, FAKE, None) == -1
+    assert f(FAKE, FAKE, 4, 96, 4, 64, FAKE, FAKE, None) == -1           # in % group_len
+    assert f(FAKE, FAKE, 4, 24, 2, 8, FAKE, FAKE, None) == -1            # in % (32 / bits)
+    assert f(FAKE, FAKE, -1, 128, 4, 128, FAKE, FAKE, None) == -1
+    assert f(FAKE + 2, FAKE, 4, 128, 8, 32, FAKE, FAKE, None) == -1      # codes alignment
+    assert f(FAKE, FAKE + 1, 4, 128, 8, 32, FAKE, FAKE, None) == -1      # scales alignment
+    assert f(None, FAKE, 4, 128, 8, 32, FAKE, FAKE, None) == -1
+    assert f(None, None, 0, 128, 2, 16, None, None, None) == 0           # empty

@@ -188,3 +188,50 @@ def test_seeded_random_quantizers_against_oracle(qmin, qmax, G, E):
     same, near = check_minimax(w, d, n, r, sol, qmin=qmin, qmax=qmax)
     check_pooled(w, d, n, r["pooled_scales"], r["pooled_objective"], sol, qmin=qmin, qmax=qmax)
     say(f"quantizer [{qmin}, {qmax}], G={G}, E={E}: bits equal {same}/{n}, near ties {near}")
+
+
+PACK_SPECS = [(2, 64, 70, 256), (8, 32, 33, 96), (4, 100, 17, 200), (2, 16, 130, 48), (8, 256, 5, 512),
+              (4, 128, 65, 384), (8, 1, 9, 20)]
+
+
+@pytest.mark.parametrize("bits,group,out,inp", PACK_SPECS, ids=[f"b{b}_g{g}_{o}x{i}" for b, g, o, i in PACK_SPECS])
+def test_pack_other_field_widths_against_oracle(bits, group, out, inp):
+    """GPTQ-v1 packing with 2-, 4- and 8-bit fields and other group lengths (ragged tiles in both
+    directions) bit for bit against the oracle's packing; 4-bit fields in groups of 128 also equal
+    the plain entry point's."""
+    rng = np.random.default_rng(bits * 1000 + group + out + inp)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    codes = rng.integers(lo, hi + 1, (out, inp)).astype(np.int8)
+    sbits = rng.integers(1, 0x7C00, (out, inp // group)).astype(np.uint16)
+    qw, sc = cq.pack_gptq_v1(dev(codes), dev(sbits.view(np.int16)), out, inp, bits=bits, group=group)
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.pack_gptq_v1(codes, sbits, out, inp, bits=bits, group=group)
+    np.testing.assert_array_equal(qw.cpu().numpy(), want_q)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint16), want_s)
+    back, _ = oracle.unpack_gptq_v1(qw.cpu().numpy(), sc.cpu().numpy().view(np.uint16), bits=bits)
+    np.testing.assert_array_equal(back, codes)
+    if bits == 4 and group == 128:
+        q2 = torch.empty_like(qw)
+        s2 = torch.empty_like(sc)
+        cq.cq_pack_gptq_v1_spec(dev(codes), dev(sbits.view(np.int16)), out, inp, 4, 128, q2, s2)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(q2.cpu().numpy(), want_q)
+
+
+def test_other_quantizer_solved_and_packed_end_to_end():
+    """A 2-bit quantizer, [-2, 1] in groups of 32: a 48 x 256 matrix solved by the full grid, its
+    codes and scales packed with 2-bit fields, and the packing unpacked again by the oracle."""
+    rng = np.random.default_rng(77)
+    out, inp, G = 48, 256, 32
+    A = W.round_bf16(rng.normal(0, 0.02, (out, inp)).astype(np.float32))
+    w = A.reshape(-1, G)
+    d = rng.lognormal(0, 1, (inp // G, 2, G)).astype(np.float32)
+    r = cq.quantize_groups(dev(w), dev(d), inp // G, method="exhaustive", qmin=-2, qmax=1)
+    qw, sc = cq.pack_gptq_v1(r["codes"].reshape(out, inp), r["scales"].reshape(out, inp // G), out, inp,
+                             bits=2, group=G)
+    torch.cuda.synchronize()
+    codes, sbits = oracle.unpack_gptq_v1(qw.cpu().numpy(), sc.cpu().numpy().view(np.uint16), bits=2)
+    np.testing.assert_array_equal(codes, r["codes"].cpu().numpy().reshape(out, inp))
+    np.testing.assert_array_equal(sbits.reshape(-1), bits_np(r["scales"]))
+    sol = oracle.solve(w, d, inp // G, n_threads=threads(), qmin=-2, qmax=1)
+    check_minimax(w, d, inp // G, r, sol, qmin=-2, qmax=1)
