@@ -184,6 +184,24 @@ int32_t cq_baseline_scales(const float *w, const float *d, int64_t d_period, int
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * cq_baseline_scales for another quantizer (CliffQuant README, "Use the solver": the solver takes
+ * a quantizer specification; the baselines as in cq_baseline_scales).  w is [n_groups][group_len],
+ * d [n_d][E][group_len]; codes in [qmin, qmax] as for cq_quantize_groups_spec.
+ *   CQ_ABSMAX       s = fp16(fl32(max_i |w_i| / qmax)), 0 -> 0x0001, overflow -> 0x7BFF (the
+ *                   largest magnitude maps to the largest positive code, as max|w| / 7 does for
+ *                   [-8, 7]); needs qmax >= 1, else CQ_EINVAL.  workspace unused.
+ *   CQ_POOLED_WMSE  the pooled policy of the full-grid search (cq_quantize_groups_spec's pooled
+ *                   outputs alone); workspace as cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups).
+ * codes (nullable) are those of the chosen scale; objective (nullable) max_e F_e (AbsMax) or
+ * (1/E) sum_e F_e (pooled), binary64.  Limits as for cq_quantize_groups_spec; w and d 4-byte
+ * aligned.  The pages' quantizer (group_len 128, [-8, 7]) is passed to cq_baseline_scales.
+ */
+int32_t cq_baseline_scales_spec(const float *w, const float *d, int32_t group_len, int32_t qmin, int32_t qmax,
+                                int64_t d_period, int32_t E, int64_t n_groups, int32_t which, uint16_t *scales,
+                                int8_t *codes, double *objective, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
  * GPTQ-v1 packing of one [out][in] matrix (Qwen3.5-0.8B-Base-CliffQuant-
  * W4A16-G128 model card, "Quantization configuration": GPTQ v1, 4-bit,
  * group size 128, symmetric).
@@ -278,6 +296,22 @@ int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64
                                       const int64_t *module_offsets, int32_t n_modules,
                                       double *module_mean, double *macro, double *per_group,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cq_proxy_worst_env_wmse_multi for another quantizer (CliffQuant README, "Use the solver": a
+ * quantizer specification; the proxy as in cq_proxy_worst_env_wmse, with 1/group_len for the
+ * pages' 1/128: the mean over the group's weights).  w is [n_groups][group_len], d_eval
+ * [n_d][E][group_len]; codes in [qmin, qmax].  Arguments, limits and workspace as for
+ * cq_proxy_worst_env_wmse_multi (w and d_eval 4-byte aligned); the pages' quantizer is passed to
+ * it.  Per-group sums run over the group's 16 lanes (each lane's weights in index order, then a
+ * fixed butterfly): within rounding of the sequential definition, bit-identical across runs.
+ */
+int32_t cq_proxy_worst_env_wmse_multi_spec(const float *w, const float *d_eval, int32_t group_len, int32_t qmin,
+                                           int32_t qmax, int64_t d_period, int32_t E, int64_t n_groups,
+                                           int32_t n_policies, const uint16_t *scales,
+                                           const int64_t *module_offsets, int32_t n_modules, double *module_mean,
+                                           double *macro, double *per_group, void *workspace,
+                                           size_t workspace_bytes, void *stream);
 
 /*
  * W4A16 matmul over the GPTQ-v1 tensors, the consumer check of the packed

@@ -28,6 +28,7 @@ __all__ = [
     "FLAG_BAD_INPUT", "FLAG_NEAR_TIE", "FLAG_EXACT_TIE", "FLAG_FALLBACK", "FLAG_FP64_SWEEP",
     "library_path", "load", "cq_abi_version", "cq_status_string", "cq_workspace_size",
     "cq_quantize_groups", "cq_quantize_groups_spec", "cq_quantize_groups_noalloc", "cq_baseline_scales",
+    "cq_baseline_scales_spec", "cq_proxy_worst_env_wmse_multi_spec",
     "cq_pack_gptq_v1", "cq_pack_gptq_v1_spec",
     "cq_pack_gptq_v1_multi", "pack_gptq_v1_multi", "cq_proxy_workspace_size",
     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "quantize_groups", "baseline_scales",
@@ -44,7 +45,8 @@ FLAG_BAD_INPUT, FLAG_NEAR_TIE, FLAG_EXACT_TIE, FLAG_FALLBACK, FLAG_FP64_SWEEP = 
 _METHODS = {"exhaustive": EXHAUSTIVE, "candidate": CANDIDATE, "bounded": BOUNDED}
 EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "cq_quantize_groups",
                     "cq_quantize_groups_spec", "cq_quantize_groups_noalloc",
-                    "cq_baseline_scales", "cq_pack_gptq_v1", "cq_pack_gptq_v1_spec", "cq_pack_gptq_v1_multi",
+                    "cq_baseline_scales", "cq_baseline_scales_spec", "cq_pack_gptq_v1", "cq_pack_gptq_v1_spec",
+                    "cq_pack_gptq_v1_multi", "cq_proxy_worst_env_wmse_multi_spec",
                     "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
@@ -91,6 +93,11 @@ def load():
         lib.cq_pack_gptq_v1.restype = I32
         lib.cq_pack_gptq_v1.argtypes = [P, P, I64, I64, P, P, P]
         lib.cq_pack_gptq_v1_spec.restype = I32
+        lib.cq_baseline_scales_spec.restype = I32
+        lib.cq_baseline_scales_spec.argtypes = [P, P, I32, I32, I32, I64, I32, I64, I32, P, P, P, P, SZ, P]
+        lib.cq_proxy_worst_env_wmse_multi_spec.restype = I32
+        lib.cq_proxy_worst_env_wmse_multi_spec.argtypes = [P, P, I32, I32, I32, I64, I32, I64, I32, P, P, I32, P, P,
+                                                           P, P, SZ, P]
         lib.cq_pack_gptq_v1_spec.argtypes = [P, P, I64, I64, I32, I32, P, P, P]
         lib.cq_pack_gptq_v1_multi.restype = I32
         lib.cq_pack_gptq_v1_multi.argtypes = [P, P, I32, P, P, P, P, P]
@@ -196,6 +203,25 @@ def cq_pack_gptq_v1(codes, grp_scales, out, inp, qweight, scales, stream=None):
                                   _stream(stream)), "cq_pack_gptq_v1")
 
 
+def cq_baseline_scales_spec(w, d, group_len, qmin, qmax, d_period, E, n_groups, which, scales, codes=None,
+                            objective=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_baseline_scales_spec(_p(w), _p(d), group_len, qmin, qmax, d_period, E, n_groups, which,
+                                          _p(scales), _p(codes), _p(objective), _p(workspace), ws_bytes,
+                                          _stream(stream)), "cq_baseline_scales_spec")
+
+
+def cq_proxy_worst_env_wmse_multi_spec(w, d_eval, group_len, qmin, qmax, d_period, E, n_groups, n_policies, scales,
+                                       module_offsets, n_modules, module_mean, macro, per_group=None,
+                                       workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cq_proxy_worst_env_wmse_multi_spec(_p(w), _p(d_eval), group_len, qmin, qmax, d_period, E,
+                                                     n_groups, n_policies, _p(scales), _p(module_offsets),
+                                                     n_modules, _p(module_mean), _p(macro), _p(per_group),
+                                                     _p(workspace), ws_bytes, _stream(stream)),
+           "cq_proxy_worst_env_wmse_multi_spec")
+
+
 def cq_pack_gptq_v1_spec(codes, grp_scales, out, inp, bits, group_len, qweight, scales, stream=None):
     _check(load().cq_pack_gptq_v1_spec(_p(codes), _p(grp_scales), out, inp, bits, group_len, _p(qweight),
                                        _p(scales), _stream(stream)), "cq_pack_gptq_v1_spec")
@@ -278,6 +304,20 @@ def _shape_check(w, d):
         raise ValueError("d must be float32 [n_d, E, 128]")
 
 
+def _spec_shape(w, d, qmin, qmax):
+    """(G, spec): G from w; spec is True unless the quantizer is the pages' (G = 128, [-8, 7])."""
+    G = w.shape[1] if w.dim() == 2 else -1
+    spec = (G, int(qmin), int(qmax)) != (GROUP, -8, 7)
+    if spec:
+        if w.dim() != 2 or not 1 <= G <= MAX_GROUP or w.dtype != torch.float32:
+            raise ValueError("w must be float32 [n_groups, G] with 1 <= G <= 256")
+        if d.dim() != 3 or d.shape[2] != G or d.dtype != torch.float32:
+            raise ValueError("d must be float32 [n_d, E, G]")
+    else:
+        _shape_check(w, d)
+    return G, spec
+
+
 def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled=False, workspace=None,
                     stream=None, qmin=-8, qmax=7):
     """Minimax scales (and codes, objective, flags; optionally the pooled policy) for every group.
@@ -290,15 +330,7 @@ def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled
     storage -> use ``.view(torch.uint16)`` or ``& 0xFFFF``), codes, objective,
     flags and, with ``pooled=True``, pooled_scales and pooled_objective.
     """
-    G = w.shape[1] if w.dim() == 2 else -1
-    spec = (G, int(qmin), int(qmax)) != (GROUP, -8, 7)
-    if spec:
-        if w.dim() != 2 or not 1 <= G <= MAX_GROUP or w.dtype != torch.float32:
-            raise ValueError("w must be float32 [n_groups, G] with 1 <= G <= 256")
-        if d.dim() != 3 or d.shape[2] != G or d.dtype != torch.float32:
-            raise ValueError("d must be float32 [n_d, E, G]")
-    else:
-        _shape_check(w, d)
+    G, spec = _spec_shape(w, d, qmin, qmax)
     n, E = w.shape[0], d.shape[1]
     d_period = d.shape[0] if d_period is None else int(d_period)
     m = _METHODS[method] if isinstance(method, str) else int(method)
@@ -324,22 +356,27 @@ def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled
 
 
 def baseline_scales(w, d, d_period=None, which="absmax", codes=True, objective=True, workspace=None,
-                    stream=None):
-    """AbsMax or pooled-WMSE scales: dict with scales, codes, objective."""
-    _shape_check(w, d)
+                    stream=None, qmin=-8, qmax=7):
+    """AbsMax or pooled-WMSE scales: dict with scales, codes, objective.  Another group length
+    (w [n_groups, G], d [n_d, E, G]) or code range goes through cq_baseline_scales_spec."""
+    G, spec = _spec_shape(w, d, qmin, qmax)
     n, E = w.shape[0], d.shape[1]
     d_period = d.shape[0] if d_period is None else int(d_period)
     k = {"absmax": ABSMAX, "pooled": POOLED_WMSE}[which] if isinstance(which, str) else int(which)
     dev = w.device
     out = {
         "scales": torch.empty(n, dtype=torch.int16, device=dev),
-        "codes": torch.empty((n, GROUP), dtype=torch.int8, device=dev) if codes else None,
+        "codes": torch.empty((n, G), dtype=torch.int8, device=dev) if codes else None,
         "objective": torch.empty(n, dtype=torch.float64, device=dev) if objective else None,
     }
     if k == POOLED_WMSE and workspace is None:
         workspace = _workspace(cq_workspace_size(EXHAUSTIVE, E, n), dev)
-    cq_baseline_scales(w, d, d_period, E, n, k, out["scales"], out["codes"], out["objective"], workspace,
-                       stream)
+    if spec:
+        cq_baseline_scales_spec(w, d, G, qmin, qmax, d_period, E, n, k, out["scales"], out["codes"],
+                                out["objective"], workspace, stream)
+    else:
+        cq_baseline_scales(w, d, d_period, E, n, k, out["scales"], out["codes"], out["objective"], workspace,
+                           stream)
     return out
 
 
@@ -384,10 +421,12 @@ def proxy_worst_env_wmse(w, d_eval, scales, module_offsets, d_period=None, per_g
     return pg, mm, macro
 
 
-def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None, per_group=True, stream=None):
+def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None, per_group=True, stream=None,
+                               qmin=-8, qmax=7):
     """The proxy for several policies at once: scales [P, n_groups] int16 on the device.
-    Returns (per_group [P, n] or None, module_mean [P, n_modules], macro [P]) as float64 device tensors."""
-    _shape_check(w, d_eval)
+    Returns (per_group [P, n] or None, module_mean [P, n_modules], macro [P]) as float64 device tensors.
+    Another group length or code range goes through cq_proxy_worst_env_wmse_multi_spec."""
+    G, spec = _spec_shape(w, d_eval, qmin, qmax)
     n, E = w.shape[0], d_eval.shape[1]
     if scales.dim() != 2 or scales.shape[1] != n:
         raise ValueError("scales must be [n_policies, n_groups]")
@@ -399,8 +438,12 @@ def proxy_worst_env_wmse_multi(w, d_eval, scales, module_offsets, d_period=None,
     macro = torch.empty(n_pol, dtype=torch.float64, device=dev)
     pg = torch.empty((n_pol, n), dtype=torch.float64, device=dev) if per_group else None
     ws = None if per_group else _workspace(cq_proxy_workspace_size(n * n_pol), dev)
-    cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n, n_pol, scales, module_offsets, n_modules, mm, macro,
-                                  pg, ws, stream)
+    if spec:
+        cq_proxy_worst_env_wmse_multi_spec(w, d_eval, G, qmin, qmax, d_period, E, n, n_pol, scales, module_offsets,
+                                           n_modules, mm, macro, pg, ws, stream)
+    else:
+        cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n, n_pol, scales, module_offsets, n_modules, mm,
+                                      macro, pg, ws, stream)
     return pg, mm, macro
 
 

@@ -179,6 +179,35 @@ int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int
     return hip_status(cqk::launch_sweep(a, E, n_groups, st));
 }
 
+int32_t cq_baseline_scales_spec(const float* w, const float* d, int32_t group_len, int32_t qmin, int32_t qmax,
+                                int64_t d_period, int32_t E, int64_t n_groups, int32_t which, uint16_t* scales,
+                                int8_t* codes, double* objective, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!spec_ok(group_len, qmin, qmax)) return CQ_EINVAL;
+    if (group_len == CQ_GROUP && qmin == -8 && qmax == 7)
+        return cq_baseline_scales(w, d, d_period, E, n_groups, which, scales, codes, objective, workspace,
+                                  workspace_bytes, stream);
+    hipStream_t st = (hipStream_t)stream;
+    if (n_groups < 0 || n_groups > INT32_MAX) return CQ_EINVAL;
+    if (which == CQ_ABSMAX) {
+        if (qmax < 1) return CQ_EINVAL;  // the largest magnitude maps to the largest positive code
+        if (n_groups == 0) return CQ_OK;
+        if (!w || !scales || !aligned(w, 4)) return CQ_EINVAL;
+        if (objective && !groups_ok(w, d, d_period, E, n_groups, 4)) return CQ_EINVAL;
+        return hip_status(cqk::launch_absmax_spec(w, d, d_period, group_len, qmin, qmax, E, n_groups, scales, codes,
+                                                  objective, st));
+    }
+    if (which != CQ_POOLED_WMSE) return CQ_EINVAL;
+    if (!groups_ok(w, d, d_period, E, n_groups, 4)) return CQ_EINVAL;
+    if (n_groups == 0) return CQ_OK;
+    if (!scales) return CQ_EINVAL;
+    if (!workspace || workspace_bytes < cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups) || !aligned(workspace, ALIGN))
+        return CQ_EWORKSPACE;
+    // the full grid's pooled policy alone; its codes are those of the pooled scale
+    return run_fullgrid(w, d, group_len, qmin, qmax, d_period, E, n_groups, nullptr, codes, nullptr, nullptr, scales,
+                        objective, 0, (uint8_t*)workspace, st);
+}
+
 int32_t cq_pack_gptq_v1(const int8_t* codes, const uint16_t* grp_scales, int64_t out, int64_t in,
                         int32_t* qweight, uint16_t* scales, void* stream) {
     if (out < 0 || in < 0 || in % CQ_GROUP != 0) return CQ_EINVAL;
@@ -255,6 +284,34 @@ int32_t cq_proxy_worst_env_wmse_multi(const float* w, const float* d_eval, int64
     }
     return hip_status(cqk::launch_proxy(w, d_eval, d_period, E, n_groups, n_policies, scales, module_offsets,
                                         n_modules, module_mean, macro, per_group, (hipStream_t)stream));
+}
+
+int32_t cq_proxy_worst_env_wmse_multi_spec(const float* w, const float* d_eval, int32_t group_len, int32_t qmin,
+                                           int32_t qmax, int64_t d_period, int32_t E, int64_t n_groups,
+                                           int32_t n_policies, const uint16_t* scales, const int64_t* module_offsets,
+                                           int32_t n_modules, double* module_mean, double* macro, double* per_group,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!spec_ok(group_len, qmin, qmax)) return CQ_EINVAL;
+    if (group_len == CQ_GROUP && qmin == -8 && qmax == 7)
+        return cq_proxy_worst_env_wmse_multi(w, d_eval, d_period, E, n_groups, n_policies, scales, module_offsets,
+                                             n_modules, module_mean, macro, per_group, workspace, workspace_bytes,
+                                             stream);
+    if (!groups_ok(w, d_eval, d_period, E, n_groups, 4)) return CQ_EINVAL;
+    if (n_policies < 1 || n_policies > CQ_MAX_POLICIES) return CQ_EINVAL;
+    if (n_modules < 1 || !module_offsets || !module_mean || !macro) return CQ_EINVAL;
+    if (n_groups > 0 && !scales) return CQ_EINVAL;
+    if ((n_groups + 15) / 16 > INT32_MAX || n_groups > INT64_MAX / 8 / n_policies) return CQ_EINVAL;
+    if (!per_group) {
+        if (!workspace || workspace_bytes < cq_proxy_workspace_size(n_groups * n_policies) ||
+            !aligned(workspace, ALIGN))
+            return CQ_EWORKSPACE;
+        per_group = (double*)workspace;
+    } else if (!aligned(per_group, 8)) {
+        return CQ_EINVAL;
+    }
+    return hip_status(cqk::launch_proxy_spec(w, d_eval, d_period, group_len, qmin, qmax, E, n_groups, n_policies,
+                                             scales, module_offsets, n_modules, module_mean, macro, per_group,
+                                             (hipStream_t)stream));
 }
 
 int32_t cq_proxy_worst_env_wmse(const float* w, const float* d_eval, int64_t d_period, int32_t E, int64_t n_groups,

@@ -129,6 +129,58 @@ __global__ __launch_bounds__(256) void absmax_objective_kernel(const float* __re
     }
 }
 
+// Another quantizer (group length G <= 256, codes in [qmin, qmax] with qmax >= 1): the scale
+// fp16(fl32(max|w| / qmax)), 0 -> 0x0001, overflow -> 0x7BFF (the largest magnitude maps to the
+// largest positive code, as max|w| / 7 does for [-8, 7]).  One thread per (group, environment) as
+// above, the weights read in index order; the codes shared by the group's threads; with the
+// objective, each environment's sum i = 0..G-1 with every operation rounded on its own.
+__global__ __launch_bounds__(256) void absmax_spec_kernel(const float* __restrict__ w, const float* __restrict__ d,
+                                                          int64_t d_period, int G, int qmin, int qmax, int E, int gpb,
+                                                          int64_t n_groups, uint16_t* scales, int8_t* codes,
+                                                          double* objective) {
+    __shared__ double fe[256];
+    const int c = threadIdx.x;
+    const int gl = c / E, e = c - gl * E;
+    const int64_t g = (int64_t)blockIdx.x * gpb + gl;
+    const bool live = gl < gpb && g < n_groups;
+    if (live) {
+        const float* wg = w + g * G;
+        float m = 0.0f;
+        for (int i = 0; i < G; ++i) m = fmaxf(m, fabsf(wg[i]));
+        uint32_t b = f32_to_half_bits_rne(m / (float)qmax);
+        if (b == 0u) b = BITS_FIRST;
+        if (b > BITS_LAST) b = BITS_LAST;
+        const float s = half_bits_value(b);
+        if (e == 0) scales[g] = (uint16_t)b;
+        if (codes) {
+            const int per = (G + E - 1) / E, i0 = e * per, i1 = i0 + per < G ? i0 + per : G;
+            for (int i = i0; i < i1; ++i)
+                codes[g * G + i] = (int8_t)exact_code_range(wg[i], s, (float)qmin, (float)qmax);
+        }
+        if (objective) {
+            const double s64 = (double)s;
+            fe[c] = env_error_f64_n(wg, d + (g % d_period) * (int64_t)(E * G) + (int64_t)e * G, 1, G, s64,
+                                    1.0 / s64, (double)qmin, (double)qmax);
+        }
+    }
+    __syncthreads();
+    if (objective && live && e == 0) {
+        double F = fe[c];
+        for (int k = 1; k < E; ++k) F = fe[c + k] > F ? fe[c + k] : F;
+        objective[g] = F;
+    }
+}
+
+hipError_t launch_absmax_spec(const float* w, const float* d, int64_t d_period, int G, int qmin, int qmax, int E,
+                              int64_t n_groups, uint16_t* scales, int8_t* codes, double* objective, hipStream_t st) {
+    const int Eu = objective ? E : 1;  // without the objective one thread per group
+    const int gpb = BLOCK / Eu;
+    const int64_t blocks = (n_groups + gpb - 1) / gpb;
+    hipLaunchKernelGGL(absmax_spec_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, st, w, d, d_period, G, qmin, qmax,
+                       Eu, gpb, n_groups, scales, codes, objective);
+    return hipGetLastError();
+}
+
 hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                          uint16_t* scales, int8_t* codes, double* objective, hipStream_t st) {
     if (objective) {

@@ -96,6 +96,8 @@ struct CandArgs {
 };
 hipError_t launch_candidate(const CandArgs& a, int E, hipStream_t st);
 
+hipError_t launch_absmax_spec(const float* w, const float* d, int64_t d_period, int G, int qmin, int qmax, int E,
+                              int64_t n_groups, uint16_t* scales, int8_t* codes, double* objective, hipStream_t st);
 hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                          uint16_t* scales, int8_t* codes, double* objective, hipStream_t st);
 
@@ -131,6 +133,9 @@ hipError_t launch_heldout(const double* pa, const double* pb, int64_t n, const i
                           const int32_t* idx, int B, double alpha, int64_t* counts, double* effect,
                           double* boot, double* ci, double* mm, double* reps, int32_t* rank, hipStream_t st);
 
+hipError_t launch_proxy_spec(const float* w, const float* d, int64_t d_period, int G, int qmin, int qmax, int E,
+                             int64_t n_groups, int P, const uint16_t* scales, const int64_t* module_offsets,
+                             int n_modules, double* module_mean, double* macro, double* per_group, hipStream_t st);
 hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups, int P,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,
                         double* module_mean, double* macro, double* per_group, hipStream_t st);

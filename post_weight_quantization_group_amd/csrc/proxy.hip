@@ -85,6 +85,47 @@ __global__ __launch_bounds__(256) void proxy_group_kernel(const float* __restric
     }
 }
 
+// Another quantizer (group length G <= 256, codes in [qmin, qmax]): p_g = max_e (1/G) sum_i ...;
+// 16 lanes per group as above, lane `sub` taking weights sub, sub + 16, ..., one policy at a time.
+__global__ __launch_bounds__(256) void proxy_group_spec_kernel(const float* __restrict__ w,
+                                                               const float* __restrict__ d, int64_t d_period, int G,
+                                                               int qmin, int qmax, int E, int64_t n_groups, int P,
+                                                               const uint16_t* __restrict__ scales,
+                                                               double* __restrict__ per_group) {
+    const int sub = threadIdx.x & 15;
+    const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (g >= n_groups) return;  // a group owns one whole DPP row
+    const float* wg = w + g * G;
+    const float* dg = d + (g % d_period) * (int64_t)E * G;
+    const int nk = (G - sub + 15) / 16;  // this lane's weights
+    const double qlo = (double)qmin, qhi = (double)qmax;
+    for (int p = 0; p < P; ++p) {
+        const double s = (double)half_bits_value(scales[(int64_t)p * n_groups + g]), inv = 1.0 / s;
+        double t2[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            t2[k] = 0.0;
+            if (k < nk) {
+                const double wi = (double)wg[sub + 16 * k];
+                double r = __builtin_rint(wi * inv);
+                r = r < qlo ? qlo : (r > qhi ? qhi : r);
+                const double t = wi - s * r;
+                t2[k] = t * t;
+            }
+        }
+        double worst = 0.0;
+        for (int e = 0; e < E; ++e) {
+            double part = 0.0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k < nk) part += (double)dg[(int64_t)e * G + sub + 16 * k] * t2[k];
+            part = row_sum_f64(part);
+            worst = e == 0 ? part : (part > worst ? part : worst);
+        }
+        if (sub == 0) per_group[(int64_t)p * n_groups + g] = worst / (double)G;
+    }
+}
+
 constexpr int MODULE_THREADS = 1024;
 
 // grid (n_modules, P)
@@ -138,6 +179,20 @@ __global__ __launch_bounds__(256) void proxy_macro_kernel(const double* __restri
         __syncthreads();
     }
     if (threadIdx.x == 0) macro[blockIdx.x] = red[0] / (double)n_modules;
+}
+
+hipError_t launch_proxy_spec(const float* w, const float* d, int64_t d_period, int G, int qmin, int qmax, int E,
+                             int64_t n_groups, int P, const uint16_t* scales, const int64_t* module_offsets,
+                             int n_modules, double* module_mean, double* macro, double* per_group, hipStream_t st) {
+    if (n_groups > 0) {
+        const int64_t blocks = (n_groups + 15) / 16;
+        hipLaunchKernelGGL(proxy_group_spec_kernel, dim3((unsigned)blocks), dim3(256), 0, st, w, d, d_period, G, qmin,
+                           qmax, E, n_groups, P, scales, per_group);
+    }
+    hipLaunchKernelGGL(proxy_module_kernel, dim3((unsigned)n_modules, (unsigned)P), dim3(MODULE_THREADS), 0, st,
+                       per_group, module_offsets, n_groups, n_modules, module_mean);
+    hipLaunchKernelGGL(proxy_macro_kernel, dim3((unsigned)P), dim3(256), 0, st, module_mean, n_modules, macro);
+    return hipGetLastError();
 }
 
 hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups, int P,

@@ -200,3 +200,21 @@ def test_pack_spec_rejects_bad_arguments():
     assert f(FAKE, FAKE + 1, 4, 128, 8, 32, FAKE, FAKE, None) == -1      # scales alignment
     assert f(None, FAKE, 4, 128, 8, 32, FAKE, FAKE, None) == -1
     assert f(None, None, 0, 128, 2, 16, None, None, None) == 0           # empty
+
+
+def test_spec_baseline_and_proxy_reject_bad_arguments():
+    lib = cq.load()
+    b = lib.cq_baseline_scales_spec
+    assert b(FAKE, FAKE, 0, -4, 3, 1, 4, 10, 0, FAKE, None, None, None, 0, None) == -1       # group length
+    assert b(FAKE, FAKE, 64, 1, 3, 1, 4, 10, 0, FAKE, None, None, None, 0, None) == -1       # qmin > 0
+    assert b(FAKE, FAKE, 64, -4, 0, 1, 4, 10, 0, FAKE, None, None, None, 0, None) == -1      # AbsMax, qmax 0
+    assert b(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 5, FAKE, None, None, None, 0, None) == -1      # which
+    assert b(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 1, FAKE, None, None, None, 0, None) == -2      # pooled: workspace
+    assert b(FAKE + 2, FAKE, 64, -4, 3, 1, 4, 10, 0, FAKE, None, None, None, 0, None) == -1  # w alignment
+    assert b(FAKE, FAKE, 64, -4, 3, 1, 4, 0, 0, None, None, None, None, 0, None) == 0         # empty
+    p = lib.cq_proxy_worst_env_wmse_multi_spec
+    assert p(FAKE, FAKE, 300, -4, 3, 1, 4, 10, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert p(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 0, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1  # policies
+    assert p(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 1, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0, None) == -1  # modules
+    assert p(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 1, FAKE, FAKE, 1, FAKE, FAKE, None, None, 0, None) == -2  # workspace
+    assert p(FAKE, FAKE, 64, -4, 3, 1, 33, 10, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1  # E

@@ -235,3 +235,57 @@ def test_other_quantizer_solved_and_packed_end_to_end():
     np.testing.assert_array_equal(sbits.reshape(-1), bits_np(r["scales"]))
     sol = oracle.solve(w, d, inp // G, n_threads=threads(), qmin=-2, qmax=1)
     check_minimax(w, d, inp // G, r, sol, qmin=-2, qmax=1)
+
+
+BASE_SPECS = [(-4, 3, 64, 4), (-2, 1, 32, 3), (-128, 127, 128, 4), (0, 15, 128, 2), (-8, 7, 256, 4),
+              (-3, 5, 38, 1), (-8, 7, 100, 9)]
+
+
+@pytest.mark.parametrize("qmin,qmax,G,E", BASE_SPECS, ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in BASE_SPECS])
+def test_baselines_for_other_quantizers(qmin, qmax, G, E):
+    """AbsMax for another quantizer (fp16(max|w| / qmax)): scales, codes and the binary64 objective
+    bit for bit against the oracle, the same scales and codes without the objective; the pooled
+    baseline equals the full grid's pooled policy."""
+    n = 3 * (256 // E) + 5  # a ragged last workgroup
+    w, d = _spec_groups(qmin, qmax, G, E, n, seed=9000 + G + qmax)
+    period = n - 2
+    d = d[:period]
+    ab = cq.baseline_scales(dev(w), dev(d), period, "absmax", qmin=qmin, qmax=qmax)
+    ab0 = cq.baseline_scales(dev(w), dev(d), period, "absmax", objective=False, qmin=qmin, qmax=qmax)
+    pl = cq.baseline_scales(dev(w), dev(d), period, "pooled", qmin=qmin, qmax=qmax)
+    r = _run(w, d, period, qmin=qmin, qmax=qmax)
+    bits = bits_np(ab["scales"])
+    np.testing.assert_array_equal(bits, oracle.absmax_bits(w, qmax))
+    np.testing.assert_array_equal(ab["codes"].cpu().numpy(), oracle.codes_for(w, bits, qmin, qmax))
+    np.testing.assert_array_equal(ab["objective"].cpu().numpy(), oracle.objective(w, d, bits, period, threads(),
+                                                                                  qmin, qmax))
+    np.testing.assert_array_equal(bits_np(ab0["scales"]), bits)
+    np.testing.assert_array_equal(ab0["codes"].cpu().numpy(), ab["codes"].cpu().numpy())
+    np.testing.assert_array_equal(bits_np(pl["scales"]), bits_np(r["pooled_scales"]))
+    np.testing.assert_array_equal(pl["objective"].cpu().numpy().view(np.uint64),
+                                  r["pooled_objective"].cpu().numpy().view(np.uint64))
+    np.testing.assert_array_equal(pl["codes"].cpu().numpy(), oracle.codes_for(w, bits_np(pl["scales"]), qmin, qmax))
+
+
+@pytest.mark.parametrize("qmin,qmax,G,E", BASE_SPECS[:5], ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in BASE_SPECS[:5]])
+def test_proxy_for_other_quantizers(qmin, qmax, G, E):
+    """The proxy for another quantizer (1/G for the pages' 1/128) for three policies in one call:
+    per-group values, module means and macro against the oracle within the proxy tolerance; a
+    ragged last workgroup and an empty module (NaN on both sides)."""
+    n = 16 * 5 + 9
+    w, d = _spec_groups(qmin, qmax, G, E, n, seed=9500 + G + qmax)
+    r = _run(w, d, n, qmin=qmin, qmax=qmax)
+    rng = np.random.default_rng(G + E)
+    bits = np.stack([bits_np(r["scales"]), bits_np(r["pooled_scales"]),
+                     rng.integers(0x1400, 0x2400, n).astype(np.uint16)])
+    off = np.array([0, 30, 30, 70, n], np.int64)
+    mods = np.repeat(np.arange(4), np.diff(off))
+    pg, mm, macro = cq.proxy_worst_env_wmse_multi(dev(w), dev(d), dev(bits.view(np.int16)), dev(off), qmin=qmin,
+                                                  qmax=qmax)
+    torch.cuda.synchronize()
+    pg, mm, macro = pg.cpu().numpy(), mm.cpu().numpy(), macro.cpu().numpy()
+    for k in range(3):
+        rp, rm, rmac = oracle.proxy(w, d, bits[k], mods, 4, n, threads(), qmin, qmax)
+        np.testing.assert_allclose(pg[k], rp, rtol=1e-6, atol=0)
+        np.testing.assert_allclose(mm[k], rm, rtol=1e-6, atol=0, equal_nan=True)
+        assert np.isnan(mm[k, 1]) and np.isnan(macro[k]) and np.isnan(rmac)
