@@ -57,9 +57,9 @@ def sources_hash(files) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-FULLGRID_SOURCES = ("fullgrid.hip", "device.h", "launch.h")
-BOUNDED_SOURCES = ("sweep.hip", "device.h", "launch.h")
-CANDIDATE_SOURCES = ("candidate.hip", "sweep.hip", "device.h", "launch.h")
+FULLGRID_SOURCES = ("fullgrid.hip", "device.h", "search_args.h")
+BOUNDED_SOURCES = ("sweep.hip", "device.h", "search_args.h")
+CANDIDATE_SOURCES = ("candidate.hip", "sweep.hip", "device.h", "search_args.h")
 
 
 def profile_values(name: str, files) -> dict:

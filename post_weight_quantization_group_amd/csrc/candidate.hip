@@ -37,7 +37,7 @@
 //     (kept runs, candidates, shortlist), the group is handed to the exhaustive
 //     sweep (flag FALLBACK).
 #include "device.h"
-#include "launch.h"
+#include "search_args.h"
 
 namespace cqk {
 namespace {

@@ -55,7 +55,7 @@
 //   lane's third key lies inside the bound (it may have dropped a fourth), or
 //   more than CAP patterns survive, the group goes to the binary64 sweep.
 #include "device.h"
-#include "launch.h"
+#include "search_args.h"
 
 namespace cqk {
 namespace full {

@@ -41,7 +41,7 @@
 //   its third is inside the bound (it may have dropped a fourth), or more than
 //   256 scales survive, the group is queued for the binary64 sweep.
 #include "device.h"
-#include "launch.h"
+#include "search_args.h"
 
 namespace cqk {
 
