@@ -13,7 +13,9 @@
 // operation rounded on its own, so each environment's sum is the sequential
 // binary64 definition bit for bit; the group's E threads share the codes (each
 // a contiguous share), environment 0's thread writes the scale, and the
-// maximum over environments goes through LDS.
+// maximum over environments goes through LDS.  When E is a power of two up to
+// 32 a group's threads are adjacent lanes of one wave and also share the
+// binary64 codes and squared residuals (absmax_shared_kernel).
 #include "device.h"
 #include "launch.h"
 
@@ -181,8 +183,118 @@ hipError_t launch_absmax_spec(const float* w, const float* d, int64_t d_period, 
     return hipGetLastError();
 }
 
+// The value of lane j of this lane's group of E adjacent lanes (E a power of two up to 32): a DPP
+// move within the quad for E <= 4, a lane shuffle beyond.
+template <int E>
+__device__ __forceinline__ uint32_t group_lane(uint32_t v, int j) {
+    if constexpr (E == 4) {
+        switch (j) {  // quad_perm [j, j, j, j]
+            case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
+            case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
+            case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
+            default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
+        }
+    } else if constexpr (E == 2) {  // quad_perm [j, j, 2 + j, 2 + j]
+        return (uint32_t)(j == 0 ? __builtin_amdgcn_mov_dpp((int)v, 0xA0, 0xF, 0xF, false)
+                                 : __builtin_amdgcn_mov_dpp((int)v, 0xF5, 0xF, 0xF, false));
+    } else {
+        const int lane = threadIdx.x & 63;
+        return (uint32_t)__shfl((int)v, (lane & ~(E - 1)) + j, 64);
+    }
+}
+template <int E>
+__device__ __forceinline__ double group_lane(double v, int j) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = group_lane<E>((uint32_t)u, j), hi = group_lane<E>((uint32_t)(u >> 32), j);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// E a power of two from 2 to 32: a group's E threads are adjacent lanes of one wave, so they share
+// the codes and squared residuals.  Lane e forms them for the weights i = E k + e and the group's
+// lanes pass them round, so that each environment's thread adds the 128 terms d_e (w - s q)^2 in
+// index order from the same values with the same operations as above (the same sums bit for bit),
+// with 1/E of the binary64 code work per thread.  Lanes of a group past n_groups read group 0 and
+// write nothing, so that every lane takes part in the exchanges.
+template <int E>
+__global__ __launch_bounds__(256) void absmax_shared_kernel(const float* __restrict__ w, const float* __restrict__ d,
+                                                            int64_t d_period, int64_t n_groups, uint16_t* scales,
+                                                            int8_t* codes, double* objective) {
+    constexpr int GPB = BLOCK / E, K = G / E;
+    __shared__ double fe[BLOCK];
+    const int c = threadIdx.x, e = c & (E - 1);
+    const int64_t g = (int64_t)blockIdx.x * GPB + c / E;
+    const bool live = g < n_groups;
+    const int64_t gs = live ? g : 0;
+    const float* wg = w + gs * G;
+    float wq[K];  // weights E k + e
+#pragma unroll
+    for (int k = 0; k < K; ++k) wq[k] = wg[E * k + e];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) m = fmaxf(m, fabsf(wq[k]));
+#pragma unroll
+    for (int o = 1; o < E; o <<= 1) m = fmaxf(m, lane_xor(m, o));
+    const uint32_t b = absmax_bits(m);
+    const float s = half_bits_value(b);
+    if (live && e == 0) scales[g] = (uint16_t)b;
+    if (live && codes)
+#pragma unroll
+        for (int k = 0; k < K; ++k) codes[g * G + E * k + e] = (int8_t)exact_code(wq[k], s);
+    const double s64 = (double)s, inv = 1.0 / s64;
+    const float4* dr = (const float4*)(d + (gs % d_period) * (int64_t)(E * G) + (int64_t)e * G);
+    double F = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float dl[G / 2];
+#pragma unroll
+        for (int q = 0; q < G / 8; ++q) {
+            const float4 v = dr[h * (G / 8) + q];
+            dl[4 * q] = v.x; dl[4 * q + 1] = v.y; dl[4 * q + 2] = v.z; dl[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int k = h * (K / 2); k < (h + 1) * (K / 2); ++k) {
+            // the operations of env_error_f64 for weight E k + e, then the group's E of them in order
+            const double wi = (double)wq[k];
+            const double r = __builtin_fmin(__builtin_fmax(__builtin_rint(wi * inv), -8.0), 7.0);
+            const double sq = s64 * r;
+            const double t = wi - sq;
+            const double t2 = t * t;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const double term = (double)dl[E * k + j - h * (G / 2)] * group_lane<E>(t2, j);
+                F = F + term;
+            }
+        }
+    }
+    fe[c] = F;
+    __syncthreads();
+    if (live && e == 0) {
+        double Fm = fe[c];
+#pragma unroll
+        for (int k = 1; k < E; ++k) Fm = fe[c + k] > Fm ? fe[c + k] : Fm;
+        objective[g] = Fm;
+    }
+}
+
 hipError_t launch_absmax(const float* w, const float* d, int64_t d_period, int E, int64_t n_groups,
                          uint16_t* scales, int8_t* codes, double* objective, hipStream_t st) {
+    if (objective && (E & (E - 1)) == 0 && E >= 2 && E <= 32) {
+        const int64_t blocks = (n_groups + BLOCK / E - 1) / (BLOCK / E);
+        const dim3 grid((unsigned)blocks), block(BLOCK);
+        switch (E) {
+            case 2: hipLaunchKernelGGL(absmax_shared_kernel<2>, grid, block, 0, st, w, d, d_period, n_groups, scales, codes,
+                                       objective); break;
+            case 4: hipLaunchKernelGGL(absmax_shared_kernel<4>, grid, block, 0, st, w, d, d_period, n_groups, scales, codes,
+                                       objective); break;
+            case 8: hipLaunchKernelGGL(absmax_shared_kernel<8>, grid, block, 0, st, w, d, d_period, n_groups, scales, codes,
+                                       objective); break;
+            case 16: hipLaunchKernelGGL(absmax_shared_kernel<16>, grid, block, 0, st, w, d, d_period, n_groups, scales,
+                                        codes, objective); break;
+            default: hipLaunchKernelGGL(absmax_shared_kernel<32>, grid, block, 0, st, w, d, d_period, n_groups, scales,
+                                        codes, objective); break;
+        }
+        return hipGetLastError();
+    }
     if (objective) {
         const int gpb = BLOCK / E;
         const int64_t blocks = (n_groups + gpb - 1) / gpb;
