@@ -194,7 +194,8 @@ int32_t cq_baseline_scales(const float *w, const float *d, int64_t d_period, int
  *                   outputs alone); workspace as cq_workspace_size(CQ_EXHAUSTIVE, E, n_groups).
  * codes (nullable) are those of the chosen scale; objective (nullable) max_e F_e (AbsMax) or
  * (1/E) sum_e F_e (pooled), binary64.  Limits as for cq_quantize_groups_spec; w and d 4-byte
- * aligned.  The pages' quantizer (group_len 128, [-8, 7]) is passed to cq_baseline_scales.
+ * aligned.  The pages' quantizer (group_len 128, [-8, 7]) is cq_baseline_scales itself, with its
+ * alignment rules.
  */
 int32_t cq_baseline_scales_spec(const float *w, const float *d, int32_t group_len, int32_t qmin, int32_t qmax,
                                 int64_t d_period, int32_t E, int64_t n_groups, int32_t which, uint16_t *scales,
@@ -302,8 +303,8 @@ int32_t cq_proxy_worst_env_wmse_multi(const float *w, const float *d_eval, int64
  * quantizer specification; the proxy as in cq_proxy_worst_env_wmse, with 1/group_len for the
  * pages' 1/128: the mean over the group's weights).  w is [n_groups][group_len], d_eval
  * [n_d][E][group_len]; codes in [qmin, qmax].  Arguments, limits and workspace as for
- * cq_proxy_worst_env_wmse_multi (w and d_eval 4-byte aligned); the pages' quantizer is passed to
- * it.  Per-group sums run over the group's 16 lanes (each lane's weights in index order, then a
+ * cq_proxy_worst_env_wmse_multi (w and d_eval 4-byte aligned); the pages' quantizer is
+ * cq_proxy_worst_env_wmse_multi itself, with its alignment rules.  Per-group sums run over the group's 16 lanes (each lane's weights in index order, then a
  * fixed butterfly): within rounding of the sequential definition, bit-identical across runs.
  */
 int32_t cq_proxy_worst_env_wmse_multi_spec(const float *w, const float *d_eval, int32_t group_len, int32_t qmin,
