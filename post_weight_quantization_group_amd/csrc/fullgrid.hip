@@ -23,7 +23,11 @@
 //     x = w' * r (r the reciprocal of s', below),  q = rint(x) (clipped when the
 //     chunk can clip),  e = fma(-s', q, w'),  e^2,  then E fmas into the sums.
 // A chunk cannot clip when every |w'| is at most (range end + 1/4) times its
-// smallest scale; the clip is then left out (it cannot change any code).
+// smallest scale; the clip is then left out (it cannot change any code).  In a
+// chunk that can clip, a weight whose |w'| is at least (range end - 1/4) times
+// the chunk's largest scale has the range end as its code at every scale of the
+// chunk: its terms are formed from that code, without the quotient (the vector
+// path keeps its rows in clip-ratio order, so these weights are one run).
 // Patterns are rotated over the lanes from chunk to chunk so that scales a power
 // of two apart (which tie exactly when one outlier alone carries a code) land in
 // different lanes.  Each lane keeps its best three (value, pattern) keys per
@@ -54,6 +58,8 @@
 //   when the smallest value is 0 the lowest such pattern wins directly.  When a
 //   lane's third key lies inside the bound (it may have dropped a fourth), or
 //   more than CAP patterns survive, the group goes to the binary64 sweep.
+#include <type_traits>
+
 #include "device.h"
 #include "search_args.h"
 
@@ -85,6 +91,9 @@ constexpr int min_blocks_for(int E) { return E <= 4 ? 5 : (E == 8 ? 4 : (E == 16
 // 45.7 ms for 32,768 groups (its E fmas per term are most of the work there, and the operands
 // come from one 4-byte LDS read per four environments instead of 16-byte broadcasts).
 constexpr bool use_mfma(int E) { return E >= 16; }
+// The vector path orders its rows by clip ratio and gives a clipping chunk's weights that keep one
+// code their own run (below); the matrix-core path keeps the rows in index order.
+constexpr bool sorted_rows(int E) { return !use_mfma(E); }
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int E>
@@ -109,6 +118,7 @@ struct Smem {
     double win_F[2];
     uint8_t win_flags[2];
 };
+static_assert(sizeof(double) * CAP >= sizeof(int) * GMAX, "the staging ranks and clip ratios live in cand_F and cand_P");
 
 // The value of a finite binary16 pattern by one hardware conversion (exact).
 __device__ __forceinline__ float half_value_hw(uint32_t b) {
@@ -135,25 +145,36 @@ __device__ __forceinline__ float in_vgpr(float x) {
     return r;
 }
 
-// One chunk: every lane runs the n weights against its NS scales, the per-environment sums in
-// registers.  The weight and its E diagonals are LDS broadcasts shared by the NS scales.
-template <int E, int NS, bool CLIP>
+// How a run of weights forms its codes in a chunk: the quotient, rounded, then clipped (CLIP); the
+// same without the clip, for weights that cannot leave the range at any scale of the chunk (FREE);
+// or, for weights that clip at every scale of the chunk, the range end on their side, kept in the
+// row (FIXED).  Every mode gives each term exactly the value the clipped path gives it.
+enum TermMode { FREE = 0, CLIP = 1, FIXED = 2 };
+
+// One run of rows [0, n): every lane runs the n weights against its NS scales, the per-environment
+// sums in registers.  The weight and its E diagonals are LDS broadcasts shared by the NS scales.
+template <int E, int NS, int MODE>
 __device__ __forceinline__ void chunk_terms(const float* __restrict__ rows, int n,
                                             const float (&nsv)[NS], const float (&inv)[NS], float qlo, float qhi,
                                             float (&acc)[NS][E]) {
     constexpr int RS = row_for(E);
-#pragma unroll 4
+    // rows in flight per iteration: fewer in the runs of clipping chunks from E = 8 on (measured)
+    constexpr int UNROLL = MODE == FIXED || (MODE == CLIP && E > 4) ? 2 : 4;
+#pragma unroll UNROLL
     for (int i = 0; i < n; ++i) {
         const float* row = rows + i * RS;
         const float wi = row[0];
         float di[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) di[e] = row[doff_for(E) + e];
+        const float qi = MODE == FIXED ? row[1] : 0.0f;  // the code this row keeps over the chunk
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-            const float x = wi * inv[t];
-            float r = __builtin_rintf(x);
-            if (CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
+            float r = qi;
+            if (MODE != FIXED) {
+                r = __builtin_rintf(wi * inv[t]);
+                if (MODE == CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
+            }
             const float ev = __builtin_fmaf(nsv[t], r, wi);
             const float e2 = ev * ev;
 #pragma unroll
@@ -162,16 +183,17 @@ __device__ __forceinline__ void chunk_terms(const float* __restrict__ rows, int 
     }
 }
 
-// The same chunk with the environment sums on the matrix cores.  v_mfma_f32_4x4x1f32 treats the
+// The same run with the environment sums on the matrix cores.  v_mfma_f32_4x4x1f32 treats the
 // wave as 16 blocks of four lanes: block b forms D[i][j] = C[i][j] + A_(4b+i) * B_(4b+j), kept in
 // register i of lane 4b+j.  With A the diagonal of environment 4k + (lane & 3) and B the lane's own
 // e^2, register i of lane L accumulates environment 4k + i of L's own scale: the same sums as the
 // vector path, one fused multiply-add per term, and the vector unit is left the quotient, the
 // rounding, the clip, the residual and the square.
-template <int E, int NS, bool CLIP>
+template <int E, int NS, int MODE>
 __device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, int n,
                                                const float (&nsv)[NS], const float (&inv)[NS], float qlo,
                                                float qhi, int lane4, v4f (&acc)[NS][E / 4]) {
+    static_assert(MODE != FIXED, "the matrix-core rows hold no code");
     constexpr int RS = row_for(E);
     for (int i = 0; i < n; ++i) {
         const float* row = rows + i * RS;
@@ -181,15 +203,39 @@ __device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, i
         for (int k = 0; k < E / 4; ++k) dl[k] = row[doff_for(E) + 4 * k + lane4];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-            const float x = wi * inv[t];
-            float r = __builtin_rintf(x);
-            if (CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
+            float r = __builtin_rintf(wi * inv[t]);
+            if (MODE == CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
             const float ev = __builtin_fmaf(nsv[t], r, wi);
             const float e2 = ev * ev;
 #pragma unroll
             for (int k = 0; k < E / 4; ++k) acc[t][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(dl[k], e2, acc[t][k], 0, 0, 0);
         }
     }
+}
+
+// The runs of a clipping chunk on the vector path.  With s0 <= s <= s1 the chunk's scales and
+// u = 2^-24 (the quotient x~ within 2.0001 u |x| of w'/s, as for the screen's bound):
+//   * w' >= (qmax - 1/4) s1 (1 + 2^-20) > 0 gives x~ > qmax - 1/4 at every scale: code qmax;
+//   * w' <= (qmin + 1/4) s1 (1 + 2^-20) < 0 gives x~ < qmin + 1/4 at every scale: code qmin.
+// The thresholds themselves take two roundings (4 u in all), far inside the 2^-20 margin.  The
+// rows are in descending order of |w| over the end of the range on its side (staging), so the
+// weights with one code over the chunk lead: the chunk runs [0, f) with each row's own code, f the
+// first row that meets neither condition, and [f, G) clipped.  (A third run, the unclipped tail,
+// would save one instruction on about 8% of the terms but pushes the kernel past the registers of
+// five workgroups per CU.)  The sums meet the terms in row order whatever the runs.  The
+// matrix-core rows hold no code: that path clips the whole chunk.
+__device__ __forceinline__ int fixed_run_end(const float* __restrict__ rows, int RS, int G, int qmin, int qmax,
+                                             float s1) {
+    const int lane = threadIdx.x & 63;
+    const float tA = qmin < 0 ? ((float)qmin + 0.25f) * s1 * (1.0f + 0x1p-20f) : -__builtin_inff();
+    const float tF = qmax > 0 ? ((float)qmax - 0.25f) * s1 * (1.0f + 0x1p-20f) : __builtin_inff();
+    for (int k0 = 0; k0 < G; k0 += 64) {
+        const int k = k0 + lane;
+        const float x = k < G ? rows[k * RS] : 0.0f;
+        const uint64_t m = __ballot(k < G && !(x >= tF || x <= tA));
+        if (m != 0) return k0 + (int)__builtin_ctzll(m);
+    }
+    return G;
 }
 
 // binary64 rescoring of shortlist entries [0, n): cand_F = max_e F_e, cand_P = (sum_e F_e)/E,
@@ -277,12 +323,46 @@ __device__ int stage_group(const FullArgs& a, int64_t g, Smem<E>& sm, float& pk_
     const float* wg = a.w + g * G;
     const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
 
-    // ---- staging (environments a.E..E-1 are zero padding)
+    // ---- staging (environments a.E..E-1 are zero padding).  On the vector path the screen's rows
+    // go in descending order of the clip ratio |w| / (range end on w's side) (ties by index), so
+    // that in a chunk the weights that clip at every scale come first: weight i's row is its rank,
+    // the number of weights ahead of it.  The order changes no term, only the order of each sum's
+    // additions, which the screen's bound does not depend on.  A NaN weight may give two weights
+    // one rank (always within 0..G-1); such a group is rejected below before any row is read.
     constexpr int RS = row_for(E);
-    for (int i = tid; i < G; i += BLOCK) sm.w[i] = wg[i];
-    for (int j = tid; j < G * RS; j += BLOCK) {
-        const int i = j / RS, f = j - i * RS, e = f - doff_for(E);
-        sm.rows[j] = (e >= 0 && e < a.E) ? dg[(int64_t)e * G + i] : 0.0f;
+    int* rank = reinterpret_cast<int*>(sm.cand_F);  // free until the shortlist is rescored
+    if constexpr (sorted_rows(E)) {
+        static_assert(doff_for(E) >= 2, "a sorted row keeps its clip code in slot 1");
+        float* ratio = reinterpret_cast<float*>(sm.cand_P);
+        for (int i = tid; i < G; i += BLOCK) {
+            const float x = wg[i];
+            sm.w[i] = x;
+            ratio[i] = x > 0.0f ? (a.qmax > 0 ? x / (float)a.qmax : 0.0f) : (a.qmin < 0 ? x / (float)a.qmin : 0.0f);
+        }
+        __syncthreads();
+        for (int i = tid; i < G; i += BLOCK) {
+            const float x = ratio[i];
+            int r = 0;
+            for (int j = 0; j < G; ++j) {
+                const float y = ratio[j];
+                r += (y > x || (y == x && j < i)) ? 1 : 0;
+            }
+            rank[i] = r;
+        }
+        __syncthreads();
+        for (int j = tid; j < G * RS; j += BLOCK) {
+            const int i = j / RS, f = j - i * RS, e = f - doff_for(E);
+            sm.rows[rank[i] * RS + f] = (e >= 0 && e < a.E) ? dg[(int64_t)e * G + i] : 0.0f;
+        }
+    } else {
+        for (int i = tid; i < G; i += BLOCK) {
+            sm.w[i] = wg[i];
+            rank[i] = i;
+        }
+        for (int j = tid; j < G * RS; j += BLOCK) {
+            const int i = j / RS, f = j - i * RS, e = f - doff_for(E);
+            sm.rows[j] = (e >= 0 && e < a.E) ? dg[(int64_t)e * G + i] : 0.0f;
+        }
     }
     __syncthreads();
 
@@ -326,7 +406,12 @@ __device__ int stage_group(const FullArgs& a, int64_t g, Smem<E>& sm, float& pk_
     }
     if (!safe) return 2;
     const float pk = ldexpf(1.0f, k);
-    for (int i = tid; i < G; i += BLOCK) sm.rows[i * RS] = sm.w[i] * pk;
+    for (int i = tid; i < G; i += BLOCK) {
+        const float x = sm.w[i];
+        sm.rows[rank[i] * RS] = x * pk;
+        // the code the weight takes at every scale where it clips (the vector rows' slot 1)
+        if (sorted_rows(E)) sm.rows[rank[i] * RS + 1] = x > 0.0f ? (float)a.qmax : (x < 0.0f ? (float)a.qmin : 0.0f);
+    }
     if (tid == 0) {
         sm.n_cand = 0;
         sm.overflow = 0;
@@ -367,6 +452,13 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
 #pragma unroll
     for (int r = 0; r < 3; ++r) { mk[r] = KEY_NONE; qk[r] = KEY_NONE; }
     for (int c = wave + 4 * slice; c < NCHUNK; c += 4 * S) {
+        const float s0 = half_value_hw(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
+        const bool clips = !(cmax <= s0);
+        int end = 0;  // clipping chunks on the vector path: rows [0, end) keep one code over the chunk
+        if (sorted_rows(E) && clips) {
+            const float s1 = half_value_hw(min(BITS_FIRST + (uint32_t)(c * CHUNK + CHUNK - 1), BITS_LAST)) * pk;
+            end = fixed_run_end(sm.rows, row_for(E), G, a.qmin, a.qmax, s1);
+        }
         float nsv[NS], inv[NS];
         float acc[NS][E];
         const int rot = (lane + 5 * c) & 63;
@@ -380,17 +472,16 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
             const float r0 = __builtin_amdgcn_rcpf(s);
             inv[t] = __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
         }
-        const float s0 = half_value_hw(BITS_FIRST + (uint32_t)(c * CHUNK)) * pk;
         if constexpr (use_mfma(E)) {
             v4f am[NS][E / 4];
 #pragma unroll
             for (int t = 0; t < NS; ++t)
 #pragma unroll
                 for (int k = 0; k < E / 4; ++k) am[t][k] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-            if (cmax <= s0)
-                chunk_terms_mf<E, NS, false>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
+            if (!clips)
+                chunk_terms_mf<E, NS, FREE>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
             else
-                chunk_terms_mf<E, NS, true>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
+                chunk_terms_mf<E, NS, CLIP>(sm.rows, G, nsv, inv, qlo, qhi, lane & 3, am);
 #pragma unroll
             for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -400,10 +491,12 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
             for (int t = 0; t < NS; ++t)
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
-            if (cmax <= s0)
-                chunk_terms<E, NS, false>(sm.rows, G, nsv, inv, qlo, qhi, acc);
-            else
-                chunk_terms<E, NS, true>(sm.rows, G, nsv, inv, qlo, qhi, acc);
+            if (!clips) {
+                chunk_terms<E, NS, FREE>(sm.rows, G, nsv, inv, qlo, qhi, acc);
+            } else {
+                if (end > 0) chunk_terms<E, NS, FIXED>(sm.rows, end, nsv, inv, qlo, qhi, acc);
+                if (end < G) chunk_terms<E, NS, CLIP>(sm.rows + end * row_for(E), G - end, nsv, inv, qlo, qhi, acc);
+            }
         }
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
@@ -434,6 +527,17 @@ __device__ void decide_and_write(const FullArgs& a, int64_t g, Smem<E>& sm) {
     if (sm.overflow || n > CAP) {
         if (tid == 0) queue_f64(a, g);
         return;
+    }
+    if (sorted_rows(E) && n > 0) {
+        // the diagonals back in index order (the screen's rows are in clip-ratio order):
+        // rescoring adds each environment's terms over i = 0..G-1
+        constexpr int RS = row_for(E);
+        const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
+        for (int j = tid; j < G * RS; j += BLOCK) {
+            const int i = j / RS, f = j - i * RS, e = f - doff_for(E);
+            sm.rows[j] = (e >= 0 && e < a.E) ? dg[(int64_t)e * G + i] : 0.0f;
+        }
+        __syncthreads();
     }
     rescore<E>(sm, n, G, a.E, (double)a.qmin, (double)a.qmax);
     if (wave < 2) {
