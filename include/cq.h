@@ -76,7 +76,8 @@ extern "C" {
  *                 every scale its error bound cannot rule out.  No scale is skipped.
  *  CQ_CANDIDATE   the production solver's idea (same section): candidates from code transitions,
  *                 quadratic vertices and environment intersections; groups whose direct
- *                 candidates tie exactly go to CQ_BOUNDED (README and model card, "Verification").
+ *                 candidates tie exactly go to CQ_BOUNDED (CQ_EXHAUSTIVE for another quantizer;
+ *                 README and model card, "Verification").
  *  CQ_BOUNDED     branch and bound over the grid: stops at the first scale >= 2 max|w| (every
  *                 larger one ties with it exactly and loses to it), takes chunk-constant codes in
  *                 closed form and skips chunks of scales whose proven lower bound exceeds the
@@ -144,8 +145,10 @@ int32_t cq_quantize_groups(const float *w, const float *d, int64_t d_period, int
  *   d      float32 [n_d][E][group_len], 4-byte aligned; group g uses slice g % d_period.
  *   codes  out, nullable, int8 [n_groups][group_len].
  * 1 <= group_len <= CQ_MAX_GROUP, -128 <= qmin <= 0 <= qmax <= 127, qmin < qmax (else
- * CQ_EINVAL).  (128, -8, 7) is cq_quantize_groups itself, with its alignment rules; any
- * other quantizer is served by CQ_EXHAUSTIVE only (CQ_EUNSUPPORTED for the other methods).
+ * CQ_EINVAL).  (128, -8, 7) is cq_quantize_groups itself, with its alignment rules.  Any
+ * other quantizer is served by CQ_EXHAUSTIVE, and by CQ_CANDIDATE when group_len <= 128 and
+ * -8 <= qmin, qmax <= 8 (its tied groups then go to CQ_EXHAUSTIVE, flag CQ_FLAG_FALLBACK;
+ * pooled outputs CQ_EUNSUPPORTED); other methods and quantizers return CQ_EUNSUPPORTED.
  * Other outputs, workspace and errors as for cq_quantize_groups.
  */
 int32_t cq_quantize_groups_spec(const float *w, const float *d, int32_t group_len, int32_t qmin, int32_t qmax,

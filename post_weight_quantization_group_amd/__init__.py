@@ -324,8 +324,9 @@ def quantize_groups(w, d, d_period=None, method="exhaustive", codes=True, pooled
 
     w is float32 [n_groups, G] and d float32 [n_d, E, G]; G = 128 with codes in [qmin, qmax] =
     [-8, 7] is the pages' quantizer, any other G <= 256 or range goes through
-    cq_quantize_groups_spec (method "exhaustive" only).  method: "exhaustive" (every scale),
-    "bounded" (branch and bound) or "candidate"; all give the same result.
+    cq_quantize_groups_spec (method "exhaustive", or "candidate" for G <= 128 and
+    -8 <= qmin, qmax <= 8).  method: "exhaustive" (every scale), "bounded" (branch and bound) or
+    "candidate"; all give the same result.
     Returns a dict of device tensors: scales (uint16 bit patterns held in int16
     storage -> use ``.view(torch.uint16)`` or ``& 0xFFFF``), codes, objective,
     flags and, with ``pooled=True``, pooled_scales and pooled_objective.
@@ -486,8 +487,9 @@ def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax:
     ``weights`` has at most 256 entries, ``environment_diagonals`` is [E][len(weights)].  For
     the pages' range [-8, 7] a group shorter than 128 is zero-padded to 128 (a zero weight adds
     nothing at any scale) and any method serves it (default "candidate"); other ranges run the
-    group at its own length through the exhaustive method.  Returns (scale as float, objective,
-    codes list).
+    group at its own length, by default through the candidate solver where it takes the
+    quantizer (at most 128 weights, -8 <= qmin, qmax <= 8) and the exhaustive method elsewhere.
+    Returns (scale as float, objective, codes list).
     """
     n = len(weights)
     if not 1 <= n <= MAX_GROUP:
@@ -495,7 +497,7 @@ def solve_breakpoint_exact(weights, environment_diagonals, qmin: int = -8, qmax:
     E = len(environment_diagonals)
     L = GROUP if (qmin, qmax) == (-8, 7) and n <= GROUP else n
     if method is None:
-        method = "candidate" if L == GROUP and (qmin, qmax) == (-8, 7) else "exhaustive"
+        method = "candidate" if L <= GROUP and qmin >= -8 and qmax <= 8 else "exhaustive"
     w = torch.zeros((1, L), dtype=torch.float32)
     w[0, :n] = torch.tensor(weights, dtype=torch.float32)
     d = torch.zeros((1, E, L), dtype=torch.float32)

@@ -32,6 +32,10 @@ bool spec_ok(int32_t G, int32_t qmin, int32_t qmax) {
     return G >= 1 && G <= CQ_MAX_GROUP && qmin >= -128 && qmin <= 0 && qmax >= 0 && qmax <= 127 && qmin < qmax;
 }
 
+// Quantizers the candidate solver takes besides the pages' own: at most 8 codes on each side of
+// zero (8 transition slots per weight) and groups of at most 128 weights.
+bool cand_spec_ok(int32_t G, int32_t qmin, int32_t qmax) { return G <= CQ_GROUP && qmin >= -8 && qmax <= 8; }
+
 int32_t run_fullgrid(const float* w, const float* d, int32_t G, int32_t qmin, int32_t qmax, int64_t d_period, int32_t E,
                      int64_t n_groups, uint16_t* scales, int8_t* codes, double* objective, uint8_t* flags,
                      uint16_t* pooled_scales, double* pooled_objective, int want_minimax, uint8_t* ws,
@@ -107,6 +111,7 @@ int32_t cq_quantize_groups(const float* w, const float* d, int64_t d_period, int
     }
     cqk::CandArgs c{};
     c.w = w; c.d = d; c.d_period = d_period; c.n_groups = n_groups;
+    c.G = CQ_GROUP; c.qmin = -8; c.qmax = 7; c.start_ratio = 1.0f / 9.0f;
     c.scales = scales; c.codes = codes; c.objective = objective; c.flags = flags;
     c.tie_count = (int32_t*)ws;
     c.tie_list = (int32_t*)(ws + ALIGN);
@@ -139,15 +144,45 @@ int32_t cq_quantize_groups_spec(const float* w, const float* d, int32_t group_le
     if (group_len == CQ_GROUP && qmin == -8 && qmax == 7)
         return cq_quantize_groups(w, d, d_period, E, n_groups, method, scales, codes, objective, flags, pooled_scales,
                                   pooled_objective, workspace, workspace_bytes, stream);
-    if (method != CQ_EXHAUSTIVE) return CQ_EUNSUPPORTED;
+    const bool cand = method == CQ_CANDIDATE && cand_spec_ok(group_len, qmin, qmax);
+    if (method != CQ_EXHAUSTIVE && !cand) return CQ_EUNSUPPORTED;
     if (!groups_ok(w, d, d_period, E, n_groups, 4)) return CQ_EINVAL;
     if (n_groups > 0 && !scales) return CQ_EINVAL;
     if (n_groups > INT32_MAX) return CQ_EINVAL;
+    if (cand && (pooled_scales || pooled_objective)) return CQ_EUNSUPPORTED;
     if (n_groups == 0) return CQ_OK;
     if (!workspace || workspace_bytes < cq_workspace_size(method, E, n_groups) || !aligned(workspace, ALIGN))
         return CQ_EWORKSPACE;
-    return run_fullgrid(w, d, group_len, qmin, qmax, d_period, E, n_groups, scales, codes, objective, flags,
-                        pooled_scales, pooled_objective, 1, (uint8_t*)workspace, (hipStream_t)stream);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    if (!cand)
+        return run_fullgrid(w, d, group_len, qmin, qmax, d_period, E, n_groups, scales, codes, objective, flags,
+                            pooled_scales, pooled_objective, 1, ws, st);
+    // the candidate solver; the groups whose direct candidates tied are decided by the full grid
+    // (list mode), which takes every quantizer
+    cqk::CandArgs c{};
+    c.w = w; c.d = d; c.d_period = d_period; c.n_groups = n_groups;
+    c.G = group_len; c.qmin = qmin; c.qmax = qmax;
+    c.start_ratio = 1.0f / (float)((-qmin > qmax ? -qmin : qmax) + 1);
+    c.scales = scales; c.codes = codes; c.objective = objective; c.flags = flags;
+    c.tie_count = (int32_t*)ws;
+    c.tie_list = (int32_t*)(ws + ALIGN);
+    uint8_t* fws = ws + ALIGN + round_up((size_t)n_groups * 4u);  // sweep_ws(n_groups) bytes
+    hipError_t e = cqk::launch_candidate(c, E, st);
+    if (e != hipSuccess) return CQ_EHIP;
+    cqk::FullArgs a{};
+    a.w = w; a.d = d; a.d_period = d_period; a.G = group_len; a.qmin = qmin; a.qmax = qmax;
+    a.ratio = cqk::fullgrid_ratio(group_len, qmin, qmax, E);
+    a.scales = scales; a.codes = codes; a.objective = objective; a.flags = flags;
+    a.want_minimax = 1;
+    a.want_pooled = 0;
+    a.fb_count = (int32_t*)fws;
+    a.fb_list = (int32_t*)(fws + ALIGN);
+    a.parts = (cqk::SlicePart*)(fws + full_ws(n_groups));
+    a.list = c.tie_list;
+    a.list_count = c.tie_count;
+    a.flag_or = CQ_FLAG_FALLBACK;
+    return hip_status(cqk::launch_fullgrid(a, E, n_groups, st));
 }
 
 int32_t cq_baseline_scales(const float* w, const float* d, int64_t d_period, int32_t E, int64_t n_groups,

@@ -9,7 +9,8 @@
 // binary16 grid:
 //
 //  0. Window.  Scales below a bound from the best single clipped weight
-//     against F at max|w|/9 cannot be optimal; no transition below it is kept.
+//     against F at max|w|/9 (max|w|/(X + 1) for another code range, X its larger
+//     end magnitude) cannot be optimal; no transition below it is kept.
 //  1. Code transitions.  For w_i != 0 and each c with |q_i| able to fall from
 //     c+1 to c, the first grid pattern t where |q_i(s_t)| <= c.  The test
 //     |q| <= c  <=>  |w| < (c+1/2) s  or  (|w| == (c+1/2) s and c even)  is
@@ -36,6 +37,12 @@
 //     value wins; if two distinct patterns tie bit for bit, or a list overflows
 //     (kept runs, candidates, shortlist), the group is handed to the exhaustive
 //     sweep (flag FALLBACK).
+//
+// Quantizers.  Besides the pages' [-8, 7] on groups of 128, the solver takes any code range
+// [qmin, qmax] with -8 <= qmin <= 0 <= qmax <= 8 on groups of up to 128 weights (the quantizer
+// specification of the README's "Use the solver"): a weight has at most max(qmax, -qmin)
+// transitions, which the 8 event slots per weight hold, and a shorter group is padded in LDS with
+// zero weights, which change no code, no sum and no transition.
 #include "device.h"
 #include "search_args.h"
 
@@ -301,12 +308,19 @@ template <int E>
 __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     constexpr int RCAP = CandSmem<E>::RCAP;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* wg = a.w + g * G;
-    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * G);
+    const int Gn = a.G;  // the group's own length; weights Gn..G-1 are zero padding
+    const float qlo = (float)a.qmin, qhi = (float)a.qmax;
+    const float* wg = a.w + g * Gn;
+    const float* dg = a.d + (g % a.d_period) * (int64_t)(a.E * Gn);
 
-    // ---- staging and input checks (environments a.E..E-1 are zero padding)
-    if (tid < G) sm.w[tid] = wg[tid];
-    for (int j = tid; j < E * G; j += BLOCK) sm.d[j] = j / G < a.E ? dg[j] : 0.0f;
+    // ---- staging and input checks (environments a.E..E-1 and weights Gn..G-1 are zero padding:
+    //      a zero weight has code 0 and residual 0 at every scale, so it adds an exact 0.0 to
+    //      every sum and starts no transition)
+    if (tid < G) sm.w[tid] = tid < Gn ? wg[tid] : 0.0f;
+    for (int j = tid; j < E * G; j += BLOCK) {
+        const int e = j / G, i = j - e * G;
+        sm.d[j] = (e < a.E && i < Gn) ? dg[e * Gn + i] : 0.0f;
+    }
     if (tid == 0) { sm.n_runs = 0; sm.n_q = 0; sm.n_cand = 0; sm.n_ev = 0; }
     __syncthreads();
     float bad = 0.0f;
@@ -319,7 +333,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     float red2[2] = {bad, tid < G ? fabsf(sm.w[tid]) : 0.0f};
     block_max_fn<2>(red2, sm.redf);
     if (red2[0] != 0.0f) {
-        if (tid < G && a.codes) a.codes[g * G + tid] = 0;
+        if (tid < Gn && a.codes) a.codes[g * Gn + tid] = 0;
         if (tid == 0) {
             a.scales[g] = 0;
             if (a.objective) a.objective[g] = __builtin_nan("");
@@ -329,10 +343,11 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     }
     const float wmax = red2[1];
 
-    // ---- 0. where the optimum can lie.  U = F at s_a = binary16(max|w|/9) (binary64) bounds
-    //         the optimum from above; the minimax optimum usually lies near there, below the
-    //         AbsMax scale, so U is tighter than at max|w|/7.  Below y_i = |w_i|/|q_i| (q_i = 7
-    //         for w_i > 0, -8 otherwise) weight i is clipped and its residual is |w_i| - |q_i| s,
+    // ---- 0. where the optimum can lie.  U = F at s_a = binary16(max|w|/(X + 1)) (binary64, X the
+    //         larger magnitude of the range ends: max|w|/9 for [-8, 7]) bounds the optimum from
+    //         above; the minimax optimum usually lies near there, below the AbsMax scale, so U is
+    //         tighter than at max|w|/7.  Below y_i = |w_i|/|q_i| (q_i = qmax for w_i > 0, qmin
+    //         otherwise) weight i is clipped and its residual is |w_i| - |q_i| s,
     //         so every scale with s <= (|w_i| - sqrt(1.0001 U / max_e d_ei)) / |q_i| has
     //         max_e F_e(s) > U: it is neither the answer nor a tie with it.  The largest such
     //         bound over the weights (less 2^-40 for the binary64 roundings) gives the first
@@ -341,13 +356,13 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     //         scan) and then its bound.
     uint32_t win_lo = BITS_FIRST;  // the window of patterns that can hold the optimum
     const uint32_t win_hi = BITS_LAST;
-    uint32_t b_a = f32_to_half_bits_rne(wmax * (1.0f / 9.0f));
+    uint32_t b_a = f32_to_half_bits_rne(wmax * a.start_ratio);
     b_a = b_a < BITS_FIRST ? BITS_FIRST : (b_a > BITS_LAST ? BITS_LAST : b_a);
     {
         const float sa = half_bits_value(b_a);
         double dmax = 0.0;
         if (wave < 2) {
-            const double r = __builtin_fma(-(double)sa, (double)exact_code(sm.w[tid], sa), (double)sm.w[tid]);
+            const double r = __builtin_fma(-(double)sa, (double)exact_code_range(sm.w[tid], sa, qlo, qhi), (double)sm.w[tid]);
             const double r2 = r * r;
             // the environments' wave sums side by side (DPP scans; lane 63 holds each total)
 #pragma unroll
@@ -362,9 +377,11 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         double U = 0.0;
         for (int e = 0; e < E; ++e) U = fmax(U, sm.part[0][e] + sm.part[1][e]);
         double lo = -1.0;
+        // (a weight whose side of the range holds only code 0 keeps its residual |w| at every
+        // scale and bounds nothing)
         if (wave < 2 && dmax > 0.0 && wmax > 0.0f) {
-            const double aw = fabs((double)sm.w[tid]), qa = sm.w[tid] > 0.0f ? 7.0 : 8.0;
-            lo = (aw - __builtin_sqrt(1.0001 * U / dmax)) / qa * (1.0 - 0x1p-40);
+            const double aw = fabs((double)sm.w[tid]), qa = sm.w[tid] > 0.0f ? (double)a.qmax : -(double)a.qmin;
+            if (qa > 0.0) lo = (aw - __builtin_sqrt(1.0001 * U / dmax)) / qa * (1.0 - 0x1p-40);
         }
         lo = -block_min_d(-lo, sm.redd);  // the largest bound over the weights
         // the first pattern above lo (never above b_a: F(s_a) <= U), the same in every thread
@@ -384,7 +401,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         const int i = tid >> 1, c0 = 4 * (tid & 1);
         const float wi = sm.w[i];
         const float aw = fabsf(wi);
-        const int cmax = wi > 0.0f ? 6 : 7;
+        const int cmax = wi > 0.0f ? a.qmax - 1 : -a.qmin - 1;  // the clip caps |q| at the range end
         int m0 = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -658,7 +675,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
     if (n_runs <= RCAP) {
         for (int j = tid; j < n_runs * G; j += BLOCK) {
             const int r = j / G, i = j % G;
-            sm.qbuf[r][i] = (uint8_t)fabsf(exact_code(sm.w[i], half_bits_value(sm.run_lo[r])));
+            sm.qbuf[r][i] = (uint8_t)fabsf(exact_code_range(sm.w[i], half_bits_value(sm.run_lo[r]), qlo, qhi));
         }
         __syncthreads();
         // four consecutive threads per (run, environment), 32 weights each
@@ -735,7 +752,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         for (int j = tid; j < nb * G; j += BLOCK) {
             const int c = j / G, i = j % G;
             const float sf = half_bits_value(sm.cand_b[base + c]);
-            const double sq = (double)sf * (double)exact_code(sm.w[i], sf);
+            const double sq = (double)sf * (double)exact_code_range(sm.w[i], sf, qlo, qhi);
             const double t = (double)sm.w[i] - sq;
             const double t2 = t * t;
 #pragma unroll
@@ -809,7 +826,7 @@ __device__ void candidate_group(const CandArgs& a, int64_t g, CandSmem<E>& sm) {
         return;
     }
     const uint32_t b = sm.win_b;
-    if (tid < G && a.codes) a.codes[g * G + tid] = (int8_t)exact_code(sm.w[tid], half_bits_value(b));
+    if (tid < Gn && a.codes) a.codes[g * Gn + tid] = (int8_t)exact_code_range(sm.w[tid], half_bits_value(b), qlo, qhi);
     if (tid == 0) {
         a.scales[g] = (uint16_t)b;
         if (a.objective) a.objective[g] = sm.win_F;

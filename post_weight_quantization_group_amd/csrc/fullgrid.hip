@@ -437,7 +437,7 @@ __device__ void write_bad(const FullArgs& a, int64_t g) {
         if (a.objective) a.objective[g] = __builtin_nan("");
         if (a.pscales) a.pscales[g] = 0;
         if (a.pobjective) a.pobjective[g] = __builtin_nan("");
-        if (a.flags) a.flags[g] = FLAG_BAD_INPUT;
+        if (a.flags) a.flags[g] = FLAG_BAD_INPUT | a.flag_or;
     }
 }
 
@@ -555,12 +555,12 @@ __device__ void decide_and_write(const FullArgs& a, int64_t g, Smem<E>& sm) {
         if (a.want_minimax) {
             a.scales[g] = (uint16_t)sm.win_b[0];
             if (a.objective) a.objective[g] = sm.win_F[0];
-            if (a.flags) a.flags[g] = sm.win_flags[0];
+            if (a.flags) a.flags[g] = sm.win_flags[0] | a.flag_or;
         }
         if (a.want_pooled) {
             if (a.pscales) a.pscales[g] = (uint16_t)sm.win_b[1];
             if (a.pobjective) a.pobjective[g] = sm.win_F[1];
-            if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1];
+            if (!a.want_minimax && a.flags) a.flags[g] = sm.win_flags[1] | a.flag_or;
         }
     }
 }
@@ -629,6 +629,22 @@ template <int E>
 __global__ __launch_bounds__(BLOCK, min_blocks_for(E)) void full_screen_kernel(FullArgs a) {
     __shared__ Smem<E> sm;
     screen_group<E>(a, (int64_t)blockIdx.x + a.group_offset, sm);
+}
+
+// List mode: the groups a.list[0 .. *a.list_count - 1], each workgroup taking every gridDim.x-th
+// entry (the count is known only on the device).  Every return inside screen_group is taken by the
+// whole workgroup, and the barrier keeps one group's LDS from being restaged under another's reads.
+// The loop around the search needs more registers than one group does: fewer workgroups per CU
+// (three at E = 4, one fewer elsewhere) keep it free of spills.
+constexpr int list_blocks_for(int E) { return E == 4 ? 3 : (min_blocks_for(E) > 1 ? min_blocks_for(E) - 1 : 1); }
+template <int E>
+__global__ __launch_bounds__(BLOCK, list_blocks_for(E)) void full_list_kernel(FullArgs a) {
+    __shared__ Smem<E> sm;
+    const int cnt = *a.list_count;
+    for (int k = blockIdx.x; k < cnt; k += gridDim.x) {
+        screen_group<E>(a, (int64_t)a.list[k], sm);
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ few groups: slices
@@ -863,12 +879,12 @@ __device__ void f64_group(const FullArgs& a, int64_t g, F64Smem<E>& sm) {
         if (a.want_minimax) {
             a.scales[g] = (uint16_t)sm.rb[0];
             if (a.objective) a.objective[g] = sm.rv[0];
-            if (a.flags) a.flags[g] = fF;
+            if (a.flags) a.flags[g] = fF | a.flag_or;
         }
         if (a.want_pooled) {
             if (a.pscales) a.pscales[g] = (uint16_t)sm.pb[0];
             if (a.pobjective) a.pobjective[g] = sm.pv[0];
-            if (!a.want_minimax && a.flags) a.flags[g] = fP;
+            if (!a.want_minimax && a.flags) a.flags[g] = fP | a.flag_or;
         }
     }
     __syncthreads();
@@ -892,13 +908,18 @@ hipError_t launch_e(const FullArgs& a_in, int64_t n_groups, hipStream_t st) {
     // few groups: S slices per group, about 2,048 workgroups in all, at most one chunk per wave
     constexpr int S_MAX = nchunk_for(E) / 4 < 32 ? nchunk_for(E) / 4 : 32;
     int S = 1;
-    if (n_groups < 1024 && a.parts) {
+    if (n_groups < 1024 && a.parts && !a.list) {
         S = (int)((2048 + n_groups - 1) / n_groups);
         S = S > S_MAX ? S_MAX : S;
         while (S > 1 && n_groups * S > SLICE_PARTS) --S;
     }
     a.slices = S;
-    if (S > 1) {
+    if (a.list) {
+        // as many workgroups as stay resident (fewer when the list cannot be that long)
+        const int64_t cap = 256 * list_blocks_for(E);
+        const int64_t nb = n_groups < cap ? n_groups : cap;
+        hipLaunchKernelGGL(full_list_kernel<E>, dim3((unsigned)nb), dim3(BLOCK), 0, st, a);
+    } else if (S > 1) {
         hipLaunchKernelGGL(full_slice_kernel<E>, dim3((unsigned)(n_groups * S)), dim3(BLOCK), 0, st, a);
         hipLaunchKernelGGL(full_merge_kernel<E>, dim3((unsigned)n_groups), dim3(BLOCK), 0, st, a);
     } else {

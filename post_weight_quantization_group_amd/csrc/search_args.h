@@ -78,15 +78,21 @@ struct FullArgs {
     int32_t* fb_list;          // n_groups entries
     SlicePart* parts;          // SLICE_PARTS entries (few groups split over slices); nullable
     int slices;                // workgroups per group (set by the launcher)
+    const int32_t* list;       // list mode: the group ids to search (nullable: groups 0..n_groups-1)
+    const int32_t* list_count; // list mode: device count of `list` (at most n_groups)
+    uint8_t flag_or;           // ORed into every flags byte written (CQ_FLAG_FALLBACK in list mode)
 };
 float fullgrid_ratio(int G, int qmin, int qmax, int E);
 hipError_t launch_fullgrid(const FullArgs& a, int E, int64_t n_groups, hipStream_t st);
 
 struct CandArgs {
-    const float* w;
-    const float* d;
+    const float* w;       // [n_groups][G]
+    const float* d;       // [n_d][E][G]
     int64_t d_period;
     int E;
+    int G;                // 1..128 weights per group (the kernel pads to 128 with zero weights)
+    int qmin, qmax;       // code range: -8 <= qmin <= 0 <= qmax <= 8, qmin < qmax
+    float start_ratio;    // binary32 1/(max(qmax, -qmin) + 1): the probe scale is max|w| times this
     int64_t n_groups;
     uint16_t* scales;
     int8_t* codes;

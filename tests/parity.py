@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import oracle
+import workloads as W
 
 GAP = 1e-9      # scale bits must match when the oracle's runner-up gap exceeds this (relative)
 OBJ_TOL = 1e-9  # otherwise the GPU objective must be within this of the oracle minimum (relative)
@@ -87,3 +88,23 @@ def check_same_result(a, b, label, keys=("scales", "codes", "objective", "pooled
         x, y = x.reshape(x.shape[0], -1).view(np.uint8), y.reshape(y.shape[0], -1).view(np.uint8)
         bad = np.nonzero(np.any((x != y).reshape(x.shape[0], -1), axis=1))[0]
         assert bad.size == 0, f"{label}: {k} differs on {bad.size} groups, e.g. {bad[:5]}"
+
+
+def spec_groups(qmin, qmax, G, E, n, seed):
+    """Seeded groups of G weights (bf16-valued normal weights with 2% outliers x8, a few tiny and
+    all-zero groups, constructed exact ties) and per-group lognormal diagonals."""
+    rng = np.random.default_rng(seed)
+    w = W.round_bf16((rng.normal(0, 0.02, (n, G)) * np.where(rng.random((n, G)) < 0.02, 8.0, 1.0))
+                     .astype(np.float32))
+    w[1] = 0.0
+    w[2] = (rng.uniform(-1, 1, G) * 1e-5).astype(np.float32)
+    # symmetric +-c n pairs: zero error at s = c and c/2 (and, for wide ranges, smaller powers)
+    c = 2.0 ** -7
+    m = rng.integers(1, min(qmax, 3) + 1, G // 2) if qmax >= 1 else np.ones(G // 2)
+    pair = np.zeros(G, np.float32)
+    pair[: 2 * (G // 2)] = np.concatenate([m * c, -m * c]).astype(np.float32)
+    w[3] = pair
+    d = rng.lognormal(0, 1, (n, E, G)).astype(np.float32)
+    if E > 1:
+        d[3, 1] = d[3, 0]
+    return w, d

@@ -75,13 +75,17 @@ def _spec(**kw):
              wsb=1 << 20)
     a.update(kw)
     return lib.cq_quantize_groups_spec(a["w"], a["d"], a["G"], a["qmin"], a["qmax"], a["d_period"], a["E"], a["n"],
-                                       a["method"], a["scales"], None, None, None, None, None, a["ws"], a["wsb"],
-                                       None)
+                                       a["method"], a["scales"], None, None, None, a.get("ps"), None, a["ws"],
+                                       a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(G=0), -1), (dict(G=257), -1), (dict(qmin=1), -1), (dict(qmax=-1), -1), (dict(qmin=0, qmax=0), -1),
-    (dict(qmin=-129), -1), (dict(qmax=128), -1), (dict(method=3), -1), (dict(method=1), -4), (dict(method=2), -4),
+    (dict(qmin=-129), -1), (dict(qmax=128), -1), (dict(method=3), -1), (dict(method=2), -4),
+    # the candidate solver takes at most 8 codes on each side of zero and groups of at most 128
+    (dict(method=1, qmin=-9), -4), (dict(method=1, qmax=9), -4), (dict(method=1, G=129), -4),
+    (dict(method=1, qmin=-16, qmax=15, G=256), -4), (dict(method=1, ps=FAKE), -4),
+    (dict(method=1, ws=None), -2), (dict(method=1, w=FAKE + 2), -1),
     (dict(w=FAKE + 2), -1), (dict(E=33), -1), (dict(scales=None), -1), (dict(ws=None), -2),
     (dict(ws=FAKE, wsb=16), -2), (dict(n=0, w=None, d=None, scales=None), 0),
     # the pages' quantizer through the spec entry takes cq_quantize_groups' checks (16-byte alignment)

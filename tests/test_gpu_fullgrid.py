@@ -10,7 +10,7 @@ import torch
 import oracle
 import post_weight_quantization_group_amd as cq
 import workloads as W
-from parity import bits_np, check_minimax, check_pooled, check_same_result, dev, say, threads
+from parity import bits_np, check_minimax, check_pooled, check_same_result, dev, say, spec_groups, threads
 
 pytestmark = pytest.mark.gpu
 
@@ -47,30 +47,10 @@ SPECS = [(-4, 3, 64, 4), (-2, 1, 32, 3), (-128, 127, 128, 4), (0, 15, 128, 2), (
          (-8, 7, 4, 2), (-8, 7, 100, 5), (-4, 3, 200, 1)]
 
 
-def _spec_groups(qmin, qmax, G, E, n, seed):
-    """Seeded groups of G weights (bf16-valued normal weights with 2% outliers x8, a few tiny and
-    all-zero groups, constructed exact ties) and per-group lognormal diagonals."""
-    rng = np.random.default_rng(seed)
-    w = W.round_bf16((rng.normal(0, 0.02, (n, G)) * np.where(rng.random((n, G)) < 0.02, 8.0, 1.0))
-                     .astype(np.float32))
-    w[1] = 0.0
-    w[2] = (rng.uniform(-1, 1, G) * 1e-5).astype(np.float32)
-    # symmetric +-c n pairs: zero error at s = c and c/2 (and, for wide ranges, smaller powers)
-    c = 2.0 ** -7
-    m = rng.integers(1, min(qmax, 3) + 1, G // 2) if qmax >= 1 else np.ones(G // 2)
-    pair = np.zeros(G, np.float32)
-    pair[: 2 * (G // 2)] = np.concatenate([m * c, -m * c]).astype(np.float32)
-    w[3] = pair
-    d = rng.lognormal(0, 1, (n, E, G)).astype(np.float32)
-    if E > 1:
-        d[3, 1] = d[3, 0]
-    return w, d
-
-
 @pytest.mark.parametrize("qmin,qmax,G,E", SPECS, ids=[f"q{a}..{b}_G{g}_E{e}" for a, b, g, e in SPECS])
 def test_quantizer_spec_against_oracle(qmin, qmax, G, E):
     n = 48
-    w, d = _spec_groups(qmin, qmax, G, E, n, seed=1000 + G + qmax)
+    w, d = spec_groups(qmin, qmax, G, E, n, seed=1000 + G + qmax)
     say(f"quantizer [{qmin}, {qmax}], G={G}, E={E}: {n} groups")
     r = _run(w, d, n, qmin=qmin, qmax=qmax)
     sol = oracle.solve(w, d, n, n_threads=threads(), qmin=qmin, qmax=qmax)
@@ -125,7 +105,7 @@ def test_sliced_small_batches_equal_one_workgroup_per_group(qmin, qmax, G, E):
     all-zero group (zero rule), constructed ties, a non-finite input and a group outside the
     binary32 screen's range (binary64 sweep)."""
     n = 1040
-    w, d = _spec_groups(qmin, qmax, G, E, n, seed=2000 + E + G)
+    w, d = spec_groups(qmin, qmax, G, E, n, seed=2000 + E + G)
     w[4, 3] = np.nan
     d[5, 0, 0] = 2.0 ** 101
     say(f"slices vs one workgroup per group: [{qmin}, {qmax}], G={G}, E={E}, {n} groups")
@@ -182,7 +162,7 @@ def test_seeded_random_quantizers_against_oracle(qmin, qmax, G, E):
     and two one-sided code ranges, 24 groups each of the same structure: minimax and pooled against
     the oracle run with the same quantizer."""
     n = 24
-    w, d = _spec_groups(qmin, qmax, G, E, n, seed=7000 + 31 * G + qmax - qmin)
+    w, d = spec_groups(qmin, qmax, G, E, n, seed=7000 + 31 * G + qmax - qmin)
     r = _run(w, d, n, qmin=qmin, qmax=qmax)
     sol = oracle.solve(w, d, n, n_threads=threads(), qmin=qmin, qmax=qmax)
     same, near = check_minimax(w, d, n, r, sol, qmin=qmin, qmax=qmax)
@@ -247,7 +227,7 @@ def test_baselines_for_other_quantizers(qmin, qmax, G, E):
     bit for bit against the oracle, the same scales and codes without the objective; the pooled
     baseline equals the full grid's pooled policy."""
     n = 3 * (256 // E) + 5  # a ragged last workgroup
-    w, d = _spec_groups(qmin, qmax, G, E, n, seed=9000 + G + qmax)
+    w, d = spec_groups(qmin, qmax, G, E, n, seed=9000 + G + qmax)
     period = n - 2
     d = d[:period]
     ab = cq.baseline_scales(dev(w), dev(d), period, "absmax", qmin=qmin, qmax=qmax)
@@ -273,7 +253,7 @@ def test_proxy_for_other_quantizers(qmin, qmax, G, E):
     per-group values, module means and macro against the oracle within the proxy tolerance; a
     ragged last workgroup and an empty module (NaN on both sides)."""
     n = 16 * 5 + 9
-    w, d = _spec_groups(qmin, qmax, G, E, n, seed=9500 + G + qmax)
+    w, d = spec_groups(qmin, qmax, G, E, n, seed=9500 + G + qmax)
     r = _run(w, d, n, qmin=qmin, qmax=qmax)
     rng = np.random.default_rng(G + E)
     bits = np.stack([bits_np(r["scales"]), bits_np(r["pooled_scales"]),
