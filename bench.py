@@ -207,7 +207,8 @@ def measure_aux() -> dict:
                               "proxy_ms": ms_p, "compare_ms": ms_h}
     # other quantizers (README, "Use the solver": a code range and a group of any length): the
     # full grid on 28,672 seeded groups each, E = 4, every scale of every weight; flops count
-    # 31,743 x G x (2E + 4) per group as for the pages' quantizer
+    # 31,743 x G x (2E + 4) per group as for the pages' quantizer; the candidate solver beside it
+    # where it takes the quantizer
     rng = np.random.default_rng(2024)
     sq = {}
     for qmin, qmax, G in ((-4, 3, 64), (-2, 1, 32), (0, 15, 128), (-128, 127, 256)):
@@ -223,7 +224,45 @@ def measure_aux() -> dict:
                                        "frac_fp32_peak": fl / (ms / 1e3) / (PEAK_FP32_TFLOPS * 1e12),
                                        "fp64_sweep_groups": int(torch.count_nonzero(r["flags"] & cq.FLAG_FP64_SWEEP).item()),
                                        "near_tie_groups": int(torch.count_nonzero(r["flags"] & cq.FLAG_NEAR_TIE).item())}
+        if G <= 128 and qmin >= -8 and qmax <= 8:
+            # the candidate solver on the same groups (its tied groups decided by the full grid)
+            rc, msc = _timed(lambda: cq.quantize_groups(wt, dt, n // 8, method="candidate", qmin=qmin, qmax=qmax),
+                             reps=3)
+            e = sq[f"q{qmin}..{qmax}_G{G}"]
+            e["candidate_ms"] = msc
+            e["candidate_groups_per_s"] = n / (msc / 1e3)
+            e["candidate_fallback_groups"] = int(torch.count_nonzero(rc["flags"] & cq.FLAG_FALLBACK).item())
+            e["candidate_vs_full_grid_scale_mismatches"] = int(torch.count_nonzero(rc["scales"] != r["scales"]).item())
     res["spec_quantizers_full_grid"] = sq
+    return res
+
+
+def issue_ceiling() -> dict:
+    """The vector units' fp32 fma ceiling as measured: the library's issue probe (eight independent
+    fma chains per thread, 2,048 workgroups of 256 threads) in both encodings, each launch timed by
+    HIP events, and the shader clock the chip held during it (shader cycles over wall-clock ticks)."""
+    import torch
+    import post_weight_quantization_group_amd as cq
+    blocks, iters = 256 * 8, 200000
+    res = {"what": "fp32 fma issue probe (cq_probe_valu_fma): 2,048 workgroups x 256 threads x 8 independent "
+                   "chains x 200,000 fmas; v_fma_f32 (three-operand encoding, vector operands), v_fmac_f32 "
+                   "(accumulate encoding, the form of the full grid's environment sums) and v_fma_f32 with a "
+                   "scalar operand"}
+    for mode, name in ((0, "v_fma_f32"), (1, "v_fmac_f32"), (2, "v_fma_f32_scalar_operands")):
+        cq.probe_valu_fma(1000, blocks, mode)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = cq.probe_valu_fma(iters, blocks, mode)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        clk = r["clocks"].cpu().numpy().astype(np.float64)
+        ghz = clk[:, 0].sum() / clk[:, 1].sum() * r["wall_clock_hz"] / 1e9
+        wave_instr = float(blocks) * 4 * 8 * iters
+        tflops = wave_instr * 64 * 2 / (ms / 1e3) / 1e12
+        res[name] = {"ms": ms, "fp32_TFLOP_per_s": tflops, "frac_of_published_peak": tflops / PEAK_FP32_TFLOPS,
+                     "clock_ghz": ghz, "issue_per_cu_clock": wave_instr / (256 * (ms / 1e3) * ghz * 1e9)}
     return res
 
 
@@ -560,6 +599,9 @@ def main():
     }
     if fg:
         line["roofline"]["counters"] = {k2: v for k2, v in fg.items() if k2 != "traffic_bytes_per_launch"}
+    ceil = issue_ceiling()
+    ceil["full_grid_frac_of_measured"] = achieved / ceil["v_fmac_f32"]["fp32_TFLOP_per_s"]
+    line["roofline"]["measured_ceiling"] = ceil
     if not args.no_bounded:
         ms_b, bnd_ms, cand_b, wall_b = timed_steps(cq.BOUNDED, args.steps, args.warmup)
         line["bounded_path"] = {

@@ -387,6 +387,27 @@ int32_t cq_heldout_compare(const double *pa, const double *pb, int64_t n_groups,
                            int64_t *counts, double *effect, double *boot, double *ci,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement aid, not part of the method: the fp32 fma issue rate the vector units reach, the
+ * ceiling against which the full-grid search's issue rate (and its fraction of the published
+ * 157.3 TFLOP/s fp32 peak: 256 CUs x 128 fma lanes x 2 flop x 2.4 GHz) is read.
+ *   iters          >= 1: fmas per chain; each thread of `blocks` workgroups of 256 threads runs
+ *                  8 independent chains, so the launch issues blocks x 4 waves x 8 x iters
+ *                  fma wave instructions (2 flop per lane each).
+ *   mode           0: the chains as x = fma(x, c, y) with c, y in vector registers (the
+ *                  three-operand encoding, v_fma_f32); 1: as x = fma(y, c, x) (the accumulate
+ *                  encoding, v_fmac_f32, which the full-grid search's environment sums use);
+ *                  2: as x = fma(x, a, b) with a, b scalar kernel arguments (v_fma_f32 with a
+ *                  scalar-register operand).  The forms issue at different rates.
+ *   out            device float [blocks * 256]: the chains' sums (kept so nothing is dead code).
+ *   clocks         device uint64 [2 * blocks]: per workgroup, the shader clock cycles and the
+ *                  constant-rate wall clock ticks between its thread 0's start and end.
+ *   wall_clock_hz  HOST double, out: the wall clock's rate (cycles / ticks x this = the clock).
+ * Returns CQ_EINVAL for iters < 1, blocks < 1, another mode or a null pointer.
+ */
+int32_t cq_probe_valu_fma(int32_t iters, int32_t blocks, int32_t mode, float *out, uint64_t *clocks,
+                          double *wall_clock_hz, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,7 @@ __all__ = [
     "pack_gptq_v1", "proxy_worst_env_wmse", "proxy_worst_env_wmse_multi", "solve_breakpoint_exact",
     "cq_heldout_workspace_size", "cq_heldout_compare", "heldout_compare", "cq_diagonals_workspace_size",
     "cq_environment_diagonals", "environment_diagonals", "cq_w4a16_matmul", "w4a16_matmul", "EXPORTED_SYMBOLS",
+    "cq_probe_valu_fma", "probe_valu_fma",
 ]
 
 GROUP = 128
@@ -50,7 +51,7 @@ EXPORTED_SYMBOLS = ("cq_abi_version", "cq_status_string", "cq_workspace_size", "
                     "cq_proxy_workspace_size",
                     "cq_proxy_worst_env_wmse", "cq_proxy_worst_env_wmse_multi", "cq_heldout_workspace_size",
                     "cq_heldout_compare", "cq_diagonals_workspace_size", "cq_environment_diagonals",
-                    "cq_w4a16_matmul")
+                    "cq_w4a16_matmul", "cq_probe_valu_fma")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -117,6 +118,8 @@ def load():
         lib.cq_heldout_workspace_size.argtypes = [I32, I32]
         lib.cq_heldout_compare.restype = I32
         lib.cq_heldout_compare.argtypes = [P, P, I64, P, I32, P, I32, ctypes.c_double, P, P, P, P, P, SZ, P]
+        lib.cq_probe_valu_fma.restype = I32
+        lib.cq_probe_valu_fma.argtypes = [I32, I32, I32, P, P, ctypes.POINTER(ctypes.c_double), P]
         _lib = lib
     return _lib
 
@@ -268,6 +271,25 @@ def w4a16_matmul(x, qweight, scales, stream=None):
     y = torch.empty((M, out), dtype=torch.float32, device=x.device)
     cq_w4a16_matmul(xb, qweight, scales, M, out, inp, y, stream)
     return y
+
+
+def cq_probe_valu_fma(iters, blocks, mode, out, clocks, stream=None) -> float:
+    """Runs the fp32 fma issue probe; returns the wall clock's rate in Hz."""
+    hz = ctypes.c_double(0.0)
+    _check(load().cq_probe_valu_fma(iters, blocks, mode, _p(out), _p(clocks), ctypes.byref(hz), _stream(stream)),
+           "cq_probe_valu_fma")
+    return hz.value
+
+
+def probe_valu_fma(iters: int, blocks: int, mode: int = 1, device="cuda", stream=None) -> dict:
+    """The issue probe on `blocks` workgroups (mode 0: v_fma_f32, 1: v_fmac_f32, 2: v_fma_f32
+    with a scalar operand): the sums,
+    per-workgroup (shader cycles, wall ticks) and the wall clock's rate.  The caller times the
+    launch."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    clocks = torch.empty((blocks, 2), dtype=torch.int64, device=device)
+    hz = cq_probe_valu_fma(iters, blocks, mode, out, clocks, stream)
+    return {"out": out, "clocks": clocks, "wall_clock_hz": hz}
 
 
 def cq_diagonals_workspace_size(E: int, T: int, inp: int) -> int:

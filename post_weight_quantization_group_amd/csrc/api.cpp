@@ -412,4 +412,14 @@ int32_t cq_heldout_compare(const double* pa, const double* pb, int64_t n_groups,
                                           counts, effect, boot, ci, mm, reps, rank, (hipStream_t)stream));
 }
 
+int32_t cq_probe_valu_fma(int32_t iters, int32_t blocks, int32_t mode, float* out, uint64_t* clocks,
+                          double* wall_clock_hz, void* stream) {
+    if (iters < 1 || blocks < 1 || (mode < 0 || mode > 2) || !out || !clocks || !wall_clock_hz) return CQ_EINVAL;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CQ_EHIP;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return CQ_EHIP;
+    *wall_clock_hz = 1e3 * (double)khz;
+    return hip_status(cqk::launch_fma_probe(iters, blocks, mode, out, clocks, (hipStream_t)stream));
+}
+
 }  // extern "C"

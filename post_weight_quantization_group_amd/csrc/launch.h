@@ -51,4 +51,8 @@ hipError_t launch_proxy(const float* w, const float* d, int64_t d_period, int E,
                         const uint16_t* scales, const int64_t* module_offsets, int n_modules,
                         double* module_mean, double* macro, double* per_group, hipStream_t st);
 
+// Vector-unit issue probe: `blocks` workgroups of 256 threads, each thread 8 independent chains of
+// `iters` fp32 fmas in the form `mode` selects (0: v_fma_f32, 1: v_fmac_f32, 2: v_fma_f32 with a scalar operand); out [blocks * 256] floats, clocks [2 * blocks] (shader cycles, wall ticks).
+hipError_t launch_fma_probe(int iters, int blocks, int mode, float* out, uint64_t* clocks, hipStream_t st);
+
 }  // namespace cqk

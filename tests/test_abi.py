@@ -222,3 +222,16 @@ def test_spec_baseline_and_proxy_reject_bad_arguments():
     assert p(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 1, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0, None) == -1  # modules
     assert p(FAKE, FAKE, 64, -4, 3, 1, 4, 10, 1, FAKE, FAKE, 1, FAKE, FAKE, None, None, 0, None) == -2  # workspace
     assert p(FAKE, FAKE, 64, -4, 3, 1, 33, 10, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 0, None) == -1  # E
+
+
+def test_probe_rejects_bad_arguments():
+    f = cq.load().cq_probe_valu_fma
+    import ctypes
+    hz = ctypes.c_double(0.0)
+    assert f(0, 8, 1, FAKE, FAKE, ctypes.byref(hz), None) == -1      # iters < 1
+    assert f(10, 0, 1, FAKE, FAKE, ctypes.byref(hz), None) == -1     # blocks < 1
+    assert f(10, 8, 3, FAKE, FAKE, ctypes.byref(hz), None) == -1     # mode
+    assert f(10, 8, -1, FAKE, FAKE, ctypes.byref(hz), None) == -1
+    assert f(10, 8, 1, None, FAKE, ctypes.byref(hz), None) == -1     # out
+    assert f(10, 8, 1, FAKE, None, ctypes.byref(hz), None) == -1     # clocks
+    assert f(10, 8, 1, FAKE, FAKE, None, None) == -1                 # wall_clock_hz
