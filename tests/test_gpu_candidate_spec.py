@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import post_weight_quantization_group_amd as cq
+import workloads as W
 from parity import bits_np, check_minimax, check_same_result, dev, say, spec_groups, threads
 
 pytestmark = pytest.mark.gpu
@@ -21,7 +22,7 @@ KEYS = ("scales", "codes", "objective")
 # (qmin, qmax, group length, environments): signed 3- and 2-bit codes, unsigned and one-sided
 # ranges, the widest accepted range, the pages' range on shorter groups, and E up to 16
 SPECS = [(-4, 3, 64, 4), (-2, 1, 32, 3), (0, 7, 128, 2), (-8, 8, 128, 4), (-8, 7, 100, 5), (-8, 7, 4, 2),
-         (-1, 1, 16, 1), (-3, 5, 128, 8), (0, 1, 77, 16), (-8, 0, 90, 2)]
+         (-1, 1, 16, 1), (-3, 5, 128, 8), (0, 1, 77, 16), (-8, 0, 90, 2), (-4, 3, 64, 20)]
 
 
 def _run(w, d, n, method, qmin, qmax):
@@ -72,6 +73,24 @@ def test_candidate_spec_many_fallbacks_take_the_list_loop():
     cs = {k: c[k][torch.from_numpy(sub).cuda()] for k in KEYS}
     same, near = check_minimax(w[sub], d[sub], sub.size, cs, sol, qmin=qmin, qmax=qmax)
     say(f"  fallbacks {int(fb.sum())}; oracle on 256 nonzero groups: bits equal {same}, near ties {near}")
+
+
+@pytest.mark.parametrize("qmin,qmax,G", [(-4, 3, 64), (-2, 1, 32)])
+def test_candidate_spec_equals_full_grid_at_matrix_size(qmin, qmax, G):
+    """28,672 seeded groups (the size of a config-1 matrix), bf16-valued N(0, 0.02) weights with 1%
+    outliers x8 and lognormal diagonals shared by every eighth group, E = 4: the candidate solver
+    and the full grid return the same scales, codes and binary64 objectives in every group."""
+    rng = np.random.default_rng(4000 + G)
+    n, E = 28672, 4
+    w = W.round_bf16((rng.normal(0, 0.02, (n, G)) * np.where(rng.random((n, G)) < 0.01, 8.0, 1.0))
+                     .astype(np.float32))
+    d = rng.lognormal(0, 1, (n // 8, E, G)).astype(np.float32)
+    c = cq.quantize_groups(dev(w), dev(d), n // 8, method="candidate", qmin=qmin, qmax=qmax)
+    f = cq.quantize_groups(dev(w), dev(d), n // 8, method="exhaustive", qmin=qmin, qmax=qmax)
+    torch.cuda.synchronize()
+    check_same_result(c, f, f"[{qmin}, {qmax}] G={G}, {n} groups", KEYS)
+    fb = int(torch.count_nonzero(c["flags"] & cq.FLAG_FALLBACK).item())
+    say(f"candidate [{qmin}, {qmax}] G={G}: {n} groups equal to the full grid, {fb} decided by its list mode")
 
 
 def test_solver_call_defaults_to_the_candidate_solver_where_it_applies():
