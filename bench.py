@@ -587,7 +587,9 @@ def main():
                      "flops_per_launch": flops_per_launch,
                      "flops_per_group": SCALES * flops_per_pattern(E),
                      "counting": "31,743 scales x 128 weights x (2E + 4) flop per group: a quotient multiply, "
-                                 "a residual fma (2), a square and E weighted fmas (2E)"},
+                                 "a residual fma (2), a square and E weighted fmas (2E); 'executed' gives the fp32 "
+                                 "work the counters show executed (terms whose code is proven constant over a "
+                                 "chunk skip the quotient)"},
         "full_grid_groups_per_s": groups_per_launch / (full_ms / 1e3),
         "candidate_launch_ms": cand_ms,
         "candidate_vs_full_grid_scale_mismatches": mism,
@@ -599,6 +601,13 @@ def main():
     }
     if fg:
         line["roofline"]["counters"] = {k2: v for k2, v in fg.items() if k2 != "traffic_bytes_per_launch"}
+        if "fp32_flop_executed_per_launch" in fg:
+            # the fp32 work the kernel executes (counters), over the same launch time: runs of weights
+            # whose code is proven constant over a chunk take it from the row, without the quotient
+            ex = fg["fp32_flop_executed_per_launch"] / (full_ms / 1e3) / 1e12
+            line["roofline"]["executed"] = {"fp32_flop_per_launch": fg["fp32_flop_executed_per_launch"],
+                                             "of_algorithmic": fg["fp32_flop_executed_per_launch"] / flops_per_launch,
+                                             "achieved": ex, "frac": ex / PEAK_FP32_TFLOPS}
     ceil = issue_ceiling()
     ceil["full_grid_frac_of_measured"] = achieved / ceil["v_fmac_f32"]["fp32_TFLOP_per_s"]
     line["roofline"]["measured_ceiling"] = ceil

@@ -27,7 +27,12 @@
 // chunk that can clip, a weight whose |w'| is at least (range end - 1/4) times
 // the chunk's largest scale has the range end as its code at every scale of the
 // chunk: its terms are formed from that code, without the quotient (the vector
-// path keeps its rows in clip-ratio order, so these weights are one run).
+// path keeps its rows in clip-ratio order, so these weights are one run).  In any
+// chunk, a weight with |w'| at most (1 - 2^-20)/2 times the chunk's smallest scale
+// has code 0 at every scale of the chunk (|x~| < 1/2); these weights end the row
+// order, and their terms too are formed from their code, 0, without the quotient.
+// Every term keeps the value the quotient path gives it, and its residual, square
+// and E weighted fmas are still formed at every scale.
 // Patterns are rotated over the lanes from chunk to chunk so that scales a power
 // of two apart (which tie exactly when one outlier alone carries a code) land in
 // different lanes.  Each lane keeps its best three (value, pattern) keys per
@@ -148,8 +153,11 @@ __device__ __forceinline__ float in_vgpr(float x) {
 // How a run of weights forms its codes in a chunk: the quotient, rounded, then clipped (CLIP); the
 // same without the clip, for weights that cannot leave the range at any scale of the chunk (FREE);
 // or, for weights that clip at every scale of the chunk, the range end on their side, kept in the
-// row (FIXED).  Every mode gives each term exactly the value the clipped path gives it.
-enum TermMode { FREE = 0, CLIP = 1, FIXED = 2 };
+// row (FIXED); or, for weights whose code is 0 at every scale of the chunk, that 0 (ZERO, from a
+// register the compiler cannot see through, so that the residual, the square and the E weighted
+// sums are still formed at every scale).  Every mode gives each term exactly the value the clipped
+// path gives it.
+enum TermMode { FREE = 0, CLIP = 1, FIXED = 2, ZERO = 3 };
 
 // One run of rows [0, n): every lane runs the n weights against its NS scales, the per-environment
 // sums in registers.  The weight and its E diagonals are LDS broadcasts shared by the NS scales.
@@ -167,11 +175,12 @@ __device__ __forceinline__ void chunk_terms(const float* __restrict__ rows, int 
         float di[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) di[e] = row[doff_for(E) + e];
-        const float qi = MODE == FIXED ? row[1] : 0.0f;  // the code this row keeps over the chunk
+        // the code this row keeps over the chunk
+        const float qi = MODE == FIXED ? row[1] : (MODE == ZERO ? in_vgpr(0.0f) : 0.0f);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             float r = qi;
-            if (MODE != FIXED) {
+            if (MODE != FIXED && MODE != ZERO) {
                 r = __builtin_rintf(wi * inv[t]);
                 if (MODE == CLIP) r = __builtin_amdgcn_fmed3f(r, qlo, qhi);
             }
@@ -224,6 +233,24 @@ __device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, i
 // would save one instruction on about 8% of the terms but pushes the kernel past the registers of
 // five workgroups per CU.)  The sums meet the terms in row order whatever the runs.  The
 // matrix-core rows hold no code: that path clips the whole chunk.
+// The first row of the suffix of rows whose code is 0 at every scale of the chunk.  With s0 the
+// chunk's smallest scale, |w'| <= s0 (1 - 2^-20) / 2 gives |x~| < 1/2 at every scale of the chunk
+// (x~ within 2.0001 u |x| of w'/s, the threshold itself one rounding), so the code is 0, which lies
+// in every code range.  The rows are in clip-ratio order, not in |w| order, so the suffix starts
+// after the last row that does not qualify.
+__device__ __forceinline__ int zero_run_start(const float* __restrict__ rows, int RS, int G, float s0) {
+    const int lane = threadIdx.x & 63;
+    const float tz = 0.5f * s0 * (1.0f - 0x1p-20f);
+    int last = -1;
+    for (int k0 = 0; k0 < G; k0 += 64) {
+        const int k = k0 + lane;
+        const float x = k < G ? rows[k * RS] : 0.0f;
+        const uint64_t m = __ballot(k < G && !(fabsf(x) <= tz));
+        if (m != 0) last = k0 + 63 - (int)__builtin_clzll(m);
+    }
+    return last + 1;
+}
+
 __device__ __forceinline__ int fixed_run_end(const float* __restrict__ rows, int RS, int G, int qmin, int qmax,
                                              float s1) {
     const int lane = threadIdx.x & 63;
@@ -491,12 +518,17 @@ __device__ void screen_keys(const FullArgs& a, Smem<E>& sm, float pk, float cmax
             for (int t = 0; t < NS; ++t)
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+            // rows [zs, G) have code 0 at every scale of the chunk (after any FIXED prefix: those
+            // rows clip, so zs >= end)
+            const int zs = zero_run_start(sm.rows, row_for(E), G, s0);
+            const int mid = zs > end ? zs : end;
             if (!clips) {
-                chunk_terms<E, NS, FREE>(sm.rows, G, nsv, inv, qlo, qhi, acc);
+                if (mid > 0) chunk_terms<E, NS, FREE>(sm.rows, mid, nsv, inv, qlo, qhi, acc);
             } else {
                 if (end > 0) chunk_terms<E, NS, FIXED>(sm.rows, end, nsv, inv, qlo, qhi, acc);
-                if (end < G) chunk_terms<E, NS, CLIP>(sm.rows + end * row_for(E), G - end, nsv, inv, qlo, qhi, acc);
+                if (mid > end) chunk_terms<E, NS, CLIP>(sm.rows + end * row_for(E), mid - end, nsv, inv, qlo, qhi, acc);
             }
+            if (mid < G) chunk_terms<E, NS, ZERO>(sm.rows + mid * row_for(E), G - mid, nsv, inv, qlo, qhi, acc);
         }
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
