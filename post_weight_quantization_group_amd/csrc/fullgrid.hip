@@ -233,13 +233,21 @@ __device__ __forceinline__ void chunk_terms_mf(const float* __restrict__ rows, i
 // would save one instruction on about 8% of the terms but pushes the kernel past the registers of
 // five workgroups per CU.)  The sums meet the terms in row order whatever the runs.  The
 // matrix-core rows hold no code: that path clips the whole chunk.
+// The lane index through a vector move of its own, so that addresses formed from it are formed
+// where they are used, not held in registers across the chunk loop.
+__device__ __forceinline__ int fresh_lane() {
+    int r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
 // The first row of the suffix of rows whose code is 0 at every scale of the chunk.  With s0 the
 // chunk's smallest scale, |w'| <= s0 (1 - 2^-20) / 2 gives |x~| < 1/2 at every scale of the chunk
 // (x~ within 2.0001 u |x| of w'/s, the threshold itself one rounding), so the code is 0, which lies
 // in every code range.  The rows are in clip-ratio order, not in |w| order, so the suffix starts
 // after the last row that does not qualify.
 __device__ __forceinline__ int zero_run_start(const float* __restrict__ rows, int RS, int G, float s0) {
-    const int lane = threadIdx.x & 63;
+    const int lane = fresh_lane();
     const float tz = 0.5f * s0 * (1.0f - 0x1p-20f);
     int last = -1;
     for (int k0 = 0; k0 < G; k0 += 64) {
@@ -253,9 +261,11 @@ __device__ __forceinline__ int zero_run_start(const float* __restrict__ rows, in
 
 __device__ __forceinline__ int fixed_run_end(const float* __restrict__ rows, int RS, int G, int qmin, int qmax,
                                              float s1) {
-    const int lane = threadIdx.x & 63;
-    const float tA = qmin < 0 ? ((float)qmin + 0.25f) * s1 * (1.0f + 0x1p-20f) : -__builtin_inff();
-    const float tF = qmax > 0 ? ((float)qmax - 0.25f) * s1 * (1.0f + 0x1p-20f) : __builtin_inff();
+    const int lane = fresh_lane();
+    // the range ends through a vector move of its own: formed here, per chunk, not held in
+    // registers across the chunk loop
+    const float tA = qmin < 0 ? (in_vgpr((float)qmin) + 0.25f) * s1 * (1.0f + 0x1p-20f) : -__builtin_inff();
+    const float tF = qmax > 0 ? (in_vgpr((float)qmax) - 0.25f) * s1 * (1.0f + 0x1p-20f) : __builtin_inff();
     for (int k0 = 0; k0 < G; k0 += 64) {
         const int k = k0 + lane;
         const float x = k < G ? rows[k * RS] : 0.0f;
